@@ -1,1 +1,13 @@
-"""MI355X-native DSA sparse-attention path (see binding module)."""
+"""MI355X-native DSA sparse-attention path: lightning indexer, top-k, sparse MLA.
+
+The compute lives in libdsa.so (HIP kernels for gfx950 behind a C ABI, see
+include/dsa.h); this package is its thin Python binding.  Importing the
+package does not load the library; the first call does, and raises if the
+library has not been built.
+"""
+from ._binding import (  # noqa: F401
+    DSA_BF16, DSA_F32, DSA_FP8_E4M3FN, DSA_MAX_SHARED_LAYERS, DSA_TOPK_MAX, DsaError, EXPORTS, LIB_PATH,
+    Layout, dsa_abi_version, dsa_index_scores, dsa_topk, dsa_topk_workspace_size, load_library,
+    mla_workspace, sparse_mla_decode, sparse_mla_decode_shared, sparse_mla_prefill,
+    sparse_mla_workspace_size,
+)

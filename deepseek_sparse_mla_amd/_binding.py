@@ -1,0 +1,265 @@
+"""ctypes binding of libdsa: argument marshalling only.
+
+Every function here has the name of the C entry point it calls, checks the
+torch tensors it is given (device, dtype, contiguity, shape), passes their
+data pointers and torch's current HIP stream, and raises on a non-OK status.
+All arithmetic happens in the HIP kernels behind the C ABI.  If libdsa.so is
+missing the first call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
+DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
+DSA_TOPK_MAX = 2048
+DSA_MAX_SHARED_LAYERS = 8
+
+EXPORTS = ("dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "sparse_mla_workspace_size",
+           "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "dsa_last_error",
+           "dsa_abi_version")
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("libdsa status %d: %s" % (status, message))
+        self.status = status
+
+
+class dsa_layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("total_q", ctypes.c_int32), ("max_ctx", ctypes.c_int64),
+                ("kv_indptr", ctypes.c_void_p), ("q_indptr", ctypes.c_void_p)]
+
+
+class dsa_mla_layer(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("kv_scale", ctypes.c_float),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("libdsa.so not found at %s: build it with "
+                               "`python -m deepseek_sparse_mla_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        P, I, L, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        LP = ctypes.POINTER(dsa_layout)
+        lib.dsa_index_scores.argtypes = [LP, I, I, I, P, P, P, I, P, L, P, L, P, L, P]
+        lib.dsa_topk_workspace_size.argtypes = [LP, L, I]
+        lib.dsa_topk_workspace_size.restype = S
+        lib.dsa_topk.argtypes = [LP, P, L, I, P, P, S, P]
+        lib.sparse_mla_workspace_size.argtypes = [LP, I, I, I, I, I]
+        lib.sparse_mla_workspace_size.restype = S
+        mla = [LP, I, I, I, F, I, P, I, P, F, P, I, I, P, P, P, S, P]
+        lib.sparse_mla_decode.argtypes = mla
+        lib.sparse_mla_prefill.argtypes = mla
+        lib.sparse_mla_decode_shared.argtypes = [LP, I, I, I, F, I, I, I, I,
+                                                 ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
+        for f in (lib.dsa_index_scores, lib.dsa_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
+                  lib.sparse_mla_decode_shared, lib.dsa_abi_version):
+            f.restype = I
+        lib.dsa_last_error.restype = ctypes.c_char_p
+        lib.dsa_last_error.argtypes = []
+        lib.dsa_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def _check(lib, st: int):
+    if st != DSA_OK:
+        raise DsaError(st, lib.dsa_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_FP8_E4M3FN
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, contiguous=True):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if contiguous and not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class Layout:
+    """Ragged layout (mirrors dsa_layout); tensors stay referenced while the object lives."""
+
+    def __init__(self, kv_indptr: torch.Tensor, q_indptr: Optional[torch.Tensor], total_q: int,
+                 max_ctx: int):
+        _dev(kv_indptr, "kv_indptr", torch.int64)
+        _dev(q_indptr, "q_indptr", torch.int32)
+        self.kv_indptr = kv_indptr
+        self.q_indptr = q_indptr
+        self.batch = kv_indptr.numel() - 1
+        self.total_q = int(total_q)
+        self.max_ctx = int(max_ctx)
+        self.c = dsa_layout(self.batch, self.total_q, self.max_ctx, kv_indptr.data_ptr(),
+                            q_indptr.data_ptr() if q_indptr is not None else None)
+
+    @staticmethod
+    def of_case(case) -> "Layout":
+        return Layout(case.kv_indptr, case.q_indptr, case.T, case.max_ctx)
+
+
+def dsa_index_scores(layout: Layout, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor,
+                     k_scale: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
+                     scores: Optional[torch.Tensor] = None, ld: Optional[int] = None,
+                     k_row_stride: Optional[int] = None, k_scale_stride: int = 1,
+                     k_dtype: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Indexer scores [T, ld] fp32.  q: [T, H_I, D_I]; k: [rows, D_I] (or a raw uint8 byte
+    buffer with k_row_stride bytes per row and k_dtype given)."""
+    lib = load_library()
+    T, H_I, D_I = q.shape
+    kd = _dt(k) if k_dtype is None else k_dtype
+    if k_row_stride is None:
+        k_row_stride = k.shape[-1] * k.element_size()
+    if ld is None:
+        ld = scores.shape[1] if scores is not None else layout.max_ctx
+    if scores is None:
+        scores = torch.empty((T, ld), dtype=torch.float32, device=q.device)
+    _dev(scores, "scores", torch.float32)
+    st = lib.dsa_index_scores(ctypes.byref(layout.c), H_I, D_I, _dt(q), _dev(q, "q"),
+                              _dev(q_scale, "q_scale", torch.float32), _dev(w, "w", torch.float32),
+                              kd, _dev(k, "k", contiguous=False), int(k_row_stride),
+                              _dev(k_scale, "k_scale", torch.float32, contiguous=False),
+                              int(k_scale_stride), scores.data_ptr(), int(ld), _stream(stream))
+    _check(lib, st)
+    return scores
+
+
+def dsa_topk_workspace_size(layout: Layout, ld: int, k: int) -> int:
+    return int(load_library().dsa_topk_workspace_size(ctypes.byref(layout.c), int(ld), int(k)))
+
+
+def dsa_topk(layout: Layout, scores: torch.Tensor, k: int, indices: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Top-k positions int32 [T, k] (score desc, position asc; -1 padding)."""
+    lib = load_library()
+    T, ld = scores.shape
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    ws_need = dsa_topk_workspace_size(layout, ld, k)
+    if ws_need and workspace is None:
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=scores.device)
+    st = lib.dsa_topk(ctypes.byref(layout.c), _dev(scores, "scores", torch.float32), int(ld), int(k),
+                      _dev(indices, "indices", torch.int32), _dev(workspace, "workspace"),
+                      workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(lib, st)
+    return indices
+
+
+def sparse_mla_workspace_size(layout: Layout, H: int, D_c: int, D_r: int, k: int, n_layers: int = 1) -> int:
+    return int(load_library().sparse_mla_workspace_size(ctypes.byref(layout.c), H, D_c, D_r, k, n_layers))
+
+
+def mla_workspace(layout: Layout, H: int, D_c: int, D_r: int, k: int, n_layers: int = 1,
+                  device="cuda") -> Optional[torch.Tensor]:
+    """A zero-filled workspace of the size the library asks for (None if it needs none)."""
+    n = sparse_mla_workspace_size(layout, H, D_c, D_r, k, n_layers)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _mla(fn_name, layout: Layout, q, kv, indices, sm_scale, D_c, kv_scale=1.0, out=None, lse=None,
+         out_dtype=None, workspace=None, kv_dtype=None, stream=None):
+    lib = load_library()
+    T, H, Dqk = q.shape
+    k = indices.shape[1]
+    if out_dtype is None:
+        out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((T, H, D_c), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        workspace = mla_workspace(layout, H, D_c, Dqk - D_c, k, 1, q.device)
+    kd = _dt(kv) if kv_dtype is None else kv_dtype
+    st = getattr(lib, fn_name)(ctypes.byref(layout.c), H, D_c, Dqk - D_c, float(sm_scale), _dt(q),
+                               _dev(q, "q"), kd, _dev(kv, "kv"), float(kv_scale),
+                               _dev(indices, "indices", torch.int32), k, _dt(out), _dev(out, "out"),
+                               _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
+                               workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(lib, st)
+    return out
+
+
+def sparse_mla_decode(layout: Layout, q, kv, indices, sm_scale, D_c, kv_scale=1.0, out=None, lse=None,
+                      out_dtype=None, workspace=None, stream=None) -> torch.Tensor:
+    """Sparse MLA output [T, H, D_c]; q [T, H, D_c+D_r]; kv [rows, D_c+D_r]."""
+    return _mla("sparse_mla_decode", layout, q, kv, indices, sm_scale, D_c, kv_scale, out, lse,
+                out_dtype, workspace, stream=stream)
+
+
+def sparse_mla_prefill(layout: Layout, q, kv, indices, sm_scale, D_c, kv_scale=1.0, out=None, lse=None,
+                       out_dtype=None, workspace=None, stream=None) -> torch.Tensor:
+    return _mla("sparse_mla_prefill", layout, q, kv, indices, sm_scale, D_c, kv_scale, out, lse,
+                out_dtype, workspace, stream=stream)
+
+
+def sparse_mla_decode_shared(layout: Layout, qs: Sequence[torch.Tensor], kvs: Sequence[torch.Tensor],
+                             kv_scales: Sequence[float], indices: torch.Tensor, sm_scale: float, D_c: int,
+                             outs: Optional[List[torch.Tensor]] = None,
+                             lses: Optional[List[Optional[torch.Tensor]]] = None, out_dtype=None,
+                             workspace=None, stream=None) -> List[torch.Tensor]:
+    """Several layers' sparse MLA over one index set, one launch."""
+    lib = load_library()
+    nl = len(qs)
+    if not (len(kvs) == nl == len(kv_scales)):
+        raise ValueError("qs, kvs and kv_scales must have one entry per layer")
+    T, H, Dqk = qs[0].shape
+    k = indices.shape[1]
+    if out_dtype is None:
+        out_dtype = torch.float32 if qs[0].dtype == torch.float32 else torch.bfloat16
+    if outs is None:
+        outs = [torch.empty((T, H, D_c), dtype=out_dtype, device=qs[0].device) for _ in range(nl)]
+    if lses is None:
+        lses = [None] * nl
+    arr = (dsa_mla_layer * max(nl, 1))()
+    for l in range(nl):
+        if qs[l].shape != qs[0].shape or kvs[l].dtype != kvs[0].dtype or qs[l].dtype != qs[0].dtype:
+            raise ValueError("every layer must have the same shapes and dtypes")
+        arr[l] = dsa_mla_layer(_dev(qs[l], "q"), _dev(kvs[l], "kv"), float(kv_scales[l]),
+                               _dev(outs[l], "out"), _dev(lses[l], "lse", torch.float32))
+    if workspace is None:
+        workspace = mla_workspace(layout, H, D_c, Dqk - D_c, k, nl, qs[0].device)
+    st = lib.sparse_mla_decode_shared(ctypes.byref(layout.c), H, D_c, Dqk - D_c, float(sm_scale),
+                                      _dt(qs[0]), _dt(kvs[0]), _dt(outs[0]), nl, arr,
+                                      _dev(indices, "indices", torch.int32), k,
+                                      _dev(workspace, "workspace"),
+                                      workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(lib, st)
+    return outs
+
+
+def dsa_abi_version() -> int:
+    return int(load_library().dsa_abi_version())

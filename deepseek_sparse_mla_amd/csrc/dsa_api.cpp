@@ -1,0 +1,343 @@
+// dsa_api.cpp -- the C ABI of libdsa: host-side argument checks, kernel choice, launch.
+//
+// Every entry point validates all of its arguments before touching HIP; a failed check
+// returns a negative dsa_status with a thread-local message and launches nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dsa_status fail(dsa_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+dsa_status ok()
+{
+    g_err.clear();
+    return DSA_OK;
+}
+
+dsa_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int elem_size(int dt)
+{
+    return dt == DSA_F32 ? 4 : dt == DSA_BF16 ? 2 : dt == DSA_FP8_E4M3FN ? 1 : 0;
+}
+
+bool aligned(const void *p, size_t a)
+{
+    return ((uintptr_t)p % a) == 0;
+}
+
+// "generic" forces the generic kernels (A/B checks); anything else picks the tuned ones.
+bool force_generic()
+{
+    const char *v = getenv("DSA_KERNEL_VARIANT");
+    return v && strcmp(v, "generic") == 0;
+}
+
+dsa_status check_layout(const dsa_layout *L)
+{
+    if (!L)
+        return fail(DSA_ERR_INVALID_ARG, "layout is NULL");
+    if (L->batch < 1)
+        return fail(DSA_ERR_INVALID_ARG, "layout.batch must be >= 1 (got %d)", L->batch);
+    if (L->total_q < 0)
+        return fail(DSA_ERR_INVALID_ARG, "layout.total_q must be >= 0 (got %d)", L->total_q);
+    if (L->max_ctx < 1)
+        return fail(DSA_ERR_INVALID_ARG, "layout.max_ctx must be >= 1 (got %lld)", (long long)L->max_ctx);
+    if (!L->kv_indptr)
+        return fail(DSA_ERR_INVALID_ARG, "layout.kv_indptr is NULL");
+    if (!L->q_indptr && L->total_q != L->batch)
+        return fail(DSA_ERR_INVALID_ARG,
+                    "layout.q_indptr is NULL (one query per sequence) but total_q %d != batch %d",
+                    L->total_q, L->batch);
+    if (L->max_ctx > (int64_t)INT32_MAX)
+        return fail(DSA_ERR_UNSUPPORTED, "layout.max_ctx %lld exceeds int32 positions",
+                    (long long)L->max_ctx);
+    return DSA_OK;
+}
+
+dsa::LayoutDev to_dev(const dsa_layout *L)
+{
+    dsa::LayoutDev d;
+    d.kv_indptr = L->kv_indptr;
+    d.q_indptr = L->q_indptr;
+    d.batch = L->batch;
+    return d;
+}
+
+struct MlaArgs {
+    int H, Dc, Dr;
+    int q_dt, kv_dt, out_dt;
+    int k;
+};
+
+dsa_status check_mla_common(const dsa_layout *L, const MlaArgs &a, const int32_t *indices)
+{
+    dsa_status st = check_layout(L);
+    if (st != DSA_OK)
+        return st;
+    if (a.H < 1 || a.Dc < 1 || a.Dr < 0)
+        return fail(DSA_ERR_INVALID_ARG, "bad MLA shape H=%d D_c=%d D_r=%d", a.H, a.Dc, a.Dr);
+    if (a.k < 1 || a.k > DSA_TOPK_MAX)
+        return fail(DSA_ERR_INVALID_ARG, "k=%d outside [1, %d]", a.k, DSA_TOPK_MAX);
+    if (!indices)
+        return fail(DSA_ERR_INVALID_ARG, "indices is NULL");
+    if (a.q_dt != DSA_F32 && a.q_dt != DSA_BF16)
+        return fail(DSA_ERR_UNSUPPORTED, "MLA q dtype %d not supported (F32 or BF16)", a.q_dt);
+    if (!elem_size(a.kv_dt))
+        return fail(DSA_ERR_UNSUPPORTED, "MLA kv dtype %d not supported", a.kv_dt);
+    if (a.out_dt != DSA_F32 && a.out_dt != DSA_BF16)
+        return fail(DSA_ERR_UNSUPPORTED, "MLA out dtype %d not supported (F32 or BF16)", a.out_dt);
+    return DSA_OK;
+}
+
+bool mla_tuned_shape(const MlaArgs &a)
+{
+    return a.H == 64 && a.Dc == 512 && a.Dr == 64 && a.q_dt == DSA_BF16 &&
+           (a.kv_dt == DSA_BF16 || a.kv_dt == DSA_FP8_E4M3FN);
+}
+
+dsa_status check_mla_layer(const MlaArgs &a, const dsa_mla_layer &l, int idx, bool tuned)
+{
+    if (!l.q || !l.kv || !l.out)
+        return fail(DSA_ERR_INVALID_ARG, "layer %d: q, kv and out must be non-NULL", idx);
+    if (!(l.kv_scale > 0.f) || !std::isfinite(l.kv_scale))
+        return fail(DSA_ERR_INVALID_ARG, "layer %d: kv_scale must be finite and > 0", idx);
+    if (tuned && (!aligned(l.q, 16) || !aligned(l.kv, 16) || !aligned(l.out, 16)))
+        return fail(DSA_ERR_INVALID_ARG, "layer %d: q, kv and out must be 16-byte aligned", idx);
+    if (!aligned(l.q, (size_t)elem_size(a.q_dt)) || !aligned(l.kv, (size_t)elem_size(a.kv_dt)) ||
+        !aligned(l.out, (size_t)elem_size(a.out_dt)) || (l.lse && !aligned(l.lse, 4)))
+        return fail(DSA_ERR_INVALID_ARG, "layer %d: pointer not aligned to its element size", idx);
+    return DSA_OK;
+}
+
+dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_layers,
+                   const dsa_mla_layer *layers, const int32_t *indices, void *workspace,
+                   size_t ws_bytes, void *stream)
+{
+    dsa_status st = check_mla_common(L, a, indices);
+    if (st != DSA_OK)
+        return st;
+    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+        return fail(DSA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+    if (n_layers < 1 || n_layers > DSA_MAX_SHARED_LAYERS)
+        return fail(DSA_ERR_INVALID_ARG, "n_layers=%d outside [1, %d]", n_layers, DSA_MAX_SHARED_LAYERS);
+    if (!layers)
+        return fail(DSA_ERR_INVALID_ARG, "layers is NULL");
+    const bool tuned = mla_tuned_shape(a) && !force_generic();
+    if (!tuned) {
+        if (a.H > 128 || a.Dc > 512 || a.Dc + a.Dr > 1024)
+            return fail(DSA_ERR_UNSUPPORTED,
+                        "MLA shape H=%d D_c=%d D_r=%d exceeds the generic kernel (H<=128, D_c<=512, D_c+D_r<=1024)",
+                        a.H, a.Dc, a.Dr);
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        st = check_mla_layer(a, layers[l], l, tuned);
+        if (st != DSA_OK)
+            return st;
+    }
+    if (!aligned(indices, 4))
+        return fail(DSA_ERR_INVALID_ARG, "indices must be 4-byte aligned");
+    const int64_t T = L->total_q;
+    size_t need = tuned ? dsa::mla_workspace_bytes(T, n_layers, a.k) : 0;
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 256))
+        return fail(DSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (T == 0)
+        return ok();
+
+    dsa::MlaLayersDev ld;
+    memset(&ld, 0, sizeof ld);
+    for (int l = 0; l < n_layers; ++l) {
+        ld.l[l].q = layers[l].q;
+        ld.l[l].kv = layers[l].kv;
+        ld.l[l].kv_scale = layers[l].kv_scale;
+        ld.l[l].out = layers[l].out;
+        ld.l[l].lse = layers[l].lse;
+    }
+    const dsa::LayoutDev dl = to_dev(L);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (tuned)
+        e = dsa::launch_mla_tuned(dl, T, ld, n_layers, a.kv_dt == DSA_FP8_E4M3FN, a.out_dt == DSA_F32,
+                                  indices, a.k, sm_scale, workspace, s);
+    else
+        e = dsa::launch_mla_generic(dl, T, a.H, a.Dc, a.Dr, ld, n_layers, a.q_dt, a.kv_dt,
+                                    a.out_dt == DSA_F32, indices, a.k, sm_scale, s);
+    return hip_status(e, "sparse MLA launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_last_error(void)
+{
+    return g_err.c_str();
+}
+
+int dsa_abi_version(void)
+{
+    return DSA_ABI_VERSION;
+}
+
+dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
+                            const void *q, const float *q_scale, const float *w, dsa_dtype k_dt,
+                            const void *k, int64_t k_row_stride, const float *k_scale,
+                            int64_t k_scale_stride, float *scores, int64_t ld, void *stream)
+{
+    dsa_status st = check_layout(layout);
+    if (st != DSA_OK)
+        return st;
+    if (H_I < 1 || D_I < 1)
+        return fail(DSA_ERR_INVALID_ARG, "bad indexer shape H_I=%d D_I=%d", H_I, D_I);
+    if (!elem_size(q_dt) || !elem_size(k_dt))
+        return fail(DSA_ERR_UNSUPPORTED, "indexer dtypes q=%d k=%d not supported", q_dt, k_dt);
+    if (!q || !w || !k || !scores)
+        return fail(DSA_ERR_INVALID_ARG, "q, w, k and scores must be non-NULL");
+    if ((q_dt == DSA_FP8_E4M3FN) != (q_scale != nullptr))
+        return fail(DSA_ERR_INVALID_ARG, "q_scale is required for fp8 q and must be NULL otherwise");
+    if ((k_dt == DSA_FP8_E4M3FN) && !k_scale)
+        return fail(DSA_ERR_INVALID_ARG, "k_scale is required for fp8 keys");
+    if (k_row_stride < (int64_t)D_I * elem_size(k_dt))
+        return fail(DSA_ERR_INVALID_ARG, "k_row_stride %lld < D_I * element size",
+                    (long long)k_row_stride);
+    if (k_row_stride % elem_size(k_dt) != 0)
+        return fail(DSA_ERR_INVALID_ARG, "k_row_stride must be a multiple of the key element size");
+    if (k_scale && k_scale_stride < 1)
+        return fail(DSA_ERR_INVALID_ARG, "k_scale_stride must be >= 1");
+    if (ld < layout->max_ctx)
+        return fail(DSA_ERR_INVALID_ARG, "ld %lld < max_ctx %lld", (long long)ld,
+                    (long long)layout->max_ctx);
+    if (!aligned(w, 4) || !aligned(scores, 4) || (k_scale && !aligned(k_scale, 4)) ||
+        (q_scale && !aligned(q_scale, 4)) || !aligned(q, (size_t)elem_size(q_dt)) ||
+        !aligned(k, (size_t)elem_size(k_dt)))
+        return fail(DSA_ERR_INVALID_ARG, "pointer not aligned to its element size");
+
+    const bool shape32 = H_I == 32 && D_I == 128 && k_dt == DSA_FP8_E4M3FN && aligned(k, 16) &&
+                         (k_row_stride % 16) == 0 && aligned(q, 16);
+    const bool tuned_decode = shape32 && q_dt == DSA_BF16 && !force_generic();
+    const bool tuned_fp8 = shape32 && q_dt == DSA_FP8_E4M3FN && !force_generic();
+    if (!tuned_decode && !tuned_fp8 && (H_I > 64 || D_I > 256))
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "indexer shape H_I=%d D_I=%d needs the generic kernel (H_I <= 64, D_I <= 256)",
+                    H_I, D_I);
+    const int64_t T = layout->total_q;
+    if (T == 0)
+        return ok();
+    const dsa::LayoutDev dl = to_dev(layout);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (tuned_decode)
+        e = dsa::launch_index_decode(dl, T, layout->max_ctx, q, w, k, k_row_stride, k_scale,
+                                     k_scale_stride, scores, ld, s);
+    else if (tuned_fp8)
+        e = dsa::launch_index_fp8(dl, T, layout->max_ctx, q, q_scale, w, k, k_row_stride, k_scale,
+                                  k_scale_stride, scores, ld, s);
+    else
+        e = dsa::launch_index_generic(dl, T, layout->max_ctx, H_I, D_I, q_dt, q, q_scale, w, k_dt, k,
+                                      k_row_stride, k_scale, k_scale_stride, scores, ld, s);
+    return hip_status(e, "indexer launch");
+}
+
+size_t dsa_topk_workspace_size(const dsa_layout *layout, int64_t ld, int k)
+{
+    (void)layout;
+    (void)ld;
+    (void)k;
+    return 0;
+}
+
+dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, int k,
+                    int32_t *indices, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    dsa_status st = check_layout(layout);
+    if (st != DSA_OK)
+        return st;
+    if (k < 1 || k > DSA_TOPK_MAX)
+        return fail(DSA_ERR_INVALID_ARG, "k=%d outside [1, %d]", k, DSA_TOPK_MAX);
+    if (!scores || !indices)
+        return fail(DSA_ERR_INVALID_ARG, "scores and indices must be non-NULL");
+    if (ld < layout->max_ctx)
+        return fail(DSA_ERR_INVALID_ARG, "ld %lld < max_ctx %lld", (long long)ld,
+                    (long long)layout->max_ctx);
+    if (!aligned(scores, 4) || !aligned(indices, 4))
+        return fail(DSA_ERR_INVALID_ARG, "scores and indices must be 4-byte aligned");
+    const int64_t T = layout->total_q;
+    if (T == 0)
+        return ok();
+    return hip_status(dsa::launch_topk(to_dev(layout), T, scores, ld, k, indices, (hipStream_t)stream),
+                      "top-k launch");
+}
+
+size_t sparse_mla_workspace_size(const dsa_layout *layout, int H, int D_c, int D_r, int k,
+                                 int n_layers)
+{
+    if (!layout || layout->total_q < 0 || n_layers < 1 || k < 1 || k > DSA_TOPK_MAX)
+        return 0;
+    if (!(H == 64 && D_c == 512 && D_r == 64))
+        return 0;
+    return dsa::mla_workspace_bytes((int64_t)layout->total_q, n_layers, k);
+}
+
+dsa_status sparse_mla_decode(const dsa_layout *layout, int H, int D_c, int D_r, float sm_scale,
+                             dsa_dtype q_dt, const void *q, dsa_dtype kv_dt, const void *kv,
+                             float kv_scale, const int32_t *indices, int k, dsa_dtype out_dt,
+                             void *out, float *lse, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    MlaArgs a{H, D_c, D_r, q_dt, kv_dt, out_dt, k};
+    dsa_mla_layer l{q, kv, kv_scale, out, lse};
+    return run_mla(layout, a, sm_scale, 1, &l, indices, workspace, workspace_bytes, stream);
+}
+
+dsa_status sparse_mla_prefill(const dsa_layout *layout, int H, int D_c, int D_r, float sm_scale,
+                              dsa_dtype q_dt, const void *q, dsa_dtype kv_dt, const void *kv,
+                              float kv_scale, const int32_t *indices, int k, dsa_dtype out_dt,
+                              void *out, float *lse, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    MlaArgs a{H, D_c, D_r, q_dt, kv_dt, out_dt, k};
+    dsa_mla_layer l{q, kv, kv_scale, out, lse};
+    return run_mla(layout, a, sm_scale, 1, &l, indices, workspace, workspace_bytes, stream);
+}
+
+dsa_status sparse_mla_decode_shared(const dsa_layout *layout, int H, int D_c, int D_r,
+                                    float sm_scale, dsa_dtype q_dt, dsa_dtype kv_dt,
+                                    dsa_dtype out_dt, int n_layers, const dsa_mla_layer *layers,
+                                    const int32_t *indices, int k, void *workspace,
+                                    size_t workspace_bytes, void *stream)
+{
+    MlaArgs a{H, D_c, D_r, q_dt, kv_dt, out_dt, k};
+    return run_mla(layout, a, sm_scale, n_layers, layers, indices, workspace, workspace_bytes,
+                   stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// dsa_common.h -- device-side helpers shared by the libdsa kernels (gfx950 only).
+//
+// Vector types for the CDNA4 matrix cores, exact fp8 -> bf16 / fp32 widening,
+// bf16 rounding and the ragged-layout row lookup used by every stage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Kernel-side copy of dsa_layout (pointers only; host sizes are launch params).
+struct LayoutDev {
+    const int64_t *kv_indptr;
+    const int32_t *q_indptr;  // nullptr: one query per sequence
+    int32_t batch;
+};
+
+struct RowInfo {
+    int32_t b;
+    int64_t kv_base;  // first cache row of the sequence
+    int64_t n;        // visible tokens of this query row (causal, inclusive)
+};
+
+// Query row i -> (sequence, first cache row, visible count).  Query j of a
+// q_len-long chunk at the end of a ctx-long sequence sees ctx - q_len + j + 1
+// tokens; with no q_indptr every sequence has one query that sees all of it.
+__device__ __forceinline__ RowInfo row_info(const LayoutDev &L, int64_t i)
+{
+    RowInfo r;
+    if (L.q_indptr == nullptr) {
+        r.b = (int32_t)i;
+        r.kv_base = L.kv_indptr[i];
+        r.n = L.kv_indptr[i + 1] - r.kv_base;
+        return r;
+    }
+    int lo = 0, hi = L.batch - 1;  // largest b with q_indptr[b] <= i
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)L.q_indptr[mid] <= i)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    r.b = lo;
+    r.kv_base = L.kv_indptr[lo];
+    int64_t ctx = L.kv_indptr[lo + 1] - r.kv_base;
+    int64_t qlen = (int64_t)L.q_indptr[lo + 1] - L.q_indptr[lo];
+    r.n = ctx - qlen + (i - L.q_indptr[lo]) + 1;
+    return r;
+}
+
+// ---- conversions -------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// Two E4M3FN codes (bytes 0,1 or 2,3 of `word`) -> two bf16; exact, since every
+// E4M3FN value is a bf16 value.  gfx950's converter reads OCP E4M3FN.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word)
+{
+    bf16x2 v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)word, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 E4M3FN codes (two dwords) -> 8 bf16 operand lanes for a bf16 MFMA.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1)
+{
+    u32x4 r;
+    r[0] = fp8x2_to_bf16x2<false>(w0);
+    r[1] = fp8x2_to_bf16x2<true>(w0);
+    r[2] = fp8x2_to_bf16x2<false>(w1);
+    r[3] = fp8x2_to_bf16x2<true>(w1);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// One E4M3FN code -> fp32, exact.
+__device__ __forceinline__ float fp8_to_f32(uint32_t code)
+{
+    f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false);
+    return v[0];
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element loaders used by the generic kernels.
+template <int DT> __device__ __forceinline__ float load_elem(const void *base, int64_t idx);
+template <> __device__ __forceinline__ float load_elem<0>(const void *base, int64_t idx)
+{
+    return ((const float *)base)[idx];
+}
+template <> __device__ __forceinline__ float load_elem<1>(const void *base, int64_t idx)
+{
+    return bf16_bits_to_f32(((const uint16_t *)base)[idx]);
+}
+template <> __device__ __forceinline__ float load_elem<2>(const void *base, int64_t idx)
+{
+    return fp8_to_f32(((const uint8_t *)base)[idx]);
+}
+
+// ---- wave / block reductions (wave64) -----------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace dsa

@@ -1,0 +1,52 @@
+// dsa_kernels.h -- internal launchers of libdsa (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+struct LayoutDev;
+
+struct MlaLayerDev {
+    const void *q;
+    const void *kv;
+    float kv_scale;
+    void *out;
+    float *lse;
+};
+struct MlaLayersDev {
+    MlaLayerDev l[DSA_MAX_SHARED_LAYERS];
+};
+
+// Sparse-MLA split heuristic: enough (query row, split) blocks to give every CU one block.
+constexpr int MLA_TARGET_BLOCKS = 256;
+
+hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
+                               const float *w, const void *k, int64_t kstride, const float *ks,
+                               int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream);
+hipError_t launch_index_fp8(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
+                            const float *qs, const float *w, const void *k, int64_t kstride,
+                            const float *ks, int64_t ks_stride, float *scores, int64_t ld,
+                            hipStream_t stream);
+hipError_t launch_index_generic(const LayoutDev &L, int64_t T, int64_t max_ctx, int H, int D,
+                                int q_dt, const void *q, const float *qs, const float *w, int k_dt,
+                                const void *k, int64_t kstride, const float *ks, int64_t ks_stride,
+                                float *scores, int64_t ld, hipStream_t stream);
+hipError_t launch_topk(const LayoutDev &L, int64_t T, const float *scores, int64_t ld, int k,
+                       int32_t *indices, hipStream_t stream);
+
+int mla_num_splits(int64_t T, int k);
+size_t mla_workspace_bytes(int64_t T, int n_layers, int k);
+hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &layers, int n_layers,
+                            bool kv_fp8, bool out_f32, const int32_t *indices, int k,
+                            float sm_scale, void *workspace, hipStream_t stream);
+hipError_t launch_mla_generic(const LayoutDev &L, int64_t T, int H, int Dc, int Dr,
+                              const MlaLayersDev &layers, int n_layers, int q_dt, int kv_dt,
+                              bool out_f32, const int32_t *indices, int k, float sm_scale,
+                              hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,318 @@
+// indexer.hip -- lightning-indexer score kernels for gfx950.
+//
+// score[i, s] = sum_h w[i,h] * ReLU(q[i,h,:] . k[s,:] * qs[i,h] * ks[s])
+// ("GLM-5.2 架构解剖", full structure diagram, Indexer box: 32 index heads x 128 dims
+// with one key per token shared by all heads; fp8 keys with a per-token scale in a
+// 132-byte index-cache entry).  Scales are positive, so ReLU(x * qs * ks) =
+// qs * ks * ReLU(x): qs folds into the head weight and ks multiplies the head sum.
+//
+// Three kernels:
+//  * idx_decode_kernel   bf16 q x fp8 k (H=32, D=128).  HBM stream of the index cache:
+//    each lane loads 64 contiguous key bytes, widens them exactly to bf16 and feeds
+//    v_mfma_f32_32x32x16_bf16 with the 32 heads as M and 32 tokens as N.
+//  * idx_fp8_kernel      fp8 q x fp8 k (H=32, D=128): the prefill GEMM on
+//    v_mfma_scale_f32_32x32x64_f8f6f4; 16 query rows per block share an LDS key tile.
+//  * idx_generic_kernel  any dtypes / H <= 64 / D <= 256, one thread per token.
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+// ------------------------------------------------------------------------------------------
+// bf16 q x fp8 k, H = 32, D = 128
+//
+// MFMA 32x32x16 bf16: lane l supplies A[row l%32][k-group l/32] and B[k-group l/32][col
+// l%32]; D[row][col] lands in lane col + 32*((row/4)%2), register 4*(row/8) + row%4.
+// Rows are heads, columns tokens.  The 128-long contraction is split so that lane half g
+// owns dims [64g, 64g+64): MFMA t consumes dims 64g + 8t .. 64g + 8t + 7 of both q and k.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
+                                                         const float *__restrict__ w,
+                                                         const uint8_t *__restrict__ k, int64_t kstride,
+                                                         const float *__restrict__ ks, int64_t ks_stride,
+                                                         float *__restrict__ scores, int64_t ld,
+                                                         int chunk)
+{
+    const int64_t i = blockIdx.y;
+    const RowInfo r = row_info(L, i);
+    const int64_t s_begin = (int64_t)blockIdx.x * chunk;
+    if (s_begin >= r.n)
+        return;
+    const int64_t s_end = min(s_begin + (int64_t)chunk, r.n);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, j = lane & 31;
+
+    bf16x8 a[8];
+    const u32x4 *qp = (const u32x4 *)(q + ((i * 32 + j) * 128 + 64 * g));
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        a[t] = __builtin_bit_cast(bf16x8, qp[t]);
+    float wr[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+        wr[rr] = w[i * 32 + 8 * (rr >> 2) + 4 * g + (rr & 3)];
+
+    float *out = scores + i * ld;
+    for (int64_t s0 = s_begin + wave * 32; s0 < s_end; s0 += 128) {
+        const int64_t s = s0 + j;
+        const int64_t row = r.kv_base + (s < s_end ? s : s_end - 1);
+        const u32x4 *kp = (const u32x4 *)(k + row * kstride + 64 * g);
+        const u32x4 k0 = kp[0], k1 = kp[1], k2 = kp[2], k3 = kp[3];
+        const float ksv = ks[row * ks_stride];
+        f32x16 acc = {};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp8x8_to_bf16x8(k0[0], k0[1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp8x8_to_bf16x8(k0[2], k0[3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], fp8x8_to_bf16x8(k1[0], k1[1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], fp8x8_to_bf16x8(k1[2], k1[3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[4], fp8x8_to_bf16x8(k2[0], k2[1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[5], fp8x8_to_bf16x8(k2[2], k2[3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp8x8_to_bf16x8(k3[0], k3[1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp8x8_to_bf16x8(k3[2], k3[3]), acc, 0, 0, 0);
+        float part = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            part = fmaf(wr[rr], fmaxf(acc[rr], 0.f), part);
+        part += __shfl_xor(part, 32, 64);
+        if (g == 0 && s < s_end)
+            out[s] = part * ksv;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// fp8 q x fp8 k, H = 32, D = 128 (prefill GEMM)
+//
+// Block = 4 waves x 4 query rows; the block streams CHUNK tokens of one sequence through an
+// LDS tile of 128 tokens (rows padded to 144 B so the 16-lane groups of ds_read_b128 hit
+// disjoint banks).  MFMA 32x32x64 f8f6f4 (E4M3 on both sides, unit block scales): lane half
+// g owns dims [64g, 64g+64) of q and k; MFMA t consumes 32 of them.
+// ------------------------------------------------------------------------------------------
+constexpr int PF_QPW = 4;                 // query rows per wave
+constexpr int PF_QPB = 4 * PF_QPW;        // query rows per block
+constexpr int PF_STAGE = 128;             // tokens per LDS stage
+constexpr int PF_ROW_U4 = 9;              // LDS row stride in 16-byte units (128 B + pad)
+constexpr int E8M0_ONE = 127;             // block scale 2^0
+
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, E8M0_ONE, 0, E8M0_ONE);
+}
+
+__global__ __launch_bounds__(256) void idx_fp8_kernel(LayoutDev L, int64_t T, const uint8_t *__restrict__ q,
+                                                      const float *__restrict__ qs,
+                                                      const float *__restrict__ w,
+                                                      const uint8_t *__restrict__ k, int64_t kstride,
+                                                      const float *__restrict__ ks, int64_t ks_stride,
+                                                      float *__restrict__ scores, int64_t ld, int chunk)
+{
+    __shared__ u32x4 ktile[PF_STAGE * PF_ROW_U4];
+    __shared__ float kscale[PF_STAGE];
+    __shared__ int64_t s_meta[PF_QPB][3];  // b, kv_base, n per block query row (b = -1: none)
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, j = lane & 31;
+    const int64_t q0 = (int64_t)blockIdx.y * PF_QPB;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+
+    if (tid < PF_QPB) {
+        const int64_t qi = q0 + tid;
+        if (qi < T) {
+            RowInfo r = row_info(L, qi);
+            s_meta[tid][0] = r.b;
+            s_meta[tid][1] = r.kv_base;
+            s_meta[tid][2] = r.n;
+        } else {
+            s_meta[tid][0] = -1;
+            s_meta[tid][1] = 0;
+            s_meta[tid][2] = 0;
+        }
+    }
+    __syncthreads();
+
+    // A operands and folded weights of this wave's query rows.
+    i32x8 a[PF_QPW][2];
+    float wq[PF_QPW][16];
+#pragma unroll
+    for (int u = 0; u < PF_QPW; ++u) {
+        const int64_t qi = q0 + wave * PF_QPW + u;
+        const int64_t qq = qi < T ? qi : 0;
+        const u32x4 *qp = (const u32x4 *)(q + (qq * 32 + j) * 128 + 64 * g);
+        u32x4 v0 = qp[0], v1 = qp[1], v2 = qp[2], v3 = qp[3];
+        a[u][0] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+        a[u][1] = i32x8{(int)v2[0], (int)v2[1], (int)v2[2], (int)v2[3], (int)v3[0], (int)v3[1], (int)v3[2], (int)v3[3]};
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int h = 8 * (rr >> 2) + 4 * g + (rr & 3);
+            wq[u][rr] = w[qq * 32 + h] * qs[qq * 32 + h];
+        }
+    }
+
+    // Query rows of one block may span several sequences: handle each in turn.
+    int first = 0;
+    while (first < PF_QPB) {
+        const int64_t b = s_meta[first][0];
+        if (b < 0)
+            break;
+        int last = first;
+        int64_t nmax = s_meta[first][2];
+        while (last + 1 < PF_QPB && s_meta[last + 1][0] == b) {
+            ++last;
+            nmax = max(nmax, s_meta[last][2]);
+        }
+        const int64_t kv_base = s_meta[first][1];
+        const int64_t s_end = min(c0 + (int64_t)chunk, nmax);
+
+        for (int64_t st = c0; st < s_end; st += PF_STAGE) {
+            __syncthreads();  // previous stage fully consumed
+            // stage 128 tokens x 128 B: 1024 16-byte pieces, 4 per thread
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int c = tid + 256 * p;
+                const int tt = c >> 3, part = c & 7;
+                const int64_t s = st + tt;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (s < s_end)
+                    v = *(const u32x4 *)(k + (kv_base + s) * kstride + part * 16);
+                ktile[tt * PF_ROW_U4 + part] = v;
+            }
+            if (tid < PF_STAGE) {
+                const int64_t s = st + tid;
+                kscale[tid] = s < s_end ? ks[(kv_base + s) * ks_stride] : 0.f;
+            }
+            __syncthreads();
+
+#pragma unroll
+            for (int sub = 0; sub < PF_STAGE / 32; ++sub) {
+                const int64_t sb = st + sub * 32;
+                if (sb >= s_end)
+                    break;
+                const u32x4 *kr = &ktile[(sub * 32 + j) * PF_ROW_U4 + 4 * g];
+                const u32x4 v0 = kr[0], v1 = kr[1], v2 = kr[2], v3 = kr[3];
+                const i32x8 b0 = {(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+                const i32x8 b1 = {(int)v2[0], (int)v2[1], (int)v2[2], (int)v2[3], (int)v3[0], (int)v3[1], (int)v3[2], (int)v3[3]};
+                const float ksv = kscale[sub * 32 + j];
+#pragma unroll
+                for (int u = 0; u < PF_QPW; ++u) {
+                    const int qb = wave * PF_QPW + u;
+                    if (qb < first || qb > last)
+                        continue;
+                    const int64_t nq = s_meta[qb][2];
+                    if (sb >= nq)
+                        continue;
+                    f32x16 acc = {};
+                    acc = mfma_fp8_32x32x64(a[u][0], b0, acc);
+                    acc = mfma_fp8_32x32x64(a[u][1], b1, acc);
+                    float part = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr)
+                        part = fmaf(wq[u][rr], fmaxf(acc[rr], 0.f), part);
+                    part += __shfl_xor(part, 32, 64);
+                    const int64_t s = sb + j;
+                    if (g == 0 && s < nq)
+                        scores[(q0 + qb) * ld + s] = part * ksv;
+                }
+            }
+        }
+        first = last + 1;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// generic: any dtypes, H <= 64, D <= 256.  One thread per token; q row in LDS as fp32.
+// ------------------------------------------------------------------------------------------
+template <int QDT, int KDT>
+__global__ __launch_bounds__(256) void idx_generic_kernel(LayoutDev L, int H, int D, const void *__restrict__ q,
+                                                          const float *__restrict__ qs,
+                                                          const float *__restrict__ w,
+                                                          const uint8_t *__restrict__ k, int64_t kstride,
+                                                          const float *__restrict__ ks, int64_t ks_stride,
+                                                          float *__restrict__ scores, int64_t ld)
+{
+    extern __shared__ float sm[];  // [H*D] q, then [H] folded weights
+    const int64_t i = blockIdx.y;
+    const RowInfo r = row_info(L, i);
+    const int64_t sblk = (int64_t)blockIdx.x * 256;
+    if (sblk >= r.n)
+        return;
+    float *sq = sm, *sw = sm + H * D;
+    for (int e = threadIdx.x; e < H * D; e += 256)
+        sq[e] = load_elem<QDT>(q, i * H * D + e);
+    for (int h = threadIdx.x; h < H; h += 256)
+        sw[h] = w[i * H + h] * (qs ? qs[i * H + h] : 1.f);
+    __syncthreads();
+    const int64_t s = sblk + threadIdx.x;
+    if (s >= r.n)
+        return;
+    const int64_t row = r.kv_base + s;
+    const uint8_t *krow = k + row * kstride;
+    float acc = 0.f;
+    for (int h = 0; h < H; ++h) {
+        float a = 0.f;
+        for (int d = 0; d < D; ++d)
+            a = fmaf(sq[h * D + d], load_elem<KDT>(krow, d), a);
+        acc = fmaf(sw[h], fmaxf(a, 0.f), acc);
+    }
+    scores[i * ld + s] = acc * (ks ? ks[row * ks_stride] : 1.f);
+}
+
+// ------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------
+hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
+                               const float *w, const void *k, int64_t kstride, const float *ks,
+                               int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream)
+{
+    // Enough blocks to cover the chip several times, at least one 32-token tile per wave.
+    int chunk = 2048;
+    while (chunk > 128 && T * ((max_ctx + chunk - 1) / chunk) < 2048)
+        chunk >>= 1;
+    dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)T);
+    hipLaunchKernelGGL(idx_decode_kernel, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
+                       (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_fp8(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
+                            const float *qs, const float *w, const void *k, int64_t kstride,
+                            const float *ks, int64_t ks_stride, float *scores, int64_t ld,
+                            hipStream_t stream)
+{
+    int chunk = 1024;
+    const int64_t qblocks = (T + PF_QPB - 1) / PF_QPB;
+    while (chunk > PF_STAGE && qblocks * ((max_ctx + chunk - 1) / chunk) < 2048)
+        chunk >>= 1;
+    dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)qblocks);
+    hipLaunchKernelGGL(idx_fp8_kernel, grid, dim3(256), 0, stream, L, T, (const uint8_t *)q, qs, w,
+                       (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
+    return hipGetLastError();
+}
+
+template <int QDT, int KDT>
+static hipError_t launch_generic_t(const LayoutDev &L, int64_t T, int64_t max_ctx, int H, int D,
+                                   const void *q, const float *qs, const float *w, const void *k,
+                                   int64_t kstride, const float *ks, int64_t ks_stride, float *scores,
+                                   int64_t ld, hipStream_t stream)
+{
+    dim3 grid((unsigned)((max_ctx + 255) / 256), (unsigned)T);
+    size_t shmem = sizeof(float) * (size_t)(H * D + H);
+    hipLaunchKernelGGL((idx_generic_kernel<QDT, KDT>), grid, dim3(256), shmem, stream, L, H, D, q, qs,
+                       w, (const uint8_t *)k, kstride, ks, ks_stride, scores, ld);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_generic(const LayoutDev &L, int64_t T, int64_t max_ctx, int H, int D,
+                                int q_dt, const void *q, const float *qs, const float *w, int k_dt,
+                                const void *k, int64_t kstride, const float *ks, int64_t ks_stride,
+                                float *scores, int64_t ld, hipStream_t stream)
+{
+#define DSA_IDX_CASE(QD, KD)                                                                     \
+    if (q_dt == QD && k_dt == KD)                                                                \
+        return launch_generic_t<QD, KD>(L, T, max_ctx, H, D, q, qs, w, k, kstride, ks, ks_stride, \
+                                        scores, ld, stream);
+    DSA_IDX_CASE(0, 0) DSA_IDX_CASE(0, 1) DSA_IDX_CASE(0, 2)
+    DSA_IDX_CASE(1, 0) DSA_IDX_CASE(1, 1) DSA_IDX_CASE(1, 2)
+    DSA_IDX_CASE(2, 0) DSA_IDX_CASE(2, 1) DSA_IDX_CASE(2, 2)
+#undef DSA_IDX_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

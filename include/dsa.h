@@ -1,0 +1,222 @@
+/*
+ * dsa.h -- C ABI of libdsa, the DeepSeek-Sparse-Attention (DSA) decode /
+ * prefill path for AMD Instinct MI355X (gfx950).
+ *
+ * The path has three stages plus reuse of one index set across layers:
+ *
+ *   dsa_index_scores         lightning indexer: one fp32 score per visible
+ *                            cached token for every query row
+ *   dsa_topk                 per-row top-k (k <= DSA_TOPK_MAX) positions
+ *   sparse_mla_decode        attention of H query heads over only the
+ *   sparse_mla_prefill       selected rows of a latent KV cache
+ *   sparse_mla_decode_shared several layers' sparse MLA over one index set
+ *
+ * Citations are to the reference pages by title and section:
+ *   [anatomy]  "GLM-5.2 架构解剖" (GLM-5.2 anatomy);
+ *   [guide]    "ATOM Model Support Guide";
+ *   [pr2980]   ATOM pull request #2980 (FP8 weight planes in mono decode).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer (HIP memory visible to
+ *   the current device) unless its comment says "host".  The caller owns
+ *   every buffer; the library keeps no pointer after a call returns and
+ *   allocates no device memory.  Buffers must stay alive until the stream
+ *   has executed the call.
+ * Streams.  Every call only enqueues work on `stream` (a hipStream_t, NULL =
+ *   the default stream) and never synchronises the host.
+ * Errors.  All arguments are checked on the host first.  A failed check
+ *   returns a negative dsa_status, sets the thread-local message read by
+ *   dsa_last_error(), and launches nothing, so no output is partially
+ *   written.  A failed launch returns DSA_ERR_HIP.  Device faults surface at
+ *   the caller's next synchronisation.  No C++ exception crosses the ABI.
+ * Determinism.  Identical inputs give bitwise-identical outputs.  There are
+ *   no floating-point atomics; every reduction has a fixed order.
+ * Preconditions the library does not check (they need device data):
+ *   kv_indptr / q_indptr are non-decreasing, every context is >= 1 and
+ *   <= max_ctx, q_len_b <= ctx_b; scales are finite and > 0; no fp8 NaN
+ *   codes (0x7F, 0xFF); the indices given to sparse MLA were produced for the
+ *   same layout (unique, < n_i, or -1).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+/* Largest k accepted by dsa_topk and the sparse MLA entry points. */
+#define DSA_TOPK_MAX 2048
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad stride          */
+    DSA_ERR_UNSUPPORTED = -2, /* dtype / shape combination not implemented   */
+    DSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+    DSA_ERR_HIP = -4          /* a HIP launch or query failed                */
+} dsa_status;
+
+typedef enum {
+    DSA_F32 = 0,
+    DSA_BF16 = 1,          /* bfloat16                                        */
+    DSA_FP8_E4M3FN = 2     /* OCP E4M3, finite-only (max 448): the fp8 format
+                              of gfx950 ([pr2980], Limitations)              */
+} dsa_dtype;
+
+/*
+ * Ragged batch layout, shared by every call ([guide], DeepSeek V2/V3: MLA
+ * attention metadata is tracked with kv_indptr).
+ *
+ * Sequence b owns cache rows kv_indptr[b] .. kv_indptr[b+1]-1 (ctx_b rows) in
+ * every per-token cache (index keys and each layer's latent KV) and query
+ * rows q_indptr[b] .. q_indptr[b+1]-1 (q_len_b rows).  Query j of sequence b
+ * sits at position p = ctx_b - q_len_b + j and sees the causal prefix
+ * 0 .. p, i.e. n = p + 1 tokens.  q_indptr == NULL means one query per
+ * sequence (decode): T = B and n = ctx_b.
+ */
+typedef struct {
+    int32_t batch;             /* B >= 1                                      */
+    int32_t total_q;           /* T: query rows (= q_indptr[B]; = B for decode) */
+    int64_t max_ctx;           /* host upper bound of every ctx_b (>= 1)      */
+    const int64_t *kv_indptr;  /* device [B+1]                                */
+    const int32_t *q_indptr;   /* device [B+1], or NULL for decode            */
+} dsa_layout;
+
+/*
+ * dsa_index_scores -- lightning-indexer scores ([anatomy], full structure
+ * diagram, Indexer box: 32 index heads x 128 dims, one key per token shared
+ * by every index head, keys stored as fp8 with a per-token scale in a
+ * 132-byte index-cache entry).  For every query row i and visible token
+ * s < n_i:
+ *
+ *     score[i, s] = sum_h w[i,h] * ReLU( (q[i,h,:] . k[s,:]) * qs[i,h] * ks[s] )
+ *
+ * with qs = 1 when q_scale is NULL and ks = 1 when k_scale is NULL.
+ *
+ *   H_I, D_I      index heads and head dim (any H_I <= 64, D_I <= 256; the
+ *                 tuned kernels take H_I = 32, D_I = 128).
+ *   q_dt, q       [T][H_I][D_I] of q_dt (F32, BF16 or FP8_E4M3FN), contiguous.
+ *   q_scale       [T][H_I] fp32, required iff q_dt is FP8_E4M3FN, else NULL.
+ *   w             [T][H_I] fp32 head weights.
+ *   k_dt, k       key row r (global cache row) starts at byte r * k_row_stride
+ *                 of k and holds D_I elements of k_dt.  k_row_stride >= D_I *
+ *                 elem size; 132 with k_scale = (float*)(k + 128) and
+ *                 k_scale_stride = 33 reads the interleaved 132-byte entries.
+ *   k_scale       fp32 scale of row r at k_scale[r * k_scale_stride];
+ *                 required iff k_dt is FP8_E4M3FN.
+ *   scores, ld    fp32 output, row i at scores + i * ld; ld >= max_ctx.  Only
+ *                 s < n_i is written.
+ * The fp8 x bf16 products are exact in fp32; sums are fp32.
+ */
+dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
+                            const void *q, const float *q_scale, const float *w,
+                            dsa_dtype k_dt, const void *k, int64_t k_row_stride,
+                            const float *k_scale, int64_t k_scale_stride, float *scores,
+                            int64_t ld, void *stream);
+
+/*
+ * dsa_topk -- per-row top-k selection ([anatomy], Indexer box: top-k = 2048
+ * written as int32 [tokens x 2048]; ATOM-side optimisations, stable_topk:
+ * ties must not be broken arbitrarily; caveats: with fewer visible tokens
+ * than k every token is taken).
+ *
+ * Row i considers scores[i * ld + s] for s < n_i and writes to
+ * indices[i * k .. i * k + k - 1] the first min(k, n_i) positions under the
+ * strict order "higher score first; equal scores (with -0 == +0) by lower
+ * position", then -1 in the remaining slots.  Positions are logical (0 ..
+ * ctx_b - 1 within the sequence).  1 <= k <= DSA_TOPK_MAX.  NaN scores are
+ * outside the contract.
+ *   workspace     device scratch of dsa_topk_workspace_size() bytes (may be
+ *                 NULL when that size is 0).
+ */
+size_t dsa_topk_workspace_size(const dsa_layout *layout, int64_t ld, int k);
+dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, int k,
+                    int32_t *indices, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sparse_mla_decode / sparse_mla_prefill -- attention over the selected
+ * latent rows ([anatomy], full structure diagram, sparse MLA box: 64 heads
+ * computed only on the 2048 selected rows of the latent KV cache, 576 = 512
+ * latent + 64 rope values per token).  The absorbed form: the key is the
+ * whole D_c + D_r row, the value is its first D_c entries, and the output
+ * stays in latent space.  For every query row i and head h, with J the
+ * non-negative entries of indices[i * k .. i * k + k - 1]:
+ *
+ *   z_j   = sm_scale * kv_scale * (q[i,h,:] . c[kv_indptr[b] + J_j, :])
+ *   o     = sum_j softmax(z)_j * kv_scale * c[kv_indptr[b] + J_j, 0:D_c]
+ *   lse   = log sum_j exp(z_j)          (o = 0, lse = -inf when J is empty)
+ *
+ *   H, D_c, D_r   heads, latent width, rope width.  Tuned kernels: H = 64,
+ *                 D_c = 512, D_r = 64, bf16 q, bf16 or fp8 KV.  Other shapes
+ *                 (H <= 128, D_c <= 512, D_c + D_r <= 1024) run a generic
+ *                 kernel.
+ *   q             [T][H][D_c + D_r] of q_dt (F32 or BF16).
+ *   kv            [rows][D_c + D_r] of kv_dt (F32, BF16 or FP8_E4M3FN) with
+ *                 one per-tensor scale kv_scale (use 1 for F32 / BF16).
+ *   indices, k    int32 [T][k] logical positions (< n_i) or -1.
+ *   out           [T][H][D_c] of out_dt (F32 or BF16).
+ *   lse           fp32 [T][H], or NULL.
+ *   workspace     device scratch of sparse_mla_workspace_size() bytes.  Its
+ *                 first use needs it zero-filled; every completed call leaves
+ *                 it that way again, so calls on one stream may reuse it.
+ *                 Calls that overlap in time must not share a workspace.
+ * The decode entry accepts any layout; prefill is the same computation with
+ * a launch shape suited to many query rows per sequence.
+ */
+size_t sparse_mla_workspace_size(const dsa_layout *layout, int H, int D_c, int D_r, int k,
+                                 int n_layers);
+dsa_status sparse_mla_decode(const dsa_layout *layout, int H, int D_c, int D_r, float sm_scale,
+                             dsa_dtype q_dt, const void *q, dsa_dtype kv_dt, const void *kv,
+                             float kv_scale, const int32_t *indices, int k, dsa_dtype out_dt,
+                             void *out, float *lse, void *workspace, size_t workspace_bytes,
+                             void *stream);
+dsa_status sparse_mla_prefill(const dsa_layout *layout, int H, int D_c, int D_r, float sm_scale,
+                              dsa_dtype q_dt, const void *q, dsa_dtype kv_dt, const void *kv,
+                              float kv_scale, const int32_t *indices, int k, dsa_dtype out_dt,
+                              void *out, float *lse, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * sparse_mla_decode_shared -- IndexShare ([anatomy], layer scheduling:
+ * "shared" layers carry no indexer and reuse the indices the previous "full"
+ * layer selected; full structure diagram: one int32 [tokens x 2048] buffer is
+ * read by every layer).  Runs sparse_mla_decode for n_layers layers, each
+ * with its own q, latent KV, scale and outputs, over the same indices, in one
+ * launch.  Layer l's result is bitwise equal to sparse_mla_decode on layer l.
+ * The index set must have been written by a full layer before (a shared layer
+ * cannot come first: it would read a buffer nobody wrote; [anatomy], layer
+ * scheduling, invariant box); the library cannot check this.
+ *   layers        HOST array of n_layers descriptors (1 <= n_layers <=
+ *                 DSA_MAX_SHARED_LAYERS); every layer uses the same dtypes.
+ */
+#define DSA_MAX_SHARED_LAYERS 8
+typedef struct {
+    const void *q;   /* [T][H][D_c + D_r] */
+    const void *kv;  /* [rows][D_c + D_r] */
+    float kv_scale;
+    void *out;       /* [T][H][D_c]       */
+    float *lse;      /* [T][H] or NULL    */
+} dsa_mla_layer;
+
+dsa_status sparse_mla_decode_shared(const dsa_layout *layout, int H, int D_c, int D_r,
+                                    float sm_scale, dsa_dtype q_dt, dsa_dtype kv_dt,
+                                    dsa_dtype out_dt, int n_layers, const dsa_mla_layer *layers,
+                                    const int32_t *indices, int k, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *dsa_last_error(void);
+
+/* DSA_ABI_VERSION of the loaded library. */
+int dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

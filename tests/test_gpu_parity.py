@@ -1,0 +1,197 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle, on the GPU.
+
+Small cases cover several tiles, ragged tails, multi-sequence blocks and the degenerate
+cases (n < k, n = 1, all-masked tiles, ties); the full-size workloads are checked on
+sampled rows.  Tolerances: see dsa_testlib.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_testlib as tl
+import deepseek_sparse_mla_amd as dsa
+from deepseek_sparse_mla_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _all_rows_check(case, scores, idx, outs, atol, rows=None):
+    n = tl.visible(case)
+    rows = range(case.T) if rows is None else rows
+    s_host = scores.cpu().numpy()
+    i_host = idx.cpu().numpy()
+    o_scores = tl.oracle_scores_rows(case, rows)
+    for r, osr in zip(rows, o_scores):
+        ni = int(n[r])
+        tl.check_scores(s_host[r, :ni], osr, "%s row %d" % (case.name, r))
+        tl.check_topk_same_array(i_host[r], s_host[r, :ni], case.topk, "%s row %d" % (case.name, r))
+        tl.check_topk_margin(i_host[r], osr, case.topk, "%s row %d" % (case.name, r))
+    worst = 0.0
+    for l, out in enumerate(outs):
+        o_or, _ = tl.oracle_mla_rows(case, rows, i_host, layer=l)
+        g = tl.to_f64(out)
+        for r, oo in zip(rows, o_or):
+            worst = max(worst, tl.check_attention(g[r], oo, atol, "%s layer %d row %d" % (case.name, l, r)))
+    return worst
+
+
+def test_tiny_config_full_path():
+    case = synth.config(1, DEV)
+    scores, idx, outs, lses = tl.gpu_path(case)
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_F32)
+    # lse too
+    _, l_or = tl.oracle_mla_rows(case, [0], idx.cpu().numpy())
+    np.testing.assert_allclose(lses[0].cpu().numpy()[0], l_or[0], atol=1e-4)
+
+
+DECODE_CASES = {
+    "bf16kv_ragged": dict(ctx=[1000, 2500, 4100, 9000], kv_dt="bf16"),
+    "fp8kv_ragged": dict(ctx=[4096, 5000, 2049, 2047, 700], kv_dt="fp8"),
+    "short_and_edge": dict(ctx=[1, 2, 64, 2048, 130], kv_dt="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_CASES))
+def test_decode_path(name):
+    case = synth.make_case(name, 2, sm_scale=1.0 / 16, device=DEV, **DECODE_CASES[name])
+    scores, idx, outs, lses = tl.gpu_path(case)
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP)
+    # lse of every row against the oracle on the same indices
+    _, l_or = tl.oracle_mla_rows(case, range(case.T), idx.cpu().numpy())
+    np.testing.assert_allclose(lses[0].cpu().numpy(), np.array(l_or), atol=1e-2, rtol=1e-3)
+
+
+def test_prefill_single_sequence_sampled_rows():
+    case = synth.make_case("prefill_small", 4, ctx=[2600], q_len=[70], iq_dt="fp8", sm_scale=1.0 / 16,
+                           kv_dt="bf16", device=DEV)
+    scores, idx, outs, _ = tl.gpu_path(case)
+    n = tl.visible(case)
+    s_host, i_host = scores.cpu().numpy(), idx.cpu().numpy()
+    for r, osr in zip(range(case.T), tl.oracle_scores_rows(case, range(case.T))):
+        tl.check_scores(s_host[r, :n[r]], osr, "row %d" % r)
+        tl.check_topk_same_array(i_host[r], s_host[r, :n[r]], case.topk, "row %d" % r)
+        tl.check_topk_margin(i_host[r], osr, case.topk, "row %d" % r)
+    rows = [0, 1, 17, 35, 68, 69]
+    o_or, _ = tl.oracle_mla_rows(case, rows, i_host)
+    g = tl.to_f64(outs[0])
+    for r, oo in zip(rows, o_or):
+        tl.check_attention(g[r], oo, tl.ATTN_ATOL_LOWP, "row %d" % r)
+
+
+def test_prefill_ragged_sequences_share_blocks():
+    """Query blocks that span two sequences (16 query rows per indexer block)."""
+    case = synth.make_case("prefill_ragged", 4, ctx=[1500, 2300, 40], q_len=[20, 37, 5], iq_dt="fp8",
+                           sm_scale=1.0 / 16, kv_dt="fp8", topk=512, device=DEV)
+    scores, idx, outs, _ = tl.gpu_path(case)
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=[0, 15, 16, 19, 20, 31, 32, 56, 57, 61])
+
+
+def test_shared_layers_match_oracle_and_single_layer_calls():
+    case = synth.make_case("shared_small", 5, ctx=[3000, 2100], sm_scale=1.0 / 16, kv_dt="fp8", n_layers=3,
+                           device=DEV)
+    scores, idx, outs, lses = tl.gpu_path(case)
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP)
+    layout = dsa.Layout.of_case(case)
+    for l, L in enumerate(case.layers):
+        lse1 = torch.empty_like(lses[l])
+        o1 = dsa.sparse_mla_decode(layout, L.q, L.kv, idx, case.sm_scale, case.Dc, L.kv_scale, lse=lse1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, outs[l]), "layer %d differs from its single-layer call" % l
+        assert torch.equal(lse1, lses[l])
+
+
+def test_recomputed_indexer_gives_identical_indices_and_outputs():
+    case = synth.make_case("determinism", 2, ctx=[5000, 3000, 2048], sm_scale=1.0 / 16, kv_dt="fp8",
+                           device=DEV)
+    a = tl.gpu_path(case)
+    b = tl.gpu_path(case)
+    n = tl.visible(case)
+    for r in range(case.T):  # only visible positions are written
+        assert torch.equal(a[0][r, :n[r]], b[0][r, :n[r]])
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2][0], b[2][0]) and torch.equal(a[3][0], b[3][0])
+
+
+def test_generic_kernels_match_oracle(monkeypatch):
+    """The generic kernels (forced) meet the same bar on a GLM-shaped case."""
+    monkeypatch.setenv("DSA_KERNEL_VARIANT", "generic")
+    case = synth.make_case("generic", 2, ctx=[900, 2100], sm_scale=1.0 / 16, kv_dt="fp8", device=DEV)
+    scores, idx, outs, _ = tl.gpu_path(case)
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP)
+
+
+def test_interleaved_132_byte_index_cache():
+    """One 132-byte slot per token (128 fp8 codes then the fp32 scale), read in place."""
+    case = synth.make_case("aos", 2, ctx=[700, 1300], sm_scale=1.0 / 16, device=DEV)
+    N = case.N
+    slab = torch.zeros((N, 132), dtype=torch.uint8, device=DEV)
+    slab[:, :128] = case.ik
+    slab[:, 128:] = case.ik_scale.view(torch.uint8).view(N, 4)
+    layout = dsa.Layout.of_case(case)
+    scale_slots = slab.view(torch.float32).view(-1)[32:]  # float 32 + 33 r = byte 128 + 132 r
+    s_aos = dsa.dsa_index_scores(layout, case.iq, case.iw, slab, k_scale=scale_slots, k_row_stride=132,
+                                 k_scale_stride=33, k_dtype=dsa.DSA_FP8_E4M3FN)
+    torch.cuda.synchronize()
+    n = tl.visible(case)
+    o = tl.oracle_scores_rows(case, range(case.T))
+    for r in range(case.T):
+        tl.check_scores(s_aos[r, :n[r]].cpu().numpy(), o[r], "aos row %d" % r)
+
+
+# ------------------------------------------------------------------------------ top-k edge cases
+
+def _topk_rows(rows, k=2048):
+    """Run dsa_topk on the given fp32 rows (one sequence per row) and compare bit-exactly."""
+    ctx = [len(r) for r in rows]
+    ld = max(ctx)
+    sc = np.zeros((len(rows), ld), np.float32)
+    for i, r in enumerate(rows):
+        sc[i, :len(r)] = r
+    kvp = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]), dtype=torch.int64, device=DEV)
+    layout = dsa.Layout(kvp, None, len(rows), ld)
+    idx = dsa.dsa_topk(layout, torch.from_numpy(sc).to(DEV), k)
+    torch.cuda.synchronize()
+    ih = idx.cpu().numpy()
+    for i, r in enumerate(rows):
+        tl.check_topk_same_array(ih[i], np.asarray(r, np.float32), k, "edge row %d (n=%d)" % (i, len(r)))
+
+
+@pytest.mark.parametrize("n", [1, 2, 2047, 2048, 2049, 4096, 4097, 9000, 70000])
+def test_topk_sizes_random(n):
+    rng = np.random.default_rng(n)
+    _topk_rows([rng.standard_normal(n).astype(np.float32) * 8])
+
+
+def test_topk_ties_and_signed_zeros():
+    rng = np.random.default_rng(7)
+    rows = [
+        np.full(5000, 1.5, np.float32),                                   # all equal: tie path
+        np.where(rng.random(6000) < 0.5, -0.0, 0.0).astype(np.float32),   # only signed zeros
+        rng.integers(-3, 4, 50000).astype(np.float32),                    # 7 distinct values
+        np.round(rng.standard_normal(30000), 1).astype(np.float32),       # heavy ties
+        np.sort(rng.standard_normal(10000)).astype(np.float32),           # ascending
+        -np.sort(-rng.standard_normal(10000)).astype(np.float32),         # descending
+        np.concatenate([np.full(3000, -np.inf), rng.standard_normal(3000)]).astype(np.float32),
+    ]
+    _topk_rows(rows)
+
+
+def test_topk_small_k_and_wide_ld():
+    rng = np.random.default_rng(9)
+    rows = [rng.standard_normal(n).astype(np.float32) for n in (100, 5000, 33000)]
+    for k in (1, 7, 64, 1000):
+        _topk_rows(rows, k=k)
+
+
+# ------------------------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("cfg,rows", [(2, [0, 7]), (3, [0, 33, 63]), (4, [0, 2047, 4095]), (5, [0, 31])])
+def test_full_size_workload_sampled_rows(cfg, rows):
+    case = synth.config(cfg, DEV)
+    scores, idx, outs, _ = tl.gpu_path(case)
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=rows)
+    del case, scores, idx, outs
+    torch.cuda.empty_cache()
