@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA decode path (indexer -> top-2048 -> sparse MLA) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|ragged|prefill|share]
+
+One step = one pass of the whole path over one batch of synthetic input.  The default
+workload is the GLM-5.2 layer decode (batch 8, context 8192, 32x128 fp8 index cache,
+top-2048, 64-head sparse MLA over bf16 latent rows).  Its working set fits in the 256 MB
+Infinity Cache, so the timed loop rotates over enough independent input sets (> 1 GB in
+total) that every step reads HBM.  Rank 0 prints one JSON line.
+
+Timing: W untimed steps, then exactly K steps between two device synchronisations.  A
+second loop of K steps records HIP events around each stage on the stream the kernels run
+on (torch's current stream) to get every kernel's average duration; the roofline object is
+reported for the kernel with the largest share of the step.  The CPU baseline is the fp64
+oracle on the host cores, on the same input bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+WORKLOADS = {"decode": 2, "ragged": 3, "prefill": 4, "share": 5}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough for > 1 GB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------------------- byte models
+
+def algorithmic_model(case):
+    """Algorithmic bytes / flops per stage for one step (the score round trip excluded from
+    the path total; it is the top-k kernel's own input and is counted for that kernel)."""
+    n = [case.ctx[b] - case.q_len[b] + j + 1 for b in range(case.B) for j in range(case.q_len[b])]
+    sum_n = float(sum(n))
+    T = case.T
+    H_I, D_I = case.H_I, case.D_I
+    q_bytes = {"f32": 4, "bf16": 2, "fp8": 1}[case.iq_dt]
+    k_row = D_I * {"f32": 4, "bf16": 2, "fp8": 1}[case.ik_dt] + (4 if case.ik_scale is not None else 0)
+    idx_bytes = sum_n * k_row + T * H_I * (D_I * q_bytes + 4 + (4 if case.iq_scale is not None else 0))
+    idx_flops = 2.0 * H_I * D_I * sum_n
+    sel = [min(case.topk, x) for x in n]
+    topk_bytes = sum_n * 4 + T * case.topk * 4
+    Dqk = case.Dc + case.Dr
+    L = len(case.layers)
+    kv_row = Dqk * {"f32": 4, "bf16": 2, "fp8": 1}[case.layers[0].kv_dt]
+    qb = {"f32": 4, "bf16": 2}[str(case.layers[0].q.dtype).split(".")[-1].replace("float32", "f32").replace("bfloat16", "bf16")]
+    ob = 4 if case.out_dt == "f32" else 2
+    mla_bytes = L * (sum(sel) * kv_row + T * case.H * (Dqk * qb + case.Dc * ob) + T * case.topk * 4)
+    mla_flops = L * 2.0 * case.H * sum(sel) * (Dqk + case.Dc)
+    return {
+        "indexer": {"bytes": idx_bytes, "flops": idx_flops},
+        "topk": {"bytes": topk_bytes, "flops": 0.0},
+        "mla": {"bytes": mla_bytes, "flops": mla_flops},
+        "path_bytes": idx_bytes + T * case.topk * 4 + mla_bytes,
+    }
+
+
+# ------------------------------------------------------------------------------- GPU bench
+
+def make_sets(cfg, nsets, device):
+    from deepseek_sparse_mla_amd import synth
+    return [synth.config(cfg, device=device, seed=s) for s in range(nsets)]
+
+
+def case_bytes(case):
+    tot = 0
+    for t in (case.iq, case.iw, case.ik, case.ik_scale, case.iq_scale):
+        if t is not None:
+            tot += t.numel() * t.element_size()
+    for L in case.layers:
+        tot += L.q.numel() * L.q.element_size() + L.kv.numel() * L.kv.element_size()
+    return tot
+
+
+class Runner:
+    """Buffers and calls of one input set (all allocations happen before timing)."""
+
+    def __init__(self, case):
+        import torch
+        import deepseek_sparse_mla_amd as dsa
+        self.dsa = dsa
+        self.case = case
+        self.layout = dsa.Layout.of_case(case)
+        dev = case.iq.device
+        self.ld = case.max_ctx
+        self.scores = torch.empty((case.T, self.ld), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((case.T, case.topk), dtype=torch.int32, device=dev)
+        odt = torch.float32 if case.out_dt == "f32" else torch.bfloat16
+        self.outs = [torch.empty((case.T, case.H, case.Dc), dtype=odt, device=dev) for _ in case.layers]
+        self.ws = dsa.mla_workspace(self.layout, case.H, case.Dc, case.Dr, case.topk, len(case.layers), dev)
+        self.prefill = case.q_indptr is not None
+
+    def indexer(self):
+        c = self.case
+        self.dsa.dsa_index_scores(self.layout, c.iq, c.iw, c.ik, k_scale=c.ik_scale, q_scale=c.iq_scale,
+                                  scores=self.scores)
+
+    def topk(self):
+        self.dsa.dsa_topk(self.layout, self.scores, self.case.topk, indices=self.idx)
+
+    def mla(self):
+        c = self.case
+        if len(c.layers) == 1:
+            L = c.layers[0]
+            fn = self.dsa.sparse_mla_prefill if self.prefill else self.dsa.sparse_mla_decode
+            fn(self.layout, L.q, L.kv, self.idx, c.sm_scale, c.Dc, L.kv_scale, out=self.outs[0],
+               workspace=self.ws)
+        else:
+            self.dsa.sparse_mla_decode_shared(self.layout, [L.q for L in c.layers], [L.kv for L in c.layers],
+                                              [L.kv_scale for L in c.layers], self.idx, c.sm_scale, c.Dc,
+                                              outs=self.outs, workspace=self.ws)
+
+    def step(self):
+        self.indexer()
+        self.topk()
+        self.mla()
+
+
+def cpu_baseline(case, target_s):
+    """Time the fp64 oracle on the host for whole query rows of the same workload."""
+    import numpy as np
+    import oracle
+    from deepseek_sparse_mla_amd import synth
+
+    kvp = synth.host(case.kv_indptr)
+    qi = synth.host(case.q_indptr)
+    idx_in = dict(q=synth.host(case.iq), w=synth.host(case.iw), k=synth.host(case.ik),
+                  k_scale=synth.host(case.ik_scale), q_scale=synth.host(case.iq_scale))
+    layers = [dict(q=synth.host(L.q), kv=synth.host(L.kv), kv_scale=L.kv_scale) for L in case.layers]
+    oracle.build()
+    rows_done = 0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.index_share(kvp, qi, idx_in, layers, case.topk, case.sm_scale, case.Dc)
+        rows_done += case.T
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    threads = oracle.num_threads()
+    return {"value": rows_done / el, "unit": "query-tokens/s", "cores": int(min(threads, case.T)),
+            "kind": "oracle",
+            "sample": "%d full passes of the %s batch (%d query rows each: indexer + top-%d + sparse MLA, "
+                      "fp64) in %.1f s on %d host threads (%d usable: OpenMP over query rows)"
+                      % (reps, case.name, case.T, case.topk, el, threads, min(threads, case.T))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from deepseek_sparse_mla_amd import synth  # noqa: F401
+
+    cfg = WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    probe = make_sets(cfg, 1, dev)[0]
+    per_set = case_bytes(probe)
+    nsets = args.sets or max(1, min(16, math.ceil(1.2e9 / per_set)))
+    cases = [probe] + (make_sets(cfg, nsets, dev)[1:] if nsets > 1 else [])
+    runners = [Runner(c) for c in cases]
+    model = algorithmic_model(probe)
+    torch.cuda.synchronize()
+
+    # warmup
+    for s in range(args.warmup):
+        runners[s % nsets].step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        runners[s % nsets].step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # per-kernel durations with HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    stages = ("indexer", "topk", "mla")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        r = runners[s % nsets]
+        e = ev[s]
+        e[0].record(stream)
+        r.indexer()
+        e[1].record(stream)
+        r.topk()
+        e[2].record(stream)
+        r.mla()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    dur = {st: sum(ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(args.steps)) / args.steps
+           for k, st in enumerate(stages)}  # ms
+
+    T = probe.T
+    value = T * args.steps / elapsed
+    dominant = max(stages, key=lambda st: dur[st])
+    st_model = model[dominant]
+    prefill = probe.q_indptr is not None
+    if dominant == "indexer" and prefill:
+        bound, unit, peak = "mfma", "TFLOP/s", FP8_PEAK_TFLOPS
+        achieved = st_model["flops"] / (dur[dominant] * 1e-3) / 1e12
+    elif dominant == "mla" and prefill:
+        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+        achieved = st_model["flops"] / (dur[dominant] * 1e-3) / 1e12
+    else:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = st_model["bytes"] / (dur[dominant] * 1e-3) / 1e9
+    kernel_names = {"indexer": "idx_fp8_kernel" if prefill else "idx_decode_kernel", "topk": "topk_kernel",
+                    "mla": "mla_kernel"}
+    path_gbs = model["path_bytes"] / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": "decode query-tokens/s (indexer+top-2048+sparse MLA) and % of peak HBM GB/s",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": probe.name, "batch": probe.B, "query_rows": T, "context": probe.ctx[0] if len(set(probe.ctx)) == 1 else "ragged",
+                   "index_heads": probe.H_I, "index_dim": probe.D_I, "topk": probe.topk, "mla_heads": probe.H,
+                   "latent": probe.Dc, "rope": probe.Dr, "kv_cache": probe.layers[0].kv_dt,
+                   "layers": len(probe.layers), "input_sets_rotated": nsets},
+        "path_hbm": {"algorithmic_bytes": model["path_bytes"], "achieved_GBps": round(path_gbs, 1),
+                     "frac_of_peak": round(path_gbs / HBM_PEAK_GBS, 4)},
+        "kernels_ms": {kernel_names[s]: round(dur[s], 5) for s in stages},
+        "roofline": {"kernel": kernel_names[dominant], "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "algorithmic": st_model["bytes"] if bound == "hbm" else st_model["flops"],
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(probe, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

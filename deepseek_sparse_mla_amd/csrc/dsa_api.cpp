@@ -161,6 +161,9 @@ dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_
     }
     if (!aligned(indices, 4))
         return fail(DSA_ERR_INVALID_ARG, "indices must be 4-byte aligned");
+    if (tuned && L->max_ctx * (int64_t)(a.Dc + a.Dr) * elem_size(a.kv_dt) > (int64_t)INT32_MAX)
+        return fail(DSA_ERR_UNSUPPORTED, "max_ctx %lld too long for 32-bit row offsets of the tuned kernel",
+                    (long long)L->max_ctx);
     const int64_t T = L->total_q;
     size_t need = tuned ? dsa::mla_workspace_bytes(T, n_layers, a.k) : 0;
     if (need > 0 && (!workspace || ws_bytes < need))

@@ -18,8 +18,12 @@
 //    swap and one LDS exchange with the partner wave;
 //  * O^T[dims x heads] += V^T . P^T, V^T read straight from the row-major tile with
 //    ds_read_b64_tr_b16 (4 consecutive keys of one dim per lane);
-//  * with several splits per row, partial (O, m, l) go to the workspace and the last block
-//    to finish (integer counter) combines them in split order -- deterministic.
+//  * softmax reference: each head's reference max is fixed at its first non-empty tile and
+//    never moves, so the accumulators are never rescaled; a split whose later logits
+//    exceed the reference by more than 2^100 is rerun with the exact maximum (exact
+//    either way, because l and O share the reference);
+//  * with several splits per row, partial (O, m, l) go to the workspace and a second
+//    kernel combines them in split order -- deterministic.
 // Generic kernel: any H <= 128, Dc <= 512, Dqk <= 1024, fp32 everywhere, two passes.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
@@ -34,6 +38,7 @@ constexpr int M_ROWB = 1168;               // LDS row stride in bytes (1152 + 16
 constexpr int M_TILEB = M_TILE * M_ROWB;   // 74752 B per tile buffer
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr int BUF_DWORD3 = 0x00020000;     // buffer descriptor word 3 for the gfx9 family
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -44,39 +49,49 @@ __device__ __forceinline__ s16x4 lds_tr16(const char *lds_generic_ptr)
             (__attribute__((address_space(3))) char *)(lds_generic_ptr)));
 }
 
+constexpr int M_THREADS = 256;             // 4 waves, one per SIMD (512 registers each)
+
 template <bool KV_FP8>
 struct StageRegs {
-    static constexpr int N = KV_FP8 ? 9 : 18;   // 16-byte pieces per thread per tile
+    static constexpr int PIECES = KV_FP8 ? 36 : 72;           // 16-byte pieces per row in HBM
+    static constexpr int TOTAL = M_TILE * PIECES;            // per tile
+    static constexpr int N = (TOTAL + M_THREADS - 1) / M_THREADS;
     u32x4 v[N];
 };
 
-// Issue the global loads of one tile (rows given by sidx) into registers.
+// Issue the gathers of one tile (rows given by sidx) into registers.  `seq` is a buffer
+// resource over the sequence's rows, so offsets are 32-bit and an index of -1 (or any
+// row past the visible count) reads as zeros.
 template <bool KV_FP8>
-__device__ __forceinline__ void stage_load(StageRegs<KV_FP8> &R, const uint8_t *__restrict__ kv,
-                                           int64_t kv_base, const int32_t *sidx, int tid)
+__device__ __forceinline__ void stage_load(StageRegs<KV_FP8> &R, __amdgpu_buffer_rsrc_t seq,
+                                           const int32_t *sidx, int tid)
 {
-    constexpr int PIECES = KV_FP8 ? 36 : 72;    // 16-byte pieces per row
+    typedef StageRegs<KV_FP8> SR;
     constexpr int ROWB = KV_FP8 ? 576 : 1152;   // bytes per row in HBM
 #pragma unroll
-    for (int u = 0; u < R.N; ++u) {
-        const int c = tid + 256 * u;
-        const int row = c / PIECES, col = c % PIECES;
-        const int32_t idx = sidx[row];
-        if (idx >= 0)
-            R.v[u] = *(const u32x4 *)(kv + (kv_base + idx) * ROWB + col * 16);
-        else
+    for (int u = 0; u < SR::N; ++u) {
+        const int c = tid + M_THREADS * u;
+        if (SR::TOTAL % M_THREADS == 0 || c < SR::TOTAL) {
+            const int row = c / SR::PIECES, col = c % SR::PIECES;
+            const int32_t off = sidx[row] * ROWB + col * 16;
+            R.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, off, 0, 0));
+        } else {
             R.v[u] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
 }
 
+// Write the staged registers to the LDS tile (fp8 widened exactly to bf16).
 template <bool KV_FP8>
 __device__ __forceinline__ void stage_store(const StageRegs<KV_FP8> &R, char *tile, int tid)
 {
-    constexpr int PIECES = KV_FP8 ? 36 : 72;
+    typedef StageRegs<KV_FP8> SR;
 #pragma unroll
-    for (int u = 0; u < R.N; ++u) {
-        const int c = tid + 256 * u;
-        const int row = c / PIECES, col = c % PIECES;
+    for (int u = 0; u < SR::N; ++u) {
+        const int c = tid + M_THREADS * u;
+        if (SR::TOTAL % M_THREADS != 0 && c >= SR::TOTAL)
+            continue;
+        const int row = c / SR::PIECES, col = c % SR::PIECES;
         if (KV_FP8) {
             u32x4 lo, hi;
             lo[0] = fp8x2_to_bf16x2<false>(R.v[u][0]);
@@ -96,43 +111,63 @@ __device__ __forceinline__ void stage_store(const StageRegs<KV_FP8> &R, char *ti
     }
 }
 
-template <bool KV_FP8, bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void mla_kernel(LayoutDev L, int64_t T, MlaLayersDev layers,
-                                                     const int32_t *__restrict__ indices, int k,
-                                                     float sm_scale, int nsplit, int tiles_per_split,
-                                                     float *__restrict__ ws_o,
-                                                     float *__restrict__ ws_ml,
-                                                     int *__restrict__ ws_cnt)
+// Block -> (output row, split).  The (row, split) pairs are cut into 8 contiguous ranges,
+// one per XCD (blocks are dispatched to the 8 XCDs round-robin), so all splits of a row
+// -- which share the row's q -- and neighbouring rows -- which share many gathered
+// latent rows -- run under one L2.
+__device__ __forceinline__ int64_t xcd_pair(int64_t pairs_per_xcd)
 {
-    __shared__ __attribute__((aligned(16))) char kt[2][M_TILEB];
-    __shared__ __attribute__((aligned(16))) u32x4 xch_p[4][64][2];   // P^T exchange (bf16)
-    __shared__ float xch_m[4][32], xch_l[4][32];
-    __shared__ int32_t sidx[2][M_TILE];
-    __shared__ int sh_last;
+    const int64_t b = blockIdx.x;
+    return (b & 7) * pairs_per_xcd + (b >> 3);
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+//
+// Wave w of the block: hh = w & 1 owns heads 32*hh .. +31 and dq = w >> 1 owns half of the
+// 576-long contraction for S and half of the 512 output dims for O.
+//   S^T partial [64 keys x 32 heads] = K . Q^T over 288 dims (2 x 18 MFMA 32x32x16);
+//   the two partials of a head half meet in LDS (dq 0 + dq 1, in that order, in both
+//   waves), each wave then runs the online softmax for its 32 heads over the 64 keys;
+//   O^T [256 dims x 32 heads] += V^T . P^T (32 MFMA), V^T read with ds_read_b64_tr_b16.
+//
+template <bool KV_FP8, bool OUT_F32>
+__global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t T, int64_t n_rows,
+                                                           MlaLayersDev layers,
+                                                           const int32_t *__restrict__ indices, int k,
+                                                           float sm_scale, int nsplit, int tiles_per_split,
+                                                           int64_t pairs_per_xcd, float *__restrict__ ws_o,
+                                                           float *__restrict__ ws_ml)
+{
+    __shared__ __attribute__((aligned(16))) char kt[M_TILEB];
+    __shared__ __attribute__((aligned(16))) f32x4 xs[4][8][64];  // S^T partials [wave][q][lane]
+    __shared__ int32_t sidx[2][M_TILE];
+    __shared__ int sh_flag;
+
+    const int64_t pair = xcd_pair(pairs_per_xcd);
+    if (pair >= n_rows * nsplit)
+        return;
+    const int64_t orow = pair / nsplit;
+    const int split = (int)(pair % nsplit);
+    const int layer = (int)(orow / T);
+    const int64_t i = orow % T;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 5, j = lane & 31;
-    const int hh = wave & 1, kh = wave >> 1;  // head half; key half (S) and dim half (O)
-    const int partner = wave ^ 2;
-    const int split = blockIdx.x;
-    const int64_t i = blockIdx.y;
-    const int layer = blockIdx.z;
+    const int hh = w & 1, dq = w >> 1;
     const MlaLayerDev Ld = layers.l[layer];
     const RowInfo r = row_info(L, i);
     const float c2 = sm_scale * Ld.kv_scale * LOG2E;
 
     const int ntiles_all = (k + M_TILE - 1) / M_TILE;
     const int t_begin = split * tiles_per_split;
-    const int t_end = min(ntiles_all, t_begin + tiles_per_split);
-    const int ntiles = max(0, t_end - t_begin);
+    const int ntiles = max(0, min(ntiles_all, t_begin + tiles_per_split) - t_begin);
     const int32_t *irow = indices + i * k;
 
-    // ---- Q^T operand: head 32*hh + j, dims 16t + 8g .. +7
-    bf16x8 qT[36];
+    // Q^T operand: head 32*hh + j, dims 288*dq + 16t + 8g .. +7 (t < 18)
+    bf16x8 qT[18];
     {
-        const uint16_t *qp = (const uint16_t *)Ld.q + ((i * M_H + 32 * hh + j) * M_DQK + 8 * g);
+        const uint16_t *qp = (const uint16_t *)Ld.q + ((i * M_H + 32 * hh + j) * M_DQK + 288 * dq + 8 * g);
 #pragma unroll
-        for (int t = 0; t < 36; ++t)
+        for (int t = 0; t < 18; ++t)
             qT[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * t));
     }
 
@@ -140,225 +175,274 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(LayoutDev L, int64_t T, Mla
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
         O[mt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
 
     auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
         const int slot = (t_begin + tt) * M_TILE + tid;
         return (tt < ntiles && slot < k) ? irow[slot] : -1;
     };
-
-    // ---- prologue: indices of tiles 0, 1; tile 0 staged
-    if (tid < M_TILE) {
-        sidx[0][tid] = load_idx(0);
-        sidx[1][tid] = load_idx(1);
-    }
-    int32_t idx_next = tid < M_TILE ? load_idx(2) : -1;
-    __syncthreads();
     StageRegs<KV_FP8> R;
-    const uint8_t *kvb = (const uint8_t *)Ld.kv;
-    if (ntiles > 0) {
-        stage_load<KV_FP8>(R, kvb, r.kv_base, sidx[0], tid);
-        stage_store<KV_FP8>(R, kt[0], tid);
-    }
-    __syncthreads();
+    constexpr int64_t ROWB = KV_FP8 ? 576 : 1152;
+    const int64_t seq_bytes = r.n * ROWB;  // host guarantees max_ctx * ROWB < 2^31
+    const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const uint8_t *)Ld.kv + r.kv_base * ROWB), (short)0, (int)seq_bytes, BUF_DWORD3);
 
-    for (int tt = 0; tt < ntiles; ++tt) {
-        const int buf = tt & 1;
-        const char *tile = kt[buf];
-        if (tt + 1 < ntiles)
-            stage_load<KV_FP8>(R, kvb, r.kv_base, sidx[buf ^ 1], tid);
-
-        const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
-
-        // ---- S^T = K . Q^T for this wave's 32 keys x 32 heads
-        f32x16 s = {};
-        {
-            const char *arow = tile + (32 * kh + j) * M_ROWB + 16 * g;
-#pragma unroll
-            for (int t = 0; t < 36; ++t) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(arow + 32 * t));
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qT[t], s, 0, 0, 0);
-            }
+    // Pass 0 fixes each head's reference max at its first non-empty tile.  If a later
+    // tile exceeds it by more than 2^100 (p would approach the fp32 range) the split is
+    // run again with the exact maximum observed in pass 0 as the reference.
+    float m_seen = -INFINITY;
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+            if (!sh_flag)
+                break;
+            m_ref = m_seen;
+            l_run = 0.f;
         }
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int key = 32 * kh + 8 * (rr >> 2) + 4 * g + (rr & 3);
-            const float z = ((valid >> key) & 1ull) ? s[rr] * c2 : -INFINITY;
-            s[rr] = z;
-            mloc = fmaxf(mloc, z);
-        }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        if (g == 0)
-            xch_m[wave][j] = mloc;
+        bool ovf = false;
         __syncthreads();
-        const float m_tile = fmaxf(mloc, xch_m[partner][j]);
-        const float m_new = fmaxf(m_run, m_tile);
-        float alpha, lloc = 0.f;
-        uint32_t pk[8];
-        if (m_new == -INFINITY) {
-            alpha = 1.f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                pk[q] = 0u;
-        } else {
-            alpha = exp2f(m_run - m_new);
-            float p[16];
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                p[rr] = exp2f(s[rr] - m_new);
-                lloc += p[rr];
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                pk[q] = pack_bf16x2(p[2 * q], p[2 * q + 1]);
-        }
-        lloc += __shfl_xor(lloc, 32, 64);
-        xch_p[wave][lane][0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        xch_p[wave][lane][1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-        if (g == 0)
-            xch_l[wave][j] = lloc;
-        __syncthreads();
-        const u32x4 pp0 = xch_p[partner][lane][0], pp1 = xch_p[partner][lane][1];
-        const float lpart = xch_l[partner][j];
-        l_run = l_run * alpha + (kh == 0 ? (lloc + lpart) : (lpart + lloc));
-        m_run = m_new;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-                O[mt][rr] *= alpha;
-
-        // ---- O^T += V^T . P^T over the 64 keys (4 steps of 16)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int khu = u >> 1, jj = u & 1;
-            u32x4 bw;
-            if (khu == kh)
-                bw = (jj == 0) ? u32x4{pk[0], pk[1], pk[2], pk[3]} : u32x4{pk[4], pk[5], pk[6], pk[7]};
-            else
-                bw = (jj == 0) ? pp0 : pp1;
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-            const int key0 = 32 * khu + 16 * jj + 4 * g + ((lane & 15) >> 2);
-            const char *p0 = tile + key0 * M_ROWB;
-            const char *p1 = p0 + 8 * M_ROWB;
-            const int dcol = 256 * kh + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const int boff = 2 * (dcol + 32 * mt);
-                const s16x4 lo = lds_tr16(p0 + boff);
-                const s16x4 hi = lds_tr16(p1 + boff);
-                typedef short s16x8 __attribute__((ext_vector_type(8)));
-                const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), bop,
-                                                                O[mt], 0, 0, 0);
-            }
-        }
-
-        if (tt + 1 < ntiles)
-            stage_store<KV_FP8>(R, kt[buf ^ 1], tid);
         if (tid < M_TILE) {
-            sidx[buf][tid] = idx_next;  // tile tt + 2
-            idx_next = load_idx(tt + 3);
+            sidx[0][tid] = load_idx(0);
+            sidx[1][tid] = load_idx(1);
         }
+        if (tid == 0)
+            sh_flag = 0;
+        int32_t idx_next = tid < M_TILE ? load_idx(2) : -1;
+        __syncthreads();
+        if (ntiles > 0) {
+            stage_load<KV_FP8>(R, seq, sidx[0], tid);
+            stage_store<KV_FP8>(R, kt, tid);
+        }
+        __syncthreads();
+
+        for (int tt = 0; tt < ntiles; ++tt) {
+            const int buf = tt & 1;
+            if (tt + 1 < ntiles)
+                stage_load<KV_FP8>(R, seq, sidx[buf ^ 1], tid);
+            const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
+            const bool restart = (pass == 1 && tt == 0);
+            // ---- S^T partials for keys 0..31 (S[0]) and 32..63 (S[1]) over this wave's dims;
+            // operands are read three k-steps ahead of the MFMAs that use them.
+            f32x16 S[2] = {f32x16{}, f32x16{}};
+            {
+                const char *arow = kt + j * M_ROWB + 2 * (288 * dq + 8 * g);
+                u32x4 A[2][3][2];
+    #pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    A[0][t][0] = *(const u32x4 *)(arow + 32 * t);
+                    A[0][t][1] = *(const u32x4 *)(arow + 32 * M_ROWB + 32 * t);
+                }
+    #pragma unroll
+                for (int c = 0; c < 6; ++c) {
+                    const int cur = c & 1;
+                    if (c + 1 < 6) {
+    #pragma unroll
+                        for (int t = 0; t < 3; ++t) {
+                            const int tn = 3 * (c + 1) + t;
+                            A[cur ^ 1][t][0] = *(const u32x4 *)(arow + 32 * tn);
+                            A[cur ^ 1][t][1] = *(const u32x4 *)(arow + 32 * M_ROWB + 32 * tn);
+                        }
+                    }
+    #pragma unroll
+                    for (int t = 0; t < 3; ++t) {
+                        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[cur][t][0]),
+                                                                       qT[3 * c + t], S[0], 0, 0, 0);
+                        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[cur][t][1]),
+                                                                       qT[3 * c + t], S[1], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+    #pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+    #pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    xs[w][4 * kk + q4][lane] = f32x4{S[kk][4 * q4], S[kk][4 * q4 + 1], S[kk][4 * q4 + 2], S[kk][4 * q4 + 3]};
+            __syncthreads();
+            const int wp = w ^ 2;  // same heads, other half of the contraction
+    #pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+    #pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 o = xs[wp][4 * kk + q4][lane];
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[kk][4 * q4 + e] = (dq == 0) ? S[kk][4 * q4 + e] + o[e] : o[e] + S[kk][4 * q4 + e];
+                }
+
+            // ---- online softmax over the 64 keys of the tile for head 32*hh + j
+            float mloc = -INFINITY;
+    #pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+    #pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int key = 32 * kk + 8 * (rr >> 2) + 4 * g + (rr & 3);
+                    const float z = ((valid >> key) & 1ull) ? S[kk][rr] * c2 : -INFINITY;
+                    S[kk][rr] = z;
+                    mloc = fmaxf(mloc, z);
+                }
+            const float m_tile = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            m_seen = fmaxf(m_seen, m_tile);
+            if (m_ref == -INFINITY)
+                m_ref = m_tile;  // first non-empty tile: O and l are still zero
+            ovf |= m_tile > m_ref + 100.f;
+            float lt = 0.f;
+            uint32_t pk[2][8];
+    #pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+    #pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float p0 = (m_ref == -INFINITY) ? 0.f : exp2f(S[kk][2 * q] - m_ref);
+                    const float p1 = (m_ref == -INFINITY) ? 0.f : exp2f(S[kk][2 * q + 1] - m_ref);
+                    lt += p0 + p1;
+                    pk[kk][q] = pack_bf16x2(p0, p1);
+                }
+            lt += __shfl_xor(lt, 32, 64);
+            l_run += lt;
+
+            // ---- O^T += V^T . P^T over the 64 keys (4 steps of 16 keys); the transposed V
+            // operands of step u + 1 are read while step u's MFMAs run.
+            {
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const int dcol = 256 * dq + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                const char *vbase = kt + (4 * g + ((lane & 15) >> 2)) * M_ROWB + 2 * dcol;
+                s16x4 V[2][8][2];
+    #pragma unroll
+                for (int mt = 0; mt < 8; ++mt) {
+                    V[0][mt][0] = lds_tr16(vbase + 64 * mt);
+                    V[0][mt][1] = lds_tr16(vbase + 8 * M_ROWB + 64 * mt);
+                }
+    #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int cur = u & 1;
+                    if (u + 1 < 4) {
+                        const int un = u + 1;
+                        const char *vb = vbase + (32 * (un >> 1) + 16 * (un & 1)) * M_ROWB;
+    #pragma unroll
+                        for (int mt = 0; mt < 8; ++mt) {
+                            V[cur ^ 1][mt][0] = lds_tr16(vb + 64 * mt);
+                            V[cur ^ 1][mt][1] = lds_tr16(vb + 8 * M_ROWB + 64 * mt);
+                        }
+                    }
+                    const int khu = u >> 1, jj = u & 1;
+                    const bf16x8 bop = __builtin_bit_cast(
+                        bf16x8, u32x4{pk[khu][4 * jj], pk[khu][4 * jj + 1], pk[khu][4 * jj + 2], pk[khu][4 * jj + 3]});
+    #pragma unroll
+                    for (int mt = 0; mt < 8; ++mt) {
+                        const s16x4 lo = V[cur][mt][0], hi = V[cur][mt][1];
+                        const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        if (restart && u == 0)  // first MFMA of a rerun: drop pass 0's sums
+                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), bop,
+                                                                            f32x16{}, 0, 0, 0);
+                        else
+                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), bop,
+                                                                            O[mt], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __syncthreads();  // tile and S partials fully consumed
+            if (tt + 1 < ntiles)
+                stage_store<KV_FP8>(R, kt, tid);
+            if (tid < M_TILE) {
+                sidx[buf][tid] = idx_next;  // tile tt + 2
+                idx_next = load_idx(tt + 3);
+            }
+            __syncthreads();
+        }
+        if (ovf)
+            sh_flag = 1;
         __syncthreads();
     }
 
-    // ---- epilogue
-    const int64_t orow = (int64_t)layer * T + i;
+    // ---- epilogue: wave owns dims 256*dq + 32*mt + 8*q4 + 4*g + 0..3 of head 32*hh + j
     const int head = 32 * hh + j;
     if (nsplit == 1) {
         const float inv = (l_run > 0.f) ? Ld.kv_scale / l_run : 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 256 * kh + 32 * mt + 8 * q4 + 4 * g;
+                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
                 const int64_t o = (i * M_H + head) * M_DC + d;
-                if (OUT_F32) {
-                    *(f32x4 *)((float *)Ld.out + o) =
-                        f32x4{O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv, O[mt][4 * q4 + 2] * inv,
-                              O[mt][4 * q4 + 3] * inv};
-                } else {
-                    *(u32x2 *)((uint16_t *)Ld.out + o) =
-                        u32x2{pack_bf16x2(O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv),
-                              pack_bf16x2(O[mt][4 * q4 + 2] * inv, O[mt][4 * q4 + 3] * inv)};
-                }
+                const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
+                const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
+                if (OUT_F32)
+                    *(f32x4 *)((float *)Ld.out + o) = f32x4{v0, v1, v2, v3};
+                else
+                    *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
             }
-        }
-        if (Ld.lse && kh == 0 && g == 0)
-            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+        if (Ld.lse && dq == 0 && g == 0)
+            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
         return;
     }
-
-    // several splits: write the partial, count, and let the last block combine
     float *po = ws_o + ((orow * nsplit + split) * M_H + head) * M_DC;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 256 * kh + 32 * mt + 8 * q4 + 4 * g;
+            const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
             *(f32x4 *)(po + d) = f32x4{O[mt][4 * q4], O[mt][4 * q4 + 1], O[mt][4 * q4 + 2], O[mt][4 * q4 + 3]};
         }
-    if (kh == 0 && g == 0) {
+    if (dq == 0 && g == 0) {
         float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
-        pml[0] = m_run;
+        pml[0] = m_ref;
         pml[1] = l_run;
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const int old = atomicAdd(&ws_cnt[orow], 1);
-        sh_last = (old == nsplit - 1);
-    }
-    __syncthreads();
-    if (!sh_last)
-        return;
-    __threadfence();
+}
 
-    // combine weights per (split, head) into LDS (the tile buffers are free now)
-    float *wts = (float *)kt[0];          // [nsplit][64]
-    float *hstat = wts + nsplit * M_H;    // [64] lse
-    if (tid < M_H) {
-        const float *ml = ws_ml + (orow * nsplit * M_H + tid) * 2;
+// Combine the split partials of every (output row, group of 8 heads), in split order.
+constexpr int C_HEADS = 8;
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void mla_combine_kernel(int64_t T, MlaLayersDev layers, int nsplit,
+                                                          const float *__restrict__ ws_o,
+                                                          const float *__restrict__ ws_ml)
+{
+    __shared__ float wts[32][C_HEADS];
+    __shared__ float lse_s[C_HEADS];
+    const int64_t orow = blockIdx.x;
+    const int hg = blockIdx.y;
+    const int layer = (int)(orow / T);
+    const int64_t i = orow % T;
+    const MlaLayerDev Ld = layers.l[layer];
+    const int tid = threadIdx.x;
+    if (tid < C_HEADS) {
+        const int head = hg * C_HEADS + tid;
+        const float *ml = ws_ml + (orow * nsplit * M_H + head) * 2;
         float mx = -INFINITY;
         for (int sp = 0; sp < nsplit; ++sp)
             mx = fmaxf(mx, ml[sp * M_H * 2]);
         float tot = 0.f;
         for (int sp = 0; sp < nsplit; ++sp) {
-            const float ms = ml[sp * M_H * 2];
-            const float e = (mx == -INFINITY) ? 0.f : exp2f(ms - mx);
-            wts[sp * M_H + tid] = e;
+            const float e = (mx == -INFINITY) ? 0.f : exp2f(ml[sp * M_H * 2] - mx);
+            wts[sp][tid] = e;
             tot += e * ml[sp * M_H * 2 + 1];
         }
         const float inv = tot > 0.f ? Ld.kv_scale / tot : 0.f;
         for (int sp = 0; sp < nsplit; ++sp)
-            wts[sp * M_H + tid] *= inv;
-        hstat[tid] = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
+            wts[sp][tid] *= inv;
+        lse_s[tid] = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
     }
     __syncthreads();
-    const float *pbase = ws_o + orow * nsplit * M_H * M_DC;
-    for (int e4 = tid; e4 < M_H * M_DC / 4; e4 += 256) {
-        const int hd = (e4 * 4) / M_DC;
+    const float *pbase = ws_o + (orow * nsplit * M_H + hg * C_HEADS) * M_DC;
+    for (int e4 = tid; e4 < C_HEADS * M_DC / 4; e4 += 256) {
+        const int hl = (e4 * 4) / M_DC;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < nsplit; ++sp) {
             const f32x4 v = *(const f32x4 *)(pbase + (int64_t)sp * M_H * M_DC + e4 * 4);
-            const float wgt = wts[sp * M_H + hd];
+            const float wgt = wts[sp][hl];
             acc[0] = fmaf(wgt, v[0], acc[0]);
             acc[1] = fmaf(wgt, v[1], acc[1]);
             acc[2] = fmaf(wgt, v[2], acc[2]);
             acc[3] = fmaf(wgt, v[3], acc[3]);
         }
-        const int64_t o = i * M_H * M_DC + (int64_t)e4 * 4;
+        const int64_t o = (i * M_H + hg * C_HEADS) * M_DC + (int64_t)e4 * 4;
         if (OUT_F32)
             *(f32x4 *)((float *)Ld.out + o) = acc;
         else
             *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
     }
-    if (Ld.lse && tid < M_H)
-        Ld.lse[i * M_H + tid] = hstat[tid];
-    if (tid == 0)
-        ws_cnt[orow] = 0;  // leave the counter zeroed for the next call
+    if (Ld.lse && tid < C_HEADS)
+        Ld.lse[i * M_H + hg * C_HEADS + tid] = lse_s[tid];
 }
 
 // ------------------------------------------------------------------------------------------
@@ -451,6 +535,8 @@ int mla_num_splits(int64_t T, int k)
     int64_t ns = (MLA_TARGET_BLOCKS + T - 1) / T;
     if (ns > ntiles)
         ns = ntiles;
+    if (ns > 32)
+        ns = 32;
     if (ns < 1)
         ns = 1;
     const int tps = (ntiles + (int)ns - 1) / (int)ns;  // equal tiles per split
@@ -463,10 +549,9 @@ size_t mla_workspace_bytes(int64_t T, int n_layers, int k)
     if (ns <= 1)
         return 0;
     const size_t rows = (size_t)T * n_layers;
-    size_t cnt = (rows * sizeof(int) + 255) & ~(size_t)255;
     size_t o = rows * ns * M_H * M_DC * sizeof(float);
     size_t ml = rows * ns * M_H * 2 * sizeof(float);
-    return cnt + o + ml;
+    return o + ml;
 }
 
 hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &layers, int n_layers,
@@ -477,18 +562,17 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
     const int ns = mla_num_splits(T, k);
     const int ntiles = (k + M_TILE - 1) / M_TILE;
     const int tps = (ntiles + ns - 1) / ns;
-    int *cnt = nullptr;
     float *wo = nullptr, *wml = nullptr;
     if (ns > 1) {
-        size_t cntb = ((size_t)rows * sizeof(int) + 255) & ~(size_t)255;
-        cnt = (int *)workspace;
-        wo = (float *)((char *)workspace + cntb);
+        wo = (float *)workspace;
         wml = wo + (size_t)rows * ns * M_H * M_DC;
     }
-    dim3 grid((unsigned)ns, (unsigned)T, (unsigned)n_layers);
+    const int64_t pairs = rows * ns;
+    const int64_t ppx = (pairs + 7) / 8;
+    dim3 grid((unsigned)(8 * ppx));
 #define DSA_MLA_LAUNCH(F8, OF)                                                                   \
-    hipLaunchKernelGGL((mla_kernel<F8, OF>), grid, dim3(256), 0, stream, L, T, layers, indices, k, \
-                       sm_scale, ns, tps, wo, wml, cnt)
+    hipLaunchKernelGGL((mla_kernel<F8, OF>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,  \
+                       indices, k, sm_scale, ns, tps, ppx, wo, wml)
     if (kv_fp8) {
         if (out_f32)
             DSA_MLA_LAUNCH(true, true);
@@ -501,6 +585,14 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
             DSA_MLA_LAUNCH(false, false);
     }
 #undef DSA_MLA_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns == 1)
+        return e;
+    dim3 cgrid((unsigned)rows, M_H / C_HEADS);
+    if (out_f32)
+        hipLaunchKernelGGL((mla_combine_kernel<true>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml);
+    else
+        hipLaunchKernelGGL((mla_combine_kernel<false>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml);
     return hipGetLastError();
 }
 

@@ -161,10 +161,11 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
  *   indices, k    int32 [T][k] logical positions (< n_i) or -1.
  *   out           [T][H][D_c] of out_dt (F32 or BF16).
  *   lse           fp32 [T][H], or NULL.
- *   workspace     device scratch of sparse_mla_workspace_size() bytes.  Its
- *                 first use needs it zero-filled; every completed call leaves
- *                 it that way again, so calls on one stream may reuse it.
+ *   workspace     device scratch of sparse_mla_workspace_size() bytes (the
+ *                 split partials of the index list; none is needed when one
+ *                 block covers a whole row).  No initial contents are needed.
  *                 Calls that overlap in time must not share a workspace.
+ * The tuned kernel needs max_ctx * (D_c + D_r) * element size < 2^31.
  * The decode entry accepts any layout; prefill is the same computation with
  * a launch shape suited to many query rows per sequence.
  */

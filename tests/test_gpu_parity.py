@@ -195,3 +195,32 @@ def test_full_size_workload_sampled_rows(cfg, rows):
     _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=rows)
     del case, scores, idx, outs
     torch.cuda.empty_cache()
+
+
+def test_extreme_logit_spread_takes_exact_rerun():
+    """A late tile whose logit exceeds the first tile's maximum by far more than 2^100 (in
+    exp2 units) makes the tuned kernel rerun its split with the exact maximum; the output
+    must still match the oracle.  256 one-query sequences give one block per row, so all
+    32 tiles of the index list run in the same block."""
+    B, ctx, H, Dc, Dr = 256, 2048, 64, 512, 64
+    g = torch.Generator(device=DEV).manual_seed(123)
+    kv = torch.randn((B * ctx, Dc + Dr), generator=g, device=DEV)
+    q = torch.randn((B, H, Dc + Dr), generator=g, device=DEV)
+    for b in (0, 1):
+        kv[b * ctx:(b + 1) * ctx, 0] = 0.0
+        kv[b * ctx + 1500, 0] = 64.0
+        q[b, :, 0] = 64.0
+    kv = kv.to(torch.bfloat16)
+    q = q.to(torch.bfloat16)
+    kvp = torch.arange(0, (B + 1) * ctx, ctx, dtype=torch.int64, device=DEV)
+    layout = dsa.Layout(kvp, None, B, ctx)
+    idx = torch.arange(ctx, dtype=torch.int32, device=DEV).repeat(B, 1).contiguous()
+    lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    out = dsa.sparse_mla_decode(layout, q, kv, idx, 1.0 / 16, Dc, lse=lse)
+    torch.cuda.synchronize()
+    import oracle
+    for b in (0, 1, 2):
+        o, l = oracle.sparse_mla([0, ctx], None, synth.host(q[b:b + 1]), synth.host(kv[b * ctx:(b + 1) * ctx]),
+                                 idx[b:b + 1].cpu().numpy(), 1.0 / 16, Dc)
+        tl.check_attention(tl.to_f64(out[b]), o[0], tl.ATTN_ATOL_LOWP, "row %d" % b)
+        np.testing.assert_allclose(lse[b].cpu().numpy(), l[0], rtol=1e-4, atol=1e-3)
