@@ -109,6 +109,7 @@ class Runner:
         odt = torch.float32 if case.out_dt == "f32" else torch.bfloat16
         self.outs = [torch.empty((case.T, case.H, case.Dc), dtype=odt, device=dev) for _ in case.layers]
         self.ws = dsa.mla_workspace(self.layout, case.H, case.Dc, case.Dr, case.topk, len(case.layers), dev)
+        self.tk_ws = dsa.topk_workspace(self.layout, self.ld, case.topk, dev)
         self.prefill = case.q_indptr is not None
 
     def indexer(self):
@@ -117,7 +118,7 @@ class Runner:
                                   scores=self.scores)
 
     def topk(self):
-        self.dsa.dsa_topk(self.layout, self.scores, self.case.topk, indices=self.idx)
+        self.dsa.dsa_topk(self.layout, self.scores, self.case.topk, indices=self.idx, workspace=self.tk_ws)
 
     def mla(self):
         c = self.case

@@ -164,6 +164,12 @@ def dsa_topk_workspace_size(layout: Layout, ld: int, k: int) -> int:
     return int(load_library().dsa_topk_workspace_size(ctypes.byref(layout.c), int(ld), int(k)))
 
 
+def topk_workspace(layout: Layout, ld: int, k: int, device="cuda") -> Optional[torch.Tensor]:
+    """A zero-filled top-k workspace of the size the library asks for (None if none)."""
+    n = dsa_topk_workspace_size(layout, ld, k)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
 def dsa_topk(layout: Layout, scores: torch.Tensor, k: int, indices: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Top-k positions int32 [T, k] (score desc, position asc; -1 padding)."""
@@ -171,9 +177,8 @@ def dsa_topk(layout: Layout, scores: torch.Tensor, k: int, indices: Optional[tor
     T, ld = scores.shape
     if indices is None:
         indices = torch.empty((T, k), dtype=torch.int32, device=scores.device)
-    ws_need = dsa_topk_workspace_size(layout, ld, k)
-    if ws_need and workspace is None:
-        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=scores.device)
+    if workspace is None:
+        workspace = topk_workspace(layout, ld, k, scores.device)
     st = lib.dsa_topk(ctypes.byref(layout.c), _dev(scores, "scores", torch.float32), int(ld), int(k),
                       _dev(indices, "indices", torch.int32), _dev(workspace, "workspace"),
                       workspace.numel() if workspace is not None else 0, _stream(stream))

@@ -270,17 +270,16 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
 
 size_t dsa_topk_workspace_size(const dsa_layout *layout, int64_t ld, int k)
 {
-    (void)layout;
     (void)ld;
     (void)k;
-    return 0;
+    if (!layout || layout->total_q < 0)
+        return 0;
+    return dsa::topk_workspace_bytes(layout->total_q, layout->max_ctx);
 }
 
 dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, int k,
                     int32_t *indices, void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     dsa_status st = check_layout(layout);
     if (st != DSA_OK)
         return st;
@@ -293,10 +292,17 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
                     (long long)layout->max_ctx);
     if (!aligned(scores, 4) || !aligned(indices, 4))
         return fail(DSA_ERR_INVALID_ARG, "scores and indices must be 4-byte aligned");
+    const size_t need = dsa::topk_workspace_bytes(layout->total_q, layout->max_ctx);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(DSA_ERR_WORKSPACE, "top-k workspace of %zu bytes required, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 256))
+        return fail(DSA_ERR_WORKSPACE, "top-k workspace must be 256-byte aligned");
     const int64_t T = layout->total_q;
     if (T == 0)
         return ok();
-    return hip_status(dsa::launch_topk(to_dev(layout), T, scores, ld, k, indices, (hipStream_t)stream),
+    return hip_status(dsa::launch_topk(to_dev(layout), T, layout->max_ctx, scores, ld, k, indices, workspace,
+                                       (hipStream_t)stream),
                       "top-k launch");
 }
 

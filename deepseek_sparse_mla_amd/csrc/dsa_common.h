@@ -101,9 +101,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return u >> 16;
 }
 
+// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Element loaders used by the generic kernels.

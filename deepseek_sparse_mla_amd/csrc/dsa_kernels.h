@@ -36,8 +36,9 @@ hipError_t launch_index_generic(const LayoutDev &L, int64_t T, int64_t max_ctx, 
                                 int q_dt, const void *q, const float *qs, const float *w, int k_dt,
                                 const void *k, int64_t kstride, const float *ks, int64_t ks_stride,
                                 float *scores, int64_t ld, hipStream_t stream);
-hipError_t launch_topk(const LayoutDev &L, int64_t T, const float *scores, int64_t ld, int k,
-                       int32_t *indices, hipStream_t stream);
+size_t topk_workspace_bytes(int64_t T, int64_t max_ctx);
+hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const float *scores, int64_t ld,
+                       int k, int32_t *indices, void *workspace, hipStream_t stream);
 
 int mla_num_splits(int64_t T, int k);
 size_t mla_workspace_bytes(int64_t T, int n_layers, int k);

@@ -123,11 +123,15 @@ __device__ __forceinline__ int64_t xcd_pair(int64_t pairs_per_xcd)
 
 //
 // Wave w of the block: hh = w & 1 owns heads 32*hh .. +31 and dq = w >> 1 owns half of the
-// 576-long contraction for S and half of the 512 output dims for O.
-//   S^T partial [64 keys x 32 heads] = K . Q^T over 288 dims (2 x 18 MFMA 32x32x16);
-//   the two partials of a head half meet in LDS (dq 0 + dq 1, in that order, in both
-//   waves), each wave then runs the online softmax for its 32 heads over the 64 keys;
-//   O^T [256 dims x 32 heads] += V^T . P^T (32 MFMA), V^T read with ds_read_b64_tr_b16.
+// 576-long contraction for S, the keys 32*dq .. +31 of each tile for the softmax, and half
+// of the 512 output dims for O.  Per 64-row tile:
+//   1. S^T partials [64 keys x 32 heads] = K . Q^T over the wave's 288 dims (2 x 18 MFMA);
+//   2. the two waves of a head half swap the partial of each other's key half through LDS
+//      and add it (dq 0 + dq 1, in that order) -> full S^T for the wave's own 32 keys;
+//   3. online softmax on those 32 keys against the fixed reference, P packed to bf16 and
+//      swapped with the partner so both hold P^T for all 64 keys;
+//   4. O^T [256 dims x 32 heads] += V^T . P^T (32 MFMA), V^T read with ds_read_b64_tr_b16.
+// Each wave keeps the row sum l of its own keys; the pair adds theirs once at the end.
 //
 template <bool KV_FP8, bool OUT_F32>
 __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t T, int64_t n_rows,
@@ -138,7 +142,9 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                                                            float *__restrict__ ws_ml)
 {
     __shared__ __attribute__((aligned(16))) char kt[M_TILEB];
-    __shared__ __attribute__((aligned(16))) f32x4 xs[4][8][64];  // S^T partials [wave][q][lane]
+    __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
+    __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
+    __shared__ float xm[4][32];                                    // per-head stats swap
     __shared__ int32_t sidx[2][M_TILE];
     __shared__ int sh_flag;
 
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 5, j = lane & 31;
-    const int hh = w & 1, dq = w >> 1;
+    const int hh = w & 1, dq = w >> 1, wp = w ^ 2;
     const MlaLayerDev Ld = layers.l[layer];
     const RowInfo r = row_info(L, i);
     const float c2 = sm_scale * Ld.kv_scale * LOG2E;
@@ -175,7 +181,6 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
         O[mt] = f32x16{};
-    float m_ref = -INFINITY, l_run = 0.f;
 
     auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
         const int slot = (t_begin + tt) * M_TILE + tid;
@@ -190,13 +195,18 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     // Pass 0 fixes each head's reference max at its first non-empty tile.  If a later
     // tile exceeds it by more than 2^100 (p would approach the fp32 range) the split is
     // run again with the exact maximum observed in pass 0 as the reference.
-    float m_seen = -INFINITY;
+    float m_ref = -INFINITY;   // shared by the wave pair of a head half
+    float m_seen = -INFINITY;  // max over this wave's own keys
+    float l_own = 0.f;         // sum of p over this wave's own keys (this lane's 16)
     for (int pass = 0; pass < 2; ++pass) {
         if (pass == 1) {
             if (!sh_flag)
                 break;
-            m_ref = m_seen;
-            l_run = 0.f;
+            if (g == 0)
+                xm[w][j] = m_seen;
+            __syncthreads();
+            m_ref = fmaxf(m_seen, xm[wp][j]);
+            l_own = 0.f;
         }
         bool ovf = false;
         __syncthreads();
@@ -220,29 +230,30 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                 stage_load<KV_FP8>(R, seq, sidx[buf ^ 1], tid);
             const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
             const bool restart = (pass == 1 && tt == 0);
-            // ---- S^T partials for keys 0..31 (S[0]) and 32..63 (S[1]) over this wave's dims;
-            // operands are read three k-steps ahead of the MFMAs that use them.
+
+            // ---- 1. S^T partials for keys 0..31 (S[0]) and 32..63 (S[1]) over this wave's
+            // dims; operands are read three k-steps ahead of the MFMAs that use them.
             f32x16 S[2] = {f32x16{}, f32x16{}};
             {
                 const char *arow = kt + j * M_ROWB + 2 * (288 * dq + 8 * g);
                 u32x4 A[2][3][2];
-    #pragma unroll
+#pragma unroll
                 for (int t = 0; t < 3; ++t) {
                     A[0][t][0] = *(const u32x4 *)(arow + 32 * t);
                     A[0][t][1] = *(const u32x4 *)(arow + 32 * M_ROWB + 32 * t);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int c = 0; c < 6; ++c) {
                     const int cur = c & 1;
                     if (c + 1 < 6) {
-    #pragma unroll
+#pragma unroll
                         for (int t = 0; t < 3; ++t) {
                             const int tn = 3 * (c + 1) + t;
                             A[cur ^ 1][t][0] = *(const u32x4 *)(arow + 32 * tn);
                             A[cur ^ 1][t][1] = *(const u32x4 *)(arow + 32 * M_ROWB + 32 * tn);
                         }
                     }
-    #pragma unroll
+#pragma unroll
                     for (int t = 0; t < 3; ++t) {
                         S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[cur][t][0]),
                                                                        qT[3 * c + t], S[0], 0, 0, 0);
@@ -252,81 +263,90 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-    #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-    #pragma unroll
+
+            // ---- 2. swap the half partials; s = full S^T for keys 32*dq + .. (this wave's)
+            {
+                const f32x16 give = dq ? S[0] : S[1];
+#pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    xs[w][4 * kk + q4][lane] = f32x4{S[kk][4 * q4], S[kk][4 * q4 + 1], S[kk][4 * q4 + 2], S[kk][4 * q4 + 3]};
+                    xs[w][q4][lane] = f32x4{give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]};
+            }
             __syncthreads();
-            const int wp = w ^ 2;  // same heads, other half of the contraction
-    #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-    #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 o = xs[wp][4 * kk + q4][lane];
-    #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        S[kk][4 * q4 + e] = (dq == 0) ? S[kk][4 * q4 + e] + o[e] : o[e] + S[kk][4 * q4 + e];
-                }
+            f32x16 s = dq ? S[1] : S[0];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 o = xs[wp][q4][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s[4 * q4 + e] = dq ? (o[e] + s[4 * q4 + e]) : (s[4 * q4 + e] + o[e]);
+            }
 
-            // ---- online softmax over the 64 keys of the tile for head 32*hh + j
+            // ---- 3. softmax numerators of the own 32 keys
+            const uint32_t vkeys = (uint32_t)(valid >> (32 * dq)) >> (4 * g);
+            const bool full = valid == ~0ull;
             float mloc = -INFINITY;
-    #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-    #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int key = 32 * kk + 8 * (rr >> 2) + 4 * g + (rr & 3);
-                    const float z = ((valid >> key) & 1ull) ? S[kk][rr] * c2 : -INFINITY;
-                    S[kk][rr] = z;
-                    mloc = fmaxf(mloc, z);
-                }
-            const float m_tile = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            m_seen = fmaxf(m_seen, m_tile);
-            if (m_ref == -INFINITY)
-                m_ref = m_tile;  // first non-empty tile: O and l are still zero
-            ovf |= m_tile > m_ref + 100.f;
-            float lt = 0.f;
-            uint32_t pk[2][8];
-    #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-    #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const float p0 = (m_ref == -INFINITY) ? 0.f : exp2f(S[kk][2 * q] - m_ref);
-                    const float p1 = (m_ref == -INFINITY) ? 0.f : exp2f(S[kk][2 * q + 1] - m_ref);
-                    lt += p0 + p1;
-                    pk[kk][q] = pack_bf16x2(p0, p1);
-                }
-            lt += __shfl_xor(lt, 32, 64);
-            l_run += lt;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const bool ok = full || ((vkeys >> (8 * (rr >> 2) + (rr & 3))) & 1u);
+                s[rr] = ok ? s[rr] * c2 : -INFINITY;
+                mloc = fmaxf(mloc, s[rr]);
+            }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));  // this wave's 32 keys, head j
+            if (m_ref == -INFINITY && valid != 0ull) {
+                // first non-empty tile (block-uniform): the pair agrees on the reference
+                if (g == 0)
+                    xm[w][j] = mloc;
+                __syncthreads();
+                m_ref = fmaxf(mloc, xm[wp][j]);
+                __syncthreads();
+            }
+            m_seen = fmaxf(m_seen, mloc);
+            ovf |= mloc > m_ref + 100.f;
+            uint32_t pk[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float p0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q] - m_ref);
+                const float p1 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q + 1] - m_ref);
+                l_own += p0 + p1;
+                pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+            }
+            xp[w][0][lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            xp[w][1][lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+            __syncthreads();
+            const u32x4 pp0 = xp[wp][0][lane], pp1 = xp[wp][1][lane];
 
-            // ---- O^T += V^T . P^T over the 64 keys (4 steps of 16 keys); the transposed V
+            // ---- 4. O^T += V^T . P^T over the 64 keys (4 steps of 16 keys); the transposed V
             // operands of step u + 1 are read while step u's MFMAs run.
             {
                 typedef short s16x8 __attribute__((ext_vector_type(8)));
                 const int dcol = 256 * dq + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
                 const char *vbase = kt + (4 * g + ((lane & 15) >> 2)) * M_ROWB + 2 * dcol;
                 s16x4 V[2][8][2];
-    #pragma unroll
+#pragma unroll
                 for (int mt = 0; mt < 8; ++mt) {
                     V[0][mt][0] = lds_tr16(vbase + 64 * mt);
                     V[0][mt][1] = lds_tr16(vbase + 8 * M_ROWB + 64 * mt);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int cur = u & 1;
                     if (u + 1 < 4) {
                         const int un = u + 1;
                         const char *vb = vbase + (32 * (un >> 1) + 16 * (un & 1)) * M_ROWB;
-    #pragma unroll
+#pragma unroll
                         for (int mt = 0; mt < 8; ++mt) {
                             V[cur ^ 1][mt][0] = lds_tr16(vb + 64 * mt);
                             V[cur ^ 1][mt][1] = lds_tr16(vb + 8 * M_ROWB + 64 * mt);
                         }
                     }
                     const int khu = u >> 1, jj = u & 1;
-                    const bf16x8 bop = __builtin_bit_cast(
-                        bf16x8, u32x4{pk[khu][4 * jj], pk[khu][4 * jj + 1], pk[khu][4 * jj + 2], pk[khu][4 * jj + 3]});
-    #pragma unroll
+                    u32x4 bw;
+                    if (khu == dq)
+                        bw = jj ? u32x4{pk[4], pk[5], pk[6], pk[7]} : u32x4{pk[0], pk[1], pk[2], pk[3]};
+                    else
+                        bw = jj ? pp1 : pp0;
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
                     for (int mt = 0; mt < 8; ++mt) {
                         const s16x4 lo = V[cur][mt][0], hi = V[cur][mt][1];
                         const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -340,7 +360,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            __syncthreads();  // tile and S partials fully consumed
+            __syncthreads();  // tile, S partials and P fully consumed
             if (tt + 1 < ntiles)
                 stage_store<KV_FP8>(R, kt, tid);
             if (tid < M_TILE) {
@@ -353,6 +373,14 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
             sh_flag = 1;
         __syncthreads();
     }
+
+    // ---- row sum over all keys: lane halves, then the pair (dq 0 + dq 1)
+    float l_run = l_own + __shfl_xor(l_own, 32, 64);
+    __syncthreads();
+    if (g == 0)
+        xm[w][j] = l_run;
+    __syncthreads();
+    l_run = dq ? (xm[wp][j] + l_run) : (l_run + xm[wp][j]);
 
     // ---- epilogue: wave owns dims 256*dq + 32*mt + 8*q4 + 4*g + 0..3 of head 32*hh + j
     const int head = 32 * hh + j;
@@ -390,59 +418,56 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     }
 }
 
-// Combine the split partials of every (output row, group of 8 heads), in split order.
-constexpr int C_HEADS = 8;
+// Combine the split partials of every (output row, head), in split order.  One 128-thread
+// block per (row, head); thread t owns dims 4t .. 4t + 3.
 template <bool OUT_F32>
-__global__ __launch_bounds__(256) void mla_combine_kernel(int64_t T, MlaLayersDev layers, int nsplit,
+__global__ __launch_bounds__(128) void mla_combine_kernel(int64_t T, MlaLayersDev layers, int nsplit,
                                                           const float *__restrict__ ws_o,
                                                           const float *__restrict__ ws_ml)
 {
-    __shared__ float wts[32][C_HEADS];
-    __shared__ float lse_s[C_HEADS];
+    __shared__ float wts[32];
+    __shared__ float lse_s;
     const int64_t orow = blockIdx.x;
-    const int hg = blockIdx.y;
+    const int head = blockIdx.y;
     const int layer = (int)(orow / T);
     const int64_t i = orow % T;
     const MlaLayerDev Ld = layers.l[layer];
     const int tid = threadIdx.x;
-    if (tid < C_HEADS) {
-        const int head = hg * C_HEADS + tid;
+    if (tid < 64) {
         const float *ml = ws_ml + (orow * nsplit * M_H + head) * 2;
-        float mx = -INFINITY;
-        for (int sp = 0; sp < nsplit; ++sp)
-            mx = fmaxf(mx, ml[sp * M_H * 2]);
+        const int sp = tid;
+        const float ms = sp < nsplit ? ml[sp * M_H * 2] : -INFINITY;
+        const float ls = sp < nsplit ? ml[sp * M_H * 2 + 1] : 0.f;
+        const float mx = wave_max(ms);
+        const float e = (mx == -INFINITY || sp >= nsplit) ? 0.f : exp2f(ms - mx);
+        // fixed-order total: splits are summed in index order by lane 0
         float tot = 0.f;
-        for (int sp = 0; sp < nsplit; ++sp) {
-            const float e = (mx == -INFINITY) ? 0.f : exp2f(ml[sp * M_H * 2] - mx);
-            wts[sp][tid] = e;
-            tot += e * ml[sp * M_H * 2 + 1];
-        }
+        for (int s2 = 0; s2 < nsplit; ++s2)
+            tot += __shfl(e * ls, s2, 64);
         const float inv = tot > 0.f ? Ld.kv_scale / tot : 0.f;
-        for (int sp = 0; sp < nsplit; ++sp)
-            wts[sp][tid] *= inv;
-        lse_s[tid] = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
+        if (sp < nsplit)
+            wts[sp] = e * inv;
+        if (tid == 0)
+            lse_s = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
     }
     __syncthreads();
-    const float *pbase = ws_o + (orow * nsplit * M_H + hg * C_HEADS) * M_DC;
-    for (int e4 = tid; e4 < C_HEADS * M_DC / 4; e4 += 256) {
-        const int hl = (e4 * 4) / M_DC;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < nsplit; ++sp) {
-            const f32x4 v = *(const f32x4 *)(pbase + (int64_t)sp * M_H * M_DC + e4 * 4);
-            const float wgt = wts[sp][hl];
-            acc[0] = fmaf(wgt, v[0], acc[0]);
-            acc[1] = fmaf(wgt, v[1], acc[1]);
-            acc[2] = fmaf(wgt, v[2], acc[2]);
-            acc[3] = fmaf(wgt, v[3], acc[3]);
-        }
-        const int64_t o = (i * M_H + hg * C_HEADS) * M_DC + (int64_t)e4 * 4;
-        if (OUT_F32)
-            *(f32x4 *)((float *)Ld.out + o) = acc;
-        else
-            *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    const float *pbase = ws_o + (orow * nsplit * M_H + head) * M_DC + 4 * tid;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const f32x4 v = *(const f32x4 *)(pbase + (int64_t)sp * M_H * M_DC);
+        const float wgt = wts[sp];
+        acc[0] = fmaf(wgt, v[0], acc[0]);
+        acc[1] = fmaf(wgt, v[1], acc[1]);
+        acc[2] = fmaf(wgt, v[2], acc[2]);
+        acc[3] = fmaf(wgt, v[3], acc[3]);
     }
-    if (Ld.lse && tid < C_HEADS)
-        Ld.lse[i * M_H + hg * C_HEADS + tid] = lse_s[tid];
+    const int64_t o = (i * M_H + head) * M_DC + 4 * tid;
+    if (OUT_F32)
+        *(f32x4 *)((float *)Ld.out + o) = acc;
+    else
+        *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    if (Ld.lse && tid == 0)
+        Ld.lse[i * M_H + head] = lse_s;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -588,11 +613,11 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1)
         return e;
-    dim3 cgrid((unsigned)rows, M_H / C_HEADS);
+    dim3 cgrid((unsigned)rows, M_H);
     if (out_f32)
-        hipLaunchKernelGGL((mla_combine_kernel<true>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml);
+        hipLaunchKernelGGL((mla_combine_kernel<true>), cgrid, dim3(128), 0, stream, T, layers, ns, wo, wml);
     else
-        hipLaunchKernelGGL((mla_combine_kernel<false>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml);
+        hipLaunchKernelGGL((mla_combine_kernel<false>), cgrid, dim3(128), 0, stream, T, layers, ns, wo, wml);
     return hipGetLastError();
 }
 
