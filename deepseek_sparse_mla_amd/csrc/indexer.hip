@@ -13,10 +13,18 @@
 //  * idx_fp8_kernel      fp8 q x fp8 k (H=32, D=128): the prefill GEMM on
 //    v_mfma_scale_f32_32x32x64_f8f6f4; 16 query rows per block share an LDS key tile.
 //  * idx_generic_kernel  any dtypes / H <= 64 / D <= 256, one thread per token.
+#include <cstdlib>
+
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
 namespace dsa {
+
+// ReLU in one instruction (v_med3_f32); MFMA results are never NaN here.
+__device__ __forceinline__ float relu(float x)
+{
+    return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f);
+}
 
 // ------------------------------------------------------------------------------------------
 // bf16 q x fp8 k, H = 32, D = 128
@@ -39,7 +47,8 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(LayoutDev L, const uint
     if (s_begin >= r.n)
         return;
     const int64_t s_end = min(s_begin + (int64_t)chunk, r.n);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform loop bounds
     const int g = lane >> 5, j = lane & 31;
 
     bf16x8 a[8];
@@ -53,28 +62,56 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(LayoutDev L, const uint
         wr[rr] = w[i * 32 + 8 * (rr >> 2) + 4 * g + (rr & 3)];
 
     float *out = scores + i * ld;
-    for (int64_t s0 = s_begin + wave * 32; s0 < s_end; s0 += 128) {
+    // Double-buffered: the next tile's 64 key bytes per lane (and its scale) are requested
+    // before the current tile's MFMAs, so every wave keeps a tile in flight.
+    auto load_tile = [&](int64_t s0, u32x4 (&kv)[4], float &ksv) {
         const int64_t s = s0 + j;
         const int64_t row = r.kv_base + (s < s_end ? s : s_end - 1);
         const u32x4 *kp = (const u32x4 *)(k + row * kstride + 64 * g);
-        const u32x4 k0 = kp[0], k1 = kp[1], k2 = kp[2], k3 = kp[3];
-        const float ksv = ks[row * ks_stride];
+        kv[0] = kp[0];
+        kv[1] = kp[1];
+        kv[2] = kp[2];
+        kv[3] = kp[3];
+        ksv = ks[row * ks_stride];
+    };
+    auto compute_tile = [&](int64_t s0, const u32x4 (&kv)[4], float ksv) {
         f32x16 acc = {};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp8x8_to_bf16x8(k0[0], k0[1]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp8x8_to_bf16x8(k0[2], k0[3]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], fp8x8_to_bf16x8(k1[0], k1[1]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], fp8x8_to_bf16x8(k1[2], k1[3]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[4], fp8x8_to_bf16x8(k2[0], k2[1]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[5], fp8x8_to_bf16x8(k2[2], k2[3]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp8x8_to_bf16x8(k3[0], k3[1]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp8x8_to_bf16x8(k3[2], k3[3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp8x8_to_bf16x8(kv[0][0], kv[0][1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp8x8_to_bf16x8(kv[0][2], kv[0][3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], fp8x8_to_bf16x8(kv[1][0], kv[1][1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], fp8x8_to_bf16x8(kv[1][2], kv[1][3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[4], fp8x8_to_bf16x8(kv[2][0], kv[2][1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[5], fp8x8_to_bf16x8(kv[2][2], kv[2][3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp8x8_to_bf16x8(kv[3][0], kv[3][1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp8x8_to_bf16x8(kv[3][2], kv[3][3]), acc, 0, 0, 0);
         float part = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
-            part = fmaf(wr[rr], fmaxf(acc[rr], 0.f), part);
+            part = fmaf(wr[rr], relu(acc[rr]), part);
         part += __shfl_xor(part, 32, 64);
+        const int64_t s = s0 + j;
         if (g == 0 && s < s_end)
             out[s] = part * ksv;
+    };
+    // Ping-pong over two register buffers (no copies, so only the tile being computed is
+    // waited for while the other one is in flight).
+    // The prefetches are unconditional (rows past the end are clamped to the last visible
+    // row), so the loop body is straight-line code and only the computed tile is waited for.
+    u32x4 bufA[4], bufB[4];
+    float kA = 0.f, kB = 0.f;
+    int64_t s0 = s_begin + wave * 32;
+    if (s0 >= s_end)
+        return;
+    load_tile(s0, bufA, kA);
+    for (; s0 < s_end; s0 += 256) {
+        load_tile(s0 + 128, bufB, kB);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the wait below
+        compute_tile(s0, bufA, kA);
+        if (s0 + 128 >= s_end)
+            break;
+        load_tile(s0 + 256, bufA, kA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile(s0 + 128, bufB, kB);
     }
 }
 
@@ -204,7 +241,7 @@ __global__ __launch_bounds__(256) void idx_fp8_kernel(LayoutDev L, int64_t T, co
                     float part = 0.f;
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr)
-                        part = fmaf(wq[u][rr], fmaxf(acc[rr], 0.f), part);
+                        part = fmaf(wq[u][rr], relu(acc[rr]), part);
                     part += __shfl_xor(part, 32, 64);
                     const int64_t s = sb + j;
                     if (g == 0 && s < nq)
@@ -261,10 +298,17 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
                                const float *w, const void *k, int64_t kstride, const float *ks,
                                int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream)
 {
-    // Enough blocks to cover the chip several times, at least one 32-token tile per wave.
-    int chunk = 2048;
+    // Short-lived waves (at most 8 tiles each) and enough blocks to cover the chip
+    // several times, at least one 32-token tile per wave.  DSA_INDEXER_CHUNK (a power of
+    // two in [128, 8192]) overrides the tokens per block for launch-shape tuning.
+    int chunk = 1024;
     while (chunk > 128 && T * ((max_ctx + chunk - 1) / chunk) < 2048)
         chunk >>= 1;
+    if (const char *env = getenv("DSA_INDEXER_CHUNK")) {
+        const int c = atoi(env);
+        if (c >= 128 && c <= 8192 && (c & (c - 1)) == 0)
+            chunk = c;
+    }
     dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)T);
     hipLaunchKernelGGL(idx_decode_kernel, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
                        (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);

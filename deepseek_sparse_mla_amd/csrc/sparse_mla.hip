@@ -25,6 +25,8 @@
 //  * with several splits per row, partial (O, m, l) go to the workspace and a second
 //    kernel combines them in split order -- deterministic.
 // Generic kernel: any H <= 128, Dc <= 512, Dqk <= 1024, fp32 everywhere, two passes.
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -418,6 +420,358 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// fp8 latent rows: gathered straight into double-buffered LDS with the buffer DMA path and
+// kept as fp8 there (2 x 37 KB); operands are widened to bf16 in registers when read.
+// ------------------------------------------------------------------------------------------
+constexpr int F_ROWB = 592;                   // fp8 LDS row stride (576 + 16 pad)
+constexpr int F_TILEB = M_TILE * F_ROWB;      // 37888 B per tile buffer
+constexpr int F_DMA = F_TILEB / 1024;         // 37 wave-wide 1 KB loads per tile
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Barrier that waits only for this wave's LDS traffic (in-flight gathers stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Barrier that also waits for this wave's gathers (LDS DMA) and loads.  The wait is issued
+// through the builtin so that the compiler's own wait-count tracking sees the gathers as
+// complete (it does not read inline asm) and adds no waits for them later.
+__device__ __forceinline__ void tile_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
+{
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (i32x2 __attribute__((address_space(3))) *)((__attribute__((address_space(3))) char *)(lds_generic_ptr)));
+}
+
+// Gather one 64-row tile (rows given by sidx) into an LDS buffer: 37 wave-wide 1 KB DMA
+// loads shared by the 4 waves; the 16 pad bytes of each row and rows with index -1 get an
+// out-of-range offset, which reads zeros.  The row indices are read first so that the LDS
+// reads are waited for once.
+constexpr int F_DMA_PER_WAVE = (F_DMA + 3) / 4;  // 10 (the last only on wave 0)
+
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t seq, char *buf, const int32_t *sidx, int w,
+                                         int lane)
+{
+    int voff[F_DMA_PER_WAVE];
+#pragma unroll
+    for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
+        const int o = 1024 * (4 * q + w) + 16 * lane;
+        const int row = min(o / F_ROWB, M_TILE - 1);  // u >= 37 (not issued) is clamped
+        const int col = o - row * F_ROWB;
+        const int32_t idx = sidx[row];
+        voff[q] = (col < 576 && idx >= 0) ? idx * 576 + col : (int)0x80000000;
+    }
+#pragma unroll
+    for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
+        const int u = 4 * q + w;
+        if (q + 1 < F_DMA_PER_WAVE || u < F_DMA)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                seq, (void __attribute__((address_space(3))) *)((__attribute__((address_space(3))) char *)(buf + 1024 * u)),
+                16, voff[q], 0, 0, 0);
+    }
+}
+
+// Shared epilogue: normalised output (one split) or the split partial.
+template <bool OUT_F32>
+__device__ __forceinline__ void mla_store(const f32x16 (&O)[8], float l_run, float m_ref, const MlaLayerDev &Ld,
+                                          int64_t i, int64_t orow, int split, int nsplit, int dq, int g, int head,
+                                          float *__restrict__ ws_o, float *__restrict__ ws_ml)
+{
+    if (nsplit == 1) {
+        const float inv = (l_run > 0.f) ? Ld.kv_scale / l_run : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
+                const int64_t o = (i * M_H + head) * M_DC + d;
+                const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
+                const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
+                if (OUT_F32)
+                    *(f32x4 *)((float *)Ld.out + o) = f32x4{v0, v1, v2, v3};
+                else
+                    *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            }
+        if (Ld.lse && dq == 0 && g == 0)
+            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
+        return;
+    }
+    float *po = ws_o + ((orow * nsplit + split) * M_H + head) * M_DC;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
+            *(f32x4 *)(po + d) = f32x4{O[mt][4 * q4], O[mt][4 * q4 + 1], O[mt][4 * q4 + 2], O[mt][4 * q4 + 3]};
+        }
+    if (dq == 0 && g == 0) {
+        float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
+        pml[0] = m_ref;
+        pml[1] = l_run;
+    }
+}
+
+//
+// Same wave roles and math as mla_kernel (see above); differences:
+//  * tile t + 1 is gathered by DMA into the other LDS buffer while tile t is computed, and
+//    the barriers inside a tile wait only for LDS traffic;
+//  * S operands: 16 fp8 bytes per lane (two k-steps) widened to bf16; Q^T is loaded in the
+//    same permuted dim order (k-step 2p + h of lane half g covers dims 288dq + 32p + 16g +
+//    8h .. +7), which leaves the contraction unchanged;
+//  * V^T operands: ds_read_b64_tr_b8 gives a lane 8 consecutive keys of one dim; P is put
+//    in the same consecutive-key order by one v_permlane32_swap per dword.
+//
+template <bool OUT_F32>
+__global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int64_t T, int64_t n_rows,
+                                                               MlaLayersDev layers,
+                                                               const int32_t *__restrict__ indices, int k,
+                                                               float sm_scale, int nsplit, int tiles_per_split,
+                                                               int64_t pairs_per_xcd, float *__restrict__ ws_o,
+                                                               float *__restrict__ ws_ml)
+{
+    // two separate arrays (not one indexed by parity): the compiler then knows that reads
+    // of one buffer do not wait for the gathers into the other
+    __shared__ __attribute__((aligned(16))) char ktA[F_TILEB];
+    __shared__ __attribute__((aligned(16))) char ktB[F_TILEB];
+    __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
+    __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
+    __shared__ float xm[4][32];
+    __shared__ int32_t sidx[2][M_TILE];
+    __shared__ int sh_flag;
+
+    const int64_t pair = xcd_pair(pairs_per_xcd);
+    if (pair >= n_rows * nsplit)
+        return;
+    const int64_t orow = pair / nsplit;
+    const int split = (int)(pair % nsplit);
+    const int layer = (int)(orow / T);
+    const int64_t i = orow % T;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, j = lane & 31;
+    const int hh = w & 1, dq = w >> 1, wp = w ^ 2;
+    const MlaLayerDev Ld = layers.l[layer];
+    const RowInfo r = row_info(L, i);
+    const float c2 = sm_scale * Ld.kv_scale * LOG2E;
+
+    const int ntiles_all = (k + M_TILE - 1) / M_TILE;
+    const int t_begin = split * tiles_per_split;
+    const int ntiles = max(0, min(ntiles_all, t_begin + tiles_per_split) - t_begin);
+    const int32_t *irow = indices + i * k;
+
+    // Q^T operand in the permuted dim order (see above)
+    bf16x8 qT[18];
+    {
+        const uint16_t *qp = (const uint16_t *)Ld.q + ((i * M_H + 32 * hh + j) * M_DQK + 288 * dq + 16 * g);
+#pragma unroll
+        for (int t = 0; t < 18; ++t)
+            qT[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * (t >> 1) + 8 * (t & 1)));
+    }
+
+    f32x16 O[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+        O[mt] = f32x16{};
+
+    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
+        const int slot = (t_begin + tt) * M_TILE + tid;
+        return (tt < ntiles && slot < k) ? irow[slot] : -1;
+    };
+    const int64_t seq_bytes = r.n * 576;  // host guarantees max_ctx * 576 < 2^31
+    const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const uint8_t *)Ld.kv + r.kv_base * 576), (short)0, (int)seq_bytes, BUF_DWORD3);
+
+    // rows with index -1 may be skipped by the DMA: start from finite (zero) data
+    for (int e = tid; e < F_TILEB / 16; e += M_THREADS) {
+        ((u32x4 *)ktA)[e] = u32x4{0u, 0u, 0u, 0u};
+        ((u32x4 *)ktB)[e] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // V^T read geometry: 16-lane group G covers dims +16 * (G & 1), keys +8 * (G >> 1)
+    const int mq = lane & 15;
+    const int voffs = (8 * (lane >> 5) + (mq >> 1)) * F_ROWB + 256 * dq + 16 * ((lane >> 4) & 1) + 8 * (mq & 1);
+
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_own = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+            if (!sh_flag)
+                break;
+            if (g == 0)
+                xm[w][j] = m_seen;
+            __syncthreads();
+            m_ref = fmaxf(m_seen, xm[wp][j]);
+            l_own = 0.f;
+        }
+        bool ovf = false;
+        __syncthreads();
+        if (tid < M_TILE) {
+            sidx[0][tid] = load_idx(0);
+            sidx[1][tid] = load_idx(1);
+        }
+        if (tid == 0)
+            sh_flag = 0;
+        __syncthreads();
+        if (ntiles > 0)
+            dma_tile(seq, ktA, sidx[0], w, lane);
+        int32_t idx_next = tid < M_TILE ? load_idx(2) : -1;
+        tile_barrier();
+
+        // one tile; BUF (compile-time) picks the LDS buffer that holds it
+        auto tile_step = [&](auto buf_tag, int tt) {
+            constexpr int buf = decltype(buf_tag)::value;
+            const char *tile = buf ? ktB : ktA;
+            if (tt + 1 < ntiles)
+                dma_tile(seq, buf ? ktA : ktB, sidx[buf ^ 1], w, lane);
+            const int32_t idx_after = tid < M_TILE ? load_idx(tt + 3) : -1;
+            const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
+            const bool restart = (pass == 1 && tt == 0);
+
+            // ---- 1. S^T partials (keys 0..31 -> S[0], 32..63 -> S[1]) over this wave's dims
+            f32x16 S[2] = {f32x16{}, f32x16{}};
+            {
+                const char *arow = tile + j * F_ROWB + 288 * dq + 16 * g;
+                u32x4 A[2][2];
+                A[0][0] = *(const u32x4 *)(arow);
+                A[0][1] = *(const u32x4 *)(arow + 32 * F_ROWB);
+#pragma unroll
+                for (int p = 0; p < 9; ++p) {
+                    const int cur = p & 1;
+                    if (p + 1 < 9) {
+                        A[cur ^ 1][0] = *(const u32x4 *)(arow + 32 * (p + 1));
+                        A[cur ^ 1][1] = *(const u32x4 *)(arow + 32 * F_ROWB + 32 * (p + 1));
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const u32x4 a = A[cur][kk];
+                        S[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(a[0], a[1]), qT[2 * p],
+                                                                        S[kk], 0, 0, 0);
+                        S[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(a[2], a[3]), qT[2 * p + 1],
+                                                                        S[kk], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            // ---- 2. swap the half partials; s = full S^T for keys 32*dq + .. (this wave's)
+            {
+                const f32x16 give = dq ? S[0] : S[1];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    xs[w][q4][lane] = f32x4{give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]};
+            }
+            lds_barrier();
+            f32x16 s = dq ? S[1] : S[0];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 o = xs[wp][q4][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s[4 * q4 + e] = dq ? (o[e] + s[4 * q4 + e]) : (s[4 * q4 + e] + o[e]);
+            }
+
+            // ---- 3. softmax numerators of the own 32 keys
+            const uint32_t vkeys = (uint32_t)(valid >> (32 * dq)) >> (4 * g);
+            const bool full = valid == ~0ull;
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const bool ok = full || ((vkeys >> (8 * (rr >> 2) + (rr & 3))) & 1u);
+                s[rr] = ok ? s[rr] * c2 : -INFINITY;
+                mloc = fmaxf(mloc, s[rr]);
+            }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            if (m_ref == -INFINITY && valid != 0ull) {  // first non-empty tile (block-uniform)
+                if (g == 0)
+                    xm[w][j] = mloc;
+                lds_barrier();
+                m_ref = fmaxf(mloc, xm[wp][j]);
+                lds_barrier();
+            }
+            m_seen = fmaxf(m_seen, mloc);
+            ovf |= mloc > m_ref + 100.f;
+            uint32_t pk[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float p0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q] - m_ref);
+                const float p1 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q + 1] - m_ref);
+                l_own += p0 + p1;
+                pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+            }
+            xp[w][0][lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            xp[w][1][lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+            lds_barrier();
+            const u32x4 pp0 = xp[wp][0][lane], pp1 = xp[wp][1][lane];
+
+            // ---- 4. O^T += V^T . P^T over the 64 keys (4 steps of 16 keys)
+            {
+                i32x2 V[2][8];
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+                    V[0][mt] = lds_tr8(tile + voffs + 32 * mt);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int cur = u & 1;
+                    if (u + 1 < 4) {
+                        const int un = u + 1;
+                        const char *vb = tile + voffs + (32 * (un >> 1) + 16 * (un & 1)) * F_ROWB;
+#pragma unroll
+                        for (int mt = 0; mt < 8; ++mt)
+                            V[cur ^ 1][mt] = lds_tr8(vb + 32 * mt);
+                    }
+                    const int khu = u >> 1, jj = u & 1;
+                    u32x4 pw;
+                    if (khu == dq)
+                        pw = jj ? u32x4{pk[4], pk[5], pk[6], pk[7]} : u32x4{pk[0], pk[1], pk[2], pk[3]};
+                    else
+                        pw = jj ? pp1 : pp0;
+                    // keys 4g..4g+3 (dwords 0,1) and 8+4g..8+4g+3 (dwords 2,3) -> 8g'..8g'+7
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{s0[0], s1[0], s0[1], s1[1]});
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt) {
+                        const bf16x8 a8 = fp8x8_to_bf16x8((uint32_t)V[cur][mt][0], (uint32_t)V[cur][mt][1]);
+                        if (restart && u == 0)  // first MFMA of a rerun: drop pass 0's sums
+                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, bop, f32x16{}, 0, 0, 0);
+                        else
+                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, bop, O[mt], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (tid < M_TILE)
+                sidx[buf][tid] = idx_next;  // tile tt + 2
+            idx_next = idx_after;
+            tile_barrier();  // tile tt + 1 has landed; this buffer is free
+        };
+        for (int tt = 0; tt < ntiles; tt += 2) {
+            tile_step(std::integral_constant<int, 0>{}, tt);
+            if (tt + 1 >= ntiles)
+                break;
+            tile_step(std::integral_constant<int, 1>{}, tt + 1);
+        }
+        if (ovf)
+            sh_flag = 1;
+        __syncthreads();
+    }
+
+    float l_run = l_own + __shfl_xor(l_own, 32, 64);
+    __syncthreads();
+    if (g == 0)
+        xm[w][j] = l_run;
+    __syncthreads();
+    l_run = dq ? (xm[wp][j] + l_run) : (l_run + xm[wp][j]);
+    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml);
+}
+
 // Combine the split partials of every (output row, head), in split order.  One 128-thread
 // block per (row, head); thread t owns dims 4t .. 4t + 3.
 template <bool OUT_F32>
@@ -600,9 +954,11 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
                        indices, k, sm_scale, ns, tps, ppx, wo, wml)
     if (kv_fp8) {
         if (out_f32)
-            DSA_MLA_LAUNCH(true, true);
+            hipLaunchKernelGGL((mla_fp8_kernel<true>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, tps, ppx, wo, wml);
         else
-            DSA_MLA_LAUNCH(true, false);
+            hipLaunchKernelGGL((mla_fp8_kernel<false>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, tps, ppx, wo, wml);
     } else {
         if (out_f32)
             DSA_MLA_LAUNCH(false, true);
