@@ -117,6 +117,20 @@ __device__ __forceinline__ void stage_store(const StageRegs<KV_FP8> &R, char *ti
 // one per XCD (blocks are dispatched to the 8 XCDs round-robin), so all splits of a row
 // -- which share the row's q -- and neighbouring rows -- which share many gathered
 // latent rows -- run under one L2.
+// Barrier that waits only for this wave's LDS traffic (in-flight gathers stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Barrier that also waits for this wave's gathers (LDS DMA) and loads.  The wait is issued
+// through the builtin so that the compiler's own wait-count tracking sees the gathers as
+// complete (it does not read inline asm) and adds no waits for them later.
+__device__ __forceinline__ void tile_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int64_t xcd_pair(int64_t pairs_per_xcd)
 {
     const int64_t b = blockIdx.x;
@@ -170,6 +184,19 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     const int ntiles = max(0, min(ntiles_all, t_begin + tiles_per_split) - t_begin);
     const int32_t *irow = indices + i * k;
 
+    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
+        const int slot = (t_begin + tt) * M_TILE + tid;
+        return (tt < ntiles && slot < k) ? irow[slot] : -1;
+    };
+    // the first three tiles' indices are loaded before Q so that their latency overlaps it
+    int32_t i0 = -1, i1 = -1, i2 = -1;
+    if (tid < M_TILE) {
+        i0 = load_idx(0);
+        i1 = load_idx(1);
+        i2 = load_idx(2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // Q^T operand: head 32*hh + j, dims 288*dq + 16t + 8g .. +7 (t < 18)
     bf16x8 qT[18];
     {
@@ -184,10 +211,6 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     for (int mt = 0; mt < 8; ++mt)
         O[mt] = f32x16{};
 
-    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
-        const int slot = (t_begin + tt) * M_TILE + tid;
-        return (tt < ntiles && slot < k) ? irow[slot] : -1;
-    };
     StageRegs<KV_FP8> R;
     constexpr int64_t ROWB = KV_FP8 ? 576 : 1152;
     const int64_t seq_bytes = r.n * ROWB;  // host guarantees max_ctx * ROWB < 2^31
@@ -208,23 +231,25 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                 xm[w][j] = m_seen;
             __syncthreads();
             m_ref = fmaxf(m_seen, xm[wp][j]);
-            l_own = 0.f;
+            l_own = 0.f;  // i0 .. i2 still hold the first three tiles' indices
         }
         bool ovf = false;
-        __syncthreads();
         if (tid < M_TILE) {
-            sidx[0][tid] = load_idx(0);
-            sidx[1][tid] = load_idx(1);
+            sidx[0][tid] = i0;
+            sidx[1][tid] = i1;
         }
         if (tid == 0)
             sh_flag = 0;
-        int32_t idx_next = tid < M_TILE ? load_idx(2) : -1;
-        __syncthreads();
+        int32_t idx_next = i2;
+        lds_barrier();  // Q stays in flight
         if (ntiles > 0) {
             stage_load<KV_FP8>(R, seq, sidx[0], tid);
             stage_store<KV_FP8>(R, kt, tid);
         }
-        __syncthreads();
+        // Nothing may be left in flight here (Q included): otherwise the compiler's wait
+        // for Q lands inside the loop, where it would also wait for the next tile's loads.
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+        lds_barrier();
 
         for (int tt = 0; tt < ntiles; ++tt) {
             const int buf = tt & 1;
@@ -273,7 +298,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                 for (int q4 = 0; q4 < 4; ++q4)
                     xs[w][q4][lane] = f32x4{give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]};
             }
-            __syncthreads();
+            lds_barrier();
             f32x16 s = dq ? S[1] : S[0];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -298,9 +323,9 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                 // first non-empty tile (block-uniform): the pair agrees on the reference
                 if (g == 0)
                     xm[w][j] = mloc;
-                __syncthreads();
+                lds_barrier();
                 m_ref = fmaxf(mloc, xm[wp][j]);
-                __syncthreads();
+                lds_barrier();
             }
             m_seen = fmaxf(m_seen, mloc);
             ovf |= mloc > m_ref + 100.f;
@@ -314,7 +339,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
             }
             xp[w][0][lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
             xp[w][1][lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-            __syncthreads();
+            lds_barrier();
             const u32x4 pp0 = xp[wp][0][lane], pp1 = xp[wp][1][lane];
 
             // ---- 4. O^T += V^T . P^T over the 64 keys (4 steps of 16 keys); the transposed V
@@ -362,14 +387,14 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            __syncthreads();  // tile, S partials and P fully consumed
+            lds_barrier();  // tile, S partials and P fully consumed
             if (tt + 1 < ntiles)
                 stage_store<KV_FP8>(R, kt, tid);
             if (tid < M_TILE) {
                 sidx[buf][tid] = idx_next;  // tile tt + 2
                 idx_next = load_idx(tt + 3);
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (ovf)
             sh_flag = 1;
@@ -429,20 +454,6 @@ constexpr int F_TILEB = M_TILE * F_ROWB;      // 37888 B per tile buffer
 constexpr int F_DMA = F_TILEB / 1024;         // 37 wave-wide 1 KB loads per tile
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-// Barrier that waits only for this wave's LDS traffic (in-flight gathers stay in flight).
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// Barrier that also waits for this wave's gathers (LDS DMA) and loads.  The wait is issued
-// through the builtin so that the compiler's own wait-count tracking sees the gathers as
-// complete (it does not read inline asm) and adds no waits for them later.
-__device__ __forceinline__ void tile_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
 {
@@ -567,6 +578,19 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     const int ntiles = max(0, min(ntiles_all, t_begin + tiles_per_split) - t_begin);
     const int32_t *irow = indices + i * k;
 
+    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
+        const int slot = (t_begin + tt) * M_TILE + tid;
+        return (tt < ntiles && slot < k) ? irow[slot] : -1;
+    };
+    // the first three tiles' indices are loaded before Q so that their latency overlaps it
+    int32_t i0 = -1, i1 = -1, i2 = -1;
+    if (tid < M_TILE) {
+        i0 = load_idx(0);
+        i1 = load_idx(1);
+        i2 = load_idx(2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // Q^T operand in the permuted dim order (see above)
     bf16x8 qT[18];
     {
@@ -581,10 +605,6 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     for (int mt = 0; mt < 8; ++mt)
         O[mt] = f32x16{};
 
-    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
-        const int slot = (t_begin + tt) * M_TILE + tid;
-        return (tt < ntiles && slot < k) ? irow[slot] : -1;
-    };
     const int64_t seq_bytes = r.n * 576;  // host guarantees max_ctx * 576 < 2^31
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((const uint8_t *)Ld.kv + r.kv_base * 576), (short)0, (int)seq_bytes, BUF_DWORD3);
@@ -608,20 +628,19 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
                 xm[w][j] = m_seen;
             __syncthreads();
             m_ref = fmaxf(m_seen, xm[wp][j]);
-            l_own = 0.f;
+            l_own = 0.f;  // i0 .. i2 still hold the first three tiles' indices
         }
         bool ovf = false;
-        __syncthreads();
         if (tid < M_TILE) {
-            sidx[0][tid] = load_idx(0);
-            sidx[1][tid] = load_idx(1);
+            sidx[0][tid] = i0;
+            sidx[1][tid] = i1;
         }
         if (tid == 0)
             sh_flag = 0;
-        __syncthreads();
+        lds_barrier();  // Q stays in flight
         if (ntiles > 0)
             dma_tile(seq, ktA, sidx[0], w, lane);
-        int32_t idx_next = tid < M_TILE ? load_idx(2) : -1;
+        int32_t idx_next = i2;
         tile_barrier();
 
         // one tile; BUF (compile-time) picks the LDS buffer that holds it
@@ -906,12 +925,12 @@ __global__ __launch_bounds__(G_THREADS) void mla_generic_kernel(LayoutDev L, int
 // ------------------------------------------------------------------------------------------
 // Splits depend on the query rows T only (not on the layer count), so a layer run through
 // the shared entry takes exactly the same reduction path as a single-layer call.
-int mla_num_splits(int64_t T, int k)
+int mla_num_splits(int64_t rows, int k)
 {
     const int ntiles = (k + M_TILE - 1) / M_TILE;
-    if (T <= 0)
+    if (rows <= 0)
         return 1;
-    int64_t ns = (MLA_TARGET_BLOCKS + T - 1) / T;
+    int64_t ns = (MLA_TARGET_BLOCKS + rows - 1) / rows;
     if (ns > ntiles)
         ns = ntiles;
     if (ns > 32)
@@ -924,10 +943,10 @@ int mla_num_splits(int64_t T, int k)
 
 size_t mla_workspace_bytes(int64_t T, int n_layers, int k)
 {
-    const int ns = mla_num_splits(T, k);
+    const size_t rows = (size_t)T * n_layers;
+    const int ns = mla_num_splits((int64_t)rows, k);
     if (ns <= 1)
         return 0;
-    const size_t rows = (size_t)T * n_layers;
     size_t o = rows * ns * M_H * M_DC * sizeof(float);
     size_t ml = rows * ns * M_H * 2 * sizeof(float);
     return o + ml;
@@ -938,7 +957,7 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
                             float sm_scale, void *workspace, hipStream_t stream)
 {
     const int64_t rows = T * n_layers;
-    const int ns = mla_num_splits(T, k);
+    const int ns = mla_num_splits(rows, k);
     const int ntiles = (k + M_TILE - 1) / M_TILE;
     const int tps = (ntiles + ns - 1) / ns;
     float *wo = nullptr, *wml = nullptr;

@@ -4,10 +4,12 @@
 // [tokens x 2048]; ATOM-side optimisations, stable_topk: ties must resolve the same
 // way every time; caveats: with fewer than k visible tokens every token is taken.)
 //
-// Order: higher score first; equal scores (with -0 == +0) by lower position.  Each score
-// maps to a monotone 32-bit key (sign-flipped IEEE bits, -0 folded into +0) and each
-// candidate to the 64-bit composite (key << 32) | ~position, which is unique per row, so
-// "larger composite first" is exactly that order.
+// Selection order: higher score first; equal scores (with -0 == +0) by lower position.
+// Each score maps to a monotone 32-bit key (sign-flipped IEEE bits, -0 folded into +0) and
+// each candidate to the 64-bit composite (key << 32) | ~position, which is unique per row,
+// so "larger composite first" is exactly that order.  The selected set is then written in
+// ascending position order (the attention over it does not depend on the order, and the
+// gathers it drives then walk the cache forwards).
 //
 // Rows longer than CAP take two kernels:
 //  K1  topk_hist_kernel   many blocks per row: an LDS histogram (one per wave) of the top 11
@@ -16,10 +18,10 @@
 //  K2  topk_select_kernel one 1024-thread block per row: the histogram gives the bin that
 //                         holds the k-th key; one pass gathers every score at or above that
 //                         bin into LDS (when they fit), an exact radix select over the
-//                         composites keeps exactly k, and a sort orders them (per-wave
-//                         bitonic with shuffles, then four LDS merge levels).  K2 clears
-//                         the row's histogram, so the workspace is zero again for the next
-//                         call.  Rows with at most CAP scores skip K1 and load directly.
+//                         composites finds the k-th largest, and the selected positions are
+//                         marked in an LDS bitmap and compacted in position order.  K2
+//                         clears the row's histogram, so the workspace is zero again for the
+//                         next call.  Rows with at most CAP scores skip K1 and load directly.
 // If the scores at or above the threshold bin do not fit in LDS (heavily tied data), K2
 // falls back to radix passes over the row in global memory and an ordered compaction of
 // the ties (lowest positions first).
@@ -32,7 +34,8 @@ constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_CAP = 8192;        // candidates held in LDS (64 KB of composites)
 constexpr int TK_BINS = 2048;       // 11-bit digits
-constexpr int TK_SORT = 2048;       // sort width (>= DSA_TOPK_MAX)
+constexpr int TK_BMAP_BITS = 1 << 15;  // positions marked per bitmap pass (4 KB: two blocks per CU)
+constexpr int TK_BMAP_WORDS = TK_BMAP_BITS / 32;
 constexpr int H_THREADS = 256;      // histogram kernel
 constexpr int H_CHUNK = 8192;       // scores per histogram block
 
@@ -153,83 +156,13 @@ __global__ __launch_bounds__(H_THREADS) void topk_hist_kernel(LayoutDev L, const
 // ------------------------------------------------------------------------------------------
 // K2: gather, exact select, sort, emit
 // ------------------------------------------------------------------------------------------
-// Descending sort of TK_SORT unique composites.  Lane l of wave w holds positions
-// 128w + 2l and 128w + 2l + 1: every wave first sorts its 128 with a bitonic network whose
-// partners are in the same thread or wave (shuffles, no barrier); four merge levels then
-// join runs of 128 -> 256 -> ... -> 2048 through LDS.  In a merge, an element's place is its
-// index in its own run plus the number of larger elements in the partner run (binary
-// search), which is exact because the composites are unique.  The result is left in buf
-// (TK_SORT entries; `tmp` is a second buffer of the same size).
-__device__ __forceinline__ void sort_2048_desc(uint64_t v[2], uint64_t *buf, uint64_t *tmp)
-{
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-#pragma unroll
-    for (int size = 2; size <= 128; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride == 1) {
-                const int q = 2 * lane;
-                const bool desc = (size == 128) || ((q & size) == 0);
-                const uint64_t a = v[0], b = v[1];
-                const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-                v[0] = desc ? hi : lo;
-                v[1] = desc ? lo : hi;
-            } else {
-                const int ls = stride >> 1;  // partner lane distance
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const uint64_t o = __shfl_xor(v[rr], ls, 64);
-                    const int q = 2 * lane + rr;
-                    const bool lower = (q & stride) == 0;
-                    const bool desc = (size == 128) || ((q & size) == 0);
-                    const bool keep_max = (lower == desc);
-                    v[rr] = keep_max ? (v[rr] > o ? v[rr] : o) : (v[rr] > o ? o : v[rr]);
-                }
-            }
-        }
-    }
-    uint64_t *src = buf, *dst = tmp;
-    src[128 * w + 2 * lane] = v[0];
-    src[128 * w + 2 * lane + 1] = v[1];
-    __syncthreads();
-#pragma unroll 1
-    for (int run = 128; run < TK_SORT; run <<= 1) {
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int p = 2 * tid + rr;
-            const int pair0 = p & ~(2 * run - 1);      // start of the merged pair of runs
-            const int in_b = (p & run) != 0;           // element sits in the second run
-            const int own = p - pair0 - (in_b ? run : 0);
-            const uint64_t *other = src + pair0 + (in_b ? 0 : run);
-            const uint64_t x = src[p];
-            int lo = 0, hi = run;                       // count of partner entries > x
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (other[mid] > x)
-                    lo = mid + 1;
-                else
-                    hi = mid;
-            }
-            dst[pair0 + own + lo] = x;
-        }
-        __syncthreads();
-        uint64_t *t = src;
-        src = dst;
-        dst = t;
-    }
-    if (src != buf) {  // odd number of levels: copy back
-        buf[2 * tid] = src[2 * tid];
-        buf[2 * tid + 1] = src[2 * tid + 1];
-        __syncthreads();
-    }
-}
-
 __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, const float *__restrict__ scores,
                                                                  int64_t ld, int k, int32_t *__restrict__ out,
                                                                  uint32_t *__restrict__ ghist)
 {
     __shared__ uint64_t cand[TK_CAP];
     __shared__ uint32_t hist[TK_BINS];
+    __shared__ uint32_t bmap[TK_BMAP_WORDS];
     __shared__ uint32_t wsum[TK_WAVES];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t sh_cnt;
@@ -344,37 +277,52 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
         }
     }
 
-    // ---- compact the selected composites into sort slots, pad, sort, emit
-    uint64_t v[2];
-    if (m > kk) {
-        // move the selected composites to the front of cand: every thread reads its
-        // candidates before the scan's barrier, then writes them to its ranked slots
-        uint64_t mine[TK_CAP / TK_THREADS];
-        uint32_t sel_mask = 0, cnt_mine = 0;
-#pragma unroll
-        for (int e = 0; e < TK_CAP / TK_THREADS; ++e) {
-            const uint32_t c = tid + e * TK_THREADS;
-            mine[e] = c < m ? cand[c] : 0ull;
-            if (c < m && mine[e] >= lo_comp) {
-                sel_mask |= 1u << e;
-                ++cnt_mine;
+    // ---- list the selected positions in ascending order: mark them in a bitmap (one pass
+    // per 2^15 positions), then a block scan over per-thread popcounts of consecutive
+    // words gives every set bit its output slot.  The slots are staged in hist (kk <= 2048).
+    static_assert(TK_BINS >= DSA_TOPK_MAX, "staging area");
+    uint32_t *slots = hist;
+    uint32_t done = 0;
+    for (int64_t cb = 0; cb < n && done < kk; cb += TK_BMAP_BITS) {
+        const int64_t len = min((int64_t)TK_BMAP_BITS, n - cb);
+        const int nw = (int)((len + 31) >> 5);
+        __syncthreads();  // previous pass's readers of bmap are done
+        for (int w = tid; w < nw; w += TK_THREADS)
+            bmap[w] = 0u;
+        __syncthreads();
+        for (uint32_t c = tid; c < m; c += TK_THREADS) {
+            const uint64_t v = cand[c];
+            if (m > kk && v < lo_comp)
+                continue;
+            const int64_t pos = (int64_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
+            if (pos >= cb && pos < cb + len) {
+                const uint32_t rel = (uint32_t)(pos - cb);
+                atomicOr(&bmap[rel >> 5], 1u << (rel & 31));
             }
         }
-        uint32_t tot;
-        uint32_t pos = block_excl_scan(cnt_mine, wsum, &tot);
-#pragma unroll
-        for (int e = 0; e < TK_CAP / TK_THREADS; ++e)
-            if (sel_mask & (1u << e))
-                cand[pos++] = mine[e];
         __syncthreads();
+        const int wpt = (nw + TK_THREADS - 1) / TK_THREADS;  // consecutive words per thread
+        const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
+        uint32_t cnt = 0;
+        for (int w = w0; w < w1; ++w)
+            cnt += __popc(bmap[w]);
+        uint32_t tot;
+        uint32_t slot = done + block_excl_scan(cnt, wsum, &tot);
+        for (int w = w0; w < w1; ++w) {
+            uint32_t bits = bmap[w];
+            while (bits) {
+                const int b = __ffs(bits) - 1;
+                if (slot < (uint32_t)TK_BINS)
+                    slots[slot] = (uint32_t)(cb + 32 * w + b);
+                ++slot;
+                bits &= bits - 1u;
+            }
+        }
+        done += tot;
     }
-    // unique padding below every real composite (real keys are >= 0x007FFFFF)
-    v[0] = (uint32_t)(2 * tid) < kk ? cand[2 * tid] : (uint64_t)(2 * tid);
-    v[1] = (uint32_t)(2 * tid + 1) < kk ? cand[2 * tid + 1] : (uint64_t)(2 * tid + 1);
     __syncthreads();
-    sort_2048_desc(v, cand, cand + TK_SORT);
     for (int t = tid; t < k; t += TK_THREADS)
-        orow[t] = (uint32_t)t < kk ? (int32_t)(0xFFFFFFFFu - (uint32_t)(cand[t] & 0xFFFFFFFFull)) : -1;
+        orow[t] = (uint32_t)t < kk ? (int32_t)slots[t] : -1;
 }
 
 // ------------------------------------------------------------------------------------------

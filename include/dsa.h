@@ -125,10 +125,12 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
  * ties must not be broken arbitrarily; caveats: with fewer visible tokens
  * than k every token is taken).
  *
- * Row i considers scores[i * ld + s] for s < n_i and writes to
- * indices[i * k .. i * k + k - 1] the first min(k, n_i) positions under the
- * strict order "higher score first; equal scores (with -0 == +0) by lower
- * position", then -1 in the remaining slots.  Positions are logical (0 ..
+ * Row i considers scores[i * ld + s] for s < n_i and selects the first
+ * min(k, n_i) positions under the strict order "higher score first; equal
+ * scores (with -0 == +0) by lower position".  It writes them to
+ * indices[i * k .. i * k + k - 1] in ascending position order (the attention
+ * over them does not depend on the order; the pages fix the set, not its
+ * listing), then -1 in the remaining slots.  Positions are logical (0 ..
  * ctx_b - 1 within the sequence).  1 <= k <= DSA_TOPK_MAX.  NaN scores are
  * outside the contract.
  *   workspace     device scratch of dsa_topk_workspace_size() bytes (a score

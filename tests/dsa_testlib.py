@@ -120,8 +120,17 @@ def check_scores(g_row: np.ndarray, o_row: np.ndarray, what=""):
 
 
 def check_topk_same_array(g_idx_row: np.ndarray, scores_row_f32: np.ndarray, k: int, what=""):
-    exp = oracle.topk(scores_row_f32[None].astype(np.float64), [scores_row_f32.size], k)[0]
-    assert np.array_equal(g_idx_row, exp), "%s: top-k differs from the oracle on the same scores" % what
+    """Bit-exact check on the same score array: the library lists the selected positions in
+    ascending order, the oracle in selection order (score desc, position asc); the selected
+    sets must be identical, the listing strictly ascending, and the tail padded with -1."""
+    n = scores_row_f32.size
+    exp = oracle.topk(scores_row_f32[None].astype(np.float64), [n], k)[0]
+    take = min(n, k)
+    g = np.asarray(g_idx_row, np.int64)
+    assert np.all(g[take:] == -1), "%s: padding slots are not -1" % what
+    assert np.all(np.diff(g[:take]) > 0), "%s: selected positions are not strictly ascending" % what
+    assert np.array_equal(g[:take], np.sort(np.asarray(exp[:take], np.int64))), \
+        "%s: top-k set differs from the oracle on the same scores" % what
 
 
 def check_topk_margin(g_idx_row: np.ndarray, o_scores_row: np.ndarray, k: int, what=""):

@@ -116,8 +116,12 @@ def test_mla_workspace_required(lib):
     assert need > 0
     assert _mla(lib, L, None, 0) == B.DSA_ERR_WORKSPACE
     assert _mla(lib, L, FAKE, need - 1) == B.DSA_ERR_WORKSPACE
-    # the split count depends on T only, so n layers need n times the space
-    assert lib.sparse_mla_workspace_size(ctypes.byref(L), 64, 512, 64, 2048, 4) > 3 * need
+    # the split count falls as the number of (row, layer) pairs grows; the space never shrinks
+    four = lib.sparse_mla_workspace_size(ctypes.byref(L), 64, 512, 64, 2048, 4)
+    assert four >= need
+    # enough (row, layer) pairs to fill the chip: one split, no workspace
+    big = _layout(batch=256, total_q=256)
+    assert lib.sparse_mla_workspace_size(ctypes.byref(big), 64, 512, 64, 2048, 1) == 0
 
 
 def test_shared_rejects_too_many_layers(lib):

@@ -91,8 +91,13 @@ def test_prefill_ragged_sequences_share_blocks():
 
 
 def test_shared_layers_match_oracle_and_single_layer_calls():
-    case = synth.make_case("shared_small", 5, ctx=[3000, 2100], sm_scale=1.0 / 16, kv_dt="fp8", n_layers=3,
-                           device=DEV)
+    """Every shared layer meets the oracle bar, and agrees with a single-layer call on the same
+    indices up to the rounding of a different split of the 2048 keys (the split count
+    follows the number of (row, layer) pairs): the bf16 rounding of P and of the output
+    moves by a few 1e-4 at these magnitudes, so the two calls must agree to 4e-3 absolute,
+    five times tighter than the oracle bar."""
+    case = synth.make_case("shared_small", 5, ctx=[3000, 2100, 4096, 2500, 6000, 2048, 3333, 5000],
+                           sm_scale=1.0 / 16, kv_dt="fp8", n_layers=4, device=DEV)
     scores, idx, outs, lses = tl.gpu_path(case)
     _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP)
     layout = dsa.Layout.of_case(case)
@@ -100,8 +105,12 @@ def test_shared_layers_match_oracle_and_single_layer_calls():
         lse1 = torch.empty_like(lses[l])
         o1 = dsa.sparse_mla_decode(layout, L.q, L.kv, idx, case.sm_scale, case.Dc, L.kv_scale, lse=lse1)
         torch.cuda.synchronize()
-        assert torch.equal(o1, outs[l]), "layer %d differs from its single-layer call" % l
-        assert torch.equal(lse1, lses[l])
+        d = (o1.float() - outs[l].float()).abs().max().item()
+        assert d <= 4e-3, "layer %d differs from its single-layer call by %.3g" % (l, d)
+        assert torch.allclose(lse1, lses[l], rtol=1e-5, atol=1e-5)
+    again = tl.gpu_path(case)
+    for l in range(len(case.layers)):  # the shared call itself is deterministic
+        assert torch.equal(again[2][l], outs[l]) and torch.equal(again[3][l], lses[l])
 
 
 def test_recomputed_indexer_gives_identical_indices_and_outputs():
