@@ -2,6 +2,9 @@
 """Throughput of the DSA decode path (indexer -> top-2048 -> sparse MLA) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|ragged|prefill|share]
+    python bench.py --copy-calibration MIB          # a plain device copy, for counter scaling
+    python bench.py --rocprof-summary CSV [CSV ..]  # per-kernel table of rocprofv3 output
+    python bench.py --traffic-from FETCH WRITE COPY_FETCH COPY_WRITE [--workload W] [--copy-mib M]
 
 One step = one pass of the whole path over one batch of synthetic input.  The default
 workload is the GLM-5.2 layer decode (batch 8, context 8192, 32x128 fp8 index cache,
@@ -43,6 +46,12 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough for > 1 GB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run --steps device-to-device copies of MIB MiB (counter calibration)")
+    p.add_argument("--rocprof-summary", nargs="+", metavar="CSV", help="summarise rocprofv3 CSV files")
+    p.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="HBM bytes per stage call from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+    p.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (MiB)")
     return p.parse_args()
 
 
@@ -168,12 +177,126 @@ def cpu_baseline(case, target_s):
                       % (reps, case.name, case.T, case.topk, el, threads, min(threads, case.T))}
 
 
+# ------------------------------------------------------------------------------- counters
+
+STAGE_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip"}
+STAGE_KERNELS = {"indexer": ("idx_",), "topk": ("topk_",), "mla": ("mla_",)}
+
+
+def _short(name):
+    """Kernel name without namespace, template arguments and parameter list."""
+    base = name.split("(")[0]
+    base = base.split("<")[0]
+    return base.replace("void ", "").replace("dsa::", "").strip()
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def source_digest(stage):
+    import hashlib
+    path = os.path.join(ROOT, "deepseek_sparse_mla_amd", "csrc", STAGE_SOURCES[stage])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counter_means(path):
+    """{(kernel, counter): (mean value per dispatch, dispatches)} of a counter_collection CSV."""
+    acc = {}
+    for r in _read_csv(path):
+        key = (_short(r["Kernel_Name"]), r["Counter_Name"])
+        tot, n = acc.get(key, (0.0, 0))
+        acc[key] = (tot + float(r["Counter_Value"]), n + 1)
+    return {k: (v[0] / v[1], v[1]) for k, v in acc.items()}
+
+
+def rocprof_summary(paths):
+    for path in paths:
+        rows = _read_csv(path)
+        print("# %s" % os.path.basename(path))
+        if rows and "AverageNs" in rows[0]:
+            print("%-28s %7s %12s %9s" % ("kernel", "calls", "avg_us", "share_%"))
+            for r in rows:
+                print("%-28s %7s %12.2f %9.2f" % (_short(r["Name"])[:28], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                  float(r["Percentage"])))
+        elif rows and "Counter_Name" in rows[0]:
+            print("%-28s %-12s %10s %16s" % ("kernel", "counter", "dispatches", "mean_per_dispatch"))
+            for (k, c), (m, n) in sorted(counter_means(path).items()):
+                print("%-28s %-12s %10d %16.1f" % (k[:28], c, n, m))
+
+
+def traffic_from(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, workload):
+    """HBM bytes per stage call: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) summed over a
+    stage's kernels, each scaled by what the counter reads for a copy of known size."""
+    def copy_factor(path, counter):
+        vals = [(m, n) for (k, c), (m, n) in counter_means(path).items()
+                if c == counter and "copy" in k.lower()]
+        if not vals:
+            raise SystemExit("no copy kernel in %s" % path)
+        m = max(v[0] for v in vals)  # the large copy (the fill kernel is not a copy)
+        return m * 1024.0 / copy_bytes
+    ff = copy_factor(copy_fetch_csv, "FETCH_SIZE")
+    wf = copy_factor(copy_write_csv, "WRITE_SIZE")
+    fm, wm = counter_means(fetch_csv), counter_means(write_csv)
+    out = {"workload": workload, "copy_bytes": copy_bytes, "fetch_factor": round(ff, 4),
+           "write_factor": round(wf, 4), "stages": {}}
+    for st, prefixes in STAGE_KERNELS.items():
+        kern = sorted({k for (k, c) in fm if c == "FETCH_SIZE" and k.startswith(prefixes)})
+        if not kern:
+            continue
+        # calls of the stage = dispatches of its most frequent kernel
+        calls = max(fm[(k, "FETCH_SIZE")][1] for k in kern)
+        fetch = sum(fm[(k, "FETCH_SIZE")][0] * fm[(k, "FETCH_SIZE")][1] for k in kern) / calls
+        write = sum(wm[(k, "WRITE_SIZE")][0] * wm[(k, "WRITE_SIZE")][1] for k in kern
+                    if (k, "WRITE_SIZE") in wm) / calls
+        out["stages"][st] = {"kernels": kern, "calls": calls, "fetch_kib_per_call": round(fetch, 1),
+                             "write_kib_per_call": round(write, 1),
+                             "hbm_bytes_per_call": round(fetch * 1024.0 / ff + write * 1024.0 / wf),
+                             "source_sha256": source_digest(st)}
+    print(json.dumps(out, indent=1))
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per call of a stage from the committed counter summary, or None when there is
+    none for this workload or the stage's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    st = d.get("stages", {}).get(stage)
+    if not st or st.get("source_sha256") != source_digest(stage):
+        return None
+    return st["hbm_bytes_per_call"]
+
+
+def copy_calibration(mib, copies):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(copies):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": copies}))
+
+
 def main():
     args = parse()
+    if args.rocprof_summary:
+        return rocprof_summary(args.rocprof_summary)
+    if args.traffic_from:
+        return traffic_from(*args.traffic_from, copy_bytes=args.copy_mib << 20, workload=args.workload)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps)
     import torch
     from deepseek_sparse_mla_amd import synth  # noqa: F401
 
@@ -233,8 +356,14 @@ def main():
     else:
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
         achieved = st_model["bytes"] / (dur[dominant] * 1e-3) / 1e9
-    kernel_names = {"indexer": "idx_fp8_kernel" if prefill else "idx_decode_kernel", "topk": "topk_kernel",
-                    "mla": "mla_kernel"}
+    split = runners[0].ws is not None and runners[0].ws.numel() > 0
+    kernel_names = {
+        "indexer": "dsa_index_scores: " + ("idx_fp8_kernel" if prefill else "idx_decode_kernel"),
+        "topk": "dsa_topk: " + ("topk_hist_kernel + " if probe.max_ctx > 8192 else "") + "topk_select_kernel",
+        "mla": ("sparse_mla_prefill: " if prefill else "sparse_mla_decode%s: " % ("_shared" if len(probe.layers) > 1 else ""))
+        + ("mla_fp8_kernel" if probe.layers[0].kv_dt == "fp8" else "mla_kernel")
+        + (" + mla_combine_kernel" if split else ""),
+    }
     path_gbs = model["path_bytes"] / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": "decode query-tokens/s (indexer+top-2048+sparse MLA) and % of peak HBM GB/s",
@@ -259,7 +388,7 @@ def main():
         "roofline": {"kernel": kernel_names[dominant], "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic": st_model["bytes"] if bound == "hbm" else st_model["flops"],
-                     "traffic": None},
+                     "traffic": measured_traffic(args.workload, dominant)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(probe, args.cpu_seconds)
