@@ -454,6 +454,7 @@ constexpr int F_TILEB = M_TILE * F_ROWB;      // 37888 B per tile buffer
 constexpr int F_DMA = F_TILEB / 1024;         // 37 wave-wide 1 KB loads per tile
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
 {
@@ -467,8 +468,7 @@ __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
 // reads are waited for once.
 constexpr int F_DMA_PER_WAVE = (F_DMA + 3) / 4;  // 10 (the last only on wave 0)
 
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t seq, char *buf, const int32_t *sidx, int w,
-                                         int lane)
+__device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, const int32_t *sidx, int w, int lane)
 {
     int voff[F_DMA_PER_WAVE];
 #pragma unroll
@@ -479,14 +479,22 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t seq, char *buf, 
         const int32_t idx = sidx[row];
         voff[q] = (col < 576 && idx >= 0) ? idx * 576 + col : (int)0x80000000;
     }
+    // Issued as inline asm: the compiler then neither tracks these loads nor orders LDS reads
+    // of the other buffer after them; tile_barrier() waits for them explicitly.  M0 holds the
+    // LDS destination (one wait state after writing it); nothing else in these kernels uses
+    // M0, so clobbering the reserved register is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
     for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
         const int u = 4 * q + w;
         if (q + 1 < F_DMA_PER_WAVE || u < F_DMA)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                seq, (void __attribute__((address_space(3))) *)((__attribute__((address_space(3))) char *)(buf + 1024 * u)),
-                16, voff[q], 0, 0, 0);
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(lds_base + 1024u * (uint32_t)u), "v"(voff[q]), "s"(seq)
+                         : "memory", "m0");
     }
+#pragma clang diagnostic pop
 }
 
 // Shared epilogue: normalised output (one split) or the split partial.
@@ -547,10 +555,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
                                                                int64_t pairs_per_xcd, float *__restrict__ ws_o,
                                                                float *__restrict__ ws_ml)
 {
-    // two separate arrays (not one indexed by parity): the compiler then knows that reads
-    // of one buffer do not wait for the gathers into the other
-    __shared__ __attribute__((aligned(16))) char ktA[F_TILEB];
-    __shared__ __attribute__((aligned(16))) char ktB[F_TILEB];
+    __shared__ __attribute__((aligned(16))) char kt8[2][F_TILEB];
     __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
     __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
     __shared__ float xm[4][32];
@@ -606,14 +611,19 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
         O[mt] = f32x16{};
 
     const int64_t seq_bytes = r.n * 576;  // host guarantees max_ctx * 576 < 2^31
-    const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint8_t *)Ld.kv + r.kv_base * 576), (short)0, (int)seq_bytes, BUF_DWORD3);
+    i32x4 seq;  // buffer descriptor of this sequence's rows (stride 0, range = its bytes)
+    {
+        const uint64_t base = (uint64_t)((const uint8_t *)Ld.kv + r.kv_base * 576);
+        seq[0] = (int)(uint32_t)base;
+        seq[1] = (int)((uint32_t)(base >> 32) & 0xFFFFu);
+        seq[2] = (int)seq_bytes;
+        seq[3] = BUF_DWORD3;
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&kt8[0][0];
 
     // rows with index -1 may be skipped by the DMA: start from finite (zero) data
-    for (int e = tid; e < F_TILEB / 16; e += M_THREADS) {
-        ((u32x4 *)ktA)[e] = u32x4{0u, 0u, 0u, 0u};
-        ((u32x4 *)ktB)[e] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int e = tid; e < 2 * F_TILEB / 16; e += M_THREADS)
+        ((u32x4 *)&kt8[0][0])[e] = u32x4{0u, 0u, 0u, 0u};
 
     // V^T read geometry: 16-lane group G covers dims +16 * (G & 1), keys +8 * (G >> 1)
     const int mq = lane & 15;
@@ -639,19 +649,18 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
             sh_flag = 0;
         lds_barrier();  // Q stays in flight
         if (ntiles > 0)
-            dma_tile(seq, ktA, sidx[0], w, lane);
+            dma_tile(seq, lds0, sidx[0], w, lane);
         int32_t idx_next = i2;
         tile_barrier();
 
-        // one tile; BUF (compile-time) picks the LDS buffer that holds it
-        auto tile_step = [&](auto buf_tag, int tt) {
-            constexpr int buf = decltype(buf_tag)::value;
-            const char *tile = buf ? ktB : ktA;
+        for (int tt = 0; tt < ntiles; ++tt) {
+            const int buf = tt & 1;
+            const char *tile = kt8[buf];
+            const bool restart = (pass == 1 && tt == 0);
             if (tt + 1 < ntiles)
-                dma_tile(seq, buf ? ktA : ktB, sidx[buf ^ 1], w, lane);
+                dma_tile(seq, lds0 + (uint32_t)(buf ^ 1) * F_TILEB, sidx[buf ^ 1], w, lane);
             const int32_t idx_after = tid < M_TILE ? load_idx(tt + 3) : -1;
             const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
-            const bool restart = (pass == 1 && tt == 0);
 
             // ---- 1. S^T partials (keys 0..31 -> S[0], 32..63 -> S[1]) over this wave's dims
             f32x16 S[2] = {f32x16{}, f32x16{}};
@@ -770,12 +779,6 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
                 sidx[buf][tid] = idx_next;  // tile tt + 2
             idx_next = idx_after;
             tile_barrier();  // tile tt + 1 has landed; this buffer is free
-        };
-        for (int tt = 0; tt < ntiles; tt += 2) {
-            tile_step(std::integral_constant<int, 0>{}, tt);
-            if (tt + 1 >= ntiles)
-                break;
-            tile_step(std::integral_constant<int, 1>{}, tt + 1);
         }
         if (ovf)
             sh_flag = 1;
