@@ -137,6 +137,55 @@ __device__ __forceinline__ int64_t xcd_pair(int64_t pairs_per_xcd)
     return (b & 7) * pairs_per_xcd + (b >> 3);
 }
 
+// Epilogue shared by the sparse-MLA kernels: the normalised output (one split), or this
+// split's partial: O / l in the output's precision (fp32, or bf16 for a bf16 output, like the
+// output itself) plus (reference max, l) in fp32 for the combine.  Wave (hh, dq) owns dims
+// 256*dq + 32*mt + 8*q4 + 4*g + 0..3 of head 32*hh + j.
+template <bool OUT_F32>
+__device__ __forceinline__ void mla_store(const f32x16 (&O)[8], float l_run, float m_ref, const MlaLayerDev &Ld,
+                                          int64_t i, int64_t orow, int split, int nsplit, int dq, int g, int head,
+                                          float *__restrict__ ws_o, float *__restrict__ ws_ml)
+{
+    if (nsplit == 1) {
+        const float inv = (l_run > 0.f) ? Ld.kv_scale / l_run : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
+                const int64_t o = (i * M_H + head) * M_DC + d;
+                const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
+                const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
+                if (OUT_F32)
+                    *(f32x4 *)((float *)Ld.out + o) = f32x4{v0, v1, v2, v3};
+                else
+                    *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            }
+        if (Ld.lse && dq == 0 && g == 0)
+            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
+        return;
+    }
+    const int64_t pbase = ((orow * nsplit + split) * M_H + head) * M_DC;
+    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
+            const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
+            const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
+            if (OUT_F32)
+                *(f32x4 *)(ws_o + pbase + d) = f32x4{v0, v1, v2, v3};
+            else
+                *(u32x2 *)((uint16_t *)ws_o + pbase + d) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
+    if (dq == 0 && g == 0) {
+        float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
+        pml[0] = m_ref;
+        pml[1] = l_run;
+    }
+}
+
 //
 // Wave w of the block: hh = w & 1 owns heads 32*hh .. +31 and dq = w >> 1 owns half of the
 // 576-long contraction for S, the keys 32*dq .. +31 of each tile for the softmax, and half
@@ -409,40 +458,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     __syncthreads();
     l_run = dq ? (xm[wp][j] + l_run) : (l_run + xm[wp][j]);
 
-    // ---- epilogue: wave owns dims 256*dq + 32*mt + 8*q4 + 4*g + 0..3 of head 32*hh + j
-    const int head = 32 * hh + j;
-    if (nsplit == 1) {
-        const float inv = (l_run > 0.f) ? Ld.kv_scale / l_run : 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-                const int64_t o = (i * M_H + head) * M_DC + d;
-                const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
-                const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
-                if (OUT_F32)
-                    *(f32x4 *)((float *)Ld.out + o) = f32x4{v0, v1, v2, v3};
-                else
-                    *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            }
-        if (Ld.lse && dq == 0 && g == 0)
-            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
-        return;
-    }
-    float *po = ws_o + ((orow * nsplit + split) * M_H + head) * M_DC;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-            *(f32x4 *)(po + d) = f32x4{O[mt][4 * q4], O[mt][4 * q4 + 1], O[mt][4 * q4 + 2], O[mt][4 * q4 + 3]};
-        }
-    if (dq == 0 && g == 0) {
-        float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
-        pml[0] = m_ref;
-        pml[1] = l_run;
-    }
+    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -456,6 +472,13 @@ constexpr int F_DMA = F_TILEB / 1024;         // 37 wave-wide 1 KB loads per til
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Value of lane l ^ 32 (g = lane >> 5), through one v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float other_half(float x, int g)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(g ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
 {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -468,16 +491,30 @@ __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
 // reads are waited for once.
 constexpr int F_DMA_PER_WAVE = (F_DMA + 3) / 4;  // 10 (the last only on wave 0)
 
-__device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, const int32_t *sidx, int w, int lane)
+// Lane geometry of the gather, fixed per lane: DMA instruction q of wave w covers bytes
+// 1024*(4q + w) + 16*lane of the tile, i.e. row rc & 0xFF, column rc >> 8 (0xFFFF: the
+// pad bytes, or an instruction past the tile, which reads zeros).
+__device__ __forceinline__ void dma_geometry(int w, int lane, uint32_t (&rc)[F_DMA_PER_WAVE])
+{
+#pragma unroll
+    for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
+        const int o = 1024 * (4 * q + w) + 16 * lane;
+        const int row = min(o / F_ROWB, M_TILE - 1);
+        const int col = o - (o / F_ROWB) * F_ROWB;
+        const bool real = o < F_TILEB && col < 576;
+        rc[q] = (uint32_t)row | ((real ? (uint32_t)col : 0xFFFFu) << 8);
+    }
+}
+
+__device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, const int32_t *sidx, int w,
+                                         const uint32_t (&rc)[F_DMA_PER_WAVE])
 {
     int voff[F_DMA_PER_WAVE];
 #pragma unroll
     for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
-        const int o = 1024 * (4 * q + w) + 16 * lane;
-        const int row = min(o / F_ROWB, M_TILE - 1);  // u >= 37 (not issued) is clamped
-        const int col = o - row * F_ROWB;
-        const int32_t idx = sidx[row];
-        voff[q] = (col < 576 && idx >= 0) ? idx * 576 + col : (int)0x80000000;
+        const int32_t idx = sidx[rc[q] & 0xFFu];
+        const uint32_t col = rc[q] >> 8;
+        voff[q] = (col != 0xFFFFu && idx >= 0) ? idx * 576 + (int)col : (int)0x80000000;
     }
     // Issued as inline asm: the compiler then neither tracks these loads nor orders LDS reads
     // of the other buffer after them; tile_barrier() waits for them explicitly.  M0 holds the
@@ -497,55 +534,23 @@ __device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, co
 #pragma clang diagnostic pop
 }
 
-// Shared epilogue: normalised output (one split) or the split partial.
-template <bool OUT_F32>
-__device__ __forceinline__ void mla_store(const f32x16 (&O)[8], float l_run, float m_ref, const MlaLayerDev &Ld,
-                                          int64_t i, int64_t orow, int split, int nsplit, int dq, int g, int head,
-                                          float *__restrict__ ws_o, float *__restrict__ ws_ml)
-{
-    if (nsplit == 1) {
-        const float inv = (l_run > 0.f) ? Ld.kv_scale / l_run : 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-                const int64_t o = (i * M_H + head) * M_DC + d;
-                const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
-                const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
-                if (OUT_F32)
-                    *(f32x4 *)((float *)Ld.out + o) = f32x4{v0, v1, v2, v3};
-                else
-                    *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            }
-        if (Ld.lse && dq == 0 && g == 0)
-            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
-        return;
-    }
-    float *po = ws_o + ((orow * nsplit + split) * M_H + head) * M_DC;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-            *(f32x4 *)(po + d) = f32x4{O[mt][4 * q4], O[mt][4 * q4 + 1], O[mt][4 * q4 + 2], O[mt][4 * q4 + 3]};
-        }
-    if (dq == 0 && g == 0) {
-        float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
-        pml[0] = m_ref;
-        pml[1] = l_run;
-    }
-}
 
 //
-// Same wave roles and math as mla_kernel (see above); differences:
-//  * tile t + 1 is gathered by DMA into the other LDS buffer while tile t is computed, and
-//    the barriers inside a tile wait only for LDS traffic;
+// Same wave roles and math as mla_kernel (see above), software-pipelined over tiles:
+//  * tiles are gathered by DMA into three LDS buffers, two tiles ahead, kept fp8 there and
+//    widened to bf16 in registers when read;
+//  * the MFMA phase of step t runs O^T += V^T.P^T for tile t interleaved with the S^T
+//    partials of tile t+1, so the two independent MFMA streams hide each other's operand
+//    latency; the softmax of tile t+1 follows;
 //  * S operands: 16 fp8 bytes per lane (two k-steps) widened to bf16; Q^T is loaded in the
 //    same permuted dim order (k-step 2p + h of lane half g covers dims 288dq + 32p + 16g +
 //    8h .. +7), which leaves the contraction unchanged;
 //  * V^T operands: ds_read_b64_tr_b8 gives a lane 8 consecutive keys of one dim; P is put
-//    in the same consecutive-key order by one v_permlane32_swap per dword.
+//    in the same consecutive-key order by one v_permlane32_swap per dword;
+//  * softmax without rescaling, as in mla_kernel: each head fixes its reference maximum at
+//    its first non-empty tile; if a later logit exceeds it by more than 2^100 the split is
+//    run again (a separate, cold copy of the tile loop) with the exact maximum of the first
+//    run, so the hot loop never touches O outside its MFMAs.
 //
 template <bool OUT_F32>
 __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int64_t T, int64_t n_rows,
@@ -555,11 +560,11 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
                                                                int64_t pairs_per_xcd, float *__restrict__ ws_o,
                                                                float *__restrict__ ws_ml)
 {
-    __shared__ __attribute__((aligned(16))) char kt8[2][F_TILEB];
+    __shared__ __attribute__((aligned(16))) char kt8[3][F_TILEB];
     __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
     __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
-    __shared__ float xm[4][32];
-    __shared__ int32_t sidx[2][M_TILE];
+    __shared__ float xm[4][32];                                    // per-head maxima swap
+    __shared__ int32_t sidx[3][M_TILE];
     __shared__ int sh_flag;
 
     const int64_t pair = xcd_pair(pairs_per_xcd);
@@ -587,12 +592,13 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
         const int slot = (t_begin + tt) * M_TILE + tid;
         return (tt < ntiles && slot < k) ? irow[slot] : -1;
     };
-    // the first three tiles' indices are loaded before Q so that their latency overlaps it
-    int32_t i0 = -1, i1 = -1, i2 = -1;
+    // the first tiles' indices are loaded before Q so that their latency overlaps it
+    int32_t i0 = -1, i1 = -1, i2 = -1, i3 = -1;
     if (tid < M_TILE) {
         i0 = load_idx(0);
         i1 = load_idx(1);
         i2 = load_idx(2);
+        i3 = load_idx(3);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -614,178 +620,204 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     i32x4 seq;  // buffer descriptor of this sequence's rows (stride 0, range = its bytes)
     {
         const uint64_t base = (uint64_t)((const uint8_t *)Ld.kv + r.kv_base * 576);
-        seq[0] = (int)(uint32_t)base;
-        seq[1] = (int)((uint32_t)(base >> 32) & 0xFFFFu);
-        seq[2] = (int)seq_bytes;
+        // uniform by construction; readfirstlane keeps it in SGPRs for the asm operand
+        seq[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+        seq[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
+        seq[2] = __builtin_amdgcn_readfirstlane((int)seq_bytes);
         seq[3] = BUF_DWORD3;
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&kt8[0][0];
+    uint32_t rc[F_DMA_PER_WAVE];
+    dma_geometry(w, lane, rc);
 
     // rows with index -1 may be skipped by the DMA: start from finite (zero) data
-    for (int e = tid; e < 2 * F_TILEB / 16; e += M_THREADS)
+    for (int e = tid; e < 3 * F_TILEB / 16; e += M_THREADS)
         ((u32x4 *)&kt8[0][0])[e] = u32x4{0u, 0u, 0u, 0u};
+    if (tid == 0)
+        sh_flag = 0;
 
     // V^T read geometry: 16-lane group G covers dims +16 * (G & 1), keys +8 * (G >> 1)
     const int mq = lane & 15;
     const int voffs = (8 * (lane >> 5) + (mq >> 1)) * F_ROWB + 256 * dq + 16 * ((lane >> 4) & 1) + 8 * (mq & 1);
+    const char *arow0 = &kt8[0][0] + j * F_ROWB + 288 * dq + 16 * g;  // S operand row of buffer 0
 
     float m_ref = -INFINITY, m_seen = -INFINITY, l_own = 0.f;
-    for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 1) {
-            if (!sh_flag)
-                break;
-            if (g == 0)
-                xm[w][j] = m_seen;
-            __syncthreads();
-            m_ref = fmaxf(m_seen, xm[wp][j]);
-            l_own = 0.f;  // i0 .. i2 still hold the first three tiles' indices
+    bool ovf = false;
+    f32x16 S[2];
+    bf16x8 bop[4];  // P^T operands of the tile whose PV runs next (4 steps of 16 keys)
+
+    // ---- S^T partial step p (k-steps 2p, 2p+1) of the tile in buffer kb
+    auto s_load = [&](int kb, int p, u32x4 (&A)[2]) {
+        const char *a = arow0 + kb * F_TILEB + 32 * p;
+        A[0] = *(const u32x4 *)a;
+        A[1] = *(const u32x4 *)(a + 32 * F_ROWB);
+    };
+    auto s_mfma = [&](const u32x4 (&A)[2], int p) {
+        const bf16x8 a00 = fp8x8_to_bf16x8(A[0][0], A[0][1]), a10 = fp8x8_to_bf16x8(A[1][0], A[1][1]);
+        const bf16x8 a01 = fp8x8_to_bf16x8(A[0][2], A[0][3]), a11 = fp8x8_to_bf16x8(A[1][2], A[1][3]);
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a00, qT[2 * p], S[0], 0, 0, 0);
+        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a10, qT[2 * p], S[1], 0, 0, 0);
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a01, qT[2 * p + 1], S[0], 0, 0, 0);
+        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a11, qT[2 * p + 1], S[1], 0, 0, 0);
+    };
+    // ---- PV step u (keys 16u .. 16u+15) of the tile in buffer vb, dims 256dq + 32mt + ..
+    auto v_load = [&](int vb, int u, i32x2 (&V)[8]) {
+        const char *v = &kt8[0][0] + vb * F_TILEB + voffs + (32 * (u >> 1) + 16 * (u & 1)) * F_ROWB;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            V[mt] = lds_tr8(v + 32 * mt);
+    };
+    auto pv_mfma = [&](const i32x2 (&V)[8], const bf16x8 &b, int mt0) {
+#pragma unroll
+        for (int mt = mt0; mt < mt0 + 4; ++mt)
+            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                fp8x8_to_bf16x8((uint32_t)V[mt][0], (uint32_t)V[mt][1]), b, O[mt], 0, 0, 0);
+    };
+
+    // ---- softmax of the tile whose S^T partials are in S (indices sx): fixes bop
+    auto softmax = [&](const int32_t *sx) {
+        const uint64_t valid = __ballot(sx[lane] >= 0);
+        {  // swap the half partials; s = full S^T for keys 32*dq + .. (this wave's)
+            const f32x16 give = dq ? S[0] : S[1];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                xs[w][q4][lane] = f32x4{give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]};
         }
-        bool ovf = false;
+        lds_barrier();
+        f32x16 s = dq ? S[1] : S[0];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 o = xs[wp][q4][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s[4 * q4 + e] = dq ? (o[e] + s[4 * q4 + e]) : (s[4 * q4 + e] + o[e]);
+        }
+        const uint32_t vkeys = (uint32_t)(valid >> (32 * dq)) >> (4 * g);
+        const bool full = valid == ~0ull;
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const bool ok = full || ((vkeys >> (8 * (rr >> 2) + (rr & 3))) & 1u);
+            s[rr] = ok ? s[rr] * c2 : -INFINITY;
+            mloc = fmaxf(mloc, s[rr]);
+        }
+        mloc = fmaxf(mloc, other_half(mloc, g));
+        if (m_ref == -INFINITY && valid != 0ull) {  // first non-empty tile (block-uniform)
+            if (g == 0)
+                xm[w][j] = mloc;
+            lds_barrier();
+            m_ref = fmaxf(mloc, xm[wp][j]);
+            lds_barrier();
+        }
+        m_seen = fmaxf(m_seen, mloc);
+        ovf |= mloc > m_ref + 100.f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float p0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q] - m_ref);
+            const float p1 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q + 1] - m_ref);
+            l_own += p0 + p1;
+            pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+        }
+        xp[w][0][lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        xp[w][1][lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+        lds_barrier();
+        const u32x4 pp0 = xp[wp][0][lane], pp1 = xp[wp][1][lane];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int khu = u >> 1, jj = u & 1;
+            const u32x4 own = jj ? u32x4{pk[4], pk[5], pk[6], pk[7]} : u32x4{pk[0], pk[1], pk[2], pk[3]};
+            const u32x4 pw = (khu == dq) ? own : (jj ? pp1 : pp0);
+            // keys 4g..4g+3 (dwords 0,1) and 8+4g..8+4g+3 (dwords 2,3) -> 8g'..8g'+7
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+            bop[u] = __builtin_bit_cast(bf16x8, u32x4{s0[0], s1[0], s0[1], s1[1]});
+        }
+    };
+
+    auto run = [&]() {
         if (tid < M_TILE) {
             sidx[0][tid] = i0;
             sidx[1][tid] = i1;
+            sidx[2][tid] = i2;
         }
-        if (tid == 0)
-            sh_flag = 0;
+        int32_t idx_next = tid < M_TILE ? i3 : -1;
         lds_barrier();  // Q stays in flight
         if (ntiles > 0)
-            dma_tile(seq, lds0, sidx[0], w, lane);
-        int32_t idx_next = i2;
-        tile_barrier();
+            dma_tile(seq, lds0, sidx[0], w, rc);
+        if (ntiles > 1)
+            dma_tile(seq, lds0 + F_TILEB, sidx[1], w, rc);
+        tile_barrier();  // tiles 0 and 1 (and Q) have landed
+        if (ntiles > 0) {
+            S[0] = f32x16{};
+            S[1] = f32x16{};
+            u32x4 A[2][2];
+            s_load(0, 0, A[0]);
+#pragma unroll
+            for (int p = 0; p < 9; ++p) {
+                if (p + 1 < 9)
+                    s_load(0, p + 1, A[(p + 1) & 1]);
+                s_mfma(A[p & 1], p);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            softmax(sidx[0]);
+        }
 
         for (int tt = 0; tt < ntiles; ++tt) {
-            const int buf = tt & 1;
-            const char *tile = kt8[buf];
-            const bool restart = (pass == 1 && tt == 0);
-            if (tt + 1 < ntiles)
-                dma_tile(seq, lds0 + (uint32_t)(buf ^ 1) * F_TILEB, sidx[buf ^ 1], w, lane);
-            const int32_t idx_after = tid < M_TILE ? load_idx(tt + 3) : -1;
-            const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
+            const int b0 = tt % 3, b1 = (tt + 1) % 3, b2 = (tt + 2) % 3;
+            if (tt + 2 < ntiles)
+                dma_tile(seq, lds0 + (uint32_t)b2 * F_TILEB, sidx[b2], w, rc);
+            const int32_t idx_after = tid < M_TILE ? load_idx(tt + 4) : -1;
 
-            // ---- 1. S^T partials (keys 0..31 -> S[0], 32..63 -> S[1]) over this wave's dims
-            f32x16 S[2] = {f32x16{}, f32x16{}};
+            // ---- MFMA phase: PV of tile tt interleaved with S of tile tt+1 (on the last tile the
+            // S half runs over a stale buffer and its result is dropped: finite data, no branch)
+            S[0] = f32x16{};
+            S[1] = f32x16{};
             {
-                const char *arow = tile + j * F_ROWB + 288 * dq + 16 * g;
                 u32x4 A[2][2];
-                A[0][0] = *(const u32x4 *)(arow);
-                A[0][1] = *(const u32x4 *)(arow + 32 * F_ROWB);
-#pragma unroll
-                for (int p = 0; p < 9; ++p) {
-                    const int cur = p & 1;
-                    if (p + 1 < 9) {
-                        A[cur ^ 1][0] = *(const u32x4 *)(arow + 32 * (p + 1));
-                        A[cur ^ 1][1] = *(const u32x4 *)(arow + 32 * F_ROWB + 32 * (p + 1));
-                    }
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const u32x4 a = A[cur][kk];
-                        S[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(a[0], a[1]), qT[2 * p],
-                                                                        S[kk], 0, 0, 0);
-                        S[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(a[2], a[3]), qT[2 * p + 1],
-                                                                        S[kk], 0, 0, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-
-            // ---- 2. swap the half partials; s = full S^T for keys 32*dq + .. (this wave's)
-            {
-                const f32x16 give = dq ? S[0] : S[1];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    xs[w][q4][lane] = f32x4{give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]};
-            }
-            lds_barrier();
-            f32x16 s = dq ? S[1] : S[0];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 o = xs[wp][q4][lane];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[4 * q4 + e] = dq ? (o[e] + s[4 * q4 + e]) : (s[4 * q4 + e] + o[e]);
-            }
-
-            // ---- 3. softmax numerators of the own 32 keys
-            const uint32_t vkeys = (uint32_t)(valid >> (32 * dq)) >> (4 * g);
-            const bool full = valid == ~0ull;
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const bool ok = full || ((vkeys >> (8 * (rr >> 2) + (rr & 3))) & 1u);
-                s[rr] = ok ? s[rr] * c2 : -INFINITY;
-                mloc = fmaxf(mloc, s[rr]);
-            }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            if (m_ref == -INFINITY && valid != 0ull) {  // first non-empty tile (block-uniform)
-                if (g == 0)
-                    xm[w][j] = mloc;
-                lds_barrier();
-                m_ref = fmaxf(mloc, xm[wp][j]);
-                lds_barrier();
-            }
-            m_seen = fmaxf(m_seen, mloc);
-            ovf |= mloc > m_ref + 100.f;
-            uint32_t pk[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float p0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q] - m_ref);
-                const float p1 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q + 1] - m_ref);
-                l_own += p0 + p1;
-                pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
-            }
-            xp[w][0][lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-            xp[w][1][lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-            lds_barrier();
-            const u32x4 pp0 = xp[wp][0][lane], pp1 = xp[wp][1][lane];
-
-            // ---- 4. O^T += V^T . P^T over the 64 keys (4 steps of 16 keys)
-            {
                 i32x2 V[2][8];
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-                    V[0][mt] = lds_tr8(tile + voffs + 32 * mt);
+                s_load(b1, 0, A[0]);
+                v_load(b0, 0, V[0]);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int cur = u & 1;
-                    if (u + 1 < 4) {
-                        const int un = u + 1;
-                        const char *vb = tile + voffs + (32 * (un >> 1) + 16 * (un & 1)) * F_ROWB;
-#pragma unroll
-                        for (int mt = 0; mt < 8; ++mt)
-                            V[cur ^ 1][mt] = lds_tr8(vb + 32 * mt);
-                    }
-                    const int khu = u >> 1, jj = u & 1;
-                    u32x4 pw;
-                    if (khu == dq)
-                        pw = jj ? u32x4{pk[4], pk[5], pk[6], pk[7]} : u32x4{pk[0], pk[1], pk[2], pk[3]};
-                    else
-                        pw = jj ? pp1 : pp0;
-                    // keys 4g..4g+3 (dwords 0,1) and 8+4g..8+4g+3 (dwords 2,3) -> 8g'..8g'+7
-                    const auto s0 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-                    const auto s1 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{s0[0], s1[0], s0[1], s1[1]});
-#pragma unroll
-                    for (int mt = 0; mt < 8; ++mt) {
-                        const bf16x8 a8 = fp8x8_to_bf16x8((uint32_t)V[cur][mt][0], (uint32_t)V[cur][mt][1]);
-                        if (restart && u == 0)  // first MFMA of a rerun: drop pass 0's sums
-                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, bop, f32x16{}, 0, 0, 0);
-                        else
-                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, bop, O[mt], 0, 0, 0);
-                    }
+                    if (u + 1 < 4)
+                        v_load(b0, u + 1, V[(u + 1) & 1]);
+                    s_load(b1, 2 * u + 1, A[1]);
+                    s_mfma(A[0], 2 * u);
+                    pv_mfma(V[u & 1], bop[u], 0);
+                    s_load(b1, 2 * u + 2, A[0]);
+                    s_mfma(A[1], 2 * u + 1);
+                    pv_mfma(V[u & 1], bop[u], 4);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                s_mfma(A[0], 8);
             }
+            if (tt + 1 < ntiles)
+                softmax(sidx[b1]);
             if (tid < M_TILE)
-                sidx[buf][tid] = idx_next;  // tile tt + 2
+                sidx[b0][tid] = idx_next;  // tile tt + 3
             idx_next = idx_after;
-            tile_barrier();  // tile tt + 1 has landed; this buffer is free
+            tile_barrier();  // tile tt + 2 has landed; buffer b0 is free
         }
-        if (ovf)
-            sh_flag = 1;
+    };
+    run();
+    if (ovf)
+        sh_flag = 1;
+    __syncthreads();
+    if (sh_flag) {  // rare: rerun with the exact maximum of the first run as the reference
+        if (g == 0)
+            xm[w][j] = m_seen;
         __syncthreads();
+        m_ref = fmaxf(m_seen, xm[wp][j]);
+        l_own = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            O[mt] = f32x16{};
+        __syncthreads();
+        run();
     }
 
-    float l_run = l_own + __shfl_xor(l_own, 32, 64);
+    float l_run = l_own + other_half(l_own, g);
     __syncthreads();
     if (g == 0)
         xm[w][j] = l_run;
@@ -795,7 +827,8 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
 }
 
 // Combine the split partials of every (output row, head), in split order.  One 128-thread
-// block per (row, head); thread t owns dims 4t .. 4t + 3.
+// block per (row, head); thread t owns dims 4t .. 4t + 3.  Partial s holds O_s / l_s, so
+// its weight is l_s 2^(m_s - M) / sum over splits of the same.
 template <bool OUT_F32>
 __global__ __launch_bounds__(128) void mla_combine_kernel(int64_t T, MlaLayersDev layers, int nsplit,
                                                           const float *__restrict__ ws_o,
@@ -822,15 +855,23 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int64_t T, MlaLayersDe
             tot += __shfl(e * ls, s2, 64);
         const float inv = tot > 0.f ? Ld.kv_scale / tot : 0.f;
         if (sp < nsplit)
-            wts[sp] = e * inv;
+            wts[sp] = e * ls * inv;  // partials are O / l
         if (tid == 0)
             lse_s = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
     }
     __syncthreads();
-    const float *pbase = ws_o + (orow * nsplit * M_H + head) * M_DC + 4 * tid;
+    const int64_t pbase = (orow * nsplit * M_H + head) * M_DC + 4 * tid;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int sp = 0; sp < nsplit; ++sp) {
-        const f32x4 v = *(const f32x4 *)(pbase + (int64_t)sp * M_H * M_DC);
+        const int64_t pe = pbase + (int64_t)sp * M_H * M_DC;
+        f32x4 v;
+        if (OUT_F32) {
+            v = *(const f32x4 *)(ws_o + pe);
+        } else {
+            const u32x2 b = *(const u32x2 *)((const uint16_t *)ws_o + pe);
+            v = f32x4{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xFFFF0000u),
+                      __uint_as_float(b[1] << 16), __uint_as_float(b[1] & 0xFFFF0000u)};
+        }
         const float wgt = wts[sp];
         acc[0] = fmaf(wgt, v[0], acc[0]);
         acc[1] = fmaf(wgt, v[1], acc[1]);

@@ -194,12 +194,50 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
         const DigitPick p0 = pick_digit(hist, TK_BINS, kk, wsum, sh);
         const uint32_t count_ge = p0.above + p0.count;
         if (count_ge <= (uint32_t)TK_CAP) {
+            // one pass over the row: 16-byte loads, four in flight per thread, and one LDS
+            // atomic per wave (ballot + popcount give each lane its slot)
             const uint32_t lo_key = p0.digit << 21;
-            for (int64_t s = tid; s < n; s += TK_THREADS) {
-                const uint32_t key = score_key(row[s]);
-                if (key >= lo_key)
-                    cand[atomicAdd(&sh_cnt, 1u)] = composite(key, s);
+            const int lane = tid & 63;
+            const uint64_t below = (1ull << lane) - 1ull;
+            auto take = [&](float x, int64_t s, bool in) {
+                const uint32_t key = score_key(x);
+                const bool hit = in && key >= lo_key;
+                const uint64_t b = __ballot(hit);
+                if (b == 0ull)
+                    return;
+                uint32_t base = 0;
+                if (lane == 0)
+                    base = atomicAdd(&sh_cnt, (uint32_t)__popcll(b));
+                base = __shfl(base, 0, 64);
+                if (hit)
+                    cand[base + (uint32_t)__popcll(b & below)] = composite(key, s);
+            };
+            const int64_t head = (int64_t)((4 - (((uintptr_t)row >> 2) & 3)) & 3);  // to 16-B alignment
+            const int64_t h = head < n ? head : n;
+            take(tid < h ? row[tid] : 0.f, tid, tid < h);
+            const float4 *row4 = (const float4 *)(row + h);
+            const int64_t n4 = (n - h) >> 2;
+            constexpr int U = 4;
+            for (int64_t b4 = 0; b4 < n4; b4 += (int64_t)U * TK_THREADS) {
+                float4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t j = b4 + (int64_t)u * TK_THREADS + tid;
+                    v[u] = j < n4 ? row4[j] : float4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t j = b4 + (int64_t)u * TK_THREADS + tid;
+                    const int64_t s0 = h + 4 * j;
+                    const bool in = j < n4;
+                    take(v[u].x, s0, in);
+                    take(v[u].y, s0 + 1, in);
+                    take(v[u].z, s0 + 2, in);
+                    take(v[u].w, s0 + 3, in);
+                }
             }
+            const int64_t tail0 = h + 4 * n4;  // fewer than 4 scores left
+            take(tail0 + tid < n ? row[tail0 + tid] : 0.f, tail0 + tid, tail0 + tid < n);
             m = count_ge;
             __syncthreads();
         } else {
