@@ -172,7 +172,8 @@ def topk_workspace(layout: Layout, ld: int, k: int, device="cuda") -> Optional[t
 
 def dsa_topk(layout: Layout, scores: torch.Tensor, k: int, indices: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Top-k positions int32 [T, k] (score desc, position asc; -1 padding)."""
+    """Top-k positions int32 [T, k]: the first min(k, n) positions under (score desc, position
+    asc), listed in ascending position order, then -1 padding."""
     lib = load_library()
     T, ld = scores.shape
     if indices is None:

@@ -7,24 +7,32 @@
 // Selection order: higher score first; equal scores (with -0 == +0) by lower position.
 // Each score maps to a monotone 32-bit key (sign-flipped IEEE bits, -0 folded into +0) and
 // each candidate to the 64-bit composite (key << 32) | ~position, which is unique per row,
-// so "larger composite first" is exactly that order.  The selected set is then written in
+// so "larger composite first" is exactly that order.  The selected set is written in
 // ascending position order (the attention over it does not depend on the order, and the
 // gathers it drives then walk the cache forwards).
 //
-// Rows longer than CAP take two kernels:
-//  K1  topk_hist_kernel   many blocks per row: an LDS histogram (one per wave) of the top 11
-//                         key bits of a chunk, added into the row's global histogram with
-//                         integer atomics (deterministic totals);
-//  K2  topk_select_kernel one 1024-thread block per row: the histogram gives the bin that
-//                         holds the k-th key; one pass gathers every score at or above that
-//                         bin into LDS (when they fit), an exact radix select over the
-//                         composites finds the k-th largest, and the selected positions are
-//                         marked in an LDS bitmap and compacted in position order.  K2
-//                         clears the row's histogram, so the workspace is zero again for the
-//                         next call.  Rows with at most CAP scores skip K1 and load directly.
-// If the scores at or above the threshold bin do not fit in LDS (heavily tied data), K2
-// falls back to radix passes over the row in global memory and an ordered compaction of
-// the ties (lowest positions first).
+// Method, per row of n scores (kk = min(k, n) are taken):
+//  1. a histogram of the top 11 key bits gives the bin d that holds the kk-th largest key
+//     and the count `above` of keys in higher bins;
+//  2. every position whose bin is above d is marked in a bitmap (whole 32-bit words built
+//     with one ballot per 64 positions, so no atomics); the keys in bin d (its "members")
+//     are collected as composites;
+//  3. an exact radix select over the members (11-bit digits below the first 11) finds the
+//     (kk - above)-th largest; members at or above it are marked too;
+//  4. a block scan over per-thread popcounts of consecutive bitmap words gives every marked
+//     position its output slot.
+// Three ways to run it:
+//  DIRECT  rows of at most 8192 scores: one 1024-thread block per row does everything,
+//          the histogram in LDS;
+//  ROW     many rows (prefill): topk_hist_kernel builds the histogram with many blocks per
+//          row; one block per row then reads its row once (bitmap in LDS);
+//  MB      few long rows (decode): topk_hist_kernel, then topk_mark_kernel marks the bitmap
+//          and collects the members with many blocks per row (global workspace), then one
+//          block per row selects among the members and compacts.
+// Integer atomics only; every result is bit-reproducible.  The kernels leave every byte of
+// the workspace they wrote zero again, so it can be reused as is for any layout.  If a
+// row's bin d holds more than 8192 keys (heavily tied scores), two more radix passes over
+// the row find the exact kk-th key and its ties are taken in position order.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -32,12 +40,65 @@ namespace dsa {
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_CAP = 8192;        // candidates held in LDS (64 KB of composites)
-constexpr int TK_BINS = 2048;       // 11-bit digits
-constexpr int TK_BMAP_BITS = 1 << 15;  // positions marked per bitmap pass (4 KB: two blocks per CU)
-constexpr int TK_BMAP_WORDS = TK_BMAP_BITS / 32;
-constexpr int H_THREADS = 256;      // histogram kernel
-constexpr int H_CHUNK = 8192;       // scores per histogram block
+constexpr int TK_CAP = 8192;          // members held in LDS (64 KB of composites)
+constexpr int TK_BINS = 2048;         // 11-bit digits
+constexpr int TK_ROW_BITS = 1 << 18;  // longest row of the ROW mode (32 KB LDS bitmap)
+constexpr int TK_MB_ROWS = 512;       // up to this many rows, long rows use the MB mode
+constexpr int H_THREADS = 256;        // histogram and mark kernels
+constexpr int H_CHUNK = 8192;         // scores per histogram / mark block
+
+enum TkMode { TK_DIRECT = 0, TK_ROW = 1, TK_MB = 2 };
+
+static int topk_mode(int64_t T, int64_t max_ctx)
+{
+    if (max_ctx <= TK_CAP)
+        return TK_DIRECT;
+    if (T <= TK_MB_ROWS || max_ctx > TK_ROW_BITS)
+        return TK_MB;
+    return TK_ROW;
+}
+
+// Workspace of the ROW and MB modes (MB only: counters, bitmaps and member lists).
+struct TkWs {
+    uint32_t *hist;  // [T][2048]
+    uint32_t *cnt;   // [T]
+    uint32_t *bits;  // [T][W]
+    uint64_t *memb;  // [T][TK_CAP]
+    int64_t W;       // bitmap words per row
+};
+
+static inline size_t al256(size_t x)
+{
+    return (x + 255) & ~(size_t)255;
+}
+
+size_t topk_workspace_bytes(int64_t T, int64_t max_ctx)
+{
+    const int mode = topk_mode(T, max_ctx);
+    if (mode == TK_DIRECT)
+        return 0;
+    size_t b = al256((size_t)T * TK_BINS * 4);
+    if (mode == TK_MB) {
+        const size_t W = (size_t)((max_ctx + 31) / 32);
+        b += al256((size_t)T * 4) + al256((size_t)T * W * 4) + al256((size_t)T * TK_CAP * 8);
+    }
+    return b;
+}
+
+static TkWs carve(void *ws, int64_t T, int64_t max_ctx)
+{
+    TkWs w{};
+    char *p = (char *)ws;
+    w.W = (max_ctx + 31) / 32;
+    w.hist = (uint32_t *)p;
+    p += al256((size_t)T * TK_BINS * 4);
+    w.cnt = (uint32_t *)p;
+    p += al256((size_t)T * 4);
+    w.bits = (uint32_t *)p;
+    p += al256((size_t)T * w.W * 4);
+    w.memb = (uint64_t *)p;
+    return w;
+}
 
 __device__ __forceinline__ uint32_t score_key(float x)
 {
@@ -50,6 +111,11 @@ __device__ __forceinline__ uint32_t score_key(float x)
 __device__ __forceinline__ uint64_t composite(uint32_t key, int64_t s)
 {
     return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
+}
+
+__device__ __forceinline__ uint32_t comp_pos(uint64_t v)
+{
+    return 0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull);
 }
 
 // Exclusive scan over the block (one value per thread, thread order).
@@ -78,43 +144,109 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, 
     return before + x - v;
 }
 
-// Given a histogram of nb bins (counts of candidates matching the current prefix) and the
-// number still needed, find the bin holding the need-th largest: returns the bin, the
-// count strictly above it and its own count.  Thread t owns bins nb-1-2t and nb-2-2t.
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
+    }
+    return x;
+}
+
+// Given a histogram of NB bins (a power of two, 256 .. 2048) and the number still needed
+// (1 <= need <= total), find the bin holding the need-th largest entry: the bin, the count
+// strictly above it and its own count.  Wave 0 works it out (lane l owns the NB/64 bins
+// below NB - (NB/64) l, read as 16-byte vectors; a second scan resolves the bin inside the
+// chosen lane's range); the result is broadcast through sh after a barrier that every
+// thread of the block takes.
 struct DigitPick {
     uint32_t digit, above, count;
 };
-__device__ __forceinline__ DigitPick pick_digit(const uint32_t *hist, int nb, uint32_t need, uint32_t *wsum,
-                                                uint32_t *sh)
+// Barrier that waits only for this wave's LDS traffic (global loads stay in flight).
+__device__ __forceinline__ void lds_sync()
 {
-    const int tid = threadIdx.x;
-    const int d_hi = nb - 1 - 2 * tid;
-    uint32_t c_hi = 0, c_lo = 0;
-    if (2 * tid < nb) {
-        c_hi = hist[d_hi];
-        c_lo = hist[d_hi - 1];
-    }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan(c_hi + c_lo, wsum, &tot);
-    if (2 * tid < nb) {
-        if (ex < need && need <= ex + c_hi) {
-            sh[0] = (uint32_t)d_hi;
-            sh[1] = ex;
-            sh[2] = c_hi;
-        } else if (ex + c_hi < need && need <= ex + c_hi + c_lo) {
-            sh[0] = (uint32_t)(d_hi - 1);
-            sh[1] = ex + c_hi;
-            sh[2] = c_lo;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int NB>
+__device__ __forceinline__ DigitPick pick_digit(const uint32_t *hist, uint32_t need, uint32_t *sh)
+{
+    static_assert(NB >= 256 && (NB & (NB - 1)) == 0, "bins");
+    constexpr int PER = NB / 64, Q = PER / 4;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int lo = NB - PER * (lane + 1);  // lowest bin of this lane
+        uint32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const u32x4 v = *(const u32x4 *)(hist + lo + 4 * ((q + lane) % Q));  // rotated
+            c += v[0] + v[1] + v[2] + v[3];
+        }
+        const uint32_t incl = wave_incl_scan(c, lane);
+        const uint64_t hit = __ballot(incl - c < need && need <= incl);
+        const int L = hit ? __ffsll((long long)hit) - 1 : 0;  // one lane holds it (need <= total)
+        const uint32_t exL = __shfl(incl - c, L, 64);
+        const int topL = NB - 1 - PER * L;
+        const uint32_t h = lane < PER ? hist[topL - lane] : 0u;
+        const uint32_t inc2 = wave_incl_scan(h, lane);
+        if (lane < PER && exL + inc2 - h < need && need <= exL + inc2) {
+            sh[0] = (uint32_t)(topL - lane);
+            sh[1] = exL + inc2 - h;
+            sh[2] = h;
         }
     }
-    __syncthreads();
-    DigitPick p{sh[0], sh[1], sh[2]};
-    __syncthreads();
-    return p;
+    lds_sync();
+    return DigitPick{sh[0], sh[1], sh[2]};
+}
+
+// Four consecutive scores s .. s+3 of a row (zeros past n): one 16-byte load when aligned.
+__device__ __forceinline__ f32x4 load4(const float *row, int64_t s, int64_t n)
+{
+    if (s + 3 < n && ((uintptr_t)(row + s) & 15) == 0)
+        return *(const f32x4 *)(row + s);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        v[e] = s + e < n ? row[s + e] : 0.f;
+    return v;
+}
+
+// One wave over positions base .. base+255 (base a multiple of 256; lane l holds base+4l ..
+// +3): the bitmap words of the positions whose bin is above d (lanes 8w'.. 8w'+7 build word
+// w' with three xor-shuffles; no atomics), and the keys of bin d appended to `mem` through
+// one counter atomic per wave and element.
+template <typename WordStore, typename MemberStore>
+__device__ __forceinline__ void take_wave(int64_t base, const f32x4 &x, int64_t n, uint32_t d, int lane,
+                                          WordStore store_word, MemberStore store_member)
+{
+    const int64_t s0 = base + 4 * lane;
+    uint32_t key[4], nib = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        key[e] = score_key(x[e]);
+        if (s0 + e < n && (key[e] >> 21) > d)
+            nib |= 1u << e;
+    }
+    uint32_t word = nib << (4 * (lane & 7));
+    word |= __shfl_xor(word, 1, 64);
+    word |= __shfl_xor(word, 2, 64);
+    word |= __shfl_xor(word, 4, 64);
+    if ((lane & 7) == 0 && base + 32 * (lane >> 3) < n)
+        store_word((base >> 5) + (lane >> 3), word);
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool m = s0 + e < n && (key[e] >> 21) == d;
+        const uint64_t mb = __ballot(m);
+        if (mb)
+            store_member(mb, (uint32_t)__popcll(mb & below), m, composite(key[e], s0 + e));
+    }
 }
 
 // ------------------------------------------------------------------------------------------
-// K1: per-row histogram of the top 11 key bits
+// K1: per-row histogram of the top 11 key bits (ROW and MB modes)
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(H_THREADS) void topk_hist_kernel(LayoutDev L, const float *__restrict__ scores,
                                                               int64_t ld, uint32_t *__restrict__ ghist)
@@ -131,16 +263,18 @@ __global__ __launch_bounds__(H_THREADS) void topk_hist_kernel(LayoutDev L, const
     __syncthreads();
     const int64_t s1 = min(s0 + (int64_t)H_CHUNK, r.n);
     const float *row = scores + i * ld;
-    for (int64_t s = s0 + 4 * tid; s < s1; s += 4 * H_THREADS) {
-        if (s + 3 < s1 && ((uintptr_t)(row + s) & 15) == 0) {
-            const f32x4 v = *(const f32x4 *)(row + s);
+    constexpr int U = H_CHUNK / (4 * H_THREADS);  // 8 vectors per thread, all in flight
+    f32x4 v[U];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                atomicAdd(&lh[wave][score_key(v[e]) >> 21], 1u);
-        } else {
-            for (int e = 0; e < 4 && s + e < s1; ++e)
-                atomicAdd(&lh[wave][score_key(row[s + e]) >> 21], 1u);
-        }
+    for (int u = 0; u < U; ++u)
+        v[u] = load4(row, s0 + 4 * (u * H_THREADS + tid), s1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t s = s0 + 4 * (u * H_THREADS + tid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (s + e < s1)
+                atomicAdd(&lh[wave][score_key(v[u][e]) >> 21], 1u);
     }
     __syncthreads();
     for (int b = tid; b < TK_BINS; b += H_THREADS) {
@@ -154,209 +288,325 @@ __global__ __launch_bounds__(H_THREADS) void topk_hist_kernel(LayoutDev L, const
 }
 
 // ------------------------------------------------------------------------------------------
-// K2: gather, exact select, sort, emit
+// K2 (MB mode): mark the bitmap words and collect the members of one 8192-score chunk
 // ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const float *__restrict__ scores,
+                                                              int64_t ld, int k, TkWs ws)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
+    __shared__ uint64_t lmem[H_CHUNK];  // this chunk's members, before one reservation
+    __shared__ uint32_t sh[4];
+    __shared__ uint32_t lcnt, gbase;
+    const int64_t i = blockIdx.y;
+    const RowInfo r = row_info(L, i);
+    const int64_t n = r.n > 0 ? r.n : 0;
+    const int64_t s0 = (int64_t)blockIdx.x * H_CHUNK;
+    if (s0 >= n)
+        return;
+    const uint32_t kk = (uint32_t)min((int64_t)k, n);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float *row = scores + i * ld;
+    uint32_t *bits = ws.bits + i * ws.W;
+    // the row's histogram first, then this chunk's scores: waiting for the histogram (in
+    // issue order) leaves the score loads in flight through the digit pick
+    const uint32_t *gh = ws.hist + i * TK_BINS;
+    constexpr int HB = TK_BINS / H_THREADS;
+    uint32_t hv[HB];
+#pragma unroll
+    for (int e = 0; e < HB; ++e)
+        hv[e] = gh[e * H_THREADS + tid];
+    constexpr int U = H_CHUNK / (4 * H_THREADS);  // 8 wave steps of 256 positions
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = load4(row, s0 + (int64_t)u * 4 * H_THREADS + 256 * wave + 4 * lane, n);
+#pragma unroll
+    for (int e = 0; e < HB; ++e)
+        hist[e * H_THREADS + tid] = hv[e];
+    if (tid == 0)
+        lcnt = 0u;
+    lds_sync();
+    const uint32_t d = pick_digit<TK_BINS>(hist, kk, sh).digit;
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t base = s0 + (int64_t)u * 4 * H_THREADS + 256 * wave;
+        if (base < n)
+            take_wave(
+                base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bits[w] = word; },
+                [&](uint64_t mb, uint32_t rank, bool m, uint64_t comp) {
+                    uint32_t at = 0;
+                    if (lane == 0)
+                        at = atomicAdd(&lcnt, (uint32_t)__popcll(mb));
+                    at = __shfl(at, 0, 64) + rank;
+                    if (m)
+                        lmem[at] = comp;  // at < H_CHUNK: one slot per position
+                });
+    }
+    __syncthreads();
+    // one reservation per block in the row's member list, then a coalesced copy
+    const uint32_t m = lcnt;
+    if (m == 0u)
+        return;
+    if (tid == 0)
+        gbase = atomicAdd(ws.cnt + i, m);
+    __syncthreads();
+    uint64_t *memb = ws.memb + i * TK_CAP;
+    for (uint32_t e = tid; e < m; e += H_THREADS) {
+        const uint32_t at = gbase + e;
+        if (at < (uint32_t)TK_CAP)
+            memb[at] = lmem[e];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// K3: exact selection and ordered output, one 1024-thread block per row
+// ------------------------------------------------------------------------------------------
+template <int MODE>
 __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, const float *__restrict__ scores,
                                                                  int64_t ld, int k, int32_t *__restrict__ out,
-                                                                 uint32_t *__restrict__ ghist)
+                                                                 TkWs ws)
 {
     __shared__ uint64_t cand[TK_CAP];
-    __shared__ uint32_t hist[TK_BINS];
-    __shared__ uint32_t bmap[TK_BMAP_WORDS];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
     __shared__ uint32_t wsum[TK_WAVES];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t sh_cnt;
+    extern __shared__ uint32_t bmap_lds[];  // DIRECT / ROW: the row's bitmap
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t i = blockIdx.x;
     const RowInfo r = row_info(L, i);
     const int64_t n = r.n > 0 ? r.n : 0;
     const float *row = scores + i * ld;
     int32_t *orow = out + i * k;
     const uint32_t kk = (uint32_t)min((int64_t)k, n);
+    if (kk == 0) {
+        for (int t = tid; t < k; t += TK_THREADS)
+            orow[t] = -1;
+        return;
+    }
+    const int nw = (int)((n + 31) >> 5);
+    // MB rows keep their bitmap in global memory unless it fits the LDS one
+    const bool gbm = MODE == TK_MB && ws.W > TK_ROW_BITS / 32;
+    uint32_t *bm = gbm ? ws.bits + i * ws.W : bmap_lds;
+    const uint64_t below = (1ull << lane) - 1ull;
 
+    // ---- 1. threshold bin d from the histogram of the top 11 key bits
     if (tid == 0)
         sh_cnt = 0u;
-    uint32_t m;  // candidates in cand
-    if (n <= TK_CAP) {
-        for (int64_t s = tid; s < n; s += TK_THREADS)
-            cand[s] = composite(score_key(row[s]), s);
-        m = (uint32_t)n;
-        __syncthreads();
-    } else {
-        // threshold bin from the row histogram (then clear it for the next call)
-        uint32_t *gh = ghist + i * TK_BINS;
-        for (int b = tid; b < TK_BINS; b += TK_THREADS) {
-            hist[b] = gh[b];
-            gh[b] = 0u;
-        }
-        __syncthreads();
-        const DigitPick p0 = pick_digit(hist, TK_BINS, kk, wsum, sh);
-        const uint32_t count_ge = p0.above + p0.count;
-        if (count_ge <= (uint32_t)TK_CAP) {
-            // one pass over the row: 16-byte loads, four in flight per thread, and one LDS
-            // atomic per wave (ballot + popcount give each lane its slot)
-            const uint32_t lo_key = p0.digit << 21;
-            const int lane = tid & 63;
-            const uint64_t below = (1ull << lane) - 1ull;
-            auto take = [&](float x, int64_t s, bool in) {
-                const uint32_t key = score_key(x);
-                const bool hit = in && key >= lo_key;
-                const uint64_t b = __ballot(hit);
-                if (b == 0ull)
-                    return;
-                uint32_t base = 0;
-                if (lane == 0)
-                    base = atomicAdd(&sh_cnt, (uint32_t)__popcll(b));
-                base = __shfl(base, 0, 64);
-                if (hit)
-                    cand[base + (uint32_t)__popcll(b & below)] = composite(key, s);
-            };
-            const int64_t head = (int64_t)((4 - (((uintptr_t)row >> 2) & 3)) & 3);  // to 16-B alignment
-            const int64_t h = head < n ? head : n;
-            take(tid < h ? row[tid] : 0.f, tid, tid < h);
-            const float4 *row4 = (const float4 *)(row + h);
-            const int64_t n4 = (n - h) >> 2;
-            constexpr int U = 4;
-            for (int64_t b4 = 0; b4 < n4; b4 += (int64_t)U * TK_THREADS) {
-                float4 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int64_t j = b4 + (int64_t)u * TK_THREADS + tid;
-                    v[u] = j < n4 ? row4[j] : float4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int64_t j = b4 + (int64_t)u * TK_THREADS + tid;
-                    const int64_t s0 = h + 4 * j;
-                    const bool in = j < n4;
-                    take(v[u].x, s0, in);
-                    take(v[u].y, s0 + 1, in);
-                    take(v[u].z, s0 + 2, in);
-                    take(v[u].w, s0 + 3, in);
-                }
-            }
-            const int64_t tail0 = h + 4 * n4;  // fewer than 4 scores left
-            take(tail0 + tid < n ? row[tail0 + tid] : 0.f, tail0 + tid, tail0 + tid < n);
-            m = count_ge;
-            __syncthreads();
+    for (int b = tid; b < TK_BINS; b += TK_THREADS) {
+        if (MODE == TK_DIRECT) {
+            hist[b] = 0u;
         } else {
-            // Too many scores share the threshold bin: refine with two more passes over the
-            // row, then take keys above tau and the lowest positions among its copies.
-            uint32_t prefix = p0.digit, above = p0.above, need = kk - p0.above;
-            int shift = 21;
-            const int widths[2] = {11, 10};
-            for (int pass = 0; pass < 2; ++pass) {
-                const int width = widths[pass], nshift = shift - width;
-                const uint32_t dmask = (1u << width) - 1u;
-                for (int b = tid; b < TK_BINS; b += TK_THREADS)
-                    hist[b] = 0u;
-                __syncthreads();
-                for (int64_t s = tid; s < n; s += TK_THREADS) {
-                    const uint32_t key = score_key(row[s]);
-                    if ((key >> shift) == prefix)
-                        atomicAdd(&hist[(key >> nshift) & dmask], 1u);
-                }
-                __syncthreads();
-                const DigitPick p = pick_digit(hist, 1 << width, need, wsum, sh);
-                above += p.above;
-                need -= p.above;
-                prefix = (prefix << width) | p.digit;
-                shift = nshift;
-            }
-            const uint32_t tau = prefix;
-            for (int64_t s = tid; s < n; s += TK_THREADS) {
-                const uint32_t key = score_key(row[s]);
-                if (key > tau)
-                    cand[atomicAdd(&sh_cnt, 1u)] = composite(key, s);
-            }
-            uint32_t taken = 0;
-            for (int64_t base = 0; base < n && taken < need; base += TK_THREADS) {
-                const int64_t s = base + tid;
-                const uint32_t flag = (s < n && score_key(row[s]) == tau) ? 1u : 0u;
-                uint32_t tot;
-                const uint32_t rank = block_excl_scan(flag, wsum, &tot);
-                if (flag && taken + rank < need)
-                    cand[above + taken + rank] = composite(tau, s);
-                taken += tot;
-            }
-            m = kk;
-            __syncthreads();
+            uint32_t *gh = ws.hist + i * TK_BINS;
+            hist[b] = gh[b];
+            gh[b] = 0u;  // the workspace is left zero for the next call
         }
     }
+    __syncthreads();
+    constexpr int DU = TK_CAP / TK_THREADS;  // 8 scores per thread in the DIRECT mode
+    uint32_t dkey[DU];
+    if (MODE == TK_DIRECT) {
+#pragma unroll
+        for (int e = 0; e < DU; ++e) {
+            const int64_t s = (int64_t)e * TK_THREADS + tid;
+            dkey[e] = s < n ? score_key(row[s]) : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < DU; ++e)
+            if ((int64_t)e * TK_THREADS + tid < n)
+                atomicAdd(&hist[dkey[e] >> 21], 1u);
+        __syncthreads();
+    }
+    const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
+    const uint32_t d = p0.digit;
+    const uint32_t need = kk - p0.above;  // 1 .. p0.count members of bin d are taken
 
-    // ---- exact selection of the kk largest composites among the m candidates (unique)
-    uint64_t lo_comp = 0;  // every selected composite is >= lo_comp
-    if (m > kk) {
-        uint64_t prefix = 0;
-        uint32_t need = kk;
-        int shift = 64;
-        while (true) {
-            const int width = shift >= 11 ? 11 : shift;
-            const int nshift = shift - width;
-            const uint64_t dmask = (1ull << width) - 1ull;
+    // ---- 2. bitmap of the positions above bin d; members of bin d into cand
+    auto take_step = [&](int64_t base, uint32_t key) {  // one wave: positions base .. base+63
+        const int64_t s = base + lane;
+        const bool in = s < n;
+        const uint32_t bin = key >> 21;
+        const uint64_t up = __ballot(in && bin > d);
+        if (lane == 0)
+            bm[base >> 5] = (uint32_t)up;
+        if (lane == 32 && base + 32 < n)
+            bm[(base >> 5) + 1] = (uint32_t)(up >> 32);
+        const bool mem = in && bin == d;
+        const uint64_t mb = __ballot(mem);
+        if (mb) {
+            uint32_t at = 0;
+            if (lane == 0)
+                at = atomicAdd(&sh_cnt, (uint32_t)__popcll(mb));
+            at = __shfl(at, 0, 64) + (uint32_t)__popcll(mb & below);
+            if (mem && at < (uint32_t)TK_CAP)
+                cand[at] = composite(key, s);
+        }
+    };
+    uint32_t c;  // members of bin d
+    if (MODE == TK_DIRECT) {
+#pragma unroll
+        for (int e = 0; e < DU; ++e) {
+            const int64_t base = (int64_t)e * TK_THREADS + 64 * wave;
+            if (base < n)
+                take_step(base, dkey[e]);
+        }
+        __syncthreads();
+        c = sh_cnt;
+    } else if (MODE == TK_ROW) {
+        constexpr int U = 4;  // 4 vectors per thread: 16384 positions per round
+#pragma unroll 1
+        for (int64_t b0 = 0; b0 < n; b0 += (int64_t)U * 4 * TK_THREADS) {
+            f32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = load4(row, b0 + (int64_t)u * 4 * TK_THREADS + 256 * wave + 4 * lane, n);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t base = b0 + (int64_t)u * 4 * TK_THREADS + 256 * wave;
+                if (base < n)
+                    take_wave(
+                        base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bm[w] = word; },
+                        [&](uint64_t mb, uint32_t rank, bool m, uint64_t comp) {
+                            uint32_t at = 0;
+                            if (lane == 0)
+                                at = atomicAdd(&sh_cnt, (uint32_t)__popcll(mb));
+                            at = __shfl(at, 0, 64) + rank;
+                            if (m && at < (uint32_t)TK_CAP)
+                                cand[at] = comp;
+                        });
+            }
+        }
+        __syncthreads();
+        c = sh_cnt;
+    } else {
+        if (!gbm) {  // copy the bitmap into LDS, leaving the global words zero
+            uint32_t *g = ws.bits + i * ws.W;
+            for (int w = tid; w < nw; w += TK_THREADS) {
+                bmap_lds[w] = g[w];
+                g[w] = 0u;
+            }
+        }
+        c = ws.cnt[i];  // written by topk_mark_kernel
+        uint64_t *memb = ws.memb + i * TK_CAP;
+        for (uint32_t e = tid; e < min(c, (uint32_t)TK_CAP); e += TK_THREADS) {
+            if (c <= (uint32_t)TK_CAP)
+                cand[e] = memb[e];
+            memb[e] = 0ull;  // everything this call wrote is left zero for the next one
+        }
+        __syncthreads();
+        if (tid == 0)
+            ws.cnt[i] = 0u;
+    }
+
+    // ---- 3. the need-th largest member; it and every member above it are marked
+    if (c <= (uint32_t)TK_CAP) {
+        uint64_t lo = 0;  // every selected member is >= lo
+        if (need < c) {
+            uint64_t prefix = d;
+            uint32_t nd = need;
+            int shift = 53;
+            while (true) {
+                const int width = shift >= 11 ? 11 : shift;
+                const int nshift = shift - width;
+                const int nb = 1 << width;
+                for (int b = tid; b < nb; b += TK_THREADS)
+                    hist[b] = 0u;
+                __syncthreads();
+                for (uint32_t e = tid; e < c; e += TK_THREADS) {
+                    const uint64_t v = cand[e];
+                    if ((v >> shift) == prefix)
+                        atomicAdd(&hist[(uint32_t)((v >> nshift) & (uint64_t)(nb - 1))], 1u);
+                }
+                __syncthreads();
+                const DigitPick p = nb == TK_BINS ? pick_digit<TK_BINS>(hist, nd, sh) : pick_digit<512>(hist, nd, sh);
+                prefix = (prefix << width) | p.digit;
+                nd -= p.above;
+                shift = nshift;
+                if (p.count == nd || shift == 0) {  // the whole sub-bin is taken
+                    lo = prefix << shift;
+                    break;
+                }
+            }
+        }
+        for (uint32_t e = tid; e < c; e += TK_THREADS) {
+            const uint64_t v = cand[e];
+            if (v >= lo) {
+                const uint32_t pos = comp_pos(v);
+                atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+            }
+        }
+    } else {
+        // Bin d holds more than TK_CAP keys: find the exact kk-th key tau with two more
+        // radix passes over the row, mark the keys of bin d above tau, then the first ties
+        // of tau in position order.
+        uint32_t prefix = d, nd = need;
+        int shift = 21;
+        const int widths[2] = {11, 10};
+        for (int pass = 0; pass < 2; ++pass) {
+            const int width = widths[pass], nshift = shift - width;
+            const uint32_t dmask = (1u << width) - 1u;
             for (int b = tid; b < TK_BINS; b += TK_THREADS)
                 hist[b] = 0u;
             __syncthreads();
-            for (uint32_t c = tid; c < m; c += TK_THREADS) {
-                const uint64_t v = cand[c];
-                if (shift == 64 || (v >> shift) == prefix)
-                    atomicAdd(&hist[(uint32_t)((v >> nshift) & dmask)], 1u);
+            for (int64_t s = tid; s < n; s += TK_THREADS) {
+                const uint32_t key = score_key(row[s]);
+                if ((key >> shift) == prefix)
+                    atomicAdd(&hist[(key >> nshift) & dmask], 1u);
             }
             __syncthreads();
-            const DigitPick p = pick_digit(hist, 1 << width, need, wsum, sh);
-            prefix = (shift == 64 ? 0ull : (prefix << width)) | p.digit;
+            const DigitPick p = width == 11 ? pick_digit<TK_BINS>(hist, nd, sh) : pick_digit<1024>(hist, nd, sh);
+            nd -= p.above;
+            prefix = (prefix << width) | p.digit;
             shift = nshift;
-            need -= p.above;
-            if (p.count == need || shift == 0) {  // the whole bin is taken
-                lo_comp = prefix << shift;
-                break;
-            }
+        }
+        const uint32_t tau = prefix;
+        for (int64_t s = tid; s < n; s += TK_THREADS) {
+            const uint32_t key = score_key(row[s]);
+            if ((key >> 21) == d && key > tau)
+                atomicOr(&bm[s >> 5], 1u << (s & 31));
+        }
+        uint32_t taken = 0;
+        for (int64_t b0 = 0; b0 < n && taken < nd; b0 += TK_THREADS) {
+            const int64_t s = b0 + tid;
+            const uint32_t flag = (s < n && score_key(row[s]) == tau) ? 1u : 0u;
+            uint32_t tot;
+            const uint32_t rank = block_excl_scan(flag, wsum, &tot);
+            if (flag && taken + rank < nd)
+                atomicOr(&bm[s >> 5], 1u << (s & 31));
+            taken += tot;
         }
     }
+    __syncthreads();
 
-    // ---- list the selected positions in ascending order: mark them in a bitmap (one pass
-    // per 2^15 positions), then a block scan over per-thread popcounts of consecutive
-    // words gives every set bit its output slot.  The slots are staged in hist (kk <= 2048).
+    // ---- 4. ordered output: per-thread popcounts of consecutive words, a block scan, then
+    // every set bit its slot (staged in hist: kk <= 2048 slots)
     static_assert(TK_BINS >= DSA_TOPK_MAX, "staging area");
     uint32_t *slots = hist;
-    uint32_t done = 0;
-    for (int64_t cb = 0; cb < n && done < kk; cb += TK_BMAP_BITS) {
-        const int64_t len = min((int64_t)TK_BMAP_BITS, n - cb);
-        const int nw = (int)((len + 31) >> 5);
-        __syncthreads();  // previous pass's readers of bmap are done
-        for (int w = tid; w < nw; w += TK_THREADS)
-            bmap[w] = 0u;
-        __syncthreads();
-        for (uint32_t c = tid; c < m; c += TK_THREADS) {
-            const uint64_t v = cand[c];
-            if (m > kk && v < lo_comp)
-                continue;
-            const int64_t pos = (int64_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
-            if (pos >= cb && pos < cb + len) {
-                const uint32_t rel = (uint32_t)(pos - cb);
-                atomicOr(&bmap[rel >> 5], 1u << (rel & 31));
-            }
+    const int wpt = (nw + TK_THREADS - 1) / TK_THREADS;
+    const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
+    auto word = [&](int w) -> uint32_t {
+        if (gbm)  // written by other CUs and by atomics: read past the L1
+            return __hip_atomic_load(&bm[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return bm[w];
+    };
+    uint32_t cnt_mine = 0;
+    for (int w = w0; w < w1; ++w)
+        cnt_mine += __popc(word(w));
+    uint32_t tot;
+    uint32_t slot = block_excl_scan(cnt_mine, wsum, &tot);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t b = word(w);
+        if (gbm)
+            bm[w] = 0u;  // left zero for the next call
+        while (b) {
+            const int bit = __ffs(b) - 1;
+            if (slot < (uint32_t)TK_BINS)
+                slots[slot] = (uint32_t)(32 * w + bit);
+            ++slot;
+            b &= b - 1u;
         }
-        __syncthreads();
-        const int wpt = (nw + TK_THREADS - 1) / TK_THREADS;  // consecutive words per thread
-        const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
-        uint32_t cnt = 0;
-        for (int w = w0; w < w1; ++w)
-            cnt += __popc(bmap[w]);
-        uint32_t tot;
-        uint32_t slot = done + block_excl_scan(cnt, wsum, &tot);
-        for (int w = w0; w < w1; ++w) {
-            uint32_t bits = bmap[w];
-            while (bits) {
-                const int b = __ffs(bits) - 1;
-                if (slot < (uint32_t)TK_BINS)
-                    slots[slot] = (uint32_t)(cb + 32 * w + b);
-                ++slot;
-                bits &= bits - 1u;
-            }
-        }
-        done += tot;
     }
     __syncthreads();
     for (int t = tid; t < k; t += TK_THREADS)
@@ -364,24 +614,34 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
 }
 
 // ------------------------------------------------------------------------------------------
-size_t topk_workspace_bytes(int64_t T, int64_t max_ctx)
-{
-    return max_ctx > TK_CAP ? (size_t)T * TK_BINS * sizeof(uint32_t) : 0;
-}
-
 hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const float *scores, int64_t ld,
                        int k, int32_t *indices, void *workspace, hipStream_t stream)
 {
-    uint32_t *ghist = (uint32_t *)workspace;
-    if (max_ctx > TK_CAP) {
-        dim3 hgrid((unsigned)((max_ctx + H_CHUNK - 1) / H_CHUNK), (unsigned)T);
-        hipLaunchKernelGGL(topk_hist_kernel, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, ghist);
+    const int mode = topk_mode(T, max_ctx);
+    const TkWs ws = mode == TK_DIRECT ? TkWs{} : carve(workspace, T, max_ctx);
+    const dim3 hgrid((unsigned)((max_ctx + H_CHUNK - 1) / H_CHUNK), (unsigned)T);
+    if (mode != TK_DIRECT) {
+        hipLaunchKernelGGL(topk_hist_kernel, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, ws.hist);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, L, scores, ld, k,
-                       indices, ghist);
+    if (mode == TK_MB) {
+        hipLaunchKernelGGL(topk_mark_kernel, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, k, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const size_t dyn = max_ctx <= TK_ROW_BITS ? (size_t)((max_ctx + 31) / 32) * 4 : 0;
+    if (mode == TK_DIRECT)
+        hipLaunchKernelGGL(topk_select_kernel<TK_DIRECT>, dim3((unsigned)T), dim3(TK_THREADS), dyn, stream, L,
+                           scores, ld, k, indices, ws);
+    else if (mode == TK_ROW)
+        hipLaunchKernelGGL(topk_select_kernel<TK_ROW>, dim3((unsigned)T), dim3(TK_THREADS), dyn, stream, L,
+                           scores, ld, k, indices, ws);
+    else
+        hipLaunchKernelGGL(topk_select_kernel<TK_MB>, dim3((unsigned)T), dim3(TK_THREADS), dyn, stream, L,
+                           scores, ld, k, indices, ws);
     return hipGetLastError();
 }
 

@@ -133,11 +133,14 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
  * listing), then -1 in the remaining slots.  Positions are logical (0 ..
  * ctx_b - 1 within the sequence).  1 <= k <= DSA_TOPK_MAX.  NaN scores are
  * outside the contract.
- *   workspace     device scratch of dsa_topk_workspace_size() bytes (a score
- *                 histogram per row, needed when max_ctx exceeds what one block
- *                 holds in LDS; may be NULL when the size is 0).  It must be
+ *   workspace     device scratch of dsa_topk_workspace_size() bytes, needed
+ *                 when max_ctx exceeds what one block holds in LDS (8192): a
+ *                 score histogram per row and, for up to 512 long rows, each
+ *                 row's bitmap of selected positions and its threshold-bin
+ *                 candidates; may be NULL when the size is 0.  It must be
  *                 zero-filled before its first use; every completed call leaves
- *                 it zero again.  Calls that overlap in time must not share it.
+ *                 all of it zero again, whatever the layout.  Calls that overlap
+ *                 in time must not share it.
  */
 size_t dsa_topk_workspace_size(const dsa_layout *layout, int64_t ld, int k);
 dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, int k,

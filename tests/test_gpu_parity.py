@@ -152,7 +152,7 @@ def test_interleaved_132_byte_index_cache():
 
 # ------------------------------------------------------------------------------ top-k edge cases
 
-def _topk_rows(rows, k=2048):
+def _topk_rows(rows, k=2048, workspace=None):
     """Run dsa_topk on the given fp32 rows (one sequence per row) and compare bit-exactly."""
     ctx = [len(r) for r in rows]
     ld = max(ctx)
@@ -161,11 +161,12 @@ def _topk_rows(rows, k=2048):
         sc[i, :len(r)] = r
     kvp = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]), dtype=torch.int64, device=DEV)
     layout = dsa.Layout(kvp, None, len(rows), ld)
-    idx = dsa.dsa_topk(layout, torch.from_numpy(sc).to(DEV), k)
+    idx = dsa.dsa_topk(layout, torch.from_numpy(sc).to(DEV), k, workspace=workspace)
     torch.cuda.synchronize()
     ih = idx.cpu().numpy()
     for i, r in enumerate(rows):
         tl.check_topk_same_array(ih[i], np.asarray(r, np.float32), k, "edge row %d (n=%d)" % (i, len(r)))
+    return layout
 
 
 @pytest.mark.parametrize("n", [1, 2, 2047, 2048, 2049, 4096, 4097, 9000, 70000])
@@ -186,6 +187,41 @@ def test_topk_ties_and_signed_zeros():
         np.concatenate([np.full(3000, -np.inf), rng.standard_normal(3000)]).astype(np.float32),
     ]
     _topk_rows(rows)
+
+
+def test_topk_threshold_bin_overflow():
+    """More than 8192 keys share the bin of the k-th key: the exact refinement over the row,
+    with the ties taken in position order."""
+    rng = np.random.default_rng(11)
+    rows = [
+        np.full(20000, 1.5, np.float32),
+        rng.integers(0, 2, 30000).astype(np.float32),
+        np.concatenate([rng.standard_normal(1000) + 10, np.full(15000, 2.0), rng.standard_normal(5000)]).astype(np.float32),
+    ]
+    _topk_rows(rows)
+
+
+def test_topk_many_long_rows():
+    """More than 512 rows longer than 8192 (the per-row mode), ragged."""
+    rng = np.random.default_rng(12)
+    rows = [rng.standard_normal(int(n)).astype(np.float32) for n in rng.integers(8193, 12000, 520)]
+    rows[5] = np.round(rows[5], 1)
+    rows[9] = np.full(9000, -2.0, np.float32)
+    _topk_rows(rows)
+
+
+def test_topk_workspace_reused_across_layouts():
+    """One workspace serves calls with different layouts and is all zero after each call."""
+    rng = np.random.default_rng(13)
+    big = [rng.standard_normal(n).astype(np.float32) for n in (70000, 20000, 9000, 131072)]
+    small = [rng.standard_normal(n).astype(np.float32) for n in [40000] * 9]
+    lay_b = _topk_rows(big, workspace=None)
+    lay_s = _topk_rows(small, workspace=None)
+    nb = max(dsa.dsa_topk_workspace_size(lay_b, 131072, 2048), dsa.dsa_topk_workspace_size(lay_s, 40000, 2048))
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    for rows in (big, small, big):
+        _topk_rows(rows, workspace=ws)
+        assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
 
 
 def test_topk_small_k_and_wide_ld():
