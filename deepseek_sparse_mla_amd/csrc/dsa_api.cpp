@@ -245,7 +245,9 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
     const bool shape32 = H_I == 32 && D_I == 128 && k_dt == DSA_FP8_E4M3FN && aligned(k, 16) &&
                          (k_row_stride % 16) == 0 && aligned(q, 16);
     const bool tuned_decode = shape32 && q_dt == DSA_BF16 && !force_generic();
-    const bool tuned_fp8 = shape32 && q_dt == DSA_FP8_E4M3FN && !force_generic();
+    // the prefill kernel addresses a sequence's keys with 32-bit buffer offsets
+    const bool tuned_fp8 = shape32 && q_dt == DSA_FP8_E4M3FN && !force_generic() &&
+                           layout->max_ctx * k_row_stride < (int64_t)INT32_MAX;
     if (!tuned_decode && !tuned_fp8 && (H_I > 64 || D_I > 256))
         return fail(DSA_ERR_UNSUPPORTED,
                     "indexer shape H_I=%d D_I=%d needs the generic kernel (H_I <= 64, D_I <= 256)",

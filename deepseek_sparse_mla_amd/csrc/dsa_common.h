@@ -17,6 +17,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Kernel-side copy of dsa_layout (pointers only; host sizes are launch params).
 struct LayoutDev {
@@ -138,6 +140,58 @@ __device__ __forceinline__ float wave_sum(float v)
     for (int o = 32; o > 0; o >>= 1)
         v += __shfl_xor(v, o, 64);
     return v;
+}
+
+
+// Barrier that waits only for this wave's LDS traffic (global loads and LDS DMA stay in
+// flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Barrier that also waits for this wave's global loads and LDS DMA.  The wait is issued
+// through the builtin as well so that the compiler's own wait-count tracking sees every
+// load as complete (it does not read inline asm) and adds no waits for them later.
+__device__ __forceinline__ void tile_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer descriptor (stride 0, range = bytes) over base; every field uniform.
+__device__ __forceinline__ i32x4 buffer_desc(const void *base, int64_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    i32x4 d;
+    d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    d[3] = 0x00020000;  // buffer descriptor word 3 for the gfx9 family
+    return d;
+}
+
+// One wave-wide 16-byte-per-lane load from a buffer straight into LDS: lane l writes LDS
+// bytes lds_addr + 16 l .. +15 with the bytes at voff of the buffer (zeros when voff is past
+// its range).  Issued as inline asm, so the compiler neither tracks it nor orders LDS reads
+// of other buffers after it: tile_barrier() waits for it.  M0 holds the LDS destination
+// (one wait state after writing it); nothing else in these kernels uses M0, so clobbering
+// the reserved register is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const i32x4 &desc, uint32_t lds_addr, int voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(desc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a __shared__ object (for M0).
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
 }
 
 }  // namespace dsa

@@ -118,34 +118,47 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(LayoutDev L, const uint
 // ------------------------------------------------------------------------------------------
 // fp8 q x fp8 k, H = 32, D = 128 (prefill GEMM)
 //
-// Block = 4 waves x 4 query rows; the block streams CHUNK tokens of one sequence through an
-// LDS tile of 128 tokens (rows padded to 144 B so the 16-lane groups of ds_read_b128 hit
-// disjoint banks).  MFMA 32x32x64 f8f6f4 (E4M3 on both sides, unit block scales): lane half
-// g owns dims [64g, 64g+64) of q and k; MFMA t consumes 32 of them.
+// Block = 8 waves x 2 query rows; the block streams CHUNK tokens of one sequence through two
+// LDS tiles of 256 tokens (rows padded to 144 B so the 16-lane groups of ds_read_b128 hit
+// disjoint banks), filled by buffer-to-LDS DMA one tile ahead of the MFMAs.  MFMA 32x32x64
+// f8f6f4 (E4M3 on both sides, unit block scales): lane half g owns dims [64g, 64g+64) of q
+// and k; MFMA t consumes 32 of them.  The weighted-ReLU head sum runs on the VALU.
 // ------------------------------------------------------------------------------------------
-constexpr int PF_QPW = 4;                 // query rows per wave
-constexpr int PF_QPB = 4 * PF_QPW;        // query rows per block
-constexpr int PF_STAGE = 128;             // tokens per LDS stage
-constexpr int PF_ROW_U4 = 9;              // LDS row stride in 16-byte units (128 B + pad)
-constexpr int E8M0_ONE = 127;             // block scale 2^0
+constexpr int PF_WAVES = 8;                     // waves per block (two per SIMD)
+constexpr int PF_QPW = 2;                       // query rows per wave
+constexpr int PF_QPB = PF_WAVES * PF_QPW;       // query rows per block
+constexpr int PF_STAGE = 256;                   // tokens per LDS tile
+constexpr int PF_ROWB = 144;                    // LDS row stride in bytes (128 + pad)
+constexpr int PF_TILEB = PF_STAGE * PF_ROWB;    // 18432
+constexpr int PF_DMA = PF_TILEB / 1024;         // 36 wave-wide 1 KB loads per tile
+constexpr int PF_DMA_PER_WAVE = (PF_DMA + PF_WAVES - 1) / PF_WAVES;  // 5 (the last only on waves 0-3)
+constexpr int E8M0_ONE = 127;                   // block scale 2^0
 
 __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 &b, const f32x16 &c)
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, E8M0_ONE, 0, E8M0_ONE);
 }
 
-__global__ __launch_bounds__(256) void idx_fp8_kernel(LayoutDev L, int64_t T, const uint8_t *__restrict__ q,
+// Value of lane l ^ 32 (g = lane >> 5), through one v_permlane32_swap.
+__device__ __forceinline__ float idx_other_half(float x, int g)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(g ? r[0] : r[1]);
+}
+
+__global__ __launch_bounds__(64 * PF_WAVES) void idx_fp8_kernel(LayoutDev L, int64_t T, const uint8_t *__restrict__ q,
                                                       const float *__restrict__ qs,
                                                       const float *__restrict__ w,
                                                       const uint8_t *__restrict__ k, int64_t kstride,
                                                       const float *__restrict__ ks, int64_t ks_stride,
                                                       float *__restrict__ scores, int64_t ld, int chunk)
 {
-    __shared__ u32x4 ktile[PF_STAGE * PF_ROW_U4];
-    __shared__ float kscale[PF_STAGE];
+    __shared__ __attribute__((aligned(16))) char ktile[2][PF_TILEB];
+    __shared__ float kscale[2][PF_STAGE];
     __shared__ int64_t s_meta[PF_QPB][3];  // b, kv_base, n per block query row (b = -1: none)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, j = lane & 31;
     const int64_t q0 = (int64_t)blockIdx.y * PF_QPB;
     const int64_t c0 = (int64_t)blockIdx.x * chunk;
@@ -163,7 +176,6 @@ __global__ __launch_bounds__(256) void idx_fp8_kernel(LayoutDev L, int64_t T, co
             s_meta[tid][2] = 0;
         }
     }
-    __syncthreads();
 
     // A operands and folded weights of this wave's query rows.
     i32x8 a[PF_QPW][2];
@@ -182,6 +194,18 @@ __global__ __launch_bounds__(256) void idx_fp8_kernel(LayoutDev L, int64_t T, co
             wq[u][rr] = w[qq * 32 + h] * qs[qq * 32 + h];
         }
     }
+    __syncthreads();
+
+    // DMA geometry, fixed per lane: load qd of this wave covers tile bytes 1024 (8 qd + wave)
+    // + 16 lane, i.e. one row and column (-1: pad columns, or a load past the tile).
+    int toff[PF_DMA_PER_WAVE];
+#pragma unroll
+    for (int qd = 0; qd < PF_DMA_PER_WAVE; ++qd) {
+        const int o = 1024 * (PF_WAVES * qd + wave) + 16 * lane;
+        const int row = o / PF_ROWB, col = o - (o / PF_ROWB) * PF_ROWB;
+        toff[qd] = (o < PF_TILEB && col < 128) ? row * (int)kstride + col : -1;
+    }
+    const uint32_t lds0 = lds_addr_of(&ktile[0][0]);
 
     // Query rows of one block may span several sequences: handle each in turn.
     int first = 0;
@@ -197,57 +221,82 @@ __global__ __launch_bounds__(256) void idx_fp8_kernel(LayoutDev L, int64_t T, co
         }
         const int64_t kv_base = s_meta[first][1];
         const int64_t s_end = min(c0 + (int64_t)chunk, nmax);
-
-        for (int64_t st = c0; st < s_end; st += PF_STAGE) {
-            __syncthreads();  // previous stage fully consumed
-            // stage 128 tokens x 128 B: 1024 16-byte pieces, 4 per thread
+        int64_t nq[PF_QPW];  // visible tokens of this wave's rows in this segment (0: not in it)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int c = tid + 256 * p;
-                const int tt = c >> 3, part = c & 7;
-                const int64_t s = st + tt;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (s < s_end)
-                    v = *(const u32x4 *)(k + (kv_base + s) * kstride + part * 16);
-                ktile[tt * PF_ROW_U4 + part] = v;
+        for (int u = 0; u < PF_QPW; ++u) {
+            const int qb = wave * PF_QPW + u;
+            nq[u] = (qb >= first && qb <= last) ? s_meta[qb][2] : 0;
+        }
+        if (c0 >= s_end) {
+            first = last + 1;
+            continue;
+        }
+        // the sequence's key rows; offsets past nmax rows read zeros
+        const i32x4 desc = buffer_desc(k + kv_base * kstride, nmax * kstride);
+        auto fetch = [&](int64_t st, int buf) {  // DMA of tokens st .. st+255 into ktile[buf]
+            const int base = (int)(st * kstride);
+#pragma unroll
+            for (int qd = 0; qd < PF_DMA_PER_WAVE; ++qd) {
+                const int u = PF_WAVES * qd + wave;
+                if (qd + 1 < PF_DMA_PER_WAVE || u < PF_DMA)
+                    dma16(desc, lds0 + (uint32_t)(buf * PF_TILEB + 1024 * u),
+                          toff[qd] >= 0 ? base + toff[qd] : (int)0x80000000);
             }
-            if (tid < PF_STAGE) {
-                const int64_t s = st + tid;
-                kscale[tid] = s < s_end ? ks[(kv_base + s) * ks_stride] : 0.f;
-            }
-            __syncthreads();
+        };
+        auto fetch_scale = [&](int64_t st) -> float {
+            const int64_t s = st + tid;
+            return (tid < PF_STAGE && s < nmax) ? ks[(kv_base + s) * ks_stride] : 0.f;
+        };
 
+        fetch(c0, 0);
+        float sc = fetch_scale(c0);
+        if (tid < PF_STAGE)
+            kscale[0][tid] = sc;
+        tile_barrier();
+        int buf = 0;
+        for (int64_t st = c0; st < s_end; st += PF_STAGE, buf ^= 1) {
+            const bool more = st + PF_STAGE < s_end;
+            if (more) {
+                fetch(st + PF_STAGE, buf ^ 1);
+                sc = fetch_scale(st + PF_STAGE);
+            }
+            const char *kt = &ktile[buf][0];
 #pragma unroll
             for (int sub = 0; sub < PF_STAGE / 32; ++sub) {
                 const int64_t sb = st + sub * 32;
                 if (sb >= s_end)
                     break;
-                const u32x4 *kr = &ktile[(sub * 32 + j) * PF_ROW_U4 + 4 * g];
+                const u32x4 *kr = (const u32x4 *)(kt + (sub * 32 + j) * PF_ROWB + 64 * g);
                 const u32x4 v0 = kr[0], v1 = kr[1], v2 = kr[2], v3 = kr[3];
                 const i32x8 b0 = {(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
                 const i32x8 b1 = {(int)v2[0], (int)v2[1], (int)v2[2], (int)v2[3], (int)v3[0], (int)v3[1], (int)v3[2], (int)v3[3]};
-                const float ksv = kscale[sub * 32 + j];
+                const float ksv = kscale[buf][sub * 32 + j];
+                f32x16 acc[PF_QPW];
 #pragma unroll
                 for (int u = 0; u < PF_QPW; ++u) {
-                    const int qb = wave * PF_QPW + u;
-                    if (qb < first || qb > last)
-                        continue;
-                    const int64_t nq = s_meta[qb][2];
-                    if (sb >= nq)
-                        continue;
-                    f32x16 acc = {};
-                    acc = mfma_fp8_32x32x64(a[u][0], b0, acc);
-                    acc = mfma_fp8_32x32x64(a[u][1], b1, acc);
+                    acc[u] = mfma_fp8_32x32x64(a[u][0], b0, f32x16{});
+                    acc[u] = mfma_fp8_32x32x64(a[u][1], b1, acc[u]);
+                }
+                // epilogues unconditional (only the stores are masked), so both rows' MFMAs
+                // issue back to back and the first epilogue overlaps the second row's MFMAs
+                // (the empty asm pins both results here: no pass may sink an MFMA to its use)
+                static_assert(PF_QPW == 2, "pin below");
+                asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+#pragma unroll
+                for (int u = 0; u < PF_QPW; ++u) {
                     float part = 0.f;
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr)
-                        part = fmaf(wq[u][rr], relu(acc[rr]), part);
-                    part += __shfl_xor(part, 32, 64);
+                        part = fmaf(wq[u][rr], relu(acc[u][rr]), part);
+                    part += idx_other_half(part, g);
                     const int64_t s = sb + j;
-                    if (g == 0 && s < nq)
-                        scores[(q0 + qb) * ld + s] = part * ksv;
+                    if (g == 0 && s < nq[u])
+                        scores[(q0 + wave * PF_QPW + u) * ld + s] = part * ksv;
                 }
             }
+            if (more && tid < PF_STAGE)
+                kscale[buf ^ 1][tid] = sc;
+            tile_barrier();  // the next tile has landed; this one is free
         }
         first = last + 1;
     }
@@ -325,7 +374,7 @@ hipError_t launch_index_fp8(const LayoutDev &L, int64_t T, int64_t max_ctx, cons
     while (chunk > PF_STAGE && qblocks * ((max_ctx + chunk - 1) / chunk) < 2048)
         chunk >>= 1;
     dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)qblocks);
-    hipLaunchKernelGGL(idx_fp8_kernel, grid, dim3(256), 0, stream, L, T, (const uint8_t *)q, qs, w,
+    hipLaunchKernelGGL(idx_fp8_kernel, grid, dim3(64 * PF_WAVES), 0, stream, L, T, (const uint8_t *)q, qs, w,
                        (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
     return hipGetLastError();
 }

@@ -117,20 +117,6 @@ __device__ __forceinline__ void stage_store(const StageRegs<KV_FP8> &R, char *ti
 // one per XCD (blocks are dispatched to the 8 XCDs round-robin), so all splits of a row
 // -- which share the row's q -- and neighbouring rows -- which share many gathered
 // latent rows -- run under one L2.
-// Barrier that waits only for this wave's LDS traffic (in-flight gathers stay in flight).
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// Barrier that also waits for this wave's gathers (LDS DMA) and loads.  The wait is issued
-// through the builtin so that the compiler's own wait-count tracking sees the gathers as
-// complete (it does not read inline asm) and adds no waits for them later.
-__device__ __forceinline__ void tile_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 __device__ __forceinline__ int64_t xcd_pair(int64_t pairs_per_xcd)
 {
     const int64_t b = blockIdx.x;
@@ -469,8 +455,6 @@ constexpr int F_ROWB = 592;                   // fp8 LDS row stride (576 + 16 pa
 constexpr int F_TILEB = M_TILE * F_ROWB;      // 37888 B per tile buffer
 constexpr int F_DMA = F_TILEB / 1024;         // 37 wave-wide 1 KB loads per tile
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Value of lane l ^ 32 (g = lane >> 5), through one v_permlane32_swap (no LDS round trip).
 __device__ __forceinline__ float other_half(float x, int g)
@@ -516,22 +500,12 @@ __device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, co
         const uint32_t col = rc[q] >> 8;
         voff[q] = (col != 0xFFFFu && idx >= 0) ? idx * 576 + (int)col : (int)0x80000000;
     }
-    // Issued as inline asm: the compiler then neither tracks these loads nor orders LDS reads
-    // of the other buffer after them; tile_barrier() waits for them explicitly.  M0 holds the
-    // LDS destination (one wait state after writing it); nothing else in these kernels uses
-    // M0, so clobbering the reserved register is safe here.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
     for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
         const int u = 4 * q + w;
         if (q + 1 < F_DMA_PER_WAVE || u < F_DMA)
-            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                         :
-                         : "s"(lds_base + 1024u * (uint32_t)u), "v"(voff[q]), "s"(seq)
-                         : "memory", "m0");
+            dma16(seq, lds_base + 1024u * (uint32_t)u, voff[q]);
     }
-#pragma clang diagnostic pop
 }
 
 
@@ -617,16 +591,8 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
         O[mt] = f32x16{};
 
     const int64_t seq_bytes = r.n * 576;  // host guarantees max_ctx * 576 < 2^31
-    i32x4 seq;  // buffer descriptor of this sequence's rows (stride 0, range = its bytes)
-    {
-        const uint64_t base = (uint64_t)((const uint8_t *)Ld.kv + r.kv_base * 576);
-        // uniform by construction; readfirstlane keeps it in SGPRs for the asm operand
-        seq[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-        seq[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
-        seq[2] = __builtin_amdgcn_readfirstlane((int)seq_bytes);
-        seq[3] = BUF_DWORD3;
-    }
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&kt8[0][0];
+    const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + r.kv_base * 576, seq_bytes);  // this sequence's rows
+    const uint32_t lds0 = lds_addr_of(&kt8[0][0]);
     uint32_t rc[F_DMA_PER_WAVE];
     dma_geometry(w, lane, rc);
 
