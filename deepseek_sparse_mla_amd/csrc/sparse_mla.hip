@@ -25,6 +25,7 @@
 //  * with several splits per row, partial (O, m, l) go to the workspace and a second
 //    kernel combines them in split order -- deterministic.
 // Generic kernel: any H <= 128, Dc <= 512, Dqk <= 1024, fp32 everywhere, two passes.
+#include <cstdlib>
 #include <type_traits>
 
 #include "dsa_common.h"
@@ -941,6 +942,15 @@ int mla_num_splits(int64_t rows, int k)
     if (rows <= 0)
         return 1;
     int64_t ns = (MLA_TARGET_BLOCKS + rows - 1) / rows;
+    // at least two tiles per split: a second tile hides the first one's fixed costs better
+    // than a second wave of split partials does (measured on 8-row decode)
+    if (ns > ntiles / 2)
+        ns = ntiles / 2;
+    if (const char *env = getenv("DSA_MLA_SPLITS")) {  // tuning sweeps: a fixed split count
+        const long v = strtol(env, nullptr, 10);
+        if (v >= 1 && v <= 32)
+            ns = v;
+    }
     if (ns > ntiles)
         ns = ntiles;
     if (ns > 32)
