@@ -118,17 +118,25 @@ __device__ __forceinline__ uint32_t comp_pos(uint64_t v)
     return 0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull);
 }
 
+// Inclusive scan over the 64 lanes of a wave with DPP moves (no LDS round trips): shifts of
+// 1, 2, 4, 8 inside each 16-lane row, then lane 15 of each row added into the next row
+// (rows 1, 3) and lane 31 into rows 2, 3.  Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
 // Exclusive scan over the block (one value per thread, thread order).
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, uint32_t *total)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o)
-            x += y;
-    }
+    const uint32_t x = wave_incl_scan(v, lane);
     if (lane == 63)
         wsum[wave] = x;
     __syncthreads();
@@ -144,17 +152,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, 
     return before + x - v;
 }
 
-// Inclusive scan over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane)
-{
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o)
-            x += y;
-    }
-    return x;
-}
 
 // Given a histogram of NB bins (a power of two, 256 .. 2048) and the number still needed
 // (1 <= need <= total), find the bin holding the need-th largest entry: the bin, the count
@@ -338,7 +335,7 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
                     uint32_t at = 0;
                     if (lane == 0)
                         at = atomicAdd(&lcnt, (uint32_t)__popcll(mb));
-                    at = __shfl(at, 0, 64) + rank;
+                    at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at) + rank;
                     if (m)
                         lmem[at] = comp;  // at < H_CHUNK: one slot per position
                 });
@@ -439,7 +436,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
             uint32_t at = 0;
             if (lane == 0)
                 at = atomicAdd(&sh_cnt, (uint32_t)__popcll(mb));
-            at = __shfl(at, 0, 64) + (uint32_t)__popcll(mb & below);
+            at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at) + (uint32_t)__popcll(mb & below);
             if (mem && at < (uint32_t)TK_CAP)
                 cand[at] = composite(key, s);
         }
@@ -472,7 +469,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
                             uint32_t at = 0;
                             if (lane == 0)
                                 at = atomicAdd(&sh_cnt, (uint32_t)__popcll(mb));
-                            at = __shfl(at, 0, 64) + rank;
+                            at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at) + rank;
                             if (m && at < (uint32_t)TK_CAP)
                                 cand[at] = comp;
                         });
