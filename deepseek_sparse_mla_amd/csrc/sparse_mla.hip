@@ -128,45 +128,57 @@ __device__ __forceinline__ int64_t xcd_pair(int64_t pairs_per_xcd)
 // split's partial: O / l in the output's precision (fp32, or bf16 for a bf16 output, like the
 // output itself) plus (reference max, l) in fp32 for the combine.  Wave (hh, dq) owns dims
 // 256*dq + 32*mt + 8*q4 + 4*g + 0..3 of head 32*hh + j.
+//
+// A bf16 block result (64 heads x 512 dims) is one contiguous 64 KB range of the output or of
+// the partial buffer.  It is staged through LDS (`stage`, free once the tiles are consumed;
+// rows padded to 1040 B so that the 32 heads of one write fall on distinct banks) and then
+// stored as whole 1 KB head rows, 16 B per lane: the direct stores from the MFMA layout would
+// write 16-byte pieces of 32 different rows per instruction.  fp32 results are stored directly.
+constexpr int E_ROWB = 1040;
+constexpr int E_STAGE_BYTES = M_H * E_ROWB;  // 66560
+static_assert(E_STAGE_BYTES <= M_TILEB, "output staging must fit in a tile buffer");
+
 template <bool OUT_F32>
 __device__ __forceinline__ void mla_store(const f32x16 (&O)[8], float l_run, float m_ref, const MlaLayerDev &Ld,
                                           int64_t i, int64_t orow, int split, int nsplit, int dq, int g, int head,
-                                          float *__restrict__ ws_o, float *__restrict__ ws_ml)
+                                          float *__restrict__ ws_o, float *__restrict__ ws_ml, char *stage,
+                                          int tid)
 {
-    if (nsplit == 1) {
-        const float inv = (l_run > 0.f) ? Ld.kv_scale / l_run : 0.f;
+    const float inv = (l_run > 0.f) ? (nsplit == 1 ? Ld.kv_scale / l_run : 1.f / l_run) : 0.f;
+    if (OUT_F32) {
+        float *dst = (nsplit == 1) ? (float *)Ld.out + (i * M_H + head) * M_DC
+                                   : ws_o + ((orow * nsplit + split) * M_H + head) * M_DC;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-                const int64_t o = (i * M_H + head) * M_DC + d;
-                const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
-                const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
-                if (OUT_F32)
-                    *(f32x4 *)((float *)Ld.out + o) = f32x4{v0, v1, v2, v3};
-                else
-                    *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                *(f32x4 *)(dst + d) = f32x4{O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv,
+                                            O[mt][4 * q4 + 2] * inv, O[mt][4 * q4 + 3] * inv};
             }
+    } else {
+        char *srow = stage + head * E_ROWB;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
+                *(u32x2 *)(srow + 2 * d) = u32x2{pack_bf16x2(O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv),
+                                                 pack_bf16x2(O[mt][4 * q4 + 2] * inv, O[mt][4 * q4 + 3] * inv)};
+            }
+        __syncthreads();
+        char *dst = (nsplit == 1) ? (char *)((uint16_t *)Ld.out + i * M_H * M_DC)
+                                  : (char *)((uint16_t *)ws_o + (orow * nsplit + split) * M_H * M_DC);
+#pragma unroll
+        for (int u = 0; u < M_H * M_DC * 2 / (16 * M_THREADS); ++u) {
+            const int c = tid + M_THREADS * u, h = c >> 6, c16 = c & 63;
+            *(u32x4 *)(dst + h * (M_DC * 2) + 16 * c16) = *(const u32x4 *)(stage + h * E_ROWB + 16 * c16);
+        }
+    }
+    if (nsplit == 1) {
         if (Ld.lse && dq == 0 && g == 0)
             Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
-        return;
-    }
-    const int64_t pbase = ((orow * nsplit + split) * M_H + head) * M_DC;
-    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-            const float v0 = O[mt][4 * q4] * inv, v1 = O[mt][4 * q4 + 1] * inv;
-            const float v2 = O[mt][4 * q4 + 2] * inv, v3 = O[mt][4 * q4 + 3] * inv;
-            if (OUT_F32)
-                *(f32x4 *)(ws_o + pbase + d) = f32x4{v0, v1, v2, v3};
-            else
-                *(u32x2 *)((uint16_t *)ws_o + pbase + d) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        }
-    if (dq == 0 && g == 0) {
+    } else if (dq == 0 && g == 0) {
         float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
         pml[0] = m_ref;
         pml[1] = l_run;
@@ -445,7 +457,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     __syncthreads();
     l_run = dq ? (xm[wp][j] + l_run) : (l_run + xm[wp][j]);
 
-    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml);
+    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml, kt, tid);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -455,6 +467,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
 constexpr int F_ROWB = 592;                   // fp8 LDS row stride (576 + 16 pad)
 constexpr int F_TILEB = M_TILE * F_ROWB;      // 37888 B per tile buffer
 constexpr int F_DMA = F_TILEB / 1024;         // 37 wave-wide 1 KB loads per tile
+static_assert(E_STAGE_BYTES <= 3 * F_TILEB, "output staging must fit in the tile buffers");
 
 
 // Value of lane l ^ 32 (g = lane >> 5), through one v_permlane32_swap (no LDS round trip).
@@ -790,7 +803,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
         xm[w][j] = l_run;
     __syncthreads();
     l_run = dq ? (xm[wp][j] + l_run) : (l_run + xm[wp][j]);
-    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml);
+    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml, &kt8[0][0], tid);
 }
 
 // Combine the split partials of every (output row, head), in split order.  One 128-thread
