@@ -22,8 +22,10 @@
 //  4. a block scan over per-thread popcounts of consecutive bitmap words gives every marked
 //     position its output slot.
 // Three ways to run it:
-//  DIRECT  rows of at most 8192 scores: one 1024-thread block per row does everything,
-//          the histogram in LDS;
+//  DIRECT  rows of at most 8192 scores: one 1024-thread block per row holds its row in
+//          registers and does everything; its histogram bins are equal-width value bins
+//          over the row's range (see topk_direct_kernel), and it writes the output slots
+//          from a block scan over the positions themselves, without a bitmap;
 //  ROW     many rows (prefill): topk_hist_kernel builds the histogram with many blocks per
 //          row; one block per row then reads its row once (bitmap in LDS);
 //  MB      few long rows (decode): topk_hist_kernel, then topk_mark_kernel marks the bitmap
@@ -357,7 +359,195 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
 }
 
 // ------------------------------------------------------------------------------------------
-// K3: exact selection and ordered output, one 1024-thread block per row
+// DIRECT mode: rows of at most 8192 scores, one 1024-thread block per row; thread t holds
+// the 8 consecutive positions 8t .. 8t+7 in registers, so the row is read once.
+//  1. the row's minimum and maximum cut [min, max] into 2048 bins of equal width; the bin of
+//     a score, trunc((x - min) * 2048 / (max - min)) clamped to 2047, never decreases as the
+//     score grows (each rounding step is monotone), so every score in a bin above the
+//     threshold bin d is taken and none below it.  A row whose range is zero or not finite
+//     uses the top 11 key bits instead (also monotone).  Equal-width bins spread typical
+//     score rows far more evenly than the exponent-led key bits, so the LDS histogram
+//     atomics rarely collide and bin d holds only a handful of members;
+//  2. the members of bin d go to LDS as composites and the (kk - above)-th largest of them is
+//     found by counting (up to TD_COUNT members) or by a radix select over the composites;
+//  3. each thread counts its taken positions, one block scan gives its first output slot,
+//     and it writes them: the output is in ascending position order.
+// ------------------------------------------------------------------------------------------
+constexpr int TD_PER = TK_CAP / TK_THREADS;  // 8 positions per thread
+constexpr uint32_t TD_COUNT = 256;          // members ranked by counting up to this many
+
+__global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, const float *__restrict__ scores,
+                                                                 int64_t ld, int k, int32_t *__restrict__ out)
+{
+    __shared__ uint64_t cand[TK_CAP];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
+    __shared__ float red[2][TK_WAVES];
+    __shared__ uint32_t wsum[TK_WAVES];
+    __shared__ uint32_t sh[4];
+    __shared__ uint32_t sh_cnt;
+    __shared__ uint64_t sh_lo;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t i = blockIdx.x;
+    const RowInfo r = row_info(L, i);
+    const int64_t n = min(r.n > 0 ? r.n : (int64_t)0, (int64_t)TK_CAP);  // the host keeps n <= 8192
+    int32_t *orow = out + i * k;
+    const uint32_t kk = (uint32_t)min((int64_t)k, n);
+    if (kk == 0) {
+        for (int t = tid; t < k; t += TK_THREADS)
+            orow[t] = -1;
+        return;
+    }
+    const float *row = scores + i * ld;
+    const int64_t s0 = (int64_t)TD_PER * tid;
+    float x[TD_PER];
+    {
+        const f32x4 a = load4(row, s0, n), b = load4(row, s0 + 4, n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[e];
+            x[4 + e] = b[e];
+        }
+    }
+    uint32_t valid = 0;  // bit e: position s0 + e < n
+#pragma unroll
+    for (int e = 0; e < TD_PER; ++e)
+        valid |= (s0 + e < n) ? (1u << e) : 0u;
+
+    // ---- 1. range of the row, histogram of the value bins
+    float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+    for (int e = 0; e < TD_PER; ++e)
+        if ((valid >> e) & 1u) {
+            mx = fmaxf(mx, x[e]);
+            mn = fminf(mn, x[e]);
+        }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        mn = fminf(mn, __shfl_xor(mn, o, 64));
+    }
+    if (lane == 0) {
+        red[0][wave] = mx;
+        red[1][wave] = mn;
+    }
+    for (int b = tid; b < TK_BINS; b += TK_THREADS)
+        hist[b] = 0u;
+    if (tid == 0)
+        sh_cnt = 0u;
+    __syncthreads();
+    mx = red[0][0];
+    mn = red[1][0];
+#pragma unroll
+    for (int w2 = 1; w2 < TK_WAVES; ++w2) {
+        mx = fmaxf(mx, red[0][w2]);
+        mn = fminf(mn, red[1][w2]);
+    }
+    const float range = mx - mn;
+    float scale = 0.f;
+    bool lin = range > 0.f && range < INFINITY;
+    if (lin) {
+        scale = (float)TK_BINS / range;
+        lin = scale < INFINITY;
+    }
+    uint32_t key[TD_PER], bin[TD_PER];
+#pragma unroll
+    for (int e = 0; e < TD_PER; ++e) {
+        key[e] = score_key(x[e]);
+        bin[e] = lin ? min((uint32_t)((x[e] - mn) * scale), (uint32_t)(TK_BINS - 1)) : key[e] >> 21;
+    }
+#pragma unroll
+    for (int e = 0; e < TD_PER; ++e)
+        if ((valid >> e) & 1u)
+            atomicAdd(&hist[bin[e]], 1u);
+    __syncthreads();
+    const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
+    const uint32_t d = p0.digit, c = p0.count;
+    const uint32_t need = kk - p0.above;  // 1 .. c members of bin d are taken
+
+    // ---- 2. members of bin d into cand (one counter atomic per wave)
+    uint32_t mm = 0;
+#pragma unroll
+    for (int e = 0; e < TD_PER; ++e)
+        mm |= (((valid >> e) & 1u) && bin[e] == d) ? (1u << e) : 0u;
+    if (need < c) {  // block-uniform
+        const uint32_t cm = (uint32_t)__popc(mm);
+        const uint32_t incl = wave_incl_scan(cm, lane);
+        uint32_t at = 0;
+        if (lane == 63 && incl != 0u)
+            at = atomicAdd(&sh_cnt, incl);
+        at = (uint32_t)__shfl((int)at, 63, 64) + incl - cm;
+#pragma unroll
+        for (int e = 0; e < TD_PER; ++e)
+            if ((mm >> e) & 1u)
+                cand[at++] = composite(key[e], s0 + e);
+        __syncthreads();
+    }
+
+    // ---- 3. lo: the need-th largest member (every member >= lo is taken)
+    uint64_t lo = 0;
+    if (need < c) {
+        if (c <= TD_COUNT) {
+            if ((uint32_t)tid < c) {
+                const uint64_t v = cand[tid];
+                uint32_t above = 0;
+                for (uint32_t u = 0; u < c; ++u)
+                    above += cand[u] > v ? 1u : 0u;
+                if (above == need - 1u)  // composites are unique: exactly one member
+                    sh_lo = v;
+            }
+            __syncthreads();
+            lo = sh_lo;
+        } else {
+            // MSD radix select over the 64-bit composites: 11-bit digits from the top
+            uint64_t prefix = 0;
+            uint32_t nd = need;
+            int shift = 64;
+            while (true) {
+                const int width = shift >= 11 ? 11 : shift;
+                const int nshift = shift - width;
+                const uint32_t nb = 1u << width;
+                for (uint32_t b = tid; b < nb; b += TK_THREADS)
+                    hist[b] = 0u;
+                __syncthreads();
+                for (uint32_t e = tid; e < c; e += TK_THREADS) {
+                    const uint64_t v = cand[e];
+                    if (shift == 64 || (v >> shift) == prefix)
+                        atomicAdd(&hist[(uint32_t)((v >> nshift) & (uint64_t)(nb - 1))], 1u);
+                }
+                __syncthreads();
+                const DigitPick p = nb == (uint32_t)TK_BINS ? pick_digit<TK_BINS>(hist, nd, sh)
+                                                              : pick_digit<512>(hist, nd, sh);
+                prefix = (prefix << width) | p.digit;
+                nd -= p.above;
+                shift = nshift;
+                if (p.count == nd || shift == 0) {  // the whole sub-bin is taken
+                    lo = prefix << shift;
+                    break;
+                }
+            }
+        }
+    }
+
+    // ---- 4. output slots in position order
+    uint32_t take = 0;
+#pragma unroll
+    for (int e = 0; e < TD_PER; ++e) {
+        const bool t = ((valid >> e) & 1u) && (bin[e] > d || (bin[e] == d && composite(key[e], s0 + e) >= lo));
+        take |= t ? (1u << e) : 0u;
+    }
+    uint32_t tot;
+    uint32_t slot = block_excl_scan((uint32_t)__popc(take), wsum, &tot);
+#pragma unroll
+    for (int e = 0; e < TD_PER; ++e)
+        if ((take >> e) & 1u)
+            orow[slot++] = (int32_t)(s0 + e);
+    for (int t = (int)kk + tid; t < k; t += TK_THREADS)
+        orow[t] = -1;
+}
+
+// ------------------------------------------------------------------------------------------
+// K3 (ROW and MB modes): exact selection and ordered output, one 1024-thread block per row
 // ------------------------------------------------------------------------------------------
 template <int MODE>
 __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, const float *__restrict__ scores,
@@ -369,7 +559,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
     __shared__ uint32_t wsum[TK_WAVES];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t sh_cnt;
-    extern __shared__ uint32_t bmap_lds[];  // DIRECT / ROW: the row's bitmap
+    extern __shared__ uint32_t bmap_lds[];  // the row's bitmap (ROW, and MB rows that fit)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t i = blockIdx.x;
@@ -387,71 +577,23 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
     // MB rows keep their bitmap in global memory unless it fits the LDS one
     const bool gbm = MODE == TK_MB && ws.W > TK_ROW_BITS / 32;
     uint32_t *bm = gbm ? ws.bits + i * ws.W : bmap_lds;
-    const uint64_t below = (1ull << lane) - 1ull;
 
     // ---- 1. threshold bin d from the histogram of the top 11 key bits
     if (tid == 0)
         sh_cnt = 0u;
     for (int b = tid; b < TK_BINS; b += TK_THREADS) {
-        if (MODE == TK_DIRECT) {
-            hist[b] = 0u;
-        } else {
-            uint32_t *gh = ws.hist + i * TK_BINS;
-            hist[b] = gh[b];
-            gh[b] = 0u;  // the workspace is left zero for the next call
-        }
+        uint32_t *gh = ws.hist + i * TK_BINS;
+        hist[b] = gh[b];
+        gh[b] = 0u;  // the workspace is left zero for the next call
     }
     __syncthreads();
-    constexpr int DU = TK_CAP / TK_THREADS;  // 8 scores per thread in the DIRECT mode
-    uint32_t dkey[DU];
-    if (MODE == TK_DIRECT) {
-#pragma unroll
-        for (int e = 0; e < DU; ++e) {
-            const int64_t s = (int64_t)e * TK_THREADS + tid;
-            dkey[e] = s < n ? score_key(row[s]) : 0u;
-        }
-#pragma unroll
-        for (int e = 0; e < DU; ++e)
-            if ((int64_t)e * TK_THREADS + tid < n)
-                atomicAdd(&hist[dkey[e] >> 21], 1u);
-        __syncthreads();
-    }
     const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
     const uint32_t d = p0.digit;
     const uint32_t need = kk - p0.above;  // 1 .. p0.count members of bin d are taken
 
     // ---- 2. bitmap of the positions above bin d; members of bin d into cand
-    auto take_step = [&](int64_t base, uint32_t key) {  // one wave: positions base .. base+63
-        const int64_t s = base + lane;
-        const bool in = s < n;
-        const uint32_t bin = key >> 21;
-        const uint64_t up = __ballot(in && bin > d);
-        if (lane == 0)
-            bm[base >> 5] = (uint32_t)up;
-        if (lane == 32 && base + 32 < n)
-            bm[(base >> 5) + 1] = (uint32_t)(up >> 32);
-        const bool mem = in && bin == d;
-        const uint64_t mb = __ballot(mem);
-        if (mb) {
-            uint32_t at = 0;
-            if (lane == 0)
-                at = atomicAdd(&sh_cnt, (uint32_t)__popcll(mb));
-            at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at) + (uint32_t)__popcll(mb & below);
-            if (mem && at < (uint32_t)TK_CAP)
-                cand[at] = composite(key, s);
-        }
-    };
     uint32_t c;  // members of bin d
-    if (MODE == TK_DIRECT) {
-#pragma unroll
-        for (int e = 0; e < DU; ++e) {
-            const int64_t base = (int64_t)e * TK_THREADS + 64 * wave;
-            if (base < n)
-                take_step(base, dkey[e]);
-        }
-        __syncthreads();
-        c = sh_cnt;
-    } else if (MODE == TK_ROW) {
+    if (MODE == TK_ROW) {
         constexpr int U = 4;  // 4 vectors per thread: 16384 positions per round
 #pragma unroll 1
         for (int64_t b0 = 0; b0 < n; b0 += (int64_t)U * 4 * TK_THREADS) {
@@ -631,8 +773,8 @@ hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const flo
     }
     const size_t dyn = max_ctx <= TK_ROW_BITS ? (size_t)((max_ctx + 31) / 32) * 4 : 0;
     if (mode == TK_DIRECT)
-        hipLaunchKernelGGL(topk_select_kernel<TK_DIRECT>, dim3((unsigned)T), dim3(TK_THREADS), dyn, stream, L,
-                           scores, ld, k, indices, ws);
+        hipLaunchKernelGGL(topk_direct_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, L, scores, ld, k,
+                           indices);
     else if (mode == TK_ROW)
         hipLaunchKernelGGL(topk_select_kernel<TK_ROW>, dim3((unsigned)T), dim3(TK_THREADS), dyn, stream, L,
                            scores, ld, k, indices, ws);

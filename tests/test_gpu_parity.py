@@ -189,6 +189,41 @@ def test_topk_ties_and_signed_zeros():
     _topk_rows(rows)
 
 
+def test_topk_single_block_rows():
+    """Rows of at most 8192 scores: one block per row bins by value over the row's range,
+    falling back to key bits when the range is zero or not finite; the threshold bin's
+    members are ranked by counting (few) or by a radix select (many)."""
+    rng = np.random.default_rng(21)
+    f = np.float32
+    rows = [
+        np.full(5000, 1.5, f),                                            # zero range, all tied
+        np.where(rng.random(6000) < 0.5, -0.0, 0.0).astype(f),            # only signed zeros
+        rng.integers(-3, 4, 8192).astype(f),                              # 7 distinct values
+        np.round(rng.standard_normal(8192), 1).astype(f),                 # heavy ties
+        np.sort(rng.standard_normal(8191)).astype(f),                     # ascending; ld % 4 != 0
+        -np.sort(-rng.standard_normal(7000)).astype(f),                   # descending
+        np.concatenate([np.full(3000, -np.inf), rng.standard_normal(3000)]).astype(f),
+        np.concatenate([rng.standard_normal(4000), [np.inf, np.inf]]).astype(f),
+        (1.0 + (np.arange(6000) % 97) * np.finfo(f).eps).astype(f),       # a range of 96 ulps
+        (rng.standard_normal(6000) * 1e-41).astype(f),                    # subnormal range
+        (np.clip(rng.standard_normal(6000), -3.3, 3.3) * 1e38).astype(f),  # the range overflows
+        np.concatenate([rng.standard_normal(1500) + 10, np.full(3000, 2.0),
+                        rng.standard_normal(3000)]).astype(f),            # 3000 tied members
+        np.concatenate([rng.standard_normal(1900) + 50, rng.uniform(1.0, 1.0001, 300),
+                        rng.standard_normal(5000)]).astype(f),            # > 256 members: radix
+        np.concatenate([rng.standard_normal(1900) + 50, rng.uniform(1.0, 1.0001, 150),
+                        rng.standard_normal(5000)]).astype(f),            # < 256 members: counting
+        rng.standard_normal(2047).astype(f), rng.standard_normal(2048).astype(f), np.zeros(1, f),
+    ]
+    for r in rows:
+        rng.shuffle(r)
+    rows[4] = np.sort(rows[4])
+    rows[5] = -np.sort(-rows[5])
+    _topk_rows(rows)
+    for k in (1, 7, 64, 1000):
+        _topk_rows(rows, k=k)
+
+
 def test_topk_threshold_bin_overflow():
     """More than 8192 keys share the bin of the k-th key: the exact refinement over the row,
     with the ties taken in position order."""
