@@ -139,14 +139,7 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, E8M0_ONE, 0, E8M0_ONE);
 }
 
-// Value of lane l ^ 32 (g = lane >> 5), through one v_permlane32_swap.
-__device__ __forceinline__ float idx_other_half(float x, int g)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(g ? r[0] : r[1]);
-}
-
-__global__ __launch_bounds__(64 * PF_WAVES) void idx_fp8_kernel(LayoutDev L, int64_t T, const uint8_t *__restrict__ q,
+__global__ __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void idx_fp8_kernel(LayoutDev L, int64_t T, const uint8_t *__restrict__ q,
                                                       const float *__restrict__ qs,
                                                       const float *__restrict__ w,
                                                       const uint8_t *__restrict__ k, int64_t kstride,
@@ -156,6 +149,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void idx_fp8_kernel(LayoutDev L, int
     __shared__ __attribute__((aligned(16))) char ktile[2][PF_TILEB];
     __shared__ float kscale[2][PF_STAGE];
     __shared__ int64_t s_meta[PF_QPB][3];  // b, kv_base, n per block query row (b = -1: none)
+    __shared__ __attribute__((aligned(16))) float s_wq[PF_QPB][32];  // folded head weights w * qs
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -177,9 +171,10 @@ __global__ __launch_bounds__(64 * PF_WAVES) void idx_fp8_kernel(LayoutDev L, int
         }
     }
 
-    // A operands and folded weights of this wave's query rows.
+    // A operands of this wave's query rows; the block's folded weights go to LDS (read back
+    // as four 16-byte broadcasts per row and tile, which keeps the wave under 128 VGPRs:
+    // two blocks per CU).
     i32x8 a[PF_QPW][2];
-    float wq[PF_QPW][16];
 #pragma unroll
     for (int u = 0; u < PF_QPW; ++u) {
         const int64_t qi = q0 + wave * PF_QPW + u;
@@ -188,11 +183,11 @@ __global__ __launch_bounds__(64 * PF_WAVES) void idx_fp8_kernel(LayoutDev L, int
         u32x4 v0 = qp[0], v1 = qp[1], v2 = qp[2], v3 = qp[3];
         a[u][0] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
         a[u][1] = i32x8{(int)v2[0], (int)v2[1], (int)v2[2], (int)v2[3], (int)v3[0], (int)v3[1], (int)v3[2], (int)v3[3]};
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int h = 8 * (rr >> 2) + 4 * g + (rr & 3);
-            wq[u][rr] = w[qq * 32 + h] * qs[qq * 32 + h];
-        }
+    }
+    for (int e = tid; e < PF_QPB * 32; e += 64 * PF_WAVES) {
+        const int64_t qi = q0 + e / 32;
+        const int64_t qq = qi < T ? qi : 0;
+        s_wq[e / 32][e % 32] = w[qq * 32 + e % 32] * qs[qq * 32 + e % 32];
     }
     __syncthreads();
 
@@ -221,11 +216,17 @@ __global__ __launch_bounds__(64 * PF_WAVES) void idx_fp8_kernel(LayoutDev L, int
         }
         const int64_t kv_base = s_meta[first][1];
         const int64_t s_end = min(c0 + (int64_t)chunk, nmax);
-        int64_t nq[PF_QPW];  // visible tokens of this wave's rows in this segment (0: not in it)
-#pragma unroll
-        for (int u = 0; u < PF_QPW; ++u) {
-            const int qb = wave * PF_QPW + u;
-            nq[u] = (qb >= first && qb <= last) ? s_meta[qb][2] : 0;
+        // this wave's rows in this segment: output from token c0 on, and how many of the
+        // chunk's tokens each row sees (0: the row is not in this segment)
+        // (lane half g stores the scores of the wave's row g)
+        static_assert(PF_QPW == 2, "one row per lane half");
+        float *myrow;
+        int mylim;
+        {
+            const int qb = wave * PF_QPW + g;
+            const int64_t nq = (qb >= first && qb <= last) ? s_meta[qb][2] : 0;
+            mylim = (int)max((int64_t)0, min(nq - c0, (int64_t)chunk));
+            myrow = scores + (q0 + qb) * ld + c0;
         }
         if (c0 >= s_end) {
             first = last + 1;
@@ -282,17 +283,24 @@ __global__ __launch_bounds__(64 * PF_WAVES) void idx_fp8_kernel(LayoutDev L, int
                 // (the empty asm pins both results here: no pass may sink an MFMA to its use)
                 static_assert(PF_QPW == 2, "pin below");
                 asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+                float part[PF_QPW];
 #pragma unroll
                 for (int u = 0; u < PF_QPW; ++u) {
-                    float part = 0.f;
+                    const f32x4 *wrow = (const f32x4 *)&s_wq[wave * PF_QPW + u][4 * g];
+                    part[u] = 0.f;
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr)
-                        part = fmaf(wq[u][rr], relu(acc[u][rr]), part);
-                    part += idx_other_half(part, g);
-                    const int64_t s = sb + j;
-                    if (g == 0 && s < nq[u])
-                        scores[(q0 + wave * PF_QPW + u) * ld + s] = part * ksv;
+                        part[u] = fmaf(wrow[2 * (rr >> 2)][rr & 3], relu(acc[u][rr]), part[u]);
                 }
+                // one swap of the two halves: lanes of half 0 get (row 0 here, row 0 of lane +32),
+                // lanes of half 1 get (row 1 of lane -32, row 1 here); each adds the (half 0,
+                // half 1) pair and stores its row's score for token j
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                                 false, false);
+                const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                const int so = (int)(sb - c0) + j;  // offset in the chunk
+                if (so < mylim)
+                    myrow[so] = tot * ksv;
             }
             if (more && tid < PF_STAGE)
                 kscale[buf ^ 1][tid] = sc;
@@ -369,10 +377,17 @@ hipError_t launch_index_fp8(const LayoutDev &L, int64_t T, int64_t max_ctx, cons
                             const float *ks, int64_t ks_stride, float *scores, int64_t ld,
                             hipStream_t stream)
 {
-    int chunk = 1024;
+    // Long chunks amortise each block's start (q, weights, first tile); halve them only
+    // while the grid would not fill two rounds of the chip's 512 block slots (2 per CU).
+    int chunk = 8192;
     const int64_t qblocks = (T + PF_QPB - 1) / PF_QPB;
-    while (chunk > PF_STAGE && qblocks * ((max_ctx + chunk - 1) / chunk) < 2048)
+    while (chunk > PF_STAGE && qblocks * ((max_ctx + chunk - 1) / chunk) < 1024)
         chunk >>= 1;
+    if (const char *env = getenv("DSA_INDEXER_CHUNK")) {  // launch-shape tuning (power of two)
+        const int c = atoi(env);
+        if (c >= PF_STAGE && c <= 8192 && (c & (c - 1)) == 0)
+            chunk = c;
+    }
     dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)qblocks);
     hipLaunchKernelGGL(idx_fp8_kernel, grid, dim3(64 * PF_WAVES), 0, stream, L, T, (const uint8_t *)q, qs, w,
                        (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
