@@ -359,7 +359,7 @@ def main():
     split = runners[0].ws is not None and runners[0].ws.numel() > 0
     kernel_names = {
         "indexer": "dsa_index_scores: " + ("idx_fp8_kernel" if prefill else "idx_decode_kernel"),
-        "topk": "dsa_topk: " + ("topk_direct_kernel" if probe.max_ctx <= 8192 else
+        "topk": "dsa_topk: " + ("topk_direct_kernel" if probe.max_ctx <= 32768 else
                                 "topk_hist_kernel + topk_mark_kernel + topk_select_kernel"
                                 if probe.T <= 512 or probe.max_ctx > (1 << 18) else
                                 "topk_hist_kernel + topk_select_kernel"),

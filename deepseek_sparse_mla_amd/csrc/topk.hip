@@ -46,6 +46,7 @@ constexpr int TK_CAP = 8192;          // members held in LDS (64 KB of composite
 constexpr int TK_BINS = 2048;         // 11-bit digits
 constexpr int TK_ROW_BITS = 1 << 18;  // longest row of the ROW mode (32 KB LDS bitmap)
 constexpr int TK_MB_ROWS = 512;       // up to this many rows, long rows use the MB mode
+constexpr int TD_MAX_PER = 32;        // longest DIRECT row: 1024 threads x 32 = 32768 scores
 constexpr int H_THREADS = 256;        // histogram and mark kernels
 constexpr int H_CHUNK = 8192;         // scores per histogram / mark block
 
@@ -53,7 +54,7 @@ enum TkMode { TK_DIRECT = 0, TK_ROW = 1, TK_MB = 2 };
 
 static int topk_mode(int64_t T, int64_t max_ctx)
 {
-    if (max_ctx <= TK_CAP)
+    if (max_ctx <= (int64_t)TK_THREADS * TD_MAX_PER)
         return TK_DIRECT;
     if (T <= TK_MB_ROWS || max_ctx > TK_ROW_BITS)
         return TK_MB;
@@ -359,8 +360,10 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
 }
 
 // ------------------------------------------------------------------------------------------
-// DIRECT mode: rows of at most 8192 scores, one 1024-thread block per row; thread t holds
-// the 8 consecutive positions 8t .. 8t+7 in registers, so the row is read once.
+// DIRECT mode: rows of at most 1024 PER scores (PER = 8, 16: in registers; 32: in LDS), one
+// 1024-thread block per row, which reads its row once.  Thread t owns the positions
+// 4096 q + 4 t + e (q < PER / 4, e < 4): every load instruction reads 1 KB of consecutive
+// scores.
 //  1. the row's minimum and maximum cut [min, max] into 2048 bins of equal width; the bin of
 //     a score, trunc((x - min) * 2048 / (max - min)) clamped to 2047, never decreases as the
 //     score grows (each rounding step is monotone), so every score in a bin above the
@@ -368,21 +371,30 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
 //     uses the top 11 key bits instead (also monotone).  Equal-width bins spread typical
 //     score rows far more evenly than the exponent-led key bits, so the LDS histogram
 //     atomics rarely collide and bin d holds only a handful of members;
-//  2. the members of bin d go to LDS as composites and the (kk - above)-th largest of them is
-//     found by counting (up to TD_COUNT members) or by a radix select over the composites;
-//  3. each thread counts its taken positions, one block scan gives its first output slot,
-//     and it writes them: the output is in ascending position order.
+//  2. the members of bin d go to LDS as composites (up to CAP of them), and the
+//     (kk - above)-th largest is found by counting (up to TD_COUNT members) or by an MSD radix
+//     select over the composites (from LDS, or recomputed from the row when bin d holds more
+//     than CAP members);
+//  3. each thread marks its taken positions per group q (by composite alone when step 2
+//     found an exact member, else by bin and composite); wave scans and one scan over the
+//     (q, wave) totals give every position its output slot: ascending position order.
 // ------------------------------------------------------------------------------------------
-constexpr int TD_PER = TK_CAP / TK_THREADS;  // 8 positions per thread
-constexpr uint32_t TD_COUNT = 256;          // members ranked by counting up to this many
+constexpr uint32_t TD_COUNT = 256;  // members ranked by counting up to this many
 
+template <int PER, bool LDSROW>
 __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, const float *__restrict__ scores,
                                                                  int64_t ld, int k, int32_t *__restrict__ out)
 {
-    __shared__ uint64_t cand[TK_CAP];
+    static_assert(PER % 4 == 0 && PER >= 8 && PER <= TD_MAX_PER, "positions per thread");
+    constexpr int NQ = PER / 4;                      // groups of 4 positions per thread
+    constexpr int GROUP = 4 * TK_THREADS;            // positions per group (4096)
+    constexpr int NB = NQ * TK_WAVES;                // (group, wave) totals
+    constexpr int CAP = LDSROW ? 2048 : TK_CAP;      // members held in LDS
+    __shared__ __attribute__((aligned(16))) float srow[LDSROW ? TK_THREADS * PER : 4];
+    __shared__ uint64_t cand[CAP];
     __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
     __shared__ float red[2][TK_WAVES];
-    __shared__ uint32_t wsum[TK_WAVES];
+    __shared__ uint32_t base[NB];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t sh_cnt;
     __shared__ uint64_t sh_lo;
@@ -390,38 +402,80 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t i = blockIdx.x;
     const RowInfo r = row_info(L, i);
-    const int64_t n = min(r.n > 0 ? r.n : (int64_t)0, (int64_t)TK_CAP);  // the host keeps n <= 8192
+    const int n32 = (int)min(r.n > 0 ? r.n : (int64_t)0, (int64_t)TK_THREADS * PER);  // host: n <= 1024 PER
     int32_t *orow = out + i * k;
-    const uint32_t kk = (uint32_t)min((int64_t)k, n);
+    const uint32_t kk = (uint32_t)min(k, n32);
     if (kk == 0) {
         for (int t = tid; t < k; t += TK_THREADS)
             orow[t] = -1;
         return;
     }
     const float *row = scores + i * ld;
-    const int64_t s0 = (int64_t)TD_PER * tid;
-    float x[TD_PER];
-    {
-        const f32x4 a = load4(row, s0, n), b = load4(row, s0 + 4, n);
+    auto pos = [&](int q, int e) -> int { return GROUP * q + 4 * tid + e; };
+
+    // ---- 0. the row: groups wholly inside it as one 16-byte load (16-byte aligned rows),
+    // others as four dword loads through a buffer resource over the n scores (zeros past
+    // the end, no branch per element)
+    const __amdgpu_buffer_rsrc_t rrow =
+        __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, n32 * 4, 0x00020000);
+    const bool al16 = ((uintptr_t)row & 15) == 0;
+    auto load_group = [&](int q) -> f32x4 {
+        const int p = pos(q, 0);
+        if (al16 && p + 3 < n32)
+            return *(const f32x4 *)(row + p);
+        f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[e] = a[e];
-            x[4 + e] = b[e];
+        for (int e = 0; e < 4; ++e)
+            v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrow, 4 * (p + e), 0, 0));
+        return v;
+    };
+    f32x4 xr[LDSROW ? 1 : NQ];
+    auto get = [&](int q) -> f32x4 {
+        if (LDSROW)
+            return *(const f32x4 *)&srow[pos(q, 0)];
+        return xr[q];
+    };
+    float mx = -INFINITY, mn = INFINITY;
+    auto range_of = [&](const f32x4 &v, int q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (pos(q, e) < n32) {
+                mx = fmaxf(mx, v[e]);
+                mn = fminf(mn, v[e]);
+            }
+    };
+    if (LDSROW) {
+        if (al16) {
+            // the whole row in flight at once: wave-wide 1 KB DMA loads straight into LDS (group
+            // q of wave w lands at srow[4096 q + 256 w ..]); positions past n are never used
+            const i32x4 desc = buffer_desc(row, (int64_t)n32 * 4);
+            const uint32_t lds_row = lds_addr_of(&srow[0]);
+            const int w = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                dma16(desc, lds_row + 4u * (uint32_t)(GROUP * q + 256 * w), 4 * pos(q, 0));
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                *(f32x4 *)&srow[pos(q, 0)] = load_group(q);
         }
-    }
-    uint32_t valid = 0;  // bit e: position s0 + e < n
+        // each thread reads back exactly the positions it loaded or DMA'd (its own wave's
+        // bytes): no barrier needed before this pass
 #pragma unroll
-    for (int e = 0; e < TD_PER; ++e)
-        valid |= (s0 + e < n) ? (1u << e) : 0u;
+        for (int q = 0; q < NQ; ++q)
+            range_of(get(q), q);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            xr[q] = load_group(q);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            range_of(xr[q], q);
+    }
 
     // ---- 1. range of the row, histogram of the value bins
-    float mx = -INFINITY, mn = INFINITY;
-#pragma unroll
-    for (int e = 0; e < TD_PER; ++e)
-        if ((valid >> e) & 1u) {
-            mx = fmaxf(mx, x[e]);
-            mn = fminf(mn, x[e]);
-        }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         mx = fmaxf(mx, __shfl_xor(mx, o, 64));
@@ -450,44 +504,41 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         scale = (float)TK_BINS / range;
         lin = scale < INFINITY;
     }
-    uint32_t key[TD_PER], bin[TD_PER];
+    auto bin_of = [&](float v) -> uint32_t {
+        return lin ? min((uint32_t)((v - mn) * scale), (uint32_t)(TK_BINS - 1)) : score_key(v) >> 21;
+    };
 #pragma unroll
-    for (int e = 0; e < TD_PER; ++e) {
-        key[e] = score_key(x[e]);
-        bin[e] = lin ? min((uint32_t)((x[e] - mn) * scale), (uint32_t)(TK_BINS - 1)) : key[e] >> 21;
+    for (int q = 0; q < NQ; ++q) {
+        const f32x4 v = get(q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (pos(q, e) < n32)
+                atomicAdd(&hist[bin_of(v[e])], 1u);
     }
-#pragma unroll
-    for (int e = 0; e < TD_PER; ++e)
-        if ((valid >> e) & 1u)
-            atomicAdd(&hist[bin[e]], 1u);
     __syncthreads();
     const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
     const uint32_t d = p0.digit, c = p0.count;
     const uint32_t need = kk - p0.above;  // 1 .. c members of bin d are taken
 
-    // ---- 2. members of bin d into cand (one counter atomic per wave)
-    uint32_t mm = 0;
+    // ---- 2. members of bin d into cand (a handful per row: one counter atomic each)
+    const bool in_lds = c <= (uint32_t)CAP;
+    if (need < c && in_lds) {  // block-uniform
 #pragma unroll
-    for (int e = 0; e < TD_PER; ++e)
-        mm |= (((valid >> e) & 1u) && bin[e] == d) ? (1u << e) : 0u;
-    if (need < c) {  // block-uniform
-        const uint32_t cm = (uint32_t)__popc(mm);
-        const uint32_t incl = wave_incl_scan(cm, lane);
-        uint32_t at = 0;
-        if (lane == 63 && incl != 0u)
-            at = atomicAdd(&sh_cnt, incl);
-        at = (uint32_t)__shfl((int)at, 63, 64) + incl - cm;
+        for (int q = 0; q < NQ; ++q) {
+            const f32x4 v = get(q);
 #pragma unroll
-        for (int e = 0; e < TD_PER; ++e)
-            if ((mm >> e) & 1u)
-                cand[at++] = composite(key[e], s0 + e);
+            for (int e = 0; e < 4; ++e)
+                if (pos(q, e) < n32 && bin_of(v[e]) == d)
+                    cand[atomicAdd(&sh_cnt, 1u)] = composite(score_key(v[e]), pos(q, e));
+        }
         __syncthreads();
     }
 
     // ---- 3. lo: the need-th largest member (every member >= lo is taken)
     uint64_t lo = 0;
+    const bool exact = need < c && in_lds && c <= TD_COUNT;  // lo is then a member's composite
     if (need < c) {
-        if (c <= TD_COUNT) {
+        if (exact) {
             if ((uint32_t)tid < c) {
                 const uint64_t v = cand[tid];
                 uint32_t above = 0;
@@ -499,7 +550,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
             __syncthreads();
             lo = sh_lo;
         } else {
-            // MSD radix select over the 64-bit composites: 11-bit digits from the top
+            // MSD radix select over the 64-bit composites of the members: 11-bit digits from
+            // the top, over cand or (too many members for it) over the row
             uint64_t prefix = 0;
             uint32_t nd = need;
             int shift = 64;
@@ -510,10 +562,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
                 for (uint32_t b = tid; b < nb; b += TK_THREADS)
                     hist[b] = 0u;
                 __syncthreads();
-                for (uint32_t e = tid; e < c; e += TK_THREADS) {
-                    const uint64_t v = cand[e];
+                auto count = [&](uint64_t v) {
                     if (shift == 64 || (v >> shift) == prefix)
                         atomicAdd(&hist[(uint32_t)((v >> nshift) & (uint64_t)(nb - 1))], 1u);
+                };
+                if (in_lds) {
+                    for (uint32_t e = tid; e < c; e += TK_THREADS)
+                        count(cand[e]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const f32x4 v = get(q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (pos(q, e) < n32 && bin_of(v[e]) == d)
+                                count(composite(score_key(v[e]), pos(q, e)));
+                    }
                 }
                 __syncthreads();
                 const DigitPick p = nb == (uint32_t)TK_BINS ? pick_digit<TK_BINS>(hist, nd, sh)
@@ -529,19 +593,70 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         }
     }
 
-    // ---- 4. output slots in position order
-    uint32_t take = 0;
+    // ---- 4. output slots in position order: group q of wave w starts at base[q][w].  With an
+    // exact lo (a member's composite) the taken set is simply {composite >= lo}: every score of
+    // a higher bin is larger than every member, every score of a lower bin smaller.
+    // composite >= lo  <=>  x > x_lo, or x == x_lo at a position <= p_lo (float compares: -0 == +0
+    // as for the keys; no NaN)
+    const uint32_t lo_key = (uint32_t)(lo >> 32);
+    const float x_lo = __uint_as_float((lo_key & 0x80000000u) ? (lo_key & 0x7FFFFFFFu) : ~lo_key);
+    const int p_lo = (int)comp_pos(lo);
+    auto take_mask = [&](int q) -> uint32_t {
+        const f32x4 v = get(q);
+        uint32_t m = 0;
 #pragma unroll
-    for (int e = 0; e < TD_PER; ++e) {
-        const bool t = ((valid >> e) & 1u) && (bin[e] > d || (bin[e] == d && composite(key[e], s0 + e) >= lo));
-        take |= t ? (1u << e) : 0u;
+        for (int e = 0; e < 4; ++e) {
+            bool t;
+            if (exact) {
+                t = v[e] > x_lo || (v[e] == x_lo && pos(q, e) <= p_lo);
+            } else {
+                const uint32_t bn = bin_of(v[e]);
+                t = bn > d || (bn == d && composite(score_key(v[e]), pos(q, e)) >= lo);
+            }
+            m |= (t && pos(q, e) < n32) ? (1u << e) : 0u;
+        }
+        return m;
+    };
+    static_assert(NQ <= 8, "take masks packed in 32 bits");
+    uint32_t takes = 0;  // 4 bits per group
+    uint32_t incl[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const uint32_t m = take_mask(q);
+        takes |= m << (4 * q);
+        incl[q] = wave_incl_scan((uint32_t)__popc(m), lane);
+        if (lane == 63)
+            base[q * TK_WAVES + wave] = incl[q];
     }
-    uint32_t tot;
-    uint32_t slot = block_excl_scan((uint32_t)__popc(take), wsum, &tot);
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of the NB totals in (group, wave) order
+        constexpr int PL = (NB + 63) / 64;  // consecutive entries per lane
+        uint32_t v[PL], s = 0;
 #pragma unroll
-    for (int e = 0; e < TD_PER; ++e)
-        if ((take >> e) & 1u)
-            orow[slot++] = (int32_t)(s0 + e);
+        for (int u = 0; u < PL; ++u) {
+            const int e = PL * lane + u;
+            v[u] = e < NB ? base[e] : 0u;
+            s += v[u];
+        }
+        uint32_t run = wave_incl_scan(s, lane) - s;
+#pragma unroll
+        for (int u = 0; u < PL; ++u) {
+            const int e = PL * lane + u;
+            if (e < NB)
+                base[e] = run;
+            run += v[u];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const uint32_t m = (takes >> (4 * q)) & 15u, cnt = (uint32_t)__popc(m);
+        uint32_t slot = base[q * TK_WAVES + wave] + incl[q] - cnt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if ((m >> e) & 1u)
+                orow[slot++] = pos(q, e);
+    }
     for (int t = (int)kk + tid; t < k; t += TK_THREADS)
         orow[t] = -1;
 }
@@ -772,10 +887,15 @@ hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const flo
             return e;
     }
     const size_t dyn = max_ctx <= TK_ROW_BITS ? (size_t)((max_ctx + 31) / 32) * 4 : 0;
-    if (mode == TK_DIRECT)
-        hipLaunchKernelGGL(topk_direct_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, L, scores, ld, k,
-                           indices);
-    else if (mode == TK_ROW)
+    if (mode == TK_DIRECT) {
+        const dim3 g((unsigned)T), b(TK_THREADS);
+        if (max_ctx <= 8 * TK_THREADS)
+            hipLaunchKernelGGL((topk_direct_kernel<8, false>), g, b, 0, stream, L, scores, ld, k, indices);
+        else if (max_ctx <= 16 * TK_THREADS)
+            hipLaunchKernelGGL((topk_direct_kernel<16, false>), g, b, 0, stream, L, scores, ld, k, indices);
+        else
+            hipLaunchKernelGGL((topk_direct_kernel<32, true>), g, b, 0, stream, L, scores, ld, k, indices);
+    } else if (mode == TK_ROW)
         hipLaunchKernelGGL(topk_select_kernel<TK_ROW>, dim3((unsigned)T), dim3(TK_THREADS), dyn, stream, L,
                            scores, ld, k, indices, ws);
     else
