@@ -34,19 +34,13 @@ __device__ __forceinline__ float relu(float x)
 // Rows are heads, columns tokens.  The 128-long contraction is split so that lane half g
 // owns dims [64g, 64g+64): MFMA t consumes dims 64g + 8t .. 64g + 8t + 7 of both q and k.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
-                                                         const float *__restrict__ w,
-                                                         const uint8_t *__restrict__ k, int64_t kstride,
-                                                         const float *__restrict__ ks, int64_t ks_stride,
-                                                         float *__restrict__ scores, int64_t ld,
-                                                         int chunk)
+// Tokens [s_begin, s_end) of query row i, whose keys start at cache row kv_base.
+__device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ q, const float *__restrict__ w,
+                                                   const uint8_t *__restrict__ k, int64_t kstride,
+                                                   const float *__restrict__ ks, int64_t ks_stride,
+                                                   float *__restrict__ scores, int64_t ld, int64_t i,
+                                                   int64_t kv_base, int64_t s_begin, int64_t s_end)
 {
-    const int64_t i = blockIdx.y;
-    const RowInfo r = row_info(L, i);
-    const int64_t s_begin = (int64_t)blockIdx.x * chunk;
-    if (s_begin >= r.n)
-        return;
-    const int64_t s_end = min(s_begin + (int64_t)chunk, r.n);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform loop bounds
     const int g = lane >> 5, j = lane & 31;
@@ -66,7 +60,7 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(LayoutDev L, const uint
     // before the current tile's MFMAs, so every wave keeps a tile in flight.
     auto load_tile = [&](int64_t s0, u32x4 (&kv)[4], float &ksv) {
         const int64_t s = s0 + j;
-        const int64_t row = r.kv_base + (s < s_end ? s : s_end - 1);
+        const int64_t row = kv_base + (s < s_end ? s : s_end - 1);
         const u32x4 *kp = (const u32x4 *)(k + row * kstride + 64 * g);
         kv[0] = kp[0];
         kv[1] = kp[1];
@@ -112,6 +106,49 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(LayoutDev L, const uint
         load_tile(s0 + 256, bufA, kA);
         __builtin_amdgcn_sched_barrier(0);
         compute_tile(s0 + 128, bufB, kB);
+    }
+}
+
+// Two launch shapes.  Rows that are whole sequences (one query each, as in decode): the grid
+// walks the concatenated token stream of all sequences, chunk tokens per block (a block may
+// finish one sequence and start the next), so every block has work and the blocks past the
+// last token all sit at the end of the grid.  Otherwise: one block per (chunk, query row).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
+                                                         const float *__restrict__ w,
+                                                         const uint8_t *__restrict__ k, int64_t kstride,
+                                                         const float *__restrict__ ks, int64_t ks_stride,
+                                                         float *__restrict__ scores, int64_t ld, int chunk,
+                                                         int stream)
+{
+    if (!stream) {
+        const int64_t i = blockIdx.y;
+        const RowInfo r = row_info(L, i);
+        const int64_t s_begin = (int64_t)blockIdx.x * chunk;
+        if (s_begin < r.n)
+            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin,
+                               min(s_begin + (int64_t)chunk, r.n));
+        return;
+    }
+    const int64_t t0 = (int64_t)blockIdx.x * chunk;
+    const int64_t N = L.kv_indptr[L.batch];
+    if (t0 >= N)
+        return;
+    const int64_t t1 = min(t0 + (int64_t)chunk, N);
+    int lo = 0, hi = L.batch - 1;  // the sequence holding token t0: largest b with kv_indptr[b] <= t0
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (L.kv_indptr[mid] <= t0)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    for (int b = lo; b < L.batch; ++b) {
+        const int64_t rb = L.kv_indptr[b], re = L.kv_indptr[b + 1];
+        if (rb >= t1)
+            break;
+        const int64_t sb = max(t0, rb), se = min(t1, re);
+        if (se > sb)
+            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, rb, sb - rb, se - rb);
     }
 }
 
@@ -366,9 +403,11 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
         if (c >= 128 && c <= 8192 && (c & (c - 1)) == 0)
             chunk = c;
     }
-    dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)T);
+    const int64_t nchunks = (max_ctx + chunk - 1) / chunk;
+    const bool as_stream = L.q_indptr == nullptr;  // rows are whole sequences
+    dim3 grid = as_stream ? dim3((unsigned)((T * max_ctx + chunk - 1) / chunk)) : dim3((unsigned)nchunks, (unsigned)T);
     hipLaunchKernelGGL(idx_decode_kernel, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
-                       (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
+                       (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -489,6 +489,20 @@ __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
 // reads are waited for once.
 constexpr int F_DMA_PER_WAVE = (F_DMA + 3) / 4;  // 10 (the last only on wave 0)
 
+constexpr int F_IDX = 2048;  // index slots of one split (32 tiles) held in LDS
+static_assert(F_IDX >= DSA_TOPK_MAX, "a split never holds more than k index slots");
+
+// Wait until only the DMA steps of the most recent tile (10 on wave 0, 9 on the others) may
+// still be outstanding: every earlier tile has landed.
+__device__ __forceinline__ void wait_but_last_tile8(int w)
+{
+    static_assert(F_DMA == 37 && F_DMA_PER_WAVE == 10, "DMA steps per wave");
+    if (w == 0)
+        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+}
+
 // Lane geometry of the gather, fixed per lane: DMA instruction q of wave w covers bytes
 // 1024*(4q + w) + 16*lane of the tile, i.e. row rc & 0xFF, column rc >> 8 (0xFFFF: the
 // pad bytes, or an instruction past the tile, which reads zeros).
@@ -552,7 +566,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
     __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
     __shared__ float xm[4][32];                                    // per-head maxima swap
-    __shared__ int32_t sidx[3][M_TILE];
+    __shared__ int32_t sidx[F_IDX];                                // this split's index slots
     __shared__ int sh_flag;
 
     const int64_t pair = xcd_pair(pairs_per_xcd);
@@ -576,19 +590,13 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     const int ntiles = max(0, min(ntiles_all, t_begin + tiles_per_split) - t_begin);
     const int32_t *irow = indices + i * k;
 
-    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
-        const int slot = (t_begin + tt) * M_TILE + tid;
-        return (tt < ntiles && slot < k) ? irow[slot] : -1;
-    };
-    // the first tiles' indices are loaded before Q so that their latency overlaps it
-    int32_t i0 = -1, i1 = -1, i2 = -1, i3 = -1;
-    if (tid < M_TILE) {
-        i0 = load_idx(0);
-        i1 = load_idx(1);
-        i2 = load_idx(2);
-        i3 = load_idx(3);
+    // the split's whole index list goes to LDS up front (its latency overlaps Q's), so the
+    // tile loop issues no loads the compiler would wait on together with the tile DMAs
+    {
+        const int s0 = t_begin * M_TILE, nsl = min(k - s0, ntiles * M_TILE);
+        for (int e = tid; e < ntiles * M_TILE; e += M_THREADS)
+            sidx[e] = e < nsl ? irow[s0 + e] : -1;
     }
-    __builtin_amdgcn_sched_barrier(0);
 
     // Q^T operand in the permuted dim order (see above)
     bf16x8 qT[18];
@@ -716,68 +724,61 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     };
 
     auto run = [&]() {
-        if (tid < M_TILE) {
-            sidx[0][tid] = i0;
-            sidx[1][tid] = i1;
-            sidx[2][tid] = i2;
-        }
-        int32_t idx_next = tid < M_TILE ? i3 : -1;
-        lds_barrier();  // Q stays in flight
+        __builtin_amdgcn_s_waitcnt(0x0070);  // indices and Q have landed: nothing else in flight
+        lds_barrier();
         if (ntiles > 0)
-            dma_tile(seq, lds0, sidx[0], w, rc);
-        if (ntiles > 1)
-            dma_tile(seq, lds0 + F_TILEB, sidx[1], w, rc);
-        tile_barrier();  // tiles 0 and 1 (and Q) have landed
-        if (ntiles > 0) {
-            S[0] = f32x16{};
-            S[1] = f32x16{};
-            u32x4 A[2][2];
-            s_load(0, 0, A[0]);
-#pragma unroll
-            for (int p = 0; p < 9; ++p) {
-                if (p + 1 < 9)
-                    s_load(0, p + 1, A[(p + 1) & 1]);
-                s_mfma(A[p & 1], p);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            softmax(sidx[0]);
+            dma_tile(seq, lds0, sidx, w, rc);
+        if (ntiles > 1) {
+            dma_tile(seq, lds0 + F_TILEB, sidx + M_TILE, w, rc);
+            wait_but_last_tile8(w);  // tile 0 has landed
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
+        lds_barrier();
 
         for (int tt = 0; tt < ntiles; ++tt) {
-            const int b0 = tt % 3, b1 = (tt + 1) % 3, b2 = (tt + 2) % 3;
-            if (tt + 2 < ntiles)
-                dma_tile(seq, lds0 + (uint32_t)b2 * F_TILEB, sidx[b2], w, rc);
-            const int32_t idx_after = tid < M_TILE ? load_idx(tt + 4) : -1;
+            const int b0 = tt % 3;
+            if (tt + 2 < ntiles)  // into the buffer of tile tt - 1, consumed before the last barrier
+                dma_tile(seq, lds0 + (uint32_t)((tt + 2) % 3) * F_TILEB, sidx + (tt + 2) * M_TILE, w, rc);
 
-            // ---- MFMA phase: PV of tile tt interleaved with S of tile tt+1 (on the last tile the
-            // S half runs over a stale buffer and its result is dropped: finite data, no branch)
+            // ---- S^T partials of tile tt (two key halves over this wave's 288 dims)
             S[0] = f32x16{};
             S[1] = f32x16{};
             {
                 u32x4 A[2][2];
+                s_load(b0, 0, A[0]);
+#pragma unroll
+                for (int p = 0; p < 9; ++p) {
+                    if (p + 1 < 9)
+                        s_load(b0, p + 1, A[(p + 1) & 1]);
+                    s_mfma(A[p & 1], p);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            softmax(sidx + tt * M_TILE);
+
+            // ---- O^T += V^T . P^T over the tile's 64 keys
+            {
                 i32x2 V[2][8];
-                s_load(b1, 0, A[0]);
                 v_load(b0, 0, V[0]);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     if (u + 1 < 4)
                         v_load(b0, u + 1, V[(u + 1) & 1]);
-                    s_load(b1, 2 * u + 1, A[1]);
-                    s_mfma(A[0], 2 * u);
                     pv_mfma(V[u & 1], bop[u], 0);
-                    s_load(b1, 2 * u + 2, A[0]);
-                    s_mfma(A[1], 2 * u + 1);
                     pv_mfma(V[u & 1], bop[u], 4);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                s_mfma(A[0], 8);
             }
-            if (tt + 1 < ntiles)
-                softmax(sidx[b1]);
-            if (tid < M_TILE)
-                sidx[b0][tid] = idx_next;  // tile tt + 3
-            idx_next = idx_after;
-            tile_barrier();  // tile tt + 2 has landed; buffer b0 is free
+
+            // ---- tile tt + 1 must have landed (tile tt + 2 may stay in flight)
+            if (tt + 1 < ntiles) {
+                if (tt + 2 < ntiles)
+                    wait_but_last_tile8(w);
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            lds_barrier();  // tile tt, S partials and P consumed; tile tt + 1 visible to all
         }
     };
     run();
