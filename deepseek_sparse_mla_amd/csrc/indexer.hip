@@ -392,10 +392,10 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
                                const float *w, const void *k, int64_t kstride, const float *ks,
                                int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream)
 {
-    // Short-lived waves (at most 8 tiles each) and enough blocks to cover the chip
-    // several times, at least one 32-token tile per wave.  DSA_INDEXER_CHUNK (a power of
+    // Waves of at most 16 tiles and enough blocks to cover the chip several times, at least
+    // one 32-token tile per wave.  DSA_INDEXER_CHUNK (a power of
     // two in [128, 8192]) overrides the tokens per block for launch-shape tuning.
-    int chunk = 1024;
+    int chunk = 2048;
     while (chunk > 128 && T * ((max_ctx + chunk - 1) / chunk) < 2048)
         chunk >>= 1;
     if (const char *env = getenv("DSA_INDEXER_CHUNK")) {

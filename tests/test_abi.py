@@ -86,6 +86,15 @@ def test_topk_rejects(lib):
     assert lib.dsa_topk_workspace_size(L, 4096, 2048) == 0
 
 
+def test_topk_workspace_only_for_rows_past_32768(lib):
+    """Rows up to 32768 scores are selected by one block each (no workspace); longer rows
+    need the histogram (and, for few rows, bitmap and member) workspace."""
+    for max_ctx in (8192, 16384, 32768):
+        assert lib.dsa_topk_workspace_size(ctypes.byref(_layout(max_ctx=max_ctx)), max_ctx, 2048) == 0
+    for max_ctx in (32769, 131072, 300000):
+        assert lib.dsa_topk_workspace_size(ctypes.byref(_layout(max_ctx=max_ctx)), max_ctx, 2048) > 0
+
+
 def _mla(lib, layout, ws=None, ws_bytes=0, **kw):
     a = dict(H=64, Dc=512, Dr=64, sm=0.0625, q_dt=B.DSA_BF16, q=FAKE, kv_dt=B.DSA_BF16, kv=FAKE,
              kv_scale=1.0, idx=FAKE, k=2048, out_dt=B.DSA_BF16, out=FAKE, lse=None)

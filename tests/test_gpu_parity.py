@@ -225,8 +225,9 @@ def test_topk_single_block_rows():
 
 
 def test_topk_threshold_bin_overflow():
-    """More than 8192 keys share the bin of the k-th key: the exact refinement over the row,
-    with the ties taken in position order."""
+    """More keys share the bin of the k-th key than the member list holds: the exact radix
+    refinement over the row itself, with the ties taken in position order (rows of one block
+    held in LDS, and rows whose histogram and members are spread over many blocks)."""
     rng = np.random.default_rng(11)
     rows = [
         np.full(20000, 1.5, np.float32),
@@ -234,10 +235,25 @@ def test_topk_threshold_bin_overflow():
         np.concatenate([rng.standard_normal(1000) + 10, np.full(15000, 2.0), rng.standard_normal(5000)]).astype(np.float32),
     ]
     _topk_rows(rows)
+    rows = [
+        np.full(100000, -1.25, np.float32),
+        rng.integers(0, 3, 70000).astype(np.float32),
+        np.concatenate([rng.standard_normal(1500) + 10, np.full(40000, 2.0), rng.standard_normal(60000)]).astype(np.float32),
+    ]
+    _topk_rows(rows)
+
+
+def test_topk_longest_rows_many_blocks():
+    """Rows longer than 262144 scores (a bitmap too large for LDS): histogram and marking
+    spread over many blocks per row, then one block per row selects among the members."""
+    rng = np.random.default_rng(14)
+    rows = [rng.standard_normal(300000).astype(np.float32), np.round(rng.standard_normal(270000), 2).astype(np.float32),
+            rng.standard_normal(5000).astype(np.float32), np.full(263000, 0.5, np.float32)]
+    _topk_rows(rows)
 
 
 def test_topk_many_long_rows():
-    """More than 512 rows longer than 8192 (the per-row mode), ragged."""
+    """More than 512 ragged rows longer than 8192 (one block per row, rows in registers)."""
     rng = np.random.default_rng(12)
     rows = [rng.standard_normal(int(n)).astype(np.float32) for n in rng.integers(8193, 12000, 520)]
     rows[5] = np.round(rows[5], 1)
@@ -248,11 +264,12 @@ def test_topk_many_long_rows():
 def test_topk_workspace_reused_across_layouts():
     """One workspace serves calls with different layouts and is all zero after each call."""
     rng = np.random.default_rng(13)
-    big = [rng.standard_normal(n).astype(np.float32) for n in (70000, 20000, 9000, 131072)]
-    small = [rng.standard_normal(n).astype(np.float32) for n in [40000] * 9]
+    big = [rng.standard_normal(n).astype(np.float32) for n in (270000, 20000, 9000, 300000)]
+    small = [rng.standard_normal(n).astype(np.float32) for n in [280000] * 3]
     lay_b = _topk_rows(big, workspace=None)
     lay_s = _topk_rows(small, workspace=None)
-    nb = max(dsa.dsa_topk_workspace_size(lay_b, 131072, 2048), dsa.dsa_topk_workspace_size(lay_s, 40000, 2048))
+    nb = max(dsa.dsa_topk_workspace_size(lay_b, 300000, 2048), dsa.dsa_topk_workspace_size(lay_s, 280000, 2048))
+    assert nb > 0
     ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
     for rows in (big, small, big):
         _topk_rows(rows, workspace=ws)
