@@ -364,7 +364,8 @@ def main():
                                 if probe.T <= 512 or probe.max_ctx > (1 << 18) else
                                 "topk_hist_kernel + topk_select_kernel"),
         "mla": ("sparse_mla_prefill: " if prefill else "sparse_mla_decode%s: " % ("_shared" if len(probe.layers) > 1 else ""))
-        + ("mla_fp8_kernel" if probe.layers[0].kv_dt == "fp8" else "mla_kernel")
+        + ("mla_fp8_kernel" if probe.layers[0].kv_dt == "fp8" else
+           "mla_hh_kernel" if probe.T * len(probe.layers) <= 512 else "mla_kernel")
         + (" + mla_combine_kernel" if split else ""),
     }
     path_gbs = model["path_bytes"] / (ms_per_step * 1e-3) / 1e9

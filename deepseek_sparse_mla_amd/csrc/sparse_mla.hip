@@ -807,6 +807,313 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml, &kt8[0][0], tid);
 }
 
+// ------------------------------------------------------------------------------------------
+// bf16 latent rows, half the heads per block: one 4-wave block per (row, split, head half),
+// 32-key tiles, ~56 KB of LDS and at most 256 registers per lane, so two blocks share a CU and
+// one block's MFMAs run while the other waits on its softmax, exchanges or barriers.  The two
+// head halves of a (row, split) gather the same rows; they are dealt to the same XCD, so the
+// second gather hits L2.
+// Wave w = dq: S^T partials [32 keys x 32 heads] over dims 144 dq .. +143 (9 MFMA), a 4-way
+// exchange after which wave dq holds the full logits of keys 8 dq + 4 g + 0..3 (summed in wave
+// order 0, 1, 2, 3), their softmax numerators, and O^T for dims 128 dq .. +127 of the 32 heads
+// over all 32 keys (8 MFMA; P of keys 16 u + 4 g + e comes from wave 2u, of 16 u + 8 + 4 g + e
+// from wave 2u + 1, in the key order of ds_read_b64_tr_b16).
+// ------------------------------------------------------------------------------------------
+constexpr int HH_TILE = 32;                          // keys per tile
+constexpr int64_t MLA_HH_MAX_ROWS = 512;             // bf16 rows up to this many use mla_hh_kernel
+constexpr int HH_TILEB = HH_TILE * M_ROWB;           // 37376 B
+constexpr int HH_PIECES = HH_TILE * 72;              // 16-byte pieces per tile
+constexpr int HH_N = HH_PIECES / M_THREADS;          // 9 per thread
+static_assert(HH_PIECES % M_THREADS == 0, "staging");
+constexpr int HH_EROWB = 1040;                       // output staging row stride
+static_assert(32 * HH_EROWB <= HH_TILEB, "output staging fits the tile buffer");
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void mla_hh_kernel(
+    LayoutDev L, int64_t T, int64_t n_rows, MlaLayersDev layers, const int32_t *__restrict__ indices, int k,
+    float sm_scale, int nsplit, int tiles_per_split, int64_t pairs_per_xcd, float *__restrict__ ws_o,
+    float *__restrict__ ws_ml)
+{
+    __shared__ __attribute__((aligned(16))) char kt[HH_TILEB];
+    __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];  // S^T quarter partials [from][to][lane]
+    __shared__ __attribute__((aligned(16))) u32x2 xp[4][64];     // P of each wave's keys (4 bf16)
+    __shared__ float xm[4][32];                                   // per-head stats across the waves
+    __shared__ int32_t sidx[2][HH_TILE];
+    __shared__ int sh_flag;
+
+    const int64_t pair = xcd_pair(pairs_per_xcd);  // (row, split, head half), head half fastest
+    if (pair >= n_rows * nsplit * 2)
+        return;
+    const int hh = (int)(pair & 1);
+    const int64_t rs = pair >> 1;
+    const int64_t orow = rs / nsplit;
+    const int split = (int)(rs % nsplit);
+    const int layer = (int)(orow / T);
+    const int64_t i = orow % T;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, j = lane & 31;
+    const int dq = w;
+    const MlaLayerDev Ld = layers.l[layer];
+    const RowInfo r = row_info(L, i);
+    const float c2 = sm_scale * Ld.kv_scale * LOG2E;
+
+    // this split's index slots [s0, s0 + nsl) as 32-key tiles
+    const int s0 = split * tiles_per_split * M_TILE;
+    const int nsl = max(0, min(k - s0, tiles_per_split * M_TILE));
+    const int ntiles = (nsl + HH_TILE - 1) / HH_TILE;
+    const int32_t *irow = indices + i * k + s0;
+    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 32)
+        const int e = tt * HH_TILE + tid;
+        return (tt < ntiles && e < nsl) ? irow[e] : -1;
+    };
+    int32_t i0 = -1, i1 = -1, i2 = -1;
+    if (tid < HH_TILE) {
+        i0 = load_idx(0);
+        i1 = load_idx(1);
+        i2 = load_idx(2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Q^T: head 32 hh + j, dims 144 dq + 16 t + 8 g .. +7 (t < 9)
+    bf16x8 qT[9];
+    {
+        const uint16_t *qp = (const uint16_t *)Ld.q + ((i * M_H + 32 * hh + j) * M_DQK + 144 * dq + 8 * g);
+#pragma unroll
+        for (int t = 0; t < 9; ++t)
+            qT[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * t));
+    }
+    f32x16 O[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        O[mt] = f32x16{};
+
+    const int64_t seq_bytes = r.n * (2 * M_DQK);  // host guarantees max_ctx * 1152 < 2^31
+    const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const uint8_t *)Ld.kv + r.kv_base * (2 * M_DQK)), (short)0, (int)seq_bytes, BUF_DWORD3);
+    u32x4 R[HH_N];
+    // piece tid + 256 u of the tile is row rc[u] >> 8, 16-byte column rc[u] & 255 (fixed per
+    // thread; consecutive lanes read consecutive 16 bytes of a row)
+    uint32_t rc[HH_N];
+#pragma unroll
+    for (int u = 0; u < HH_N; ++u) {
+        const int c = tid + M_THREADS * u;
+        rc[u] = ((uint32_t)(c / 72) << 8) | (uint32_t)(c % 72);
+    }
+    auto gather = [&](const int32_t *sx) {  // tile rows sx[0..31] into the staging registers
+#pragma unroll
+        for (int u = 0; u < HH_N; ++u)
+            R[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 seq, sx[rc[u] >> 8] * (2 * M_DQK) + 16 * (int)(rc[u] & 255u), 0, 0));
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int u = 0; u < HH_N; ++u)
+            *(u32x4 *)(kt + (rc[u] >> 8) * M_ROWB + 16 * (rc[u] & 255u)) = R[u];
+    };
+
+    const int aoffs = j * M_ROWB + 2 * (144 * dq + 8 * g);
+    const int voffs = (4 * g + ((lane & 15) >> 2)) * M_ROWB + 2 * (128 * dq + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+    float m_ref = -INFINITY;   // identical in the 4 waves (same reference for head j)
+    float m_seen = -INFINITY;  // max over this wave's keys
+    float l_own = 0.f;         // sum of p over this lane's keys
+    bool ovf = false;
+
+    auto run = [&]() {
+        if (tid < HH_TILE) {
+            sidx[0][tid] = i0;
+            sidx[1][tid] = i1;
+        }
+        if (tid == 0)
+            sh_flag = 0;
+        int32_t idx_next = i2;
+        lds_barrier();  // Q stays in flight
+        if (ntiles > 0) {
+            gather(sidx[0]);
+            stage();
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);  // nothing known to the compiler stays in flight
+        lds_barrier();
+        for (int tt = 0; tt < ntiles; ++tt) {
+            const int buf = tt & 1;
+            if (tt + 1 < ntiles)
+                gather(sidx[buf ^ 1]);
+            const uint32_t valid = (uint32_t)__ballot(lane < HH_TILE && sidx[buf][lane & 31] >= 0);
+
+            // ---- 1. S^T partial over this wave's 144 dims
+            f32x16 S = f32x16{};
+            {
+                const char *arow = kt + aoffs;
+                u32x4 A[2][3];
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    A[0][t] = *(const u32x4 *)(arow + 32 * t);
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    const int cur = c & 1;
+                    if (c + 1 < 3) {
+#pragma unroll
+                        for (int t = 0; t < 3; ++t)
+                            A[cur ^ 1][t] = *(const u32x4 *)(arow + 32 * (3 * (c + 1) + t));
+                    }
+#pragma unroll
+                    for (int t = 0; t < 3; ++t)
+                        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[cur][t]),
+                                                                    qT[3 * c + t], S, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            // ---- 2. quarter exchange: s = sum over waves 0..3 of their partials of this wave's keys
+            // (all four quarters go through LDS, own one included: no per-lane selects)
+#pragma unroll
+            for (int d2 = 0; d2 < 4; ++d2)
+                xs[dq][d2][lane] = f32x4{S[4 * d2], S[4 * d2 + 1], S[4 * d2 + 2], S[4 * d2 + 3]};
+            lds_barrier();
+            float s[4];
+            {
+                const f32x4 p0 = xs[0][dq][lane], p1 = xs[1][dq][lane], p2 = xs[2][dq][lane], p3 = xs[3][dq][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s[e] = ((p0[e] + p1[e]) + p2[e]) + p3[e];
+            }
+
+            // ---- 3. softmax numerators of keys 8 dq + 4 g + e of head j
+            const uint32_t vk = (valid >> (8 * dq + 4 * g)) & 15u;
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s[e] = ((vk >> e) & 1u) ? s[e] * c2 : -INFINITY;
+                mloc = fmaxf(mloc, s[e]);
+            }
+            mloc = fmaxf(mloc, other_half(mloc, g));
+            if (m_ref == -INFINITY && valid != 0u) {
+                // first non-empty tile (block-uniform): the 4 waves agree on the reference
+                if (g == 0)
+                    xm[w][j] = mloc;
+                lds_barrier();
+                m_ref = fmaxf(fmaxf(xm[0][j], xm[1][j]), fmaxf(xm[2][j], xm[3][j]));
+                lds_barrier();
+            }
+            m_seen = fmaxf(m_seen, mloc);
+            ovf |= mloc > m_ref + 100.f;
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[e] - m_ref);
+                l_own += p[e];
+            }
+            xp[w][lane] = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[0], p[1]}, bf16x2)),
+                                __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2], p[3]}, bf16x2))};
+            lds_barrier();
+
+            // ---- 4. O^T += V^T . P^T over the 32 keys (2 steps of 16 keys x 4 dim blocks)
+            {
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const char *vbase = kt + voffs;
+                s16x4 V[2][4][2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        V[u][mt][0] = lds_tr16(vbase + 16 * u * M_ROWB + 64 * mt);
+                        V[u][mt][1] = lds_tr16(vbase + (16 * u + 8) * M_ROWB + 64 * mt);
+                    }
+                const u32x2 pa0 = xp[0][lane], pa1 = xp[1][lane], pa2 = xp[2][lane], pa3 = xp[3][lane];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const u32x2 lo2 = u ? pa2 : pa0, hi2 = u ? pa3 : pa1;
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        const s16x4 lo = V[u][mt][0], hi = V[u][mt][1];
+                        const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), bop, O[mt],
+                                                                        0, 0, 0);
+                    }
+                }
+            }
+            lds_barrier();  // tile, partials and P consumed
+            if (tt + 1 < ntiles)
+                stage();
+            if (tid < HH_TILE) {
+                sidx[buf][tid] = idx_next;  // tile tt + 2
+                idx_next = load_idx(tt + 3);
+            }
+            lds_barrier();
+        }
+    };
+    run();
+    if (ovf)
+        sh_flag = 1;
+    __syncthreads();
+    if (sh_flag) {  // rare: rerun with the exact maximum of the first run as the reference
+        if (g == 0)
+            xm[w][j] = m_seen;
+        __syncthreads();
+        m_ref = fmaxf(fmaxf(xm[0][j], xm[1][j]), fmaxf(xm[2][j], xm[3][j]));
+        l_own = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            O[mt] = f32x16{};
+        __syncthreads();
+        run();
+    }
+
+    // ---- row sum of head j over all keys: lane halves, then the 4 waves in order
+    float l_w = l_own + other_half(l_own, g);
+    __syncthreads();
+    if (g == 0)
+        xm[w][j] = l_w;
+    __syncthreads();
+    const float l_run = ((xm[0][j] + xm[1][j]) + xm[2][j]) + xm[3][j];
+
+    // ---- epilogue: this block's 32 heads x 512 dims (O / l, or the normalised output)
+    const int head = 32 * hh + j;
+    const float inv = (l_run > 0.f) ? (nsplit == 1 ? Ld.kv_scale / l_run : 1.f / l_run) : 0.f;
+    if (OUT_F32) {
+        float *dst = (nsplit == 1) ? (float *)Ld.out + (i * M_H + head) * M_DC
+                                   : ws_o + ((orow * nsplit + split) * M_H + head) * M_DC;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 128 * dq + 32 * mt + 8 * q4 + 4 * g;
+                *(f32x4 *)(dst + d) = f32x4{O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv, O[mt][4 * q4 + 2] * inv,
+                                            O[mt][4 * q4 + 3] * inv};
+            }
+    } else {
+        __syncthreads();  // the tile buffer becomes the output staging area
+        char *srow = kt + j * HH_EROWB;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 128 * dq + 32 * mt + 8 * q4 + 4 * g;
+                *(u32x2 *)(srow + 2 * d) = u32x2{pack_bf16x2(O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv),
+                                                 pack_bf16x2(O[mt][4 * q4 + 2] * inv, O[mt][4 * q4 + 3] * inv)};
+            }
+        __syncthreads();
+        char *dst = (nsplit == 1) ? (char *)((uint16_t *)Ld.out + (i * M_H + 32 * hh) * M_DC)
+                                  : (char *)((uint16_t *)ws_o + ((orow * nsplit + split) * M_H + 32 * hh) * M_DC);
+#pragma unroll
+        for (int u = 0; u < 32 * M_DC * 2 / (16 * M_THREADS); ++u) {
+            const int c = tid + M_THREADS * u, h = c >> 6, c16 = c & 63;
+            *(u32x4 *)(dst + h * (M_DC * 2) + 16 * c16) = *(const u32x4 *)(kt + h * HH_EROWB + 16 * c16);
+        }
+    }
+    if (nsplit == 1) {
+        if (Ld.lse && dq == 0 && g == 0)
+            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
+    } else if (dq == 0 && g == 0) {
+        float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
+        pml[0] = m_ref;
+        pml[1] = l_run;
+    }
+}
+
 // Combine the split partials of every (output row, head), in split order.  One 128-thread
 // block per (row, head); thread t owns dims 4t .. 4t + 3.  Partial s holds O_s / l_s, so
 // its weight is l_s 2^(m_s - M) / sum over splits of the same.
@@ -1012,6 +1319,16 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
         else
             hipLaunchKernelGGL((mla_fp8_kernel<false>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
                                indices, k, sm_scale, ns, tps, ppx, wo, wml);
+    } else if (rows <= MLA_HH_MAX_ROWS) {
+        // few rows (decode): half-head blocks, two per CU
+        const int64_t hpairs = pairs * 2, hppx = (hpairs + 7) / 8;
+        dim3 hgrid((unsigned)(8 * hppx));
+        if (out_f32)
+            hipLaunchKernelGGL((mla_hh_kernel<true>), hgrid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, tps, hppx, wo, wml);
+        else
+            hipLaunchKernelGGL((mla_hh_kernel<false>), hgrid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, tps, hppx, wo, wml);
     } else {
         if (out_f32)
             DSA_MLA_LAUNCH(false, true);
