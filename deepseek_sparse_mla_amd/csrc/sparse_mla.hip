@@ -1114,6 +1114,8 @@ __global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
     }
 }
 
+constexpr int MLA_MAX_SPLITS = 32;  // the split count never exceeds this (mla_num_splits)
+
 // Combine the split partials of every (output row, head), in split order.  One 128-thread
 // block per (row, head); thread t owns dims 4t .. 4t + 3.  Partial s holds O_s / l_s, so
 // its weight is l_s 2^(m_s - M) / sum over splits of the same.
@@ -1130,6 +1132,21 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int64_t T, MlaLayersDe
     const int64_t i = orow % T;
     const MlaLayerDev Ld = layers.l[layer];
     const int tid = threadIdx.x;
+    // every split's partial is requested first (independent of the weights), so their
+    // latencies overlap each other and the weight computation
+    const int64_t pbase = (orow * nsplit * M_H + head) * M_DC + 4 * tid;
+    typedef typename std::conditional<OUT_F32, f32x4, u32x2>::type Piece;
+    Piece pv[MLA_MAX_SPLITS];
+#pragma unroll
+    for (int sp = 0; sp < MLA_MAX_SPLITS; ++sp) {
+        if (sp < nsplit) {
+            const int64_t pe = pbase + (int64_t)sp * M_H * M_DC;
+            if constexpr (OUT_F32)
+                pv[sp] = *(const f32x4 *)(ws_o + pe);
+            else
+                pv[sp] = *(const u32x2 *)((const uint16_t *)ws_o + pe);
+        }
+    }
     if (tid < 64) {
         const float *ml = ws_ml + (orow * nsplit * M_H + head) * 2;
         const int sp = tid;
@@ -1148,23 +1165,24 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int64_t T, MlaLayersDe
             lse_s = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
     }
     __syncthreads();
-    const int64_t pbase = (orow * nsplit * M_H + head) * M_DC + 4 * tid;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < nsplit; ++sp) {
-        const int64_t pe = pbase + (int64_t)sp * M_H * M_DC;
-        f32x4 v;
-        if (OUT_F32) {
-            v = *(const f32x4 *)(ws_o + pe);
-        } else {
-            const u32x2 b = *(const u32x2 *)((const uint16_t *)ws_o + pe);
-            v = f32x4{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xFFFF0000u),
-                      __uint_as_float(b[1] << 16), __uint_as_float(b[1] & 0xFFFF0000u)};
+#pragma unroll
+    for (int sp = 0; sp < MLA_MAX_SPLITS; ++sp) {
+        if (sp < nsplit) {
+            f32x4 v;
+            if constexpr (OUT_F32) {
+                v = pv[sp];
+            } else {
+                const u32x2 bw = pv[sp];
+                v = f32x4{__uint_as_float(bw[0] << 16), __uint_as_float(bw[0] & 0xFFFF0000u),
+                          __uint_as_float(bw[1] << 16), __uint_as_float(bw[1] & 0xFFFF0000u)};
+            }
+            const float wgt = wts[sp];
+            acc[0] = fmaf(wgt, v[0], acc[0]);
+            acc[1] = fmaf(wgt, v[1], acc[1]);
+            acc[2] = fmaf(wgt, v[2], acc[2]);
+            acc[3] = fmaf(wgt, v[3], acc[3]);
         }
-        const float wgt = wts[sp];
-        acc[0] = fmaf(wgt, v[0], acc[0]);
-        acc[1] = fmaf(wgt, v[1], acc[1]);
-        acc[2] = fmaf(wgt, v[2], acc[2]);
-        acc[3] = fmaf(wgt, v[3], acc[3]);
     }
     const int64_t o = (i * M_H + head) * M_DC + 4 * tid;
     if (OUT_F32)
@@ -1269,13 +1287,13 @@ int mla_num_splits(int64_t rows, int k)
         ns = ntiles / 2;
     if (const char *env = getenv("DSA_MLA_SPLITS")) {  // tuning sweeps: a fixed split count
         const long v = strtol(env, nullptr, 10);
-        if (v >= 1 && v <= 32)
+        if (v >= 1 && v <= MLA_MAX_SPLITS)
             ns = v;
     }
     if (ns > ntiles)
         ns = ntiles;
-    if (ns > 32)
-        ns = 32;
+    if (ns > MLA_MAX_SPLITS)
+        ns = MLA_MAX_SPLITS;
     if (ns < 1)
         ns = 1;
     const int tps = (ntiles + (int)ns - 1) / (int)ns;  // equal tiles per split
