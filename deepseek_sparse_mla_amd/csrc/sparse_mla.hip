@@ -539,11 +539,11 @@ __device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, co
 
 //
 // Same wave roles and math as mla_kernel (see above), software-pipelined over tiles:
-//  * tiles are gathered by DMA into three LDS buffers, two tiles ahead, kept fp8 there and
-//    widened to bf16 in registers when read;
-//  * the MFMA phase of step t runs O^T += V^T.P^T for tile t interleaved with the S^T
-//    partials of tile t+1, so the two independent MFMA streams hide each other's operand
-//    latency; the softmax of tile t+1 follows;
+//  * the split's whole index list is loaded into LDS up front; tiles are gathered by DMA into
+//    three LDS buffers, kept fp8 there and widened to bf16 in registers when read.  While
+//    tile t is computed (S partials, softmax, PV) tiles t+1 and t+2 are in flight, and the end
+//    of the step waits only for tile t+1 (a count-based wait: the newest tile's DMA steps may
+//    stay outstanding);
 //  * S operands: 16 fp8 bytes per lane (two k-steps) widened to bf16; Q^T is loaded in the
 //    same permuted dim order (k-step 2p + h of lane half g covers dims 288dq + 32p + 16g +
 //    8h .. +7), which leaves the contraction unchanged;
