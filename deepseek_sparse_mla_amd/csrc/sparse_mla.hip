@@ -7,17 +7,21 @@
 //
 //   z_j = sm_scale * kv_scale * q_h . c_j ;  o_h = kv_scale * sum_j softmax(z)_j c_j[0:512]
 //
-// Tuned kernel (H = 64, Dc = 512, Dr = 64, bf16 q, bf16 or fp8 latent rows):
-//  * one 256-thread block per (layer, query row, split of the index list); 4 waves,
-//    wave w owns heads 32*(w&1) .. +31 and key half / output-dim half (w>>1);
-//  * 64-row tiles of gathered latent rows are staged (fp8 widened exactly to bf16) into a
-//    double-buffered LDS tile [64][576 (+8 pad)]; the next tile's rows are loaded into
-//    registers while the current one is computed;
+// Tuned kernels (H = 64, Dc = 512, Dr = 64, bf16 q, bf16 or fp8 latent rows):
+//  * mla_kernel (bf16 rows, many query rows, e.g. prefill): one 256-thread block per
+//    (layer, query row, split of the index list); 4 waves, wave w owns heads 32*(w&1) .. +31
+//    and key half / output-dim half (w>>1); 64-row tiles staged through registers into one
+//    LDS tile [64][576 (+8 pad)], the next tile's rows in flight while the current one is
+//    computed;
+//  * mla_hh_kernel (bf16 rows, at most 512 (row, layer) pairs: decode): the same per
+//    (row, split, head half), 32-key tiles, small enough for two blocks per CU;
+//  * mla_fp8_kernel (fp8 rows): the mla_kernel wave roles over fp8 tiles gathered by DMA
+//    into three LDS buffers, two tiles in flight, widened to bf16 when read;
 //  * S^T[keys x heads] = K . Q^T on v_mfma_f32_32x32x16_bf16 with Q^T held in registers,
 //    so each lane owns one head column: the online-softmax max/sum need one cross-half
-//    swap and one LDS exchange with the partner wave;
+//    swap and LDS exchanges between the waves that split the contraction;
 //  * O^T[dims x heads] += V^T . P^T, V^T read straight from the row-major tile with
-//    ds_read_b64_tr_b16 (4 consecutive keys of one dim per lane);
+//    ds_read_b64_tr_b16 (4 consecutive keys of one dim per lane; _b8 for fp8 tiles);
 //  * softmax reference: each head's reference max is fixed at its first non-empty tile and
 //    never moves, so the accumulators are never rescaled; a split whose later logits
 //    exceed the reference by more than 2^100 is rerun with the exact maximum (exact
