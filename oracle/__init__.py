@@ -35,10 +35,11 @@ F32, BF16, FP8 = 0, 1, 2  # oracle-local dtype codes (see dsa_oracle.c)
 
 
 def build(force: bool = False) -> str:
-    """Compile dsa_oracle.c into _liboracle.so with gcc (OpenMP, -O2, IEEE)."""
+    """Compile dsa_oracle.c into _liboracle.so with gcc (OpenMP, -O2, IEEE, no contraction)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", _SRC,
+               "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -60,6 +61,15 @@ def _load():
             lib.orc_topk.argtypes = [L, P, P, L, I, P]
             lib.orc_sparse_mla.argtypes = [I, P, P, L, I, I, I, D, I, P, I, P, D, P, I, P, P]
             lib.orc_num_threads.argtypes = []
+            lib.orc_encode_fp8_e4m3fn.argtypes = [D]
+            lib.orc_encode_fp8_e4m3fn.restype = ctypes.c_uint8
+            lib.orc_pow2_scale.argtypes = [D]
+            lib.orc_pow2_scale.restype = D
+            F = ctypes.c_float
+            lib.orc_rope_pair_f32.argtypes = [F, F, F, F, P, P]
+            lib.orc_rope_pair_f32.restype = None
+            lib.orc_index_quant.argtypes = [L, I, I, I, P, P, P, L, I, I, P, P, L, P, L]
+            lib.orc_index_quant.restype = I
             for f in (lib.orc_visible_counts, lib.orc_index_scores, lib.orc_topk,
                       lib.orc_sparse_mla, lib.orc_num_threads):
                 f.restype = I
@@ -191,6 +201,58 @@ def index_share(kv_indptr, q_indptr, idx_inputs: dict, layers: list, k: int, sm_
     outs = [sparse_mla(kv_indptr, q_indptr, L["q"], L["kv"], ind, sm_scale, Dc, L.get("kv_scale", 1.0))
             for L in layers]
     return ind, outs
+
+
+def encode_fp8(values) -> np.ndarray:
+    """Nearest OCP E4M3FN codes (ties to even, saturating) of float64 values, one by one."""
+    lib = _load()
+    flat = np.asarray(values, dtype=np.float64).ravel()
+    return np.array([lib.orc_encode_fp8_e4m3fn(float(v)) for v in flat],
+                    dtype=np.uint8).reshape(np.shape(values))
+
+
+def pow2_scale(amax) -> np.ndarray:
+    """ue8m0 group scale: smallest 2^e (e >= -126) with amax <= 448 * 2^e; 1 for amax == 0."""
+    lib = _load()
+    flat = np.asarray(amax, dtype=np.float64).ravel()
+    return np.array([lib.orc_pow2_scale(float(a)) for a in flat]).reshape(np.shape(amax))
+
+
+def rope_pair_f32(x0, x1, c, s):
+    """One interleaved rope pair in fp32: (x0 c - x1 s, x0 s + x1 c)."""
+    lib = _load()
+    y0, y1 = ctypes.c_float(), ctypes.c_float()
+    lib.orc_rope_pair_f32(float(x0), float(x1), float(c), float(s), ctypes.byref(y0), ctypes.byref(y1))
+    return np.float32(y0.value), np.float32(y1.value)
+
+
+def index_quant(x, positions=None, cos_sin=None, rope_off=0, dst_rows=None, out_rows=None,
+                codes=None, scales=None):
+    """Rope (optional) + fp8 per-head quantisation of x [rows, H, D].
+
+    x is float32 or uint16 (bf16 bits).  cos_sin: float32 [rope_rows, D_r]
+    (cos of the D_r/2 frequencies, then their sin), positions: int64 [rows].
+    Group (r, h) goes to row dst_rows[r] (r when None; negative = skipped) of
+    codes [out_rows, H, D] uint8 and scales [out_rows, H] float32, which start
+    as the given arrays (zeros when None).  Returns (codes, scales).
+    """
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    rows, H, D = x.shape
+    if out_rows is None:
+        out_rows = rows if codes is None else codes.shape[0]
+    codes = np.zeros((out_rows, H, D), np.uint8) if codes is None else np.array(codes, np.uint8)
+    scales = np.zeros((out_rows, H), np.float32) if scales is None else np.array(scales, np.float32)
+    dst = _c(dst_rows, np.int64)
+    if dst is not None and (dst >= out_rows).any():
+        raise ValueError("dst_rows past the output")
+    pos = _c(positions, np.int64)
+    cs = _c(cos_sin, np.float32)
+    rope_rows, D_r = (0, 0) if cs is None else cs.shape
+    rc = lib.orc_index_quant(rows, H, D, _dt_code(x), _ptr(x), _ptr(pos), _ptr(cs), rope_rows, D_r,
+                             int(rope_off), _ptr(dst), _ptr(codes), H * D, _ptr(scales), H)
+    _check(rc, "index_quant")
+    return codes, scales
 
 
 def num_threads() -> int:

@@ -374,6 +374,122 @@ int orc_sparse_mla(int B, const int64_t *kv_indptr, const int32_t *q_indptr, int
     return (bad & 2) ? ORC_BAD_INDEX : bad ? ORC_BAD_ARG : ORC_OK;
 }
 
+/* ------------------------------------------------------ index-cache writer */
+
+/*
+ * The step in front of the indexer ([anatomy], full structure diagram,
+ * Indexer box: interleaved rope, then fp8 per-1x128 quantisation with a ue8m0
+ * (power-of-two) scale, written into the 132-byte index cache; ATOM-side
+ * optimisations, fused indexer kernel: q rope + fp8 quantisation + k-cache
+ * write in one pass, for index_head_dim 128 and rope dim 64).
+ *
+ * Readings (the pages give the format, not the arithmetic):
+ *  - one quantisation group is one head's D values (the "1x128" block);
+ *  - the scale is the smallest power of two s with amax / s <= 448, where
+ *    amax is the group's largest magnitude; an all-zero group takes s = 1,
+ *    and s is never taken below 2^-126 so that it stays a normal fp32;
+ *  - each code is x / s rounded to the nearest E4M3FN value, ties to the
+ *    even code, magnitudes past 448 saturating, the sign kept (so -0 and
+ *    small negatives give 0x80);
+ *  - rope acts on the D_r values starting at rope_off, in interleaved pairs
+ *    (2i, 2i+1), i < D_r / 2, with cos and sin read from a caller-supplied
+ *    table row (cos of the D_r / 2 frequencies, then their sin).  Its result
+ *    is an fp32 value that the quantiser then rounds to 8 bits, so it is
+ *    computed in fp32 with every product and sum rounded on its own (this
+ *    file is built without contraction); quantisation itself is exact.
+ */
+
+/* Nearest E4M3FN code to v (finite), by search over the 127 non-negative
+ * finite codes in value order; on a tie the even code wins. */
+uint8_t orc_encode_fp8_e4m3fn(double v)
+{
+    double a = fabs(v);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 126; ++c) {
+        double d = fabs(orc_decode_fp8_e4m3fn((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/* Smallest power of two s = 2^e, e >= -126, with amax <= 448 * s; 1 if amax == 0. */
+double orc_pow2_scale(double amax)
+{
+    int e = -126;
+    if (amax == 0.0)
+        return 1.0;
+    while (amax > ldexp(448.0, e))
+        ++e;
+    return ldexp(1.0, e);
+}
+
+/* One interleaved rope pair: (x0, x1) -> (x0 c - x1 s, x0 s + x1 c) in fp32. */
+void orc_rope_pair_f32(float x0, float x1, float c, float s, float *y0, float *y1)
+{
+    float a = x0 * c;
+    float b = x1 * s;
+    float d = x0 * s;
+    float e = x1 * c;
+    *y0 = a - b;
+    *y1 = d + e;
+}
+
+/*
+ * Quantise rows x[r][h][0..D) (dtype dt) group by group.  When cos_sin is
+ * non-NULL, row r first takes rope at position positions[r] (table row
+ * positions[r] of rope_rows, D_r floats each).  Group (r, h) is written to
+ * codes + dst * code_stride + h * D (bytes) and scales[dst * scale_stride + h]
+ * with dst = dst_rows ? dst_rows[r] : r; a negative dst is skipped.
+ */
+int orc_index_quant(int64_t rows, int H, int D, int dt, const void *x, const int64_t *positions,
+                    const float *cos_sin, int64_t rope_rows, int D_r, int rope_off,
+                    const int64_t *dst_rows, uint8_t *codes, int64_t code_stride, float *scales,
+                    int64_t scale_stride)
+{
+    int bad = 0;
+    if (rows < 0 || H < 1 || D < 1 || !x || !codes || !scales || code_stride < (int64_t)H * D ||
+        scale_stride < H)
+        return ORC_BAD_ARG;
+    if (cos_sin && (!positions || D_r < 2 || (D_r & 1) || rope_off < 0 || rope_off + D_r > D))
+        return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t dst = dst_rows ? dst_rows[r] : r;
+        float *v = (float *)malloc(sizeof(float) * (size_t)D);
+        if (!v) {
+            bad |= 1;
+            continue;
+        }
+        if (cos_sin && (positions[r] < 0 || positions[r] >= rope_rows))
+            bad |= 2;
+        for (int h = 0; h < H && dst >= 0 && !(bad & 2); ++h) {
+            double amax = 0.0, s;
+            for (int d = 0; d < D; ++d)
+                v[d] = (float)load_elem(dt, x, (r * H + h) * (int64_t)D + d);
+            if (cos_sin) {
+                const float *cs = cos_sin + positions[r] * (int64_t)D_r;
+                for (int i = 0; i < D_r / 2; ++i) {
+                    float *p = v + rope_off + 2 * i;
+                    orc_rope_pair_f32(p[0], p[1], cs[i], cs[D_r / 2 + i], &p[0], &p[1]);
+                }
+            }
+            for (int d = 0; d < D; ++d)
+                if (fabs((double)v[d]) > amax)
+                    amax = fabs((double)v[d]);
+            s = orc_pow2_scale(amax);
+            for (int d = 0; d < D; ++d)
+                codes[dst * code_stride + (int64_t)h * D + d] = orc_encode_fp8_e4m3fn((double)v[d] / s);
+            scales[dst * scale_stride + h] = (float)s;
+        }
+        free(v);
+    }
+    return (bad & 2) ? ORC_BAD_INDEX : bad ? ORC_BAD_ARG : ORC_OK;
+}
+
 /* Threads the OpenMP runtime will use for the calls above. */
 int orc_num_threads(void)
 {
