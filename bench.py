@@ -2,6 +2,7 @@
 """Throughput of the DSA decode path (indexer -> top-2048 -> sparse MLA) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|ragged|prefill|share]
+    python bench.py --workload writer               # the index-cache writer at the prefill shape
     python bench.py --copy-calibration MIB          # a plain device copy, for counter scaling
     python bench.py --rocprof-summary CSV [CSV ..]  # per-kernel table of rocprofv3 output
     python bench.py --traffic-from FETCH WRITE COPY_FETCH COPY_WRITE [--workload W] [--copy-mib M]
@@ -34,7 +35,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 
-WORKLOADS = {"decode": 2, "ragged": 3, "prefill": 4, "share": 5}
+WORKLOADS = {"decode": 2, "ragged": 3, "prefill": 4, "share": 5, "writer": 4}
 
 
 def parse():
@@ -179,8 +180,9 @@ def cpu_baseline(case, target_s):
 
 # ------------------------------------------------------------------------------- counters
 
-STAGE_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip"}
-STAGE_KERNELS = {"indexer": ("idx_",), "topk": ("topk_",), "mla": ("mla_",)}
+STAGE_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip",
+                 "writer": "index_quant.hip"}
+STAGE_KERNELS = {"indexer": ("idx_",), "topk": ("topk_",), "mla": ("mla_",), "writer": ("index_quant",)}
 
 
 def _short(name):
@@ -203,11 +205,13 @@ def source_digest(stage):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_means(path):
-    """{(kernel, counter): (mean value per dispatch, dispatches)} of a counter_collection CSV."""
+def counter_means(path, by_grid=False):
+    """{(kernel, counter): (mean value per dispatch, dispatches)} of a counter_collection CSV
+    (kernel names carry "@<grid size>" with by_grid, to tell launches of one kernel apart)."""
     acc = {}
     for r in _read_csv(path):
-        key = (_short(r["Kernel_Name"]), r["Counter_Name"])
+        name = _short(r["Kernel_Name"]) + ("@" + r["Grid_Size"] if by_grid else "")
+        key = (name, r["Counter_Name"])
         tot, n = acc.get(key, (0.0, 0))
         acc[key] = (tot + float(r["Counter_Value"]), n + 1)
     return {k: (v[0] / v[1], v[1]) for k, v in acc.items()}
@@ -240,11 +244,16 @@ def traffic_from(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_byte
         return m * 1024.0 / copy_bytes
     ff = copy_factor(copy_fetch_csv, "FETCH_SIZE")
     wf = copy_factor(copy_write_csv, "WRITE_SIZE")
-    fm, wm = counter_means(fetch_csv), counter_means(write_csv)
+    # The writer workload launches one kernel twice per step (queries, then keys); its
+    # roofline is the query launch, the larger grid.
+    writer = workload == "writer"
+    fm, wm = counter_means(fetch_csv, writer), counter_means(write_csv, writer)
     out = {"workload": workload, "copy_bytes": copy_bytes, "fetch_factor": round(ff, 4),
            "write_factor": round(wf, 4), "stages": {}}
     for st, prefixes in STAGE_KERNELS.items():
         kern = sorted({k for (k, c) in fm if c == "FETCH_SIZE" and k.startswith(prefixes)})
+        if writer and kern:
+            kern = [max(kern, key=lambda k: int(k.split("@")[1]))]
         if not kern:
             continue
         # calls of the stage = dispatches of its most frequent kernel
@@ -285,6 +294,117 @@ def copy_calibration(mib, copies):
     print(json.dumps({"copy_bytes": n, "copies": copies}))
 
 
+# ------------------------------------------------------------------------------- writer bench
+
+def writer_bytes(T, H_I):
+    """Algorithmic bytes of the writer per prefill chunk: per query head 256 B read (bf16) and
+    128 B codes + 4 B scale written; per row an 8-byte position and the 256-byte rope-table row
+    read once; per key 256 B read, 8 B position, 8 B slot, 256 B table row, 132 B written."""
+    q = T * (H_I * (256 + 128 + 4) + 8 + 256)
+    k = T * (256 + 8 + 8 + 256 + 132)
+    return q, k
+
+
+def writer_cpu_baseline(wc, tab, target_s):
+    """The oracle's writer on the host for whole rows (32 query heads + one key each)."""
+    import oracle
+    from deepseek_sparse_mla_amd import synth
+    oracle.build()
+    q, k = synth.host(wc.q), synth.host(wc.k)
+    pos, tabh = synth.host(wc.positions), synth.host(tab)
+    rows, t0, el = 0, time.perf_counter(), 0.0
+    chunk = 64
+    while el < target_s and rows < wc.q.shape[0]:
+        r = slice(rows, rows + chunk)
+        oracle.index_quant(q[r], positions=pos[r], cos_sin=tabh)
+        oracle.index_quant(k[r].reshape(-1, 1, 128), positions=pos[r], cos_sin=tabh)
+        rows += chunk
+        el = time.perf_counter() - t0
+    threads = oracle.num_threads()
+    return {"value": rows / el, "unit": "query-rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": "the first %d rows of the chunk (32 query heads + one key each, rope + fp8 "
+                      "quantisation) in %.1f s on %d host threads" % (rows, el, threads)}
+
+
+def writer_main(args):
+    import torch
+    import deepseek_sparse_mla_amd as dsa
+    from deepseek_sparse_mla_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    probe = synth.writer_case(0, dev)
+    T, H_I = probe.q.shape[:2]
+    tab = dsa.rope_cos_sin_cache(probe.cache_rows, device=dev)
+    per_set = T * H_I * (256 + 132) + T * (256 + 132)
+    nsets = args.sets or max(1, min(32, math.ceil(1.2e9 / per_set)))
+    sets = []
+    for sd in range(nsets):
+        wc = probe if sd == 0 else synth.writer_case(sd, dev)
+        sets.append(dict(wc=wc, cache=torch.zeros((wc.cache_rows, 128), dtype=torch.uint8, device=dev),
+                         scale=torch.zeros(wc.cache_rows, dtype=torch.float32, device=dev),
+                         q8=torch.empty((T, H_I, 128), dtype=torch.uint8, device=dev),
+                         qs=torch.empty((T, H_I), dtype=torch.float32, device=dev)))
+
+    def q_part(st):
+        dsa.dsa_index_q_quant(st["wc"].q, positions=st["wc"].positions, cos_sin=tab, q_fp8=st["q8"],
+                              q_scale=st["qs"])
+
+    def k_part(st):
+        dsa.dsa_index_k_cache_write(st["wc"].k, st["wc"].slots, st["cache"], st["scale"],
+                                    positions=st["wc"].positions, cos_sin=tab)
+
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        q_part(sets[s % nsets])
+        k_part(sets[s % nsets])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        q_part(sets[s % nsets])
+        k_part(sets[s % nsets])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # Per-kernel durations: HIP events around K back-to-back launches of one kind on the
+    # launch stream, so the GPU is not left waiting for the host between two events.
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for s in range(args.steps):
+        q_part(sets[s % nsets])
+    ev[1].record(stream)
+    for s in range(args.steps):
+        k_part(sets[s % nsets])
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    k_ms = ev[1].elapsed_time(ev[2]) / args.steps
+    qb, kb = writer_bytes(T, H_I)
+    achieved = qb / (q_ms * 1e-3) / 1e9
+    line = {
+        "metric": "prefill index-writer query-rows/s (rope + fp8 ue8m0 quantisation of 32 index-query "
+                  "heads and one index key per row) and % of peak HBM GB/s",
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "query-rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": probe.name, "query_rows": T, "index_heads": H_I, "index_dim": 128,
+                   "rope_dims": 64, "rope": "interleaved", "cache": "split planes",
+                   "input_sets_rotated": nsets},
+        "kernels_ms": {"dsa_index_q_quant: index_quant_kernel": round(q_ms, 5),
+                       "dsa_index_k_cache_write: index_quant_kernel": round(k_ms, 5)},
+        "roofline": {"kernel": "dsa_index_q_quant: index_quant_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic": qb,
+                     "traffic": measured_traffic("writer", "writer")},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = writer_cpu_baseline(probe, tab, min(args.cpu_seconds, 12.0))
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.rocprof_summary:
@@ -297,6 +417,8 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, args.steps)
+    if args.workload == "writer":
+        return writer_main(args)
     import torch
     from deepseek_sparse_mla_amd import synth  # noqa: F401
 

@@ -23,7 +23,7 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
 DSA_TOPK_MAX = 2048
 DSA_MAX_SHARED_LAYERS = 8
 
-EXPORTS = ("dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "sparse_mla_workspace_size",
+EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "sparse_mla_workspace_size",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "dsa_last_error",
            "dsa_abi_version")
 
@@ -61,6 +61,8 @@ def load_library(path: str = LIB_PATH):
         P, I, L, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         LP = ctypes.POINTER(dsa_layout)
         lib.dsa_index_scores.argtypes = [LP, I, I, I, P, P, P, I, P, L, P, L, P, L, P]
+        lib.dsa_index_k_cache_write.argtypes = [L, I, P, L, P, P, L, I, P, P, L, P, L, L, P]
+        lib.dsa_index_q_quant.argtypes = [L, I, I, P, L, P, P, L, I, P, P, P]
         lib.dsa_topk_workspace_size.argtypes = [LP, L, I]
         lib.dsa_topk_workspace_size.restype = S
         lib.dsa_topk.argtypes = [LP, P, L, I, P, P, S, P]
@@ -71,7 +73,7 @@ def load_library(path: str = LIB_PATH):
         lib.sparse_mla_prefill.argtypes = mla
         lib.sparse_mla_decode_shared.argtypes = [LP, I, I, I, F, I, I, I, I,
                                                  ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
-        for f in (lib.dsa_index_scores, lib.dsa_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
+        for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_scores, lib.dsa_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
                   lib.sparse_mla_decode_shared, lib.dsa_abi_version):
             f.restype = I
         lib.dsa_last_error.restype = ctypes.c_char_p
@@ -132,6 +134,95 @@ class Layout:
     @staticmethod
     def of_case(case) -> "Layout":
         return Layout(case.kv_indptr, case.q_indptr, case.T, case.max_ctx)
+
+
+def rope_cos_sin_cache(max_pos: int, rope_dim: int = 64, theta: float = 8e6,
+                       device="cuda") -> torch.Tensor:
+    """Rope table fp32 [max_pos, rope_dim]: cos of the rope_dim/2 frequencies theta^(-2i/rope_dim)
+    at each position, then their sin.  Angles and their cos/sin are taken in fp64 on the host and
+    rounded once to fp32.  theta 8e6 is GLM-5.2's rope base (anatomy page, configuration table
+    and structure diagram), which the pages give without YaRN scaling."""
+    import numpy as np
+    inv = theta ** (-np.arange(0, rope_dim, 2, dtype=np.float64) / rope_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    tab = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    return torch.from_numpy(tab).to(device)
+
+
+def _rope_args(positions, cos_sin, n):
+    if cos_sin is None:
+        return None, None, 0
+    if positions is None or positions.numel() != n:
+        raise ValueError("rope needs one int64 position per row")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 64:
+        raise ValueError("cos_sin must be [rows, 64] (32 cos then 32 sin)")
+    return (_dev(positions, "positions", torch.int64), _dev(cos_sin, "cos_sin", torch.float32),
+            cos_sin.shape[0])
+
+
+def _row_stride_bytes(x: torch.Tensor, name: str) -> int:
+    if x.stride(-1) != 1 or (x.dim() == 3 and x.shape[1] > 1 and x.stride(1) != x.shape[2]):
+        raise ValueError("%s must have unit stride inside a row" % name)
+    return x.stride(0) * x.element_size()
+
+
+def dsa_index_k_cache_write(k: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor,
+                            cache_scale: torch.Tensor, positions: Optional[torch.Tensor] = None,
+                            cos_sin: Optional[torch.Tensor] = None, rope_off: int = 0,
+                            cache_row_stride: Optional[int] = None, cache_scale_stride: int = 1,
+                            cache_rows: Optional[int] = None, stream=None) -> None:
+    """Rope (optional) + fp8 quantise k [n, 128] (bf16 / fp32, rows may be strided) into cache
+    rows slots[r] (negative = skip).  cache: uint8 [rows, 128] codes plane (or a raw byte buffer
+    with cache_row_stride and cache_rows given); cache_scale: fp32 with cache_scale_stride."""
+    lib = load_library()
+    n = k.shape[0]
+    if k.shape[-1] != 128:
+        raise ValueError("index keys are 128 wide")
+    if cache_row_stride is None:
+        cache_row_stride = cache.stride(0) * cache.element_size()
+    if cache_rows is None:
+        cache_rows = cache.shape[0]
+    if slots.numel() != n:
+        raise ValueError("slots must hold one cache row per key")
+    if cache_rows > 0:
+        need_c = (cache_rows - 1) * int(cache_row_stride) + 128
+        need_s = ((cache_rows - 1) * int(cache_scale_stride) + 1) * 4
+        if cache.numel() * cache.element_size() < need_c or \
+                cache_scale.numel() * cache_scale.element_size() < need_s:
+            raise ValueError("cache or cache_scale smaller than cache_rows entries")
+    pos, cs, rope_rows = _rope_args(positions, cos_sin, n)
+    st = lib.dsa_index_k_cache_write(n, _dt(k), _dev(k, "k", contiguous=False), _row_stride_bytes(k, "k"),
+                                     pos, cs, rope_rows, int(rope_off), _dev(slots, "slots", torch.int64),
+                                     _dev(cache, "cache", (torch.uint8, torch.float8_e4m3fn), contiguous=False),
+                                     int(cache_row_stride),
+                                     _dev(cache_scale, "cache_scale", (torch.float32, torch.uint8), contiguous=False),
+                                     int(cache_scale_stride), int(cache_rows), _stream(stream))
+    _check(lib, st)
+
+
+def dsa_index_q_quant(q: torch.Tensor, positions: Optional[torch.Tensor] = None,
+                      cos_sin: Optional[torch.Tensor] = None, rope_off: int = 0,
+                      q_fp8: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Rope (optional) + fp8 quantise index queries q [T, H_I, 128] per (row, head).
+    Returns (codes uint8 [T, H_I, 128], scales fp32 [T, H_I])."""
+    lib = load_library()
+    T, H_I, D = q.shape
+    if D != 128:
+        raise ValueError("index heads are 128 wide")
+    if q_fp8 is None:
+        q_fp8 = torch.empty((T, H_I, D), dtype=torch.uint8, device=q.device)
+    if q_scale is None:
+        q_scale = torch.empty((T, H_I), dtype=torch.float32, device=q.device)
+    if tuple(q_fp8.shape) != (T, H_I, D) or tuple(q_scale.shape) != (T, H_I):
+        raise ValueError("q_fp8 must be [T, H_I, 128] and q_scale [T, H_I]")
+    pos, cs, rope_rows = _rope_args(positions, cos_sin, T)
+    st = lib.dsa_index_q_quant(T, H_I, _dt(q), _dev(q, "q", contiguous=False), _row_stride_bytes(q, "q"),
+                               pos, cs, rope_rows, int(rope_off),
+                               _dev(q_fp8, "q_fp8", (torch.uint8, torch.float8_e4m3fn)),
+                               _dev(q_scale, "q_scale", torch.float32), _stream(stream))
+    _check(lib, st)
+    return q_fp8, q_scale
 
 
 def dsa_index_scores(layout: Layout, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor,

@@ -195,6 +195,45 @@ dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_
     return hip_status(e, "sparse MLA launch");
 }
 
+// Shared checks of the two index-cache writer entry points (rows of H groups of 128 values).
+dsa_status check_index_quant(int64_t rows, int H, dsa_dtype x_dt, const void *x, int64_t x_row_bytes,
+                             const int64_t *positions, const float *cos_sin, int64_t rope_rows,
+                             int rope_off, const void *codes, int64_t code_row_bytes,
+                             const float *scales, int64_t scale_row_stride)
+{
+    if (rows < 0 || H < 1)
+        return fail(DSA_ERR_INVALID_ARG, "bad writer shape rows=%lld H=%d", (long long)rows, H);
+    if (x_dt != DSA_F32 && x_dt != DSA_BF16)
+        return fail(DSA_ERR_UNSUPPORTED, "writer input dtype %d not supported (F32 or BF16)", x_dt);
+    if (rows == 0)
+        return DSA_OK;  // nothing to read or write: empty tensors may carry NULL pointers
+    if (!x || !codes || !scales)
+        return fail(DSA_ERR_INVALID_ARG, "input, codes and scales must be non-NULL");
+    if (x_row_bytes < (int64_t)H * 128 * elem_size(x_dt) || x_row_bytes % 16 != 0 || !aligned(x, 16))
+        return fail(DSA_ERR_INVALID_ARG,
+                    "input rows must hold H * 128 values, start 16-byte aligned and have a "
+                    "16-byte multiple stride (stride %lld)", (long long)x_row_bytes);
+    if (code_row_bytes < (int64_t)H * 128 || code_row_bytes % 4 != 0 || !aligned(codes, 4))
+        return fail(DSA_ERR_INVALID_ARG,
+                    "code rows must hold H * 128 bytes, start 4-byte aligned and have a 4-byte "
+                    "multiple stride (stride %lld)", (long long)code_row_bytes);
+    if (scale_row_stride < H || !aligned(scales, 4))
+        return fail(DSA_ERR_INVALID_ARG, "scale stride %lld < H or scales not 4-byte aligned",
+                    (long long)scale_row_stride);
+    if (cos_sin) {
+        if (!positions)
+            return fail(DSA_ERR_INVALID_ARG, "rope needs positions");
+        if (rope_rows < 1 || !aligned(cos_sin, 16))
+            return fail(DSA_ERR_INVALID_ARG, "rope table needs >= 1 row and 16-byte alignment");
+        if (rope_off != 0 && rope_off != 64)
+            return fail(DSA_ERR_INVALID_ARG, "rope_off must be 0 or 64 (got %d)", rope_off);
+    }
+    if (rows > ((int64_t)1 << 40) || rows * H > 16 * (int64_t)INT32_MAX)
+        return fail(DSA_ERR_UNSUPPORTED, "too many groups for one launch (rows %lld x H %d)",
+                    (long long)rows, H);
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,6 +307,46 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
         e = dsa::launch_index_generic(dl, T, layout->max_ctx, H_I, D_I, q_dt, q, q_scale, w, k_dt, k,
                                       k_row_stride, k_scale, k_scale_stride, scores, ld, s);
     return hip_status(e, "indexer launch");
+}
+
+dsa_status dsa_index_k_cache_write(int64_t n, dsa_dtype k_dt, const void *k, int64_t k_row_stride,
+                                   const int64_t *positions, const float *cos_sin,
+                                   int64_t rope_rows, int rope_off, const int64_t *slots,
+                                   uint8_t *cache, int64_t cache_row_stride, float *cache_scale,
+                                   int64_t cache_scale_stride, int64_t cache_rows, void *stream)
+{
+    dsa_status st = check_index_quant(n, 1, k_dt, k, k_row_stride, positions, cos_sin, rope_rows,
+                                      rope_off, cache, cache_row_stride, cache_scale,
+                                      cache_scale_stride);
+    if (st != DSA_OK)
+        return st;
+    if (n == 0)
+        return ok();
+    if (!slots)
+        return fail(DSA_ERR_INVALID_ARG, "slots must be non-NULL");
+    if (cache_rows < 0)
+        return fail(DSA_ERR_INVALID_ARG, "cache_rows must be >= 0");
+    hipError_t e = dsa::launch_index_quant(n, 1, k_dt == DSA_F32, k, k_row_stride, positions,
+                                           cos_sin, rope_rows, rope_off, slots, cache_rows, cache,
+                                           cache_row_stride, cache_scale, cache_scale_stride,
+                                           (hipStream_t)stream);
+    return hip_status(e, "index-cache writer launch");
+}
+
+dsa_status dsa_index_q_quant(int64_t T, int H_I, dsa_dtype q_dt, const void *q, int64_t q_row_stride,
+                             const int64_t *positions, const float *cos_sin, int64_t rope_rows,
+                             int rope_off, uint8_t *q_fp8, float *q_scale, void *stream)
+{
+    dsa_status st = check_index_quant(T, H_I, q_dt, q, q_row_stride, positions, cos_sin, rope_rows,
+                                      rope_off, q_fp8, (int64_t)H_I * 128, q_scale, H_I);
+    if (st != DSA_OK)
+        return st;
+    if (T == 0)
+        return ok();
+    hipError_t e = dsa::launch_index_quant(T, H_I, q_dt == DSA_F32, q, q_row_stride, positions,
+                                           cos_sin, rope_rows, rope_off, nullptr, T, q_fp8,
+                                           (int64_t)H_I * 128, q_scale, H_I, (hipStream_t)stream);
+    return hip_status(e, "index-query quantiser launch");
 }
 
 size_t dsa_topk_workspace_size(const dsa_layout *layout, int64_t ld, int k)

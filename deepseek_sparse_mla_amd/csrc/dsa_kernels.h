@@ -40,6 +40,12 @@ size_t topk_workspace_bytes(int64_t T, int64_t max_ctx);
 hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const float *scores, int64_t ld,
                        int k, int32_t *indices, void *workspace, hipStream_t stream);
 
+hipError_t launch_index_quant(int64_t rows, int H, bool in_f32, const void *x, int64_t x_row_bytes,
+                              const int64_t *positions, const float *cos_sin, int64_t rope_rows,
+                              int rope_off, const int64_t *dst_rows, int64_t out_rows,
+                              uint8_t *codes, int64_t code_row_bytes, float *scales,
+                              int64_t scale_row_stride, hipStream_t stream);
+
 int mla_num_splits(int64_t T, int k);
 size_t mla_workspace_bytes(int64_t T, int n_layers, int k);
 hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &layers, int n_layers,

@@ -235,6 +235,30 @@ def config(cfg: int, device="cpu", seed=0) -> Case:
     raise ValueError("unknown workload %r" % cfg)
 
 
+@dataclass
+class WriterCase:
+    """Inputs of the index-cache writer for one prefill chunk: the chunk's index queries
+    [T, H_I, 128] and new index keys [T, 128] (bf16, N(0, 1)), their positions (prefix ..
+    prefix + T - 1) and the cache rows the keys go to (the same positions: one sequence)."""
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    positions: torch.Tensor
+    slots: torch.Tensor
+    cache_rows: int
+
+
+_T_WQ, _T_WK = 20, 21
+
+
+def writer_case(seed=0, device="cpu", T=4096, H_I=32, prefix=28672) -> WriterCase:
+    """The prefill chunk's writer inputs: 4096 new rows after a 28672-token prefix."""
+    q = _randn((T, H_I, 128), seed, 4, _T_WQ, device).to(torch.bfloat16)
+    k = _randn((T, 128), seed, 4, _T_WK, device).to(torch.bfloat16)
+    pos = torch.arange(prefix, prefix + T, dtype=torch.int64, device=device)
+    return WriterCase("prefill_writer_%d_on_%d" % (T, prefix), q, k, pos, pos.clone(), prefix + T)
+
+
 # ----------------------------------------------------------------------------------------------
 # host views for the oracle (raw storage as numpy: float32, uint16 bf16 bits, uint8 fp8 codes)
 

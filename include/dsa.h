@@ -4,6 +4,9 @@
  *
  * The path has three stages plus reuse of one index set across layers:
  *
+ *   dsa_index_k_cache_write  index-cache writer: rope + fp8 keys with a
+ *   dsa_index_q_quant        power-of-two scale (and the same for prefill
+ *                            index queries), the step in front of the indexer
  *   dsa_index_scores         lightning indexer: one fp32 score per visible
  *                            cached token for every query row
  *   dsa_topk                 per-row top-k (k <= DSA_TOPK_MAX) positions
@@ -86,6 +89,64 @@ typedef struct {
     const int64_t *kv_indptr;  /* device [B+1]                                */
     const int32_t *q_indptr;   /* device [B+1], or NULL for decode            */
 } dsa_layout;
+
+/*
+ * dsa_index_k_cache_write / dsa_index_q_quant -- index-cache writer ([anatomy],
+ * full structure diagram, Indexer box: the index key takes interleaved rope,
+ * then fp8 per-1x128 quantisation with a ue8m0 scale, and is written into the
+ * 132-byte index cache; ATOM-side optimisations, fused indexer kernel: query
+ * rope, fp8 quantisation and key-cache write in one pass, for 128-wide index
+ * heads with 64 rope dims; section on the rope switches: GLM's indexer rope is
+ * the interleaved style).  Each group of 128 values (one key, or one head of
+ * an index query) is turned into
+ *
+ *   y     the group; if cos_sin is non-NULL, dims [rope_off, rope_off + 64)
+ *         are rotated in interleaved pairs (2i, 2i+1), i < 32, with the table
+ *         row c = cos_sin[pos * 64 + i], s = cos_sin[pos * 64 + 32 + i]:
+ *         (y0, y1) = (x0*c - x1*s, x0*s + x1*c), each product and sum an fp32
+ *         rounding of its own
+ *   scale the smallest power of two 2^e with max|y| <= 448 * 2^e and
+ *         e >= -126 (a normal fp32); 1 for an all-zero group
+ *   codes y / scale rounded to the nearest OCP E4M3FN value, ties to the even
+ *         code, with the sign kept (so -0 gives 0x80)
+ *
+ * Inputs are F32 or BF16 values, finite.  The codes are what dsa_index_scores
+ * reads as FP8_E4M3FN keys with k_scale (and prefill queries with q_scale).
+ *
+ * dsa_index_k_cache_write writes n new keys:
+ *   k, k_dt       key r (128 values) starts at byte r * k_row_stride of k; k
+ *                 16-byte aligned, k_row_stride a multiple of 16 (a column
+ *                 slice of a wider projection output works).
+ *   positions     int64 [n] rope positions; required iff cos_sin is non-NULL.
+ *   cos_sin       fp32 [rope_rows][64] (cos of the 32 frequencies, then their
+ *                 sin), 16-byte aligned, or NULL for no rope.  rope_off is 0
+ *                 or 64.  Positions outside [0, rope_rows) break the contract;
+ *                 the kernel clamps them into the table and never reads past it.
+ *   slots         int64 [n]: key r goes to cache row slots[r]; a negative slot
+ *                 is skipped (padding).  Slots >= cache_rows break the contract
+ *                 and are skipped too, so no write leaves the cache.
+ *   cache         codes of row j at cache + j * cache_row_stride (bytes; a
+ *                 multiple of 4, base 4-byte aligned).
+ *   cache_scale   fp32 scale of row j at cache_scale[j * cache_scale_stride].
+ *                 The interleaved 132-byte entries are cache_row_stride = 132,
+ *                 cache_scale = (float *)(cache + 128), cache_scale_stride = 33.
+ * Rows that no slot names keep their bytes.  Two keys with the same slot race.
+ * n = 0 (or T = 0 below) is a no-op whose pointers may be NULL.
+ *
+ * dsa_index_q_quant quantises T index-query rows of H_I heads:
+ *   q, q_dt       row t (H_I * 128 values, head-major) at byte t * q_row_stride
+ *                 of q; 16-byte alignment as for k.
+ *   positions, cos_sin, rope_rows, rope_off   as above, per row.
+ *   q_fp8         uint8 [T][H_I][128] codes; q_scale fp32 [T][H_I] scales.
+ */
+dsa_status dsa_index_k_cache_write(int64_t n, dsa_dtype k_dt, const void *k, int64_t k_row_stride,
+                                   const int64_t *positions, const float *cos_sin,
+                                   int64_t rope_rows, int rope_off, const int64_t *slots,
+                                   uint8_t *cache, int64_t cache_row_stride, float *cache_scale,
+                                   int64_t cache_scale_stride, int64_t cache_rows, void *stream);
+dsa_status dsa_index_q_quant(int64_t T, int H_I, dsa_dtype q_dt, const void *q, int64_t q_row_stride,
+                             const int64_t *positions, const float *cos_sin, int64_t rope_rows,
+                             int rope_off, uint8_t *q_fp8, float *q_scale, void *stream);
 
 /*
  * dsa_index_scores -- lightning-indexer scores ([anatomy], full structure

@@ -153,3 +153,67 @@ def test_binding_needs_device_tensors():
     with pytest.raises(ValueError):
         B._dev(torch.zeros(4), "x")
     del L
+
+
+def _kw(lib, **kw):
+    a = dict(n=4, k_dt=B.DSA_BF16, k=FAKE, kstride=256, pos=None, cs=None, rope_rows=0, rope_off=0,
+             slots=FAKE, cache=FAKE, cstride=132, cscale=FAKE + 128, csstride=33, crows=100)
+    a.update(kw)
+    return lib.dsa_index_k_cache_write(a["n"], a["k_dt"], a["k"], a["kstride"], a["pos"], a["cs"],
+                                       a["rope_rows"], a["rope_off"], a["slots"], a["cache"],
+                                       a["cstride"], a["cscale"], a["csstride"], a["crows"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), B.DSA_ERR_INVALID_ARG),
+    (dict(k_dt=B.DSA_FP8_E4M3FN), B.DSA_ERR_UNSUPPORTED),      # input is already fp8
+    (dict(k=None), B.DSA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 8), B.DSA_ERR_INVALID_ARG),                 # 16-byte alignment
+    (dict(kstride=200), B.DSA_ERR_INVALID_ARG),                # shorter than a row
+    (dict(kstride=264), B.DSA_ERR_INVALID_ARG),                # not a multiple of 16
+    (dict(slots=None), B.DSA_ERR_INVALID_ARG),
+    (dict(cstride=130), B.DSA_ERR_INVALID_ARG),                # not a multiple of 4
+    (dict(cache=FAKE + 2), B.DSA_ERR_INVALID_ARG),
+    (dict(csstride=0), B.DSA_ERR_INVALID_ARG),
+    (dict(cs=FAKE, rope_rows=10), B.DSA_ERR_INVALID_ARG),      # rope without positions
+    (dict(cs=FAKE, pos=FAKE, rope_rows=0), B.DSA_ERR_INVALID_ARG),
+    (dict(cs=FAKE, pos=FAKE, rope_rows=10, rope_off=32), B.DSA_ERR_INVALID_ARG),
+    (dict(crows=-1), B.DSA_ERR_INVALID_ARG),
+])
+def test_index_k_cache_write_rejects(lib, kw, status):
+    assert _kw(lib, **kw) == status
+    assert lib.dsa_last_error()
+
+
+def test_index_k_cache_write_accepts_empty_batch(lib):
+    """n = 0 passes every check and launches nothing (no device needed)."""
+    assert _kw(lib, n=0) == B.DSA_OK
+
+
+def test_index_q_quant_rejects(lib):
+    q = lambda **kw: lib.dsa_index_q_quant(kw.get("T", 8), kw.get("H", 32), kw.get("dt", B.DSA_BF16),
+                                           kw.get("q", FAKE), kw.get("stride", 8192), None, None, 0, 0,
+                                           kw.get("out", FAKE), kw.get("scale", FAKE), None)
+    assert q(H=0) == B.DSA_ERR_INVALID_ARG
+    assert q(stride=4096) == B.DSA_ERR_INVALID_ARG             # shorter than 32 heads of bf16
+    assert q(dt=B.DSA_FP8_E4M3FN) == B.DSA_ERR_UNSUPPORTED
+    assert q(scale=FAKE + 1) == B.DSA_ERR_INVALID_ARG
+    assert q(T=0) == B.DSA_OK
+
+
+def test_rope_table_follows_its_definition():
+    """Row p holds cos(p * theta^(-2i/64)) then sin of the same angles; row 0 is (1, 0)."""
+    import numpy as np
+    tab = dsa.rope_cos_sin_cache(300, device="cpu").numpy()
+    assert tab.shape == (300, 64) and tab.dtype == np.float32
+    assert np.all(tab[0, :32] == 1) and np.all(tab[0, 32:] == 0)
+    p, i = 257, 5
+    ang = p * 8e6 ** (-2 * i / 64)
+    assert tab[p, i] == np.float32(np.cos(ang)) and tab[p, 32 + i] == np.float32(np.sin(ang))
+    assert np.allclose(tab[:, :32] ** 2 + tab[:, 32:] ** 2, 1, atol=1e-6)
+
+
+def test_writer_empty_calls_accept_null_pointers(lib):
+    """An empty batch is a no-op; empty device tensors carry NULL data pointers."""
+    assert _kw(lib, n=0, k=None, slots=None, cache=None, cscale=None) == B.DSA_OK
+    assert lib.dsa_index_q_quant(0, 32, B.DSA_BF16, None, 8192, None, None, 0, 0, None, None, None) == B.DSA_OK

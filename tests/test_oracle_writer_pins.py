@@ -90,7 +90,7 @@ def test_scale_closed_forms(amax, scale):
 
 
 def test_scale_is_the_smallest_power_of_two():
-    """Property over 40 binades: s = 2^e, amax / s <= 448 < amax / (s / 2), or e = -126."""
+    """Property over 250 binades: s = 2^e, amax / s <= 448 < amax / (s / 2), or e = -126."""
     rng = np.random.default_rng(5)
     amax = 2.0 ** rng.uniform(-130, 120, 4000)
     s = oracle.pow2_scale(amax)
