@@ -381,6 +381,43 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
 // ------------------------------------------------------------------------------------------
 constexpr uint32_t TD_COUNT = 256;  // members ranked by counting up to this many
 
+// Maximum / minimum over the 64 lanes of a wave, returned as a wave-uniform value: the DPP
+// pattern of wave_incl_scan with max / min (lanes without a source read the identity), and
+// lane 63 holds the result.
+__device__ __forceinline__ float wave_max_f32(float x)
+{
+    constexpr int ID = (int)0xff800000u;  // -inf
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x111, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x112, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x114, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x118, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x142, 0xa, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x143, 0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+__device__ __forceinline__ float wave_min_f32(float x)
+{
+    constexpr int ID = (int)0x7f800000u;  // +inf
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x111, 0xf, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x112, 0xf, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x114, 0xf, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x118, 0xf, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x142, 0xa, 0xf, false)));
+    x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(ID, __float_as_int(x), 0x143, 0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// A block-uniform value made visibly uniform to the compiler (so branches on it are scalar).
+__device__ __forceinline__ uint32_t uni(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+__device__ __forceinline__ float uni(float x)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 template <int PER, bool LDSROW>
 __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, const float *__restrict__ scores,
                                                                  int64_t ld, int k, int32_t *__restrict__ out)
@@ -390,9 +427,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     constexpr int GROUP = 4 * TK_THREADS;            // positions per group (4096)
     constexpr int NB = NQ * TK_WAVES;                // (group, wave) totals
     constexpr int CAP = LDSROW ? 2048 : TK_CAP;      // members held in LDS
+    static_assert(PER <= 32, "per-thread masks are 32 bits");
     __shared__ __attribute__((aligned(16))) float srow[LDSROW ? TK_THREADS * PER : 4];
     __shared__ uint64_t cand[CAP];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS + 4];  // + a bin for positions past n
     __shared__ float red[2][TK_WAVES];
     __shared__ uint32_t base[NB];
     __shared__ uint32_t sh[4];
@@ -402,7 +440,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t i = blockIdx.x;
     const RowInfo r = row_info(L, i);
-    const int n32 = (int)min(r.n > 0 ? r.n : (int64_t)0, (int64_t)TK_THREADS * PER);  // host: n <= 1024 PER
+    const int n32 = (int)uni((uint32_t)min(r.n > 0 ? r.n : (int64_t)0, (int64_t)TK_THREADS * PER));  // host: n <= 1024 PER
     int32_t *orow = out + i * k;
     const uint32_t kk = (uint32_t)min(k, n32);
     if (kk == 0) {
@@ -412,17 +450,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     }
     const float *row = scores + i * ld;
     auto pos = [&](int q, int e) -> int { return GROUP * q + 4 * tid + e; };
+    // bit 4q + e: position pos(q, e) is inside the row
+    uint32_t valid = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            valid |= (pos(q, e) < n32 ? 1u : 0u) << (4 * q + e);
 
-    // ---- 0. the row: groups wholly inside it as one 16-byte load (16-byte aligned rows),
-    // others as four dword loads through a buffer resource over the n scores (zeros past
-    // the end, no branch per element)
+    // ---- 0. the row.  In registers: four dword loads per group through a buffer resource
+    // over the n scores (zeros past the end), all issued before any is used.  In LDS:
+    // wave-wide 1 KB DMA loads (16-byte aligned rows), else the same dword loads.
     const __amdgpu_buffer_rsrc_t rrow =
         __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, n32 * 4, 0x00020000);
     const bool al16 = ((uintptr_t)row & 15) == 0;
     auto load_group = [&](int q) -> f32x4 {
         const int p = pos(q, 0);
-        if (al16 && p + 3 < n32)
-            return *(const f32x4 *)(row + p);
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -438,16 +481,16 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     float mx = -INFINITY, mn = INFINITY;
     auto range_of = [&](const f32x4 &v, int q) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (pos(q, e) < n32) {
-                mx = fmaxf(mx, v[e]);
-                mn = fminf(mn, v[e]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = (valid >> (4 * q + e)) & 1u;
+            mx = fmaxf(mx, ok ? v[e] : -INFINITY);
+            mn = fminf(mn, ok ? v[e] : INFINITY);
+        }
     };
     if (LDSROW) {
         if (al16) {
-            // the whole row in flight at once: wave-wide 1 KB DMA loads straight into LDS (group
-            // q of wave w lands at srow[4096 q + 256 w ..]); positions past n are never used
+            // the whole row in flight at once: group q of wave w lands at srow[4096 q + 256 w ..];
+            // positions past n are never used
             const i32x4 desc = buffer_desc(row, (int64_t)n32 * 4);
             const uint32_t lds_row = lds_addr_of(&srow[0]);
             const int w = __builtin_amdgcn_readfirstlane(wave);
@@ -476,11 +519,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     }
 
     // ---- 1. range of the row, histogram of the value bins
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        mn = fminf(mn, __shfl_xor(mn, o, 64));
-    }
+    mx = wave_max_f32(mx);
+    mn = wave_min_f32(mn);
     if (lane == 0) {
         red[0][wave] = mx;
         red[1][wave] = mn;
@@ -497,6 +537,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         mx = fmaxf(mx, red[0][w2]);
         mn = fminf(mn, red[1][w2]);
     }
+    mx = uni(mx);
+    mn = uni(mn);
     const float range = mx - mn;
     float scale = 0.f;
     bool lin = range > 0.f && range < INFINITY;
@@ -504,34 +546,62 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         scale = (float)TK_BINS / range;
         lin = scale < INFINITY;
     }
-    auto bin_of = [&](float v) -> uint32_t {
-        return lin ? min((uint32_t)((v - mn) * scale), (uint32_t)(TK_BINS - 1)) : score_key(v) >> 21;
+    lin = uni(lin ? 1u : 0u) != 0u;
+    scale = uni(scale);
+    // The two bin functions, each straight-line; every pass below is instantiated for both
+    // under one block-uniform branch, so no per-score branch is left.
+    auto bin_lin = [&](float v) -> uint32_t { return min((uint32_t)((v - mn) * scale), (uint32_t)(TK_BINS - 1)); };
+    auto bin_key = [&](float v) -> uint32_t { return score_key(v) >> 21; };
+    auto with_bins = [&](auto &&pass) {
+        if (lin)
+            pass(bin_lin);
+        else
+            pass(bin_key);
     };
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const f32x4 v = get(q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (pos(q, e) < n32)
-                atomicAdd(&hist[bin_of(v[e])], 1u);
-    }
-    __syncthreads();
-    const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
-    const uint32_t d = p0.digit, c = p0.count;
-    const uint32_t need = kk - p0.above;  // 1 .. c members of bin d are taken
-
-    // ---- 2. members of bin d into cand (a handful per row: one counter atomic each)
-    const bool in_lds = c <= (uint32_t)CAP;
-    if (need < c && in_lds) {  // block-uniform
+    // positions past n count into the spare bin TK_BINS (never read)
+    with_bins([&](auto bin_of) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const f32x4 v = get(q);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (pos(q, e) < n32 && bin_of(v[e]) == d)
-                    cand[atomicAdd(&sh_cnt, 1u)] = composite(score_key(v[e]), pos(q, e));
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t b = bin_of(v[e]);
+                atomicAdd(&hist[((valid >> (4 * q + e)) & 1u) ? b : (uint32_t)TK_BINS], 1u);
+            }
         }
-        __syncthreads();
+    });
+    __syncthreads();
+    const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
+    const uint32_t d = uni(p0.digit), c = uni(p0.count);
+    const uint32_t need = kk - uni(p0.above);  // 1 .. c members of bin d are taken
+
+    // ---- 2. members of bin d into cand (a handful per row: one counter atomic each)
+    const bool in_lds = c <= (uint32_t)CAP;
+    uint32_t memb = 0;  // bit 4q + e: position pos(q, e) is a member of bin d
+    if (need < c) {  // block-uniform
+        with_bins([&](auto bin_of) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 v = get(q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    memb |= (bin_of(v[e]) == d ? 1u : 0u) << (4 * q + e);
+            }
+        });
+        memb &= valid;
+        if (in_lds) {
+            if (memb) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const f32x4 v = get(q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if ((memb >> (4 * q + e)) & 1u)
+                            cand[atomicAdd(&sh_cnt, 1u)] = composite(score_key(v[e]), pos(q, e));
+                }
+            }
+            __syncthreads();
+        }
     }
 
     // ---- 3. lo: the need-th largest member (every member >= lo is taken)
@@ -569,62 +639,69 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
                 if (in_lds) {
                     for (uint32_t e = tid; e < c; e += TK_THREADS)
                         count(cand[e]);
-                } else {
+                } else if (memb) {
 #pragma unroll
                     for (int q = 0; q < NQ; ++q) {
                         const f32x4 v = get(q);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (pos(q, e) < n32 && bin_of(v[e]) == d)
+                            if ((memb >> (4 * q + e)) & 1u)
                                 count(composite(score_key(v[e]), pos(q, e)));
                     }
                 }
                 __syncthreads();
                 const DigitPick p = nb == (uint32_t)TK_BINS ? pick_digit<TK_BINS>(hist, nd, sh)
                                                               : pick_digit<512>(hist, nd, sh);
-                prefix = (prefix << width) | p.digit;
-                nd -= p.above;
+                prefix = (prefix << width) | uni(p.digit);
+                nd -= uni(p.above);
                 shift = nshift;
-                if (p.count == nd || shift == 0) {  // the whole sub-bin is taken
+                if (uni(p.count) == nd || shift == 0) {  // the whole sub-bin is taken
                     lo = prefix << shift;
                     break;
                 }
             }
         }
     }
+    lo = ((uint64_t)uni((uint32_t)(lo >> 32)) << 32) | uni((uint32_t)lo);
 
     // ---- 4. output slots in position order: group q of wave w starts at base[q][w].  With an
     // exact lo (a member's composite) the taken set is simply {composite >= lo}: every score of
     // a higher bin is larger than every member, every score of a lower bin smaller.
     // composite >= lo  <=>  x > x_lo, or x == x_lo at a position <= p_lo (float compares: -0 == +0
-    // as for the keys; no NaN)
+    // as for the keys; no NaN).  need == c takes the whole bin d and everything above it.
     const uint32_t lo_key = (uint32_t)(lo >> 32);
     const float x_lo = __uint_as_float((lo_key & 0x80000000u) ? (lo_key & 0x7FFFFFFFu) : ~lo_key);
     const int p_lo = (int)comp_pos(lo);
-    auto take_mask = [&](int q) -> uint32_t {
-        const f32x4 v = get(q);
-        uint32_t m = 0;
+    uint32_t takes = 0;  // bit 4q + e: position pos(q, e) is taken
+    if (exact) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bool t;
-            if (exact) {
-                t = v[e] > x_lo || (v[e] == x_lo && pos(q, e) <= p_lo);
-            } else {
-                const uint32_t bn = bin_of(v[e]);
-                t = bn > d || (bn == d && composite(score_key(v[e]), pos(q, e)) >= lo);
+        for (int q = 0; q < NQ; ++q) {
+            const f32x4 v = get(q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool t = (v[e] > x_lo) | ((v[e] == x_lo) & (pos(q, e) <= p_lo));
+                takes |= (t ? 1u : 0u) << (4 * q + e);
             }
-            m |= (t && pos(q, e) < n32) ? (1u << e) : 0u;
         }
-        return m;
-    };
-    static_assert(NQ <= 8, "take masks packed in 32 bits");
-    uint32_t takes = 0;  // 4 bits per group
+    } else {
+        with_bins([&](auto bin_of) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 v = get(q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t bn = bin_of(v[e]);
+                    const bool t = (bn > d) | ((bn == d) & (composite(score_key(v[e]), pos(q, e)) >= lo));
+                    takes |= (t ? 1u : 0u) << (4 * q + e);
+                }
+            }
+        });
+    }
+    takes &= valid;
     uint32_t incl[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const uint32_t m = take_mask(q);
-        takes |= m << (4 * q);
-        incl[q] = wave_incl_scan((uint32_t)__popc(m), lane);
+        incl[q] = wave_incl_scan((uint32_t)__popc((takes >> (4 * q)) & 15u), lane);
         if (lane == 63)
             base[q * TK_WAVES + wave] = incl[q];
     }
