@@ -23,7 +23,7 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
 DSA_TOPK_MAX = 2048
 DSA_MAX_SHARED_LAYERS = 8
 
-EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "sparse_mla_workspace_size",
+EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "sparse_mla_workspace_size",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "dsa_last_error",
            "dsa_abi_version")
 
@@ -63,6 +63,7 @@ def load_library(path: str = LIB_PATH):
         lib.dsa_index_scores.argtypes = [LP, I, I, I, P, P, P, I, P, L, P, L, P, L, P]
         lib.dsa_index_k_cache_write.argtypes = [L, I, P, L, P, P, L, I, P, P, L, P, L, L, P]
         lib.dsa_index_q_quant.argtypes = [L, I, I, P, L, P, P, L, I, P, P, P]
+        lib.dsa_index_front_end.argtypes = [L, I, I, P, L, P, L, P, P, L, I, P, P, L, P, L, L, P, P, P]
         lib.dsa_topk_workspace_size.argtypes = [LP, L, I]
         lib.dsa_topk_workspace_size.restype = S
         lib.dsa_topk.argtypes = [LP, P, L, I, P, P, S, P]
@@ -73,7 +74,8 @@ def load_library(path: str = LIB_PATH):
         lib.sparse_mla_prefill.argtypes = mla
         lib.sparse_mla_decode_shared.argtypes = [LP, I, I, I, F, I, I, I, I,
                                                  ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
-        for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_scores, lib.dsa_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
+        for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_front_end,
+                  lib.dsa_index_scores, lib.dsa_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
                   lib.sparse_mla_decode_shared, lib.dsa_abi_version):
             f.restype = I
         lib.dsa_last_error.restype = ctypes.c_char_p
@@ -221,6 +223,53 @@ def dsa_index_q_quant(q: torch.Tensor, positions: Optional[torch.Tensor] = None,
                                pos, cs, rope_rows, int(rope_off),
                                _dev(q_fp8, "q_fp8", (torch.uint8, torch.float8_e4m3fn)),
                                _dev(q_scale, "q_scale", torch.float32), _stream(stream))
+    _check(lib, st)
+    return q_fp8, q_scale
+
+
+def dsa_index_front_end(q: torch.Tensor, k: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor,
+                        cache_scale: torch.Tensor, positions: Optional[torch.Tensor] = None,
+                        cos_sin: Optional[torch.Tensor] = None, rope_off: int = 0,
+                        q_fp8: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
+                        cache_row_stride: Optional[int] = None, cache_scale_stride: int = 1,
+                        cache_rows: Optional[int] = None, stream=None):
+    """One launch of both writer calls for T new tokens: q [T, H_I, 128] -> (codes, scales) as
+    dsa_index_q_quant returns them; k [T, 128] -> cache rows slots[t], as
+    dsa_index_k_cache_write."""
+    lib = load_library()
+    T, H_I, D = q.shape
+    if D != 128 or tuple(k.shape) != (T, 128):
+        raise ValueError("q must be [T, H_I, 128] and k [T, 128]")
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    if q_fp8 is None:
+        q_fp8 = torch.empty((T, H_I, D), dtype=torch.uint8, device=q.device)
+    if q_scale is None:
+        q_scale = torch.empty((T, H_I), dtype=torch.float32, device=q.device)
+    if tuple(q_fp8.shape) != (T, H_I, D) or tuple(q_scale.shape) != (T, H_I):
+        raise ValueError("q_fp8 must be [T, H_I, 128] and q_scale [T, H_I]")
+    if cache_row_stride is None:
+        cache_row_stride = cache.stride(0) * cache.element_size()
+    if cache_rows is None:
+        cache_rows = cache.shape[0]
+    if slots.numel() != T:
+        raise ValueError("slots must hold one cache row per key")
+    if cache_rows > 0:
+        need_c = (cache_rows - 1) * int(cache_row_stride) + 128
+        need_s = ((cache_rows - 1) * int(cache_scale_stride) + 1) * 4
+        if cache.numel() * cache.element_size() < need_c or \
+                cache_scale.numel() * cache_scale.element_size() < need_s:
+            raise ValueError("cache or cache_scale smaller than cache_rows entries")
+    pos, cs, rope_rows = _rope_args(positions, cos_sin, T)
+    st = lib.dsa_index_front_end(T, H_I, _dt(q), _dev(q, "q", contiguous=False), _row_stride_bytes(q, "q"),
+                                 _dev(k, "k", contiguous=False), _row_stride_bytes(k, "k"), pos, cs,
+                                 rope_rows, int(rope_off), _dev(slots, "slots", torch.int64),
+                                 _dev(cache, "cache", (torch.uint8, torch.float8_e4m3fn), contiguous=False),
+                                 int(cache_row_stride),
+                                 _dev(cache_scale, "cache_scale", (torch.float32, torch.uint8), contiguous=False),
+                                 int(cache_scale_stride), int(cache_rows),
+                                 _dev(q_fp8, "q_fp8", (torch.uint8, torch.float8_e4m3fn)),
+                                 _dev(q_scale, "q_scale", torch.float32), _stream(stream))
     _check(lib, st)
     return q_fp8, q_scale
 

@@ -349,6 +349,34 @@ dsa_status dsa_index_q_quant(int64_t T, int H_I, dsa_dtype q_dt, const void *q, 
     return hip_status(e, "index-query quantiser launch");
 }
 
+dsa_status dsa_index_front_end(int64_t T, int H_I, dsa_dtype dt, const void *q, int64_t q_row_stride,
+                               const void *k, int64_t k_row_stride, const int64_t *positions,
+                               const float *cos_sin, int64_t rope_rows, int rope_off,
+                               const int64_t *slots, uint8_t *cache, int64_t cache_row_stride,
+                               float *cache_scale, int64_t cache_scale_stride, int64_t cache_rows,
+                               uint8_t *q_fp8, float *q_scale, void *stream)
+{
+    dsa_status st = check_index_quant(T, H_I, dt, q, q_row_stride, positions, cos_sin, rope_rows,
+                                      rope_off, q_fp8, (int64_t)H_I * 128, q_scale, H_I);
+    if (st != DSA_OK)
+        return st;
+    st = check_index_quant(T, 1, dt, k, k_row_stride, positions, cos_sin, rope_rows, rope_off, cache,
+                           cache_row_stride, cache_scale, cache_scale_stride);
+    if (st != DSA_OK)
+        return st;
+    if (T == 0)
+        return ok();
+    if (!slots)
+        return fail(DSA_ERR_INVALID_ARG, "slots must be non-NULL");
+    if (cache_rows < 0)
+        return fail(DSA_ERR_INVALID_ARG, "cache_rows must be >= 0");
+    hipError_t e = dsa::launch_index_front(T, H_I, dt == DSA_F32, q, q_row_stride, k, k_row_stride,
+                                           positions, cos_sin, rope_rows, rope_off, slots, cache_rows,
+                                           cache, cache_row_stride, cache_scale, cache_scale_stride,
+                                           q_fp8, q_scale, (hipStream_t)stream);
+    return hip_status(e, "index front-end launch");
+}
+
 size_t dsa_topk_workspace_size(const dsa_layout *layout, int64_t ld, int k)
 {
     (void)ld;

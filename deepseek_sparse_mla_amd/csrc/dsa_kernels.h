@@ -46,6 +46,13 @@ hipError_t launch_index_quant(int64_t rows, int H, bool in_f32, const void *x, i
                               uint8_t *codes, int64_t code_row_bytes, float *scales,
                               int64_t scale_row_stride, hipStream_t stream);
 
+hipError_t launch_index_front(int64_t T, int H, bool in_f32, const void *q, int64_t q_row_bytes,
+                              const void *k, int64_t k_row_bytes, const int64_t *positions,
+                              const float *cos_sin, int64_t rope_rows, int rope_off,
+                              const int64_t *slots, int64_t cache_rows, uint8_t *cache,
+                              int64_t cache_row_bytes, float *cache_scale, int64_t cache_scale_stride,
+                              uint8_t *q_fp8, float *q_scale, hipStream_t stream);
+
 int mla_num_splits(int64_t T, int k);
 size_t mla_workspace_bytes(int64_t T, int n_layers, int k);
 hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &layers, int n_layers,

@@ -106,6 +106,26 @@ __device__ __forceinline__ void widen(const Raw<IN_F32> &a, float v[8])
     }
 }
 
+// One quantisation job: `groups` groups of 128 values, H per row of x; group (r, h) goes to
+// row dst_rows[r] (r when NULL) of codes / scales, skipped when that row is outside
+// [0, out_rows).
+struct IqArgs {
+    int64_t groups;
+    int H;
+    const uint8_t *x;
+    int64_t x_row_bytes;
+    const int64_t *positions;
+    const float *cos_sin;
+    int64_t rope_rows;
+    int rope_off;
+    const int64_t *dst_rows;
+    int64_t out_rows;
+    uint8_t *codes;
+    int64_t code_row_bytes;
+    float *scales;
+    int64_t scale_row_stride;
+};
+
 // Each 16-lane team owns NG consecutive groups of ONE row (the launcher only picks NG > 1
 // when H is a multiple of NG), so the row's destination, position and rope-table values
 // are loaded once, and the team issues all NG loads of its groups before any arithmetic:
@@ -114,15 +134,25 @@ __device__ __forceinline__ void widen(const Raw<IN_F32> &a, float v[8])
 // return), so the cross-lane maximum always sees its partners; a team's lanes agree on
 // every group's validity.
 template <bool IN_F32, int NG, bool ROPE>
-__global__ void __launch_bounds__(IQ_BLOCK)
-index_quant_kernel(int64_t groups, int H, const uint8_t *__restrict__ x, int64_t x_row_bytes,
-                   const int64_t *__restrict__ positions, const float *__restrict__ cos_sin,
-                   int64_t rope_rows, int rope_off, const int64_t *__restrict__ dst_rows,
-                   int64_t out_rows, uint8_t *__restrict__ codes, int64_t code_row_bytes,
-                   float *__restrict__ scales, int64_t scale_row_stride)
+__device__ __forceinline__ void quant_block(const IqArgs &a, int64_t block)
 {
+    const int64_t groups = a.groups;
+    const int H = a.H;
+    const uint8_t *__restrict__ x = a.x;
+    const int64_t x_row_bytes = a.x_row_bytes;
+    const int64_t *__restrict__ positions = a.positions;
+    const float *__restrict__ cos_sin = a.cos_sin;
+    const int64_t rope_rows = a.rope_rows;
+    const int rope_off = a.rope_off;
+    const int64_t *__restrict__ dst_rows = a.dst_rows;
+    const int64_t out_rows = a.out_rows;
+    uint8_t *__restrict__ codes = a.codes;
+    const int64_t code_row_bytes = a.code_row_bytes;
+    float *__restrict__ scales = a.scales;
+    const int64_t scale_row_stride = a.scale_row_stride;
+
     const int lane = threadIdx.x & (IQ_LANES - 1);
-    const int64_t g0 = ((int64_t)blockIdx.x * IQ_GROUPS + (threadIdx.x >> 4)) * NG;
+    const int64_t g0 = (block * IQ_GROUPS + (threadIdx.x >> 4)) * NG;
     // groups fit in 32 bits for every realistic call; the 64-bit division is the fallback
     const int64_t r = groups <= (int64_t)UINT32_MAX ? (int64_t)((uint32_t)g0 / (uint32_t)H) : g0 / H;
     const int h0 = (int)(g0 - r * H);
@@ -207,9 +237,37 @@ index_quant_kernel(int64_t groups, int H, const uint8_t *__restrict__ x, int64_t
     }
 }
 
+template <bool IN_F32, int NG, bool ROPE>
+__global__ void __launch_bounds__(IQ_BLOCK) index_quant_kernel(IqArgs a)
+{
+    quant_block<IN_F32, NG, ROPE>(a, blockIdx.x);
+}
+
+// The fused front end: the first qblocks blocks quantise the index queries (NGQ groups per
+// team), the rest write the keys (one group per team), in one launch.
+template <bool IN_F32, int NGQ, bool ROPE>
+__global__ void __launch_bounds__(IQ_BLOCK) index_front_kernel(IqArgs q, IqArgs k, int64_t qblocks)
+{
+    if ((int64_t)blockIdx.x < qblocks)
+        quant_block<IN_F32, NGQ, ROPE>(q, blockIdx.x);
+    else
+        quant_block<IN_F32, 1, ROPE>(k, (int64_t)blockIdx.x - qblocks);
+}
+
 // Groups per team: four when the heads of a row split into fours and there are enough
 // groups for 256 blocks of 64, else one.
 constexpr int IQ_NG_WIDE = 4;
+
+static bool iq_wide(int64_t groups, int H)
+{
+    return H % IQ_NG_WIDE == 0 && groups >= (int64_t)256 * IQ_GROUPS * IQ_NG_WIDE;
+}
+
+static int64_t iq_blocks(int64_t groups, bool wide)
+{
+    const int64_t per_block = (int64_t)IQ_GROUPS * (wide ? IQ_NG_WIDE : 1);
+    return (groups + per_block - 1) / per_block;
+}
 
 hipError_t launch_index_quant(int64_t rows, int H, bool in_f32, const void *x, int64_t x_row_bytes,
                               const int64_t *positions, const float *cos_sin, int64_t rope_rows,
@@ -217,16 +275,13 @@ hipError_t launch_index_quant(int64_t rows, int H, bool in_f32, const void *x, i
                               uint8_t *codes, int64_t code_row_bytes, float *scales,
                               int64_t scale_row_stride, hipStream_t stream)
 {
-    const int64_t groups = rows * H;
-    if (groups == 0)
+    const IqArgs a{rows * H, H, (const uint8_t *)x, x_row_bytes, positions, cos_sin, rope_rows,
+                   rope_off, dst_rows, out_rows, codes, code_row_bytes, scales, scale_row_stride};
+    if (a.groups == 0)
         return hipSuccess;
-    const bool wide = H % IQ_NG_WIDE == 0 && groups >= (int64_t)256 * IQ_GROUPS * IQ_NG_WIDE;
-    const int64_t per_block = (int64_t)IQ_GROUPS * (wide ? IQ_NG_WIDE : 1);
-    const dim3 grid((unsigned)((groups + per_block - 1) / per_block));
-#define IQ_LAUNCH(F32, NG, ROPE)                                                                  \
-    index_quant_kernel<F32, NG, ROPE><<<grid, IQ_BLOCK, 0, stream>>>(                            \
-        groups, H, (const uint8_t *)x, x_row_bytes, positions, cos_sin, rope_rows, rope_off,      \
-        dst_rows, out_rows, codes, code_row_bytes, scales, scale_row_stride)
+    const bool wide = iq_wide(a.groups, H), rope = cos_sin != nullptr;
+    const dim3 grid((unsigned)iq_blocks(a.groups, wide));
+#define IQ_LAUNCH(F32, NG, ROPE) index_quant_kernel<F32, NG, ROPE><<<grid, IQ_BLOCK, 0, stream>>>(a)
 #define IQ_LAUNCH_NG(F32, ROPE)                                                                   \
     do {                                                                                          \
         if (wide)                                                                                 \
@@ -234,7 +289,46 @@ hipError_t launch_index_quant(int64_t rows, int H, bool in_f32, const void *x, i
         else                                                                                      \
             IQ_LAUNCH(F32, 1, ROPE);                                                              \
     } while (0)
-    const bool rope = cos_sin != nullptr;
+    if (in_f32) {
+        if (rope)
+            IQ_LAUNCH_NG(true, true);
+        else
+            IQ_LAUNCH_NG(true, false);
+    } else {
+        if (rope)
+            IQ_LAUNCH_NG(false, true);
+        else
+            IQ_LAUNCH_NG(false, false);
+    }
+#undef IQ_LAUNCH_NG
+#undef IQ_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_index_front(int64_t T, int H, bool in_f32, const void *q, int64_t q_row_bytes,
+                              const void *k, int64_t k_row_bytes, const int64_t *positions,
+                              const float *cos_sin, int64_t rope_rows, int rope_off,
+                              const int64_t *slots, int64_t cache_rows, uint8_t *cache,
+                              int64_t cache_row_bytes, float *cache_scale, int64_t cache_scale_stride,
+                              uint8_t *q_fp8, float *q_scale, hipStream_t stream)
+{
+    const IqArgs qa{T * H, H, (const uint8_t *)q, q_row_bytes, positions, cos_sin, rope_rows,
+                    rope_off, nullptr, T, q_fp8, (int64_t)H * IQ_D, q_scale, H};
+    const IqArgs ka{T, 1, (const uint8_t *)k, k_row_bytes, positions, cos_sin, rope_rows, rope_off,
+                    slots, cache_rows, cache, cache_row_bytes, cache_scale, cache_scale_stride};
+    if (T == 0)
+        return hipSuccess;
+    const bool wide = iq_wide(qa.groups, H), rope = cos_sin != nullptr;
+    const int64_t qblocks = iq_blocks(qa.groups, wide);
+    const dim3 grid((unsigned)(qblocks + iq_blocks(ka.groups, false)));
+#define IQ_LAUNCH(F32, NG, ROPE) index_front_kernel<F32, NG, ROPE><<<grid, IQ_BLOCK, 0, stream>>>(qa, ka, qblocks)
+#define IQ_LAUNCH_NG(F32, ROPE)                                                                   \
+    do {                                                                                          \
+        if (wide)                                                                                 \
+            IQ_LAUNCH(F32, IQ_NG_WIDE, ROPE);                                                     \
+        else                                                                                      \
+            IQ_LAUNCH(F32, 1, ROPE);                                                              \
+    } while (0)
     if (in_f32) {
         if (rope)
             IQ_LAUNCH_NG(true, true);

@@ -6,7 +6,8 @@
  *
  *   dsa_index_k_cache_write  index-cache writer: rope + fp8 keys with a
  *   dsa_index_q_quant        power-of-two scale (and the same for prefill
- *                            index queries), the step in front of the indexer
+ *   dsa_index_front_end      index queries, or both in one launch), the step
+ *                            in front of the indexer
  *   dsa_index_scores         lightning indexer: one fp32 score per visible
  *                            cached token for every query row
  *   dsa_topk                 per-row top-k (k <= DSA_TOPK_MAX) positions
@@ -147,6 +148,21 @@ dsa_status dsa_index_k_cache_write(int64_t n, dsa_dtype k_dt, const void *k, int
 dsa_status dsa_index_q_quant(int64_t T, int H_I, dsa_dtype q_dt, const void *q, int64_t q_row_stride,
                              const int64_t *positions, const float *cos_sin, int64_t rope_rows,
                              int rope_off, uint8_t *q_fp8, float *q_scale, void *stream);
+
+/*
+ * dsa_index_front_end -- both of the above in one launch, the fused form of the
+ * step ([anatomy], ATOM-side optimisations, fused indexer kernel: query rope,
+ * fp8 quantisation and key-cache write as one kernel).  T new tokens, each with
+ * H_I index-query heads (q, as for dsa_index_q_quant) and one index key (k, as
+ * for dsa_index_k_cache_write), both of dtype dt and both roped at
+ * positions[t].  The results are bitwise those of the two separate calls.
+ */
+dsa_status dsa_index_front_end(int64_t T, int H_I, dsa_dtype dt, const void *q, int64_t q_row_stride,
+                               const void *k, int64_t k_row_stride, const int64_t *positions,
+                               const float *cos_sin, int64_t rope_rows, int rope_off,
+                               const int64_t *slots, uint8_t *cache, int64_t cache_row_stride,
+                               float *cache_scale, int64_t cache_scale_stride, int64_t cache_rows,
+                               uint8_t *q_fp8, float *q_scale, void *stream);
 
 /*
  * dsa_index_scores -- lightning-indexer scores ([anatomy], full structure

@@ -217,3 +217,20 @@ def test_writer_empty_calls_accept_null_pointers(lib):
     """An empty batch is a no-op; empty device tensors carry NULL data pointers."""
     assert _kw(lib, n=0, k=None, slots=None, cache=None, cscale=None) == B.DSA_OK
     assert lib.dsa_index_q_quant(0, 32, B.DSA_BF16, None, 8192, None, None, 0, 0, None, None, None) == B.DSA_OK
+
+
+def test_index_front_end_rejects(lib):
+    def fe(**kw):
+        a = dict(T=8, H=32, dt=B.DSA_BF16, q=FAKE, qs=8192, k=FAKE, ks=256, pos=None, cs=None, rr=0, ro=0,
+                 slots=FAKE, cache=FAKE, cstride=128, cscale=FAKE, csstride=1, crows=100, q8=FAKE, qsc=FAKE)
+        a.update(kw)
+        return lib.dsa_index_front_end(a["T"], a["H"], a["dt"], a["q"], a["qs"], a["k"], a["ks"], a["pos"],
+                                       a["cs"], a["rr"], a["ro"], a["slots"], a["cache"], a["cstride"],
+                                       a["cscale"], a["csstride"], a["crows"], a["q8"], a["qsc"], None)
+    assert fe(ks=100) == B.DSA_ERR_INVALID_ARG                   # key row shorter than 128 values
+    assert fe(qs=4096) == B.DSA_ERR_INVALID_ARG                  # query row shorter than 32 heads
+    assert fe(slots=None) == B.DSA_ERR_INVALID_ARG
+    assert fe(dt=B.DSA_FP8_E4M3FN) == B.DSA_ERR_UNSUPPORTED
+    assert fe(cs=FAKE, rr=4) == B.DSA_ERR_INVALID_ARG             # rope without positions
+    assert fe(crows=-1) == B.DSA_ERR_INVALID_ARG
+    assert fe(T=0, q=None, k=None, slots=None, cache=None, cscale=None, q8=None, qsc=None) == B.DSA_OK

@@ -239,6 +239,39 @@ def test_prefill_queries_at_full_size_sampled_rows():
     assert np.array_equal(scales[rows].cpu().numpy(), os_)
 
 
+@pytest.mark.parametrize("T,dtype", [(300, torch.bfloat16), (517, torch.float32), (4096, torch.bfloat16)])
+def test_front_end_equals_the_two_calls(T, dtype):
+    """The one-launch front end gives bitwise the separate calls' results (queries and the
+    132-byte cache entries), checked against the oracle on every row up to 517 rows and on
+    64 sampled rows of the full prefill chunk."""
+    H, rows = 32, T + 77
+    q = _randn((T, H, 128), 14).to(dtype).to(DEV)
+    k = _randn((T, 128), 15).to(dtype).to(DEV)
+    pos = torch.arange(28672, 28672 + T, dtype=torch.int64, device=DEV)
+    slots = torch.from_numpy(np.random.default_rng(16).permutation(rows)[:T].astype(np.int64)).to(DEV)
+    tab = dsa.rope_cos_sin_cache(32768, device=DEV)
+    bufs = [torch.full((rows, 132), 5, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    kw = dict(cache_row_stride=132, cache_scale_stride=33, cache_rows=rows)
+    c1, s1 = dsa.dsa_index_front_end(q, k, slots, bufs[0], bufs[0].view(-1)[128:], positions=pos,
+                                     cos_sin=tab, **kw)
+    c2, s2 = dsa.dsa_index_q_quant(q, positions=pos, cos_sin=tab)
+    dsa.dsa_index_k_cache_write(k, slots, bufs[1], bufs[1].view(-1)[128:], positions=pos, cos_sin=tab, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(bufs[0], bufs[1])
+    rows_q = np.arange(T) if T <= 517 else np.unique(
+        np.concatenate([[0, T - 1], np.random.default_rng(17).integers(0, T, 62)]))
+    oc, os_ = oracle.index_quant(_oracle_in(q[rows_q]), positions=pos.cpu().numpy()[rows_q],
+                                 cos_sin=tab.cpu().numpy())
+    assert np.array_equal(c1[rows_q].cpu().numpy(), oc)
+    assert np.array_equal(s1[rows_q].cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    kc, ks = oracle.index_quant(_oracle_in(k[rows_q]).reshape(len(rows_q), 1, 128),
+                                positions=pos.cpu().numpy()[rows_q], cos_sin=tab.cpu().numpy())
+    got = bufs[0][slots[rows_q]].cpu().numpy()
+    assert np.array_equal(got[:, :128], kc[:, 0, :])
+    assert np.array_equal(got[:, 128:].copy().view(np.float32)[:, 0].view(np.uint32), ks[:, 0].view(np.uint32))
+
+
 def test_empty_batch_writes_nothing():
     cache = torch.full((4, 128), 9, dtype=torch.uint8, device=DEV)
     scale = torch.full((4,), 3.0, device=DEV)
