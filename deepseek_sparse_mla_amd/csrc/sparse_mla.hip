@@ -66,17 +66,17 @@ struct StageRegs {
     u32x4 v[N];
 };
 
-// Issue the gathers of one tile (rows given by sidx) into registers.  `seq` is a buffer
-// resource over the sequence's rows, so offsets are 32-bit and an index of -1 (or any
-// row past the visible count) reads as zeros.
-template <bool KV_FP8>
+// Issue the gathers of one tile (rows given by sidx) into registers, pieces U0 .. U1-1 of
+// this thread.  `seq` is a buffer resource over the sequence's rows, so offsets are 32-bit
+// and an index of -1 (or any row past the visible count) reads as zeros.
+template <bool KV_FP8, int U0 = 0, int U1 = StageRegs<KV_FP8>::N>
 __device__ __forceinline__ void stage_load(StageRegs<KV_FP8> &R, __amdgpu_buffer_rsrc_t seq,
                                            const int32_t *sidx, int tid)
 {
     typedef StageRegs<KV_FP8> SR;
     constexpr int ROWB = KV_FP8 ? 576 : 1152;   // bytes per row in HBM
 #pragma unroll
-    for (int u = 0; u < SR::N; ++u) {
+    for (int u = U0; u < U1; ++u) {
         const int c = tid + M_THREADS * u;
         if (SR::TOTAL % M_THREADS == 0 || c < SR::TOTAL) {
             const int row = c / SR::PIECES, col = c % SR::PIECES;
@@ -115,6 +115,37 @@ __device__ __forceinline__ void stage_store(const StageRegs<KV_FP8> &R, char *ti
         } else {
             *(u32x4 *)(tile + row * M_ROWB + col * 16) = R.v[u];
         }
+    }
+}
+
+// bf16 rows with a fixed lane -> row map: thread t gathers rows (t >> 3) and (t >> 3) + 32 of
+// the tile, 16-byte pieces (t & 7) + 8 v (v < 9) of each, so it needs only two indices per
+// tile and every load instruction reads whole 128-byte lines of 8 rows.  R.v[v] and
+// R.v[9 + v] hold piece v of the two rows.
+constexpr int SR_V = 9;
+static_assert(StageRegs<false>::N == 2 * SR_V && StageRegs<false>::PIECES == 8 * SR_V, "bf16 row map");
+
+template <int V0, int V1>
+__device__ __forceinline__ void stage_load_rows(StageRegs<false> &R, __amdgpu_buffer_rsrc_t seq,
+                                                int32_t r0, int32_t r1, int tid)
+{
+#pragma unroll
+    for (int v = V0; v < V1; ++v) {
+        const int col = (tid & 7) + 8 * v;
+        R.v[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, r0 * 1152 + col * 16, 0, 0));
+        R.v[SR_V + v] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, r1 * 1152 + col * 16, 0, 0));
+    }
+}
+
+__device__ __forceinline__ void stage_store_rows(const StageRegs<false> &R, char *tile, int tid)
+{
+    const int row = tid >> 3;
+#pragma unroll
+    for (int v = 0; v < SR_V; ++v) {
+        const int col = (tid & 7) + 8 * v;
+        *(u32x4 *)(tile + row * M_ROWB + col * 16) = R.v[v];
+        *(u32x4 *)(tile + (row + 32) * M_ROWB + col * 16) = R.v[SR_V + v];
     }
 }
 
@@ -209,6 +240,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                                                            int64_t pairs_per_xcd, float *__restrict__ ws_o,
                                                            float *__restrict__ ws_ml)
 {
+    static_assert(!KV_FP8, "fp8 latent rows take mla_fp8_kernel");
     __shared__ __attribute__((aligned(16))) char kt[M_TILEB];
     __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
     __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
@@ -295,8 +327,8 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
         int32_t idx_next = i2;
         lds_barrier();  // Q stays in flight
         if (ntiles > 0) {
-            stage_load<KV_FP8>(R, seq, sidx[0], tid);
-            stage_store<KV_FP8>(R, kt, tid);
+            stage_load_rows<0, SR_V>(R, seq, sidx[0][tid >> 3], sidx[0][(tid >> 3) + 32], tid);
+            stage_store_rows(R, kt, tid);
         }
         // Nothing may be left in flight here (Q included): otherwise the compiler's wait
         // for Q lands inside the loop, where it would also wait for the next tile's loads.
@@ -305,13 +337,16 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
 
         for (int tt = 0; tt < ntiles; ++tt) {
             const int buf = tt & 1;
-            if (tt + 1 < ntiles)
-                stage_load<KV_FP8>(R, seq, sidx[buf ^ 1], tid);
+            const bool gather_next = tt + 1 < ntiles;
+            // the next tile's two rows of this thread (written before the last barrier)
+            const int32_t nr0 = sidx[buf ^ 1][tid >> 3], nr1 = sidx[buf ^ 1][(tid >> 3) + 32];
             const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
             const bool restart = (pass == 1 && tt == 0);
 
             // ---- 1. S^T partials for keys 0..31 (S[0]) and 32..63 (S[1]) over this wave's
-            // dims; operands are read three k-steps ahead of the MFMAs that use them.
+            // dims; operands are read three k-steps ahead of the MFMAs that use them.  The
+            // next tile's gathers are issued a sixth at a time between the k-steps, so the
+            // CU's address unit works through them while the MFMAs run.
             f32x16 S[2] = {f32x16{}, f32x16{}};
             {
                 const char *arow = kt + j * M_ROWB + 2 * (288 * dq + 8 * g);
@@ -338,6 +373,16 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
                                                                        qT[3 * c + t], S[0], 0, 0, 0);
                         S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[cur][t][1]),
                                                                        qT[3 * c + t], S[1], 0, 0, 0);
+                    }
+                    if (gather_next) {
+                        switch (c) {
+                        case 0: stage_load_rows<0, 1>(R, seq, nr0, nr1, tid); break;
+                        case 1: stage_load_rows<1, 3>(R, seq, nr0, nr1, tid); break;
+                        case 2: stage_load_rows<3, 4>(R, seq, nr0, nr1, tid); break;
+                        case 3: stage_load_rows<4, 6>(R, seq, nr0, nr1, tid); break;
+                        case 4: stage_load_rows<6, 7>(R, seq, nr0, nr1, tid); break;
+                        default: stage_load_rows<7, SR_V>(R, seq, nr0, nr1, tid); break;
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -441,7 +486,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
             }
             lds_barrier();  // tile, S partials and P fully consumed
             if (tt + 1 < ntiles)
-                stage_store<KV_FP8>(R, kt, tid);
+                stage_store_rows(R, kt, tid);
             if (tid < M_TILE) {
                 sidx[buf][tid] = idx_next;  // tile tt + 2
                 idx_next = load_idx(tt + 3);
