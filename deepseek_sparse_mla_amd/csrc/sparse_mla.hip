@@ -942,24 +942,20 @@ __global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((const uint8_t *)Ld.kv + r.kv_base * (2 * M_DQK)), (short)0, (int)seq_bytes, BUF_DWORD3);
     u32x4 R[HH_N];
-    // piece tid + 256 u of the tile is row rc[u] >> 8, 16-byte column rc[u] & 255 (fixed per
-    // thread; consecutive lanes read consecutive 16 bytes of a row)
-    uint32_t rc[HH_N];
-#pragma unroll
-    for (int u = 0; u < HH_N; ++u) {
-        const int c = tid + M_THREADS * u;
-        rc[u] = ((uint32_t)(c / 72) << 8) | (uint32_t)(c % 72);
-    }
-    auto gather = [&](const int32_t *sx) {  // tile rows sx[0..31] into the staging registers
+    // thread t stages tile row t >> 3, 16-byte pieces (t & 7) + 8 u (u < 9): one index per
+    // thread and tile, and every load instruction reads whole 128-byte lines of 8 rows
+    static_assert(HH_N * 8 == 72 && HH_TILE * 8 == M_THREADS, "one tile row per 8 threads");
+    const int hrow = tid >> 3, hcol = tid & 7;
+    auto gather = [&](int32_t row_idx) {  // this thread's pieces of the tile row row_idx
 #pragma unroll
         for (int u = 0; u < HH_N; ++u)
             R[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 seq, sx[rc[u] >> 8] * (2 * M_DQK) + 16 * (int)(rc[u] & 255u), 0, 0));
+                                                 seq, row_idx * (2 * M_DQK) + 16 * (hcol + 8 * u), 0, 0));
     };
     auto stage = [&]() {
 #pragma unroll
         for (int u = 0; u < HH_N; ++u)
-            *(u32x4 *)(kt + (rc[u] >> 8) * M_ROWB + 16 * (rc[u] & 255u)) = R[u];
+            *(u32x4 *)(kt + hrow * M_ROWB + 16 * (hcol + 8 * u)) = R[u];
     };
 
     const int aoffs = j * M_ROWB + 2 * (144 * dq + 8 * g);
@@ -980,15 +976,16 @@ __global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
         int32_t idx_next = i2;
         lds_barrier();  // Q stays in flight
         if (ntiles > 0) {
-            gather(sidx[0]);
+            gather(sidx[0][hrow]);
             stage();
         }
         __builtin_amdgcn_s_waitcnt(0x0070);  // nothing known to the compiler stays in flight
         lds_barrier();
         for (int tt = 0; tt < ntiles; ++tt) {
             const int buf = tt & 1;
-            if (tt + 1 < ntiles)
-                gather(sidx[buf ^ 1]);
+            const bool gather_next = tt + 1 < ntiles;
+            if (gather_next)  // this thread's row of the next tile, requested before any compute
+                gather(sidx[buf ^ 1][hrow]);
             const uint32_t valid = (uint32_t)__ballot(lane < HH_TILE && sidx[buf][lane & 31] >= 0);
 
             // ---- 1. S^T partial over this wave's 144 dims
