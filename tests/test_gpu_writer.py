@@ -129,6 +129,20 @@ def test_q_quant_four_groups_per_team(dtype):
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+@pytest.mark.parametrize("T,H", [(700, 5), (2100, 8)])
+def test_q_quant_other_head_counts(T, H):
+    """Head counts other than 32: an odd count (one group per team: rows' heads do not split
+    into fours) and 8 heads over 16800 groups (four per team); every row checked."""
+    q = _randn((T, H, 128), 18).to(torch.bfloat16)
+    pos = np.random.default_rng(19).integers(0, 4096, T).astype(np.int64)
+    tab = dsa.rope_cos_sin_cache(4096, device="cpu")
+    codes, scales = dsa.dsa_index_q_quant(q.to(DEV), positions=torch.from_numpy(pos).to(DEV),
+                                          cos_sin=tab.to(DEV))
+    oc, os_ = oracle.index_quant(_oracle_in(q), positions=pos, cos_sin=tab.numpy())
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
 def test_rounding_on_every_tie_and_its_neighbours():
     """Groups whose largest value is 448 (scale 1) and whose other values are every tie
     between adjacent E4M3FN codes, one fp32 step either side, and the codes themselves."""
