@@ -110,9 +110,9 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
 }
 
 // Two launch shapes.  Rows that are whole sequences (one query each, as in decode): the grid
-// walks the concatenated token stream of all sequences, chunk tokens per block (a block may
-// finish one sequence and start the next), so every block has work and the blocks past the
-// last token all sit at the end of the grid.  Otherwise: one block per (chunk, query row).
+// walks the concatenated token stream of all sequences, an equal share of it per block (a
+// block may finish one sequence and start the next), so no block waits on a longer one.
+// Otherwise: one block per (chunk, query row).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
                                                          const float *__restrict__ w,
                                                          const uint8_t *__restrict__ k, int64_t kstride,
@@ -129,11 +129,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                                min(s_begin + (int64_t)chunk, r.n));
         return;
     }
-    const int64_t t0 = (int64_t)blockIdx.x * chunk;
+    // stream: the grid's blocks split the N cached tokens evenly (N is known only here), in
+    // ranges that are multiples of 32 tokens
     const int64_t N = L.kv_indptr[L.batch];
+    const int64_t per = ((N + gridDim.x - 1) / gridDim.x + 31) & ~(int64_t)31;
+    const int64_t t0 = (int64_t)blockIdx.x * per;
     if (t0 >= N)
         return;
-    const int64_t t1 = min(t0 + (int64_t)chunk, N);
+    const int64_t t1 = min(t0 + per, N);
     int lo = 0, hi = L.batch - 1;  // the sequence holding token t0: largest b with kv_indptr[b] <= t0
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -388,14 +391,17 @@ __global__ __launch_bounds__(256) void idx_generic_kernel(LayoutDev L, int H, in
 // ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
+constexpr int IDX_STREAM_BLOCKS = 512;  // two blocks per CU: measured as good as or better than four
+
 hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
                                const float *w, const void *k, int64_t kstride, const float *ks,
                                int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream)
 {
-    // Waves of at most 16 tiles and enough blocks to cover the chip several times, at least
-    // two 32-token tiles per wave (one tile per wave re-reads q and w for too little work:
-    // 7.9 against 9.2 us on the 8-row decode).  DSA_INDEXER_CHUNK (a power of two in
-    // [128, 8192]) overrides the tokens per block for launch-shape tuning.
+    // Per (chunk, query row) blocks: waves of at most 16 tiles and enough blocks to cover the
+    // chip several times, at least two 32-token tiles per wave (one tile per wave re-reads q
+    // and w for too little work: 7.9 against 9.2 us on the 8-row decode).  DSA_INDEXER_CHUNK
+    // (a power of two in [128, 8192]) overrides the tokens per block and DSA_INDEXER_BLOCKS
+    // the stream's block count, for launch-shape tuning.
     int chunk = 2048;
     while (chunk > 256 && T * ((max_ctx + chunk - 1) / chunk) < 2048)
         chunk >>= 1;
@@ -406,7 +412,16 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
     }
     const int64_t nchunks = (max_ctx + chunk - 1) / chunk;
     const bool as_stream = L.q_indptr == nullptr;  // rows are whole sequences
-    dim3 grid = as_stream ? dim3((unsigned)((T * max_ctx + chunk - 1) / chunk)) : dim3((unsigned)nchunks, (unsigned)T);
+    // stream: two blocks per CU for long streams (one round; four per CU measured no
+    // better), fewer blocks (at least 256 tokens each) for short ones; the kernel divides
+    // the actual token count
+    int64_t sblocks = min((int64_t)IDX_STREAM_BLOCKS, (T * max_ctx + 255) / 256);
+    if (const char *env = getenv("DSA_INDEXER_BLOCKS")) {  // launch-shape tuning
+        const int nb = atoi(env);
+        if (nb >= 1 && nb <= 65536)
+            sblocks = min((int64_t)nb, T * max_ctx);
+    }
+    dim3 grid = as_stream ? dim3((unsigned)max((int64_t)1, sblocks)) : dim3((unsigned)nchunks, (unsigned)T);
     hipLaunchKernelGGL(idx_decode_kernel, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
                        (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
     return hipGetLastError();
