@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="HBM bytes per stage call from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     p.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (MiB)")
+    p.add_argument("--graph", action="store_true",
+                   help="capture each input set's step once as a HIP graph and time graph replays")
     return p.parse_args()
 
 
@@ -440,10 +442,26 @@ def main():
         runners[s % nsets].step()
     torch.cuda.synchronize()
 
+    steppers = [r.step for r in runners]
+    if args.graph:
+        # one graph per input set, each holding one whole step (the library only enqueues
+        # kernels: nothing in a step allocates, clears or synchronises)
+        graphs = []
+        for r in runners:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                r.step()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        steppers = [g.replay for g in graphs]
+        for s in range(args.warmup):
+            steppers[s % nsets]()
+        torch.cuda.synchronize()
+
     # timed region: exactly K steps
     t0 = time.perf_counter()
     for s in range(args.steps):
-        runners[s % nsets].step()
+        steppers[s % nsets]()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -509,7 +527,8 @@ def main():
         "config": {"workload": probe.name, "batch": probe.B, "query_rows": T, "context": probe.ctx[0] if len(set(probe.ctx)) == 1 else "ragged",
                    "index_heads": probe.H_I, "index_dim": probe.D_I, "topk": probe.topk, "mla_heads": probe.H,
                    "latent": probe.Dc, "rope": probe.Dr, "kv_cache": probe.layers[0].kv_dt,
-                   "layers": len(probe.layers), "input_sets_rotated": nsets},
+                   "layers": len(probe.layers), "input_sets_rotated": nsets,
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "path_hbm": {"algorithmic_bytes": model["path_bytes"], "achieved_GBps": round(path_gbs, 1),
                      "frac_of_peak": round(path_gbs / HBM_PEAK_GBS, 4)},
         "kernels_ms": {kernel_names[s]: round(dur[s], 5) for s in stages},
