@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import dsa_testlib as tl
+import oracle
 import deepseek_sparse_mla_amd as dsa
 from deepseek_sparse_mla_amd import synth
 
@@ -332,3 +333,32 @@ def test_extreme_logit_spread_takes_exact_rerun():
                                  idx[b:b + 1].cpu().numpy(), 1.0 / 16, Dc)
         tl.check_attention(tl.to_f64(out[b]), o[0], tl.ATTN_ATOL_LOWP, "row %d" % b)
         np.testing.assert_allclose(lse[b].cpu().numpy(), l[0], rtol=1e-4, atol=1e-3)
+
+
+def test_draft_steps_reuse_the_first_steps_indices():
+    """Speculative draft steps reuse the index set chosen at draft step 0 (the anatomy page's
+    MTP note: later draft steps skip the indexer and top-k).  The context grows by one
+    token per step; the reused indices (all below the step-0 context) stay valid, and each
+    step's attention meets the oracle on them, bitwise equal to the same call made on the
+    step-0 layout."""
+    c0, D = 5000, 3
+    case = synth.make_case("draft", 2, ctx=[c0 + D], kv_dt="bf16", sm_scale=1.0 / 16, device=DEV)
+    L = case.layers[0]
+    kv_ptr0 = torch.tensor([0, c0], dtype=torch.int64, device=DEV)
+    lay0 = dsa.Layout(kv_ptr0, None, 1, c0)
+    scores = dsa.dsa_index_scores(lay0, case.iq, case.iw, case.ik, k_scale=case.ik_scale)
+    idx = dsa.dsa_topk(lay0, scores, case.topk)
+    torch.cuda.synchronize()
+    i_host = idx.cpu().numpy()
+    assert i_host.max() < c0
+    g = torch.Generator(device=DEV).manual_seed(77)
+    for d in range(1, D + 1):
+        q = torch.randn((1, case.H, case.Dc + case.Dr), generator=g, device=DEV).to(torch.bfloat16)
+        lay = dsa.Layout(torch.tensor([0, c0 + d], dtype=torch.int64, device=DEV), None, 1, c0 + d)
+        out = dsa.sparse_mla_decode(lay, q, L.kv, idx, case.sm_scale, case.Dc, L.kv_scale)
+        out0 = dsa.sparse_mla_decode(lay0, q, L.kv, idx, case.sm_scale, case.Dc, L.kv_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out0)
+        o_or, _ = oracle.sparse_mla([0, c0 + d], None, synth.host(q), synth.host(L.kv[:c0 + d]), i_host,
+                                    case.sm_scale, case.Dc, L.kv_scale)
+        tl.check_attention(tl.to_f64(out)[0], o_or[0], tl.ATTN_ATOL_LOWP, "draft step %d" % d)
