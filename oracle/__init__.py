@@ -57,9 +57,9 @@ def _load():
             lib.orc_decode_fp8_e4m3fn.argtypes = [ctypes.c_uint8]
             lib.orc_decode_fp8_e4m3fn.restype = D
             lib.orc_visible_counts.argtypes = [I, P, P, L, P]
-            lib.orc_index_scores.argtypes = [I, P, P, L, I, I, I, P, P, P, I, P, L, P, L, P, L, P]
+            lib.orc_index_scores.argtypes = [I, P, P, L, I, I, I, P, P, P, I, P, L, P, L, P, L, P, P, L, L]
             lib.orc_topk.argtypes = [L, P, P, L, I, P]
-            lib.orc_sparse_mla.argtypes = [I, P, P, L, I, I, I, D, I, P, I, P, D, P, I, P, P]
+            lib.orc_sparse_mla.argtypes = [I, P, P, L, I, I, I, D, I, P, I, P, D, P, I, P, P, L]
             lib.orc_num_threads.argtypes = []
             lib.orc_encode_fp8_e4m3fn.argtypes = [D]
             lib.orc_encode_fp8_e4m3fn.restype = ctypes.c_uint8
@@ -129,11 +129,13 @@ def visible_counts(kv_indptr, q_indptr, T) -> np.ndarray:
 
 
 def index_scores(kv_indptr, q_indptr, q, w, k, k_scale=None, q_scale=None, ld=None,
-                 k_row_stride_bytes=None, k_scale_stride=1, with_magnitude=False):
+                 k_row_stride_bytes=None, k_scale_stride=1, with_magnitude=False,
+                 block_table=None, page_size=0):
     """Indexer scores, fp64 [T, ld]; entries s >= n_i are NaN.
 
     q: [T, H, D] float32 / uint16 (bf16 bits) / uint8 (fp8 codes).
     k: [rows, D] (or a raw uint8 byte buffer with k_row_stride_bytes).
+    block_table: int32 [B, pages] of physical page ids (paged caches), with page_size.
     """
     lib = _load()
     kv = _c(kv_indptr, np.int64)
@@ -151,9 +153,11 @@ def index_scores(kv_indptr, q_indptr, q, w, k, k_scale=None, q_scale=None, ld=No
     w = _c(w, np.float32)
     ks = _c(k_scale, np.float32)
     qs = _c(q_scale, np.float32)
+    bt = _c(block_table, np.int32)
     rc = lib.orc_index_scores(len(kv) - 1, _ptr(kv), _ptr(qi), T, H, D, _dt_code(q), _ptr(q),
                               _ptr(qs), _ptr(w), _dt_code(k), _ptr(k), int(k_row_stride_bytes),
-                              _ptr(ks), int(k_scale_stride), _ptr(scores), ld, _ptr(mag))
+                              _ptr(ks), int(k_scale_stride), _ptr(scores), ld, _ptr(mag), _ptr(bt),
+                              0 if bt is None else bt.shape[1], int(page_size))
     _check(rc, "index_scores")
     return (scores, mag) if with_magnitude else scores
 
@@ -169,8 +173,9 @@ def topk(scores, n, k) -> np.ndarray:
     return out
 
 
-def sparse_mla(kv_indptr, q_indptr, q, kv, indices, sm_scale, Dc, kv_scale=1.0):
-    """Sparse MLA output [T, H, Dc] and lse [T, H], both fp64."""
+def sparse_mla(kv_indptr, q_indptr, q, kv, indices, sm_scale, Dc, kv_scale=1.0, physical=False):
+    """Sparse MLA output [T, H, Dc] and lse [T, H], both fp64.  physical: the indices are
+    rows of kv (paged caches) instead of positions within each sequence."""
     lib = _load()
     kvp = _c(kv_indptr, np.int64)
     qi = _c(q_indptr, np.int32)
@@ -183,9 +188,26 @@ def sparse_mla(kv_indptr, q_indptr, q, kv, indices, sm_scale, Dc, kv_scale=1.0):
     lse = np.zeros((T, H))
     rc = lib.orc_sparse_mla(len(kvp) - 1, _ptr(kvp), _ptr(qi), T, H, Dc, Dqk - Dc, float(sm_scale),
                             _dt_code(q), _ptr(q), _dt_code(kv), _ptr(kv), float(kv_scale), _ptr(idx),
-                            k, _ptr(out), _ptr(lse))
+                            k, _ptr(out), _ptr(lse), kv.shape[0] if physical else 0)
     _check(rc, "sparse_mla")
     return out, lse
+
+
+def to_physical(kv_indptr, q_indptr, indices, block_table, page_size):
+    """Map top-k positions (logical, per sequence) to physical cache rows through a block
+    table: row = block_table[b, s // page_size] * page_size + s % page_size; -1 stays -1."""
+    kv = np.asarray(kv_indptr, np.int64)
+    idx = np.asarray(indices, np.int64)
+    bt = np.asarray(block_table, np.int64)
+    T = idx.shape[0]
+    out = np.full(idx.shape, -1, np.int32)
+    qi = None if q_indptr is None else np.asarray(q_indptr, np.int64)
+    for i in range(T):
+        b = i if qi is None else int(np.searchsorted(qi, i, side="right") - 1)
+        for j, s in enumerate(idx[i]):
+            if s >= 0:
+                out[i, j] = bt[b, s // page_size] * page_size + s % page_size
+    return out
 
 
 def index_share(kv_indptr, q_indptr, idx_inputs: dict, layers: list, k: int, sm_scale: float, Dc: int):

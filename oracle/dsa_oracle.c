@@ -138,6 +138,27 @@ static int orc_row_of(int B, const int64_t *kv_indptr, const int32_t *q_indptr, 
     return ORC_BAD_ARG;
 }
 
+/*
+ * Paged caches.  With a block table, token s of sequence b lives in physical
+ * row block_table[b * bt_stride + s / page_size] * page_size + s % page_size
+ * of every per-token cache (index keys and latent KV); kv_indptr then only
+ * gives the context lengths.  Without one (NULL), the row is kv_base + s.
+ */
+typedef struct {
+    const int32_t *block_table;
+    int64_t bt_stride;
+    int64_t page_size;
+    int64_t cache_rows;
+} orc_pages;
+
+static int64_t orc_token_row(const orc_pages *pg, const orc_row *r, int64_t s)
+{
+    if (!pg || !pg->block_table)
+        return r->kv_base + s;
+    return (int64_t)pg->block_table[r->b * pg->bt_stride + s / pg->page_size] * pg->page_size +
+           s % pg->page_size;
+}
+
 /* Visible-token count per query row (exported so tests can check layouts). */
 int orc_visible_counts(int B, const int64_t *kv_indptr, const int32_t *q_indptr, int64_t T,
                        int64_t *n_out)
@@ -164,6 +185,7 @@ int orc_visible_counts(int B, const int64_t *kv_indptr, const int32_t *q_indptr,
  * q is [T][H][D] of q_dt; q_scale is [T][H] (NULL means 1); w is [T][H];
  * key row `row` starts at byte row * k_row_stride_bytes of k and holds D
  * elements of k_dt; its scale is k_scale[row * k_scale_stride] (NULL means 1).
+ * With a block table, key row `row` is the token's physical row (see orc_pages).
  * Scores go to scores[i * ld + s] for s < n_i; other entries are untouched.
  * If mag is not NULL it receives sum_h |w_h| * qs_h * ks_s * sum_d |q_hd k_sd|,
  * the magnitude that bounds the rounding error of any summation order.
@@ -171,10 +193,14 @@ int orc_visible_counts(int B, const int64_t *kv_indptr, const int32_t *q_indptr,
 int orc_index_scores(int B, const int64_t *kv_indptr, const int32_t *q_indptr, int64_t T,
                      int H, int D, int q_dt, const void *q, const float *q_scale, const float *w,
                      int k_dt, const void *k, int64_t k_row_stride_bytes, const float *k_scale,
-                     int64_t k_scale_stride, double *scores, int64_t ld, double *mag)
+                     int64_t k_scale_stride, double *scores, int64_t ld, double *mag,
+                     const int32_t *block_table, int64_t bt_stride, int64_t page_size)
 {
     int64_t i;
     int bad = 0;
+    const orc_pages pg = {block_table, bt_stride, page_size, 0};
+    if (block_table && page_size < 1)
+        return ORC_BAD_ARG;
     if (B <= 0 || T < 0 || H <= 0 || D <= 0 || !elem_size(q_dt) || !elem_size(k_dt) || !q ||
         !w || !k || !scores || !kv_indptr)
         return ORC_BAD_ARG;
@@ -188,7 +214,7 @@ int orc_index_scores(int B, const int64_t *kv_indptr, const int32_t *q_indptr, i
             continue;
         }
         for (s = 0; s < r.n; ++s) {
-            int64_t row = r.kv_base + s;
+            int64_t row = orc_token_row(&pg, &r, s);
             const uint8_t *krow = (const uint8_t *)k + row * k_row_stride_bytes;
             double ks = k_scale ? (double)k_scale[row * k_scale_stride] : 1.0;
             double score = 0.0, m = 0.0;
@@ -292,11 +318,13 @@ int orc_topk(int64_t T, const int64_t *n, const double *scores, int64_t ld, int 
  * first Dc entries: the absorbed form in which the output stays in latent
  * space.  An empty J gives o = 0 and lse = -inf.  q is [T][H][Dc+Dr]; kv is
  * [rows][Dc+Dr]; out is [T][H][Dc]; lse is [T][H] (may be NULL).
+ * physical_rows > 0 means the indices are physical cache rows (paged caches:
+ * each must be < physical_rows); 0 means positions within the sequence.
  */
 int orc_sparse_mla(int B, const int64_t *kv_indptr, const int32_t *q_indptr, int64_t T, int H,
                    int Dc, int Dr, double sm_scale, int q_dt, const void *q, int kv_dt,
                    const void *kv, double kv_scale, const int32_t *indices, int k, double *out,
-                   double *lse)
+                   double *lse, int64_t physical_rows)
 {
     int64_t i;
     int bad = 0;
@@ -327,7 +355,7 @@ int orc_sparse_mla(int B, const int64_t *kv_indptr, const int32_t *q_indptr, int
             int32_t idx = indices[i * k + j];
             if (idx < 0)
                 continue;
-            if ((int64_t)idx >= r.n)
+            if ((int64_t)idx >= (physical_rows > 0 ? physical_rows : r.n))
                 bad |= 2;
             for (j2 = 0; j2 < nj; ++j2)
                 if (J[j2] == idx)
@@ -344,7 +372,7 @@ int orc_sparse_mla(int B, const int64_t *kv_indptr, const int32_t *q_indptr, int
             double m = -INFINITY, l = 0.0;
             double *o = out + (i * H + h) * (int64_t)Dc;
             for (j = 0; j < nj; ++j) {
-                int64_t row = r.kv_base + J[j];
+                int64_t row = physical_rows > 0 ? (int64_t)J[j] : r.kv_base + J[j];
                 double acc = 0.0;
                 for (d = 0; d < Dqk; ++d)
                     acc += load_elem(q_dt, q, qoff + d) *
@@ -356,7 +384,7 @@ int orc_sparse_mla(int B, const int64_t *kv_indptr, const int32_t *q_indptr, int
             for (e = 0; e < Dc; ++e)
                 o[e] = 0.0;
             for (j = 0; j < nj; ++j) {
-                int64_t row = r.kv_base + J[j];
+                int64_t row = physical_rows > 0 ? (int64_t)J[j] : r.kv_base + J[j];
                 double p = exp(z[j] - m);
                 l += p;
                 for (e = 0; e < Dc; ++e)
