@@ -36,7 +36,9 @@ class DsaError(RuntimeError):
 
 class dsa_layout(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("total_q", ctypes.c_int32), ("max_ctx", ctypes.c_int64),
-                ("kv_indptr", ctypes.c_void_p), ("q_indptr", ctypes.c_void_p)]
+                ("kv_indptr", ctypes.c_void_p), ("q_indptr", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("cache_rows", ctypes.c_int64)]
 
 
 class dsa_mla_layer(ctypes.Structure):
@@ -119,19 +121,31 @@ def _stream(stream) -> int:
 
 
 class Layout:
-    """Ragged layout (mirrors dsa_layout); tensors stay referenced while the object lives."""
+    """Ragged layout (mirrors dsa_layout); tensors stay referenced while the object lives.
+
+    Paged caches: block_table int32 [B, pages] of physical page ids, page_size tokens per
+    page, cache_rows rows in every per-token cache; top-k then returns physical rows and
+    sparse MLA reads them."""
 
     def __init__(self, kv_indptr: torch.Tensor, q_indptr: Optional[torch.Tensor], total_q: int,
-                 max_ctx: int):
+                 max_ctx: int, block_table: Optional[torch.Tensor] = None, page_size: int = 0,
+                 cache_rows: int = 0):
         _dev(kv_indptr, "kv_indptr", torch.int64)
         _dev(q_indptr, "q_indptr", torch.int32)
+        _dev(block_table, "block_table", torch.int32)
         self.kv_indptr = kv_indptr
         self.q_indptr = q_indptr
+        self.block_table = block_table
         self.batch = kv_indptr.numel() - 1
         self.total_q = int(total_q)
         self.max_ctx = int(max_ctx)
+        if block_table is not None and (block_table.dim() != 2 or block_table.shape[0] != self.batch):
+            raise ValueError("block_table must be [batch, pages]")
         self.c = dsa_layout(self.batch, self.total_q, self.max_ctx, kv_indptr.data_ptr(),
-                            q_indptr.data_ptr() if q_indptr is not None else None)
+                            q_indptr.data_ptr() if q_indptr is not None else None,
+                            block_table.data_ptr() if block_table is not None else None,
+                            int(block_table.shape[1]) if block_table is not None else 0,
+                            int(page_size), int(cache_rows))
 
     @staticmethod
     def of_case(case) -> "Layout":

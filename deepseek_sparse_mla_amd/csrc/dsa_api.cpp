@@ -76,7 +76,26 @@ dsa_status check_layout(const dsa_layout *L)
     if (L->max_ctx > (int64_t)INT32_MAX)
         return fail(DSA_ERR_UNSUPPORTED, "layout.max_ctx %lld exceeds int32 positions",
                     (long long)L->max_ctx);
+    if (L->block_table) {
+        if (L->page_size < 1)
+            return fail(DSA_ERR_INVALID_ARG, "layout.page_size must be >= 1 with a block table");
+        if ((int64_t)L->block_table_stride < (L->max_ctx + L->page_size - 1) / L->page_size)
+            return fail(DSA_ERR_INVALID_ARG,
+                        "layout.block_table_stride %d < pages of max_ctx (%lld tokens, page %d)",
+                        L->block_table_stride, (long long)L->max_ctx, L->page_size);
+        if (L->cache_rows < 1 || L->cache_rows > (int64_t)INT32_MAX)
+            return fail(DSA_ERR_INVALID_ARG, "layout.cache_rows must be in [1, 2^31) with a block table");
+        if (!aligned(L->block_table, 4))
+            return fail(DSA_ERR_INVALID_ARG, "layout.block_table must be 4-byte aligned");
+    }
     return DSA_OK;
+}
+
+// Paged caches whose page size the tuned kernels take (power of two, at most 4096).
+bool tuned_pages(const dsa_layout *L)
+{
+    const int p = L->page_size;
+    return !L->block_table || (p >= 1 && p <= 4096 && (p & (p - 1)) == 0);
 }
 
 dsa::LayoutDev to_dev(const dsa_layout *L)
@@ -85,6 +104,10 @@ dsa::LayoutDev to_dev(const dsa_layout *L)
     d.kv_indptr = L->kv_indptr;
     d.q_indptr = L->q_indptr;
     d.batch = L->batch;
+    d.block_table = L->block_table;
+    d.bt_stride = L->block_table ? L->block_table_stride : 0;
+    d.page_size = L->block_table ? L->page_size : 1;
+    d.cache_rows = L->block_table ? L->cache_rows : 0;
     return d;
 }
 
@@ -161,9 +184,11 @@ dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_
     }
     if (!aligned(indices, 4))
         return fail(DSA_ERR_INVALID_ARG, "indices must be 4-byte aligned");
-    if (tuned && L->max_ctx * (int64_t)(a.Dc + a.Dr) * elem_size(a.kv_dt) > (int64_t)INT32_MAX)
-        return fail(DSA_ERR_UNSUPPORTED, "max_ctx %lld too long for 32-bit row offsets of the tuned kernel",
-                    (long long)L->max_ctx);
+    const int64_t rows_addressed = L->block_table ? L->cache_rows : L->max_ctx;
+    if (tuned && rows_addressed * (int64_t)(a.Dc + a.Dr) * elem_size(a.kv_dt) > (int64_t)INT32_MAX)
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "%s %lld too long for 32-bit row offsets of the tuned kernel",
+                    L->block_table ? "cache_rows" : "max_ctx", (long long)rows_addressed);
     const int64_t T = L->total_q;
     size_t need = tuned ? dsa::mla_workspace_bytes(T, n_layers, a.k) : 0;
     if (need > 0 && (!workspace || ws_bytes < need))
@@ -282,11 +307,12 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
         return fail(DSA_ERR_INVALID_ARG, "pointer not aligned to its element size");
 
     const bool shape32 = H_I == 32 && D_I == 128 && k_dt == DSA_FP8_E4M3FN && aligned(k, 16) &&
-                         (k_row_stride % 16) == 0 && aligned(q, 16);
+                         (k_row_stride % 16) == 0 && aligned(q, 16) && tuned_pages(layout);
     const bool tuned_decode = shape32 && q_dt == DSA_BF16 && !force_generic();
     // the prefill kernel addresses a sequence's keys with 32-bit buffer offsets
     const bool tuned_fp8 = shape32 && q_dt == DSA_FP8_E4M3FN && !force_generic() &&
-                           layout->max_ctx * k_row_stride < (int64_t)INT32_MAX;
+                           (layout->block_table ? layout->cache_rows : layout->max_ctx) * k_row_stride <
+                               (int64_t)INT32_MAX;
     if (!tuned_decode && !tuned_fp8 && (H_I > 64 || D_I > 256))
         return fail(DSA_ERR_UNSUPPORTED,
                     "indexer shape H_I=%d D_I=%d needs the generic kernel (H_I <= 64, D_I <= 256)",

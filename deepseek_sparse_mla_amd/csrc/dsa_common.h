@@ -20,12 +20,27 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Kernel-side copy of dsa_layout (pointers only; host sizes are launch params).
+// Kernel-side copy of dsa_layout (host sizes other than the paging ones are launch params).
 struct LayoutDev {
     const int64_t *kv_indptr;
     const int32_t *q_indptr;  // nullptr: one query per sequence
     int32_t batch;
+    const int32_t *block_table;  // nullptr: contiguous caches
+    int32_t bt_stride;
+    int32_t page_size;
+    int64_t cache_rows;
 };
+
+// Cache row of token s of sequence b: kv_base + s for contiguous caches, the page table's
+// physical row for paged ones.  With kv_base = 0 on contiguous caches it is the position
+// itself: the form top-k writes (positions, or physical rows when paged).
+__device__ __forceinline__ int64_t token_row(const LayoutDev &L, int b, int64_t kv_base, int64_t s)
+{
+    if (L.block_table == nullptr)
+        return kv_base + s;
+    const int64_t page = s / L.page_size;
+    return (int64_t)L.block_table[(int64_t)b * L.bt_stride + page] * L.page_size + (s - page * L.page_size);
+}
 
 struct RowInfo {
     int32_t b;

@@ -34,12 +34,15 @@ __device__ __forceinline__ float relu(float x)
 // Rows are heads, columns tokens.  The 128-long contraction is split so that lane half g
 // owns dims [64g, 64g+64): MFMA t consumes dims 64g + 8t .. 64g + 8t + 7 of both q and k.
 // ------------------------------------------------------------------------------------------
-// Tokens [s_begin, s_end) of query row i, whose keys start at cache row kv_base.
+// Tokens [s_begin, s_end) of query row i, whose keys start at cache row kv_base; with paged
+// caches (pages != nullptr) token s is instead in row pages[(s >> lg) - p0] << lg | (s & page-1),
+// the segment's block-table entries having been copied to LDS.
 __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ q, const float *__restrict__ w,
                                                    const uint8_t *__restrict__ k, int64_t kstride,
                                                    const float *__restrict__ ks, int64_t ks_stride,
                                                    float *__restrict__ scores, int64_t ld, int64_t i,
-                                                   int64_t kv_base, int64_t s_begin, int64_t s_end)
+                                                   int64_t kv_base, int64_t s_begin, int64_t s_end,
+                                                   const int32_t *pages = nullptr, int lg = 0, int64_t p0 = 0)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform loop bounds
@@ -60,7 +63,9 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     // before the current tile's MFMAs, so every wave keeps a tile in flight.
     auto load_tile = [&](int64_t s0, u32x4 (&kv)[4], float &ksv) {
         const int64_t s = s0 + j;
-        const int64_t row = kv_base + (s < s_end ? s : s_end - 1);
+        const int64_t sc = s < s_end ? s : s_end - 1;
+        const int64_t row = pages ? ((int64_t)pages[(sc >> lg) - p0] << lg) | (sc & ((1 << lg) - 1))
+                                  : kv_base + sc;
         const u32x4 *kp = (const u32x4 *)(k + row * kstride + 64 * g);
         kv[0] = kp[0];
         kv[1] = kp[1];
@@ -109,6 +114,8 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     }
 }
 
+constexpr int IDX_PAGED_CHUNK = 2048;  // longest chunk with paged caches (its page table in LDS)
+
 // Two launch shapes.  Rows that are whole sequences (one query each, as in decode): the grid
 // walks the concatenated token stream of all sequences, an equal share of it per block (a
 // block may finish one sequence and start the next), so no block waits on a longer one.
@@ -124,9 +131,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         const int64_t i = blockIdx.y;
         const RowInfo r = row_info(L, i);
         const int64_t s_begin = (int64_t)blockIdx.x * chunk;
-        if (s_begin < r.n)
-            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin,
-                               min(s_begin + (int64_t)chunk, r.n));
+        if (s_begin >= r.n)
+            return;
+        const int64_t s_end = min(s_begin + (int64_t)chunk, r.n);
+        if (L.block_table == nullptr) {
+            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin, s_end);
+            return;
+        }
+        // paged caches: this chunk's block-table entries to LDS (chunk <= IDX_PAGED_CHUNK)
+        __shared__ int32_t s_pages[IDX_PAGED_CHUNK + 1];
+        const int lg = 31 - __builtin_clz((unsigned)L.page_size);  // power of two (host)
+        const int64_t p0 = s_begin >> lg, p1 = (s_end - 1) >> lg;
+        for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
+            s_pages[p - p0] = L.block_table[(int64_t)r.b * L.bt_stride + p];
+        __syncthreads();
+        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, 0, s_begin, s_end, s_pages, lg, p0);
         return;
     }
     // stream: the grid's blocks split the N cached tokens evenly (N is known only here), in
@@ -173,12 +192,14 @@ constexpr int PF_TILEB = PF_STAGE * PF_ROWB;    // 18432
 constexpr int PF_DMA = PF_TILEB / 1024;         // 36 wave-wide 1 KB loads per tile
 constexpr int PF_DMA_PER_WAVE = (PF_DMA + PF_WAVES - 1) / PF_WAVES;  // 5 (the last only on waves 0-3)
 constexpr int E8M0_ONE = 127;                   // block scale 2^0
+constexpr int PF_MAX_PAGES = 257;               // paged caches: block-table entries of one chunk
 
 __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 &b, const f32x16 &c)
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, E8M0_ONE, 0, E8M0_ONE);
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void idx_fp8_kernel(LayoutDev L, int64_t T, const uint8_t *__restrict__ q,
                                                       const float *__restrict__ qs,
                                                       const float *__restrict__ w,
@@ -190,6 +211,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(4
     __shared__ float kscale[2][PF_STAGE];
     __shared__ int64_t s_meta[PF_QPB][3];  // b, kv_base, n per block query row (b = -1: none)
     __shared__ __attribute__((aligned(16))) float s_wq[PF_QPB][32];  // folded head weights w * qs
+    __shared__ int32_t s_pg[PAGED ? PF_MAX_PAGES : 1];  // paged: the segment's block-table entries
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -233,13 +255,17 @@ __global__ __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(4
 
     // DMA geometry, fixed per lane: load qd of this wave covers tile bytes 1024 (8 qd + wave)
     // + 16 lane, i.e. one row and column (-1: pad columns, or a load past the tile).
+    // (paged caches: toff holds row | col << 16 instead, the row mapped per tile)
     int toff[PF_DMA_PER_WAVE];
 #pragma unroll
     for (int qd = 0; qd < PF_DMA_PER_WAVE; ++qd) {
         const int o = 1024 * (PF_WAVES * qd + wave) + 16 * lane;
         const int row = o / PF_ROWB, col = o - (o / PF_ROWB) * PF_ROWB;
-        toff[qd] = (o < PF_TILEB && col < 128) ? row * (int)kstride + col : -1;
+        const bool real = o < PF_TILEB && col < 128;
+        toff[qd] = !real ? -1 : PAGED ? (row | (col << 16)) : row * (int)kstride + col;
     }
+    constexpr bool paged = PAGED;
+    const int lg = PAGED ? 31 - __builtin_clz((unsigned)L.page_size) : 0;  // power of two (host)
     const uint32_t lds0 = lds_addr_of(&ktile[0][0]);
 
     // Query rows of one block may span several sequences: handle each in turn.
@@ -273,20 +299,44 @@ __global__ __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(4
             continue;
         }
         // the sequence's key rows; offsets past nmax rows read zeros
-        const i32x4 desc = buffer_desc(k + kv_base * kstride, nmax * kstride);
+        // the sequence's key rows (offsets past nmax rows read zeros), or with paged caches
+        // the whole cache, addressed through the segment's block-table entries in LDS
+        const i32x4 desc = paged ? buffer_desc(k, L.cache_rows * kstride)
+                                 : buffer_desc(k + kv_base * kstride, nmax * kstride);
+        const int64_t pg0 = c0 >> lg;
+        if (PAGED) {
+            const int64_t pg1 = (s_end - 1) >> lg;
+            const int64_t b = s_meta[first][0];
+            for (int64_t p = pg0 + tid; p <= pg1; p += 64 * PF_WAVES)
+                s_pg[p - pg0] = L.block_table[b * L.bt_stride + p];
+            __syncthreads();
+        }
+        auto prow = [&](int64_t s) -> int64_t {  // physical row of token s (paged)
+            return ((int64_t)s_pg[(s >> lg) - pg0] << lg) | (s & ((1 << lg) - 1));
+        };
         auto fetch = [&](int64_t st, int buf) {  // DMA of tokens st .. st+255 into ktile[buf]
             const int base = (int)(st * kstride);
 #pragma unroll
             for (int qd = 0; qd < PF_DMA_PER_WAVE; ++qd) {
                 const int u = PF_WAVES * qd + wave;
+                int off = (int)0x80000000;
+                if (toff[qd] >= 0) {
+                    if (PAGED) {
+                        const int64_t s = st + (toff[qd] & 0xffff);  // the table covers tokens < s_end
+                        off = s < s_end ? (int)(prow(s) * kstride) + (toff[qd] >> 16) : (int)0x80000000;
+                    } else {
+                        off = base + toff[qd];
+                    }
+                }
                 if (qd + 1 < PF_DMA_PER_WAVE || u < PF_DMA)
-                    dma16(desc, lds0 + (uint32_t)(buf * PF_TILEB + 1024 * u),
-                          toff[qd] >= 0 ? base + toff[qd] : (int)0x80000000);
+                    dma16(desc, lds0 + (uint32_t)(buf * PF_TILEB + 1024 * u), off);
             }
         };
         auto fetch_scale = [&](int64_t st) -> float {
             const int64_t s = st + tid;
-            return (tid < PF_STAGE && s < nmax) ? ks[(kv_base + s) * ks_stride] : 0.f;
+            if (tid >= PF_STAGE || s >= (PAGED ? s_end : nmax))
+                return 0.f;
+            return ks[(PAGED ? prow(s) : kv_base + s) * ks_stride];
         };
 
         fetch(c0, 0);
@@ -376,7 +426,7 @@ __global__ __launch_bounds__(256) void idx_generic_kernel(LayoutDev L, int H, in
     const int64_t s = sblk + threadIdx.x;
     if (s >= r.n)
         return;
-    const int64_t row = r.kv_base + s;
+    const int64_t row = token_row(L, r.b, r.kv_base, s);
     const uint8_t *krow = k + row * kstride;
     float acc = 0.f;
     for (int h = 0; h < H; ++h) {
@@ -410,8 +460,11 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
         if (c >= 128 && c <= 8192 && (c & (c - 1)) == 0)
             chunk = c;
     }
+    if (L.block_table && chunk > IDX_PAGED_CHUNK)
+        chunk = IDX_PAGED_CHUNK;
     const int64_t nchunks = (max_ctx + chunk - 1) / chunk;
-    const bool as_stream = L.q_indptr == nullptr;  // rows are whole sequences
+    // rows are whole sequences (and their keys contiguous: paged caches take the other grid)
+    const bool as_stream = L.q_indptr == nullptr && L.block_table == nullptr;
     // stream: two blocks per CU for long streams (one round; four per CU measured no
     // better), fewer blocks (at least 256 tokens each) for short ones; the kernel divides
     // the actual token count
@@ -443,9 +496,16 @@ hipError_t launch_index_fp8(const LayoutDev &L, int64_t T, int64_t max_ctx, cons
         if (c >= PF_STAGE && c <= 8192 && (c & (c - 1)) == 0)
             chunk = c;
     }
+    if (L.block_table)  // the chunk's block-table entries must fit the LDS table
+        while (chunk > PF_STAGE && (int64_t)chunk > (int64_t)(PF_MAX_PAGES - 1) * L.page_size)
+            chunk >>= 1;
     dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)qblocks);
-    hipLaunchKernelGGL(idx_fp8_kernel, grid, dim3(64 * PF_WAVES), 0, stream, L, T, (const uint8_t *)q, qs, w,
-                       (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
+    if (L.block_table)
+        hipLaunchKernelGGL(idx_fp8_kernel<true>, grid, dim3(64 * PF_WAVES), 0, stream, L, T, (const uint8_t *)q, qs, w,
+                           (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
+    else
+        hipLaunchKernelGGL(idx_fp8_kernel<false>, grid, dim3(64 * PF_WAVES), 0, stream, L, T, (const uint8_t *)q, qs, w,
+                           (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
     return hipGetLastError();
 }
 

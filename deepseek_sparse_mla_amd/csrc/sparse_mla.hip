@@ -297,9 +297,12 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
 
     StageRegs<KV_FP8> R;
     constexpr int64_t ROWB = KV_FP8 ? 576 : 1152;
-    const int64_t seq_bytes = r.n * ROWB;  // host guarantees max_ctx * ROWB < 2^31
+    // indices address the sequence's rows, or with paged caches the whole cache (physical
+    // rows); the host guarantees the range stays under 2^31 bytes
+    const bool paged = L.block_table != nullptr;
+    const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * ROWB;
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint8_t *)Ld.kv + r.kv_base * ROWB), (short)0, (int)seq_bytes, BUF_DWORD3);
+        (void *)((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * ROWB), (short)0, (int)seq_bytes, BUF_DWORD3);
 
     // Pass 0 fixes each head's reference max at its first non-empty tile.  If a later
     // tile exceeds it by more than 2^100 (p would approach the fp32 range) the split is
@@ -661,8 +664,10 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     for (int mt = 0; mt < 8; ++mt)
         O[mt] = f32x16{};
 
-    const int64_t seq_bytes = r.n * 576;  // host guarantees max_ctx * 576 < 2^31
-    const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + r.kv_base * 576, seq_bytes);  // this sequence's rows
+    // this sequence's rows, or with paged caches the whole cache (host: under 2^31 bytes)
+    const bool paged = L.block_table != nullptr;
+    const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * 576;
+    const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * 576, seq_bytes);
     const uint32_t lds0 = lds_addr_of(&kt8[0][0]);
     uint32_t rc[F_DMA_PER_WAVE];
     dma_geometry(w, lane, rc);
@@ -938,9 +943,12 @@ __global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int mt = 0; mt < 4; ++mt)
         O[mt] = f32x16{};
 
-    const int64_t seq_bytes = r.n * (2 * M_DQK);  // host guarantees max_ctx * 1152 < 2^31
+    // this sequence's rows, or with paged caches the whole cache (host: under 2^31 bytes)
+    const bool paged = L.block_table != nullptr;
+    const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * (2 * M_DQK);
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint8_t *)Ld.kv + r.kv_base * (2 * M_DQK)), (short)0, (int)seq_bytes, BUF_DWORD3);
+        (void *)((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * (2 * M_DQK)), (short)0, (int)seq_bytes,
+        BUF_DWORD3);
     u32x4 R[HH_N];
     // thread t stages tile row t >> 3, 16-byte pieces (t & 7) + 8 u (u < 9): one index per
     // thread and tile, and every load instruction reads whole 128-byte lines of 8 rows
@@ -1267,7 +1275,7 @@ __global__ __launch_bounds__(G_THREADS) void mla_generic_kernel(LayoutDev L, int
         const int32_t idx = indices[i * k + jj];
         float zz = -INFINITY;
         if (idx >= 0) {
-            const int64_t row = (r.kv_base + idx) * Dqk;
+            const int64_t row = ((L.block_table ? 0 : r.kv_base) + idx) * Dqk;  // physical when paged
             float acc = 0.f;
             for (int d = 0; d < Dqk; ++d)
                 acc = fmaf(sq[d], load_elem<KVDT>(Ld.kv, row + d), acc);
@@ -1303,7 +1311,7 @@ __global__ __launch_bounds__(G_THREADS) void mla_generic_kernel(LayoutDev L, int
         for (int jj = 0; jj < k; ++jj) {
             const int32_t idx = indices[i * k + jj];
             if (idx >= 0)
-                acc = fmaf(z[jj], load_elem<KVDT>(Ld.kv, (r.kv_base + idx) * Dqk + e), acc);
+                acc = fmaf(z[jj], load_elem<KVDT>(Ld.kv, ((L.block_table ? 0 : r.kv_base) + idx) * Dqk + e), acc);
         }
         const float o = acc * inv;
         const int64_t oo = ((int64_t)i * H + h) * Dc + e;

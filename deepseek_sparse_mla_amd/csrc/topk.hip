@@ -732,7 +732,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if ((m >> e) & 1u)
-                orow[slot++] = pos(q, e);
+                orow[slot++] = (int32_t)token_row(L, r.b, 0, pos(q, e));  // position, or physical row
     }
     for (int t = (int)kk + tid; t < k; t += TK_THREADS)
         orow[t] = -1;
@@ -940,8 +940,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
         }
     }
     __syncthreads();
-    for (int t = tid; t < k; t += TK_THREADS)
-        orow[t] = (uint32_t)t < kk ? (int32_t)slots[t] : -1;
+    for (int t = tid; t < k; t += TK_THREADS)  // positions, or physical rows (paged caches)
+        orow[t] = (uint32_t)t < kk ? (int32_t)token_row(L, r.b, 0, (int64_t)slots[t]) : -1;
 }
 
 // ------------------------------------------------------------------------------------------

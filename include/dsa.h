@@ -18,7 +18,8 @@
  * Citations are to the reference pages by title and section:
  *   [anatomy]  "GLM-5.2 架构解剖" (GLM-5.2 anatomy);
  *   [guide]    "ATOM Model Support Guide";
- *   [pr2980]   ATOM pull request #2980 (FP8 weight planes in mono decode).
+ *   [pr2980]   ATOM pull request #2980 (FP8 weight planes in mono decode);
+ *   [serving]  the ATOM serving and benchmarking guide.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -40,7 +41,8 @@
  *   kv_indptr / q_indptr are non-decreasing, every context is >= 1 and
  *   <= max_ctx, q_len_b <= ctx_b; scales are finite and > 0; no fp8 NaN
  *   codes (0x7F, 0xFF); the indices given to sparse MLA were produced for the
- *   same layout (unique, < n_i, or -1).
+ *   same layout (unique, < n_i, or -1; physical rows < cache_rows when
+ *   paged); block-table entries address pages inside the caches.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 /* Largest k accepted by dsa_topk and the sparse MLA entry points. */
 #define DSA_TOPK_MAX 2048
@@ -76,12 +78,23 @@ typedef enum {
  * Ragged batch layout, shared by every call ([guide], DeepSeek V2/V3: MLA
  * attention metadata is tracked with kv_indptr).
  *
- * Sequence b owns cache rows kv_indptr[b] .. kv_indptr[b+1]-1 (ctx_b rows) in
- * every per-token cache (index keys and each layer's latent KV) and query
- * rows q_indptr[b] .. q_indptr[b+1]-1 (q_len_b rows).  Query j of sequence b
- * sits at position p = ctx_b - q_len_b + j and sees the causal prefix
- * 0 .. p, i.e. n = p + 1 tokens.  q_indptr == NULL means one query per
+ * Sequence b has ctx_b = kv_indptr[b+1] - kv_indptr[b] cached tokens and
+ * query rows q_indptr[b] .. q_indptr[b+1]-1 (q_len_b rows).  Query j of
+ * sequence b sits at position p = ctx_b - q_len_b + j and sees the causal
+ * prefix 0 .. p, i.e. n = p + 1 tokens.  q_indptr == NULL means one query per
  * sequence (decode): T = B and n = ctx_b.
+ *
+ * Where a token's row is.  Contiguous caches (block_table == NULL): token s of
+ * sequence b is row kv_indptr[b] + s of every per-token cache (index keys and
+ * each layer's latent KV).  Paged caches ([serving], server options: the KV
+ * cache is kept in blocks, 16 tokens by default; [anatomy], verified
+ * deployments, note on the SGLang plugin path: full layers write a shared
+ * buffer of physical indices that shared layers read): token s of sequence b
+ * is row
+ *     block_table[b * block_table_stride + s / page_size] * page_size + s % page_size
+ * of every per-token cache, and top-k indices and sparse-MLA indices are such
+ * physical rows instead of positions.  The tuned kernels take power-of-two
+ * page sizes up to 4096; other page sizes run the generic kernels.
  */
 typedef struct {
     int32_t batch;             /* B >= 1                                      */
@@ -89,6 +102,12 @@ typedef struct {
     int64_t max_ctx;           /* host upper bound of every ctx_b (>= 1)      */
     const int64_t *kv_indptr;  /* device [B+1]                                */
     const int32_t *q_indptr;   /* device [B+1], or NULL for decode            */
+    const int32_t *block_table;   /* device [B][block_table_stride] page ids, or
+                                     NULL for contiguous caches               */
+    int32_t block_table_stride;   /* >= ceil(max_ctx / page_size) when paged  */
+    int32_t page_size;            /* tokens per page (>= 1) when paged        */
+    int64_t cache_rows;           /* rows of every per-token cache when paged
+                                     (bounds the physical rows; > 0)          */
 } dsa_layout;
 
 /*
@@ -208,8 +227,9 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
  * indices[i * k .. i * k + k - 1] in ascending position order (the attention
  * over them does not depend on the order; the pages fix the set, not its
  * listing), then -1 in the remaining slots.  Positions are logical (0 ..
- * ctx_b - 1 within the sequence).  1 <= k <= DSA_TOPK_MAX.  NaN scores are
- * outside the contract.
+ * ctx_b - 1 within the sequence), or with paged caches the tokens' physical
+ * rows (see dsa_layout).  1 <= k <= DSA_TOPK_MAX.  NaN scores are outside the
+ * contract.
  *   workspace     device scratch of dsa_topk_workspace_size() bytes, needed
  *                 when max_ctx exceeds what one block holds in LDS (8192): a
  *                 score histogram per row and, for up to 512 long rows, each
@@ -233,6 +253,7 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
  * non-negative entries of indices[i * k .. i * k + k - 1]:
  *
  *   z_j   = sm_scale * kv_scale * (q[i,h,:] . c[kv_indptr[b] + J_j, :])
+ *           (c[J_j, :] with paged caches: J_j is then a physical row)
  *   o     = sum_j softmax(z)_j * kv_scale * c[kv_indptr[b] + J_j, 0:D_c]
  *   lse   = log sum_j exp(z_j)          (o = 0, lse = -inf when J is empty)
  *
@@ -250,7 +271,8 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
  *                 split partials of the index list; none is needed when one
  *                 block covers a whole row).  No initial contents are needed.
  *                 Calls that overlap in time must not share a workspace.
- * The tuned kernel needs max_ctx * (D_c + D_r) * element size < 2^31.
+ * The tuned kernel needs max_ctx * (D_c + D_r) * element size < 2^31
+ * (cache_rows * (D_c + D_r) * element size with paged caches).
  * The decode entry accepts any layout; prefill is the same computation with
  * a launch shape suited to many query rows per sequence.
  */

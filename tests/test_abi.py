@@ -35,11 +35,11 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
 
 
-def _layout(batch=2, total_q=2, max_ctx=4096, kv=FAKE, qi=None):
-    return B.dsa_layout(batch, total_q, max_ctx, kv, qi)
+def _layout(batch=2, total_q=2, max_ctx=4096, kv=FAKE, qi=None, bt=None, bt_stride=0, page=0, rows=0):
+    return B.dsa_layout(batch, total_q, max_ctx, kv, qi, bt, bt_stride, page, rows)
 
 
 def _idx(lib, layout, **kw):
@@ -234,3 +234,15 @@ def test_index_front_end_rejects(lib):
     assert fe(cs=FAKE, rr=4) == B.DSA_ERR_INVALID_ARG             # rope without positions
     assert fe(crows=-1) == B.DSA_ERR_INVALID_ARG
     assert fe(T=0, q=None, k=None, slots=None, cache=None, cscale=None, q8=None, qsc=None) == B.DSA_OK
+
+
+def test_paged_layout_rejects(lib):
+    """A block table needs a page size, enough pages per row for max_ctx and a cache size."""
+    ok = dict(bt=FAKE, bt_stride=64, page=64, rows=1 << 20)  # never passed whole: it would launch
+    for bad in (dict(page=0), dict(bt_stride=63), dict(rows=0), dict(bt=FAKE + 2)):
+        kw = dict(ok)
+        kw.update(bad)
+        assert _idx(lib, _layout(**kw)) == B.DSA_ERR_INVALID_ARG, bad
+        assert lib.dsa_last_error()
+    L = ctypes.byref(_layout(**ok))
+    assert lib.dsa_topk(L, FAKE, 4096, 0, FAKE, None, 0, None) == B.DSA_ERR_INVALID_ARG  # k still checked

@@ -1,0 +1,161 @@
+"""Paged caches on the GPU (through the C ABI).
+
+Every per-token cache of a case (index keys, key scales, each layer's latent rows) is
+scattered page by page over a larger pool in a shuffled order, the rest of the pool filled
+with unrelated values, and the path is run on the paged layout.  Each token's bytes and the
+order of every reduction are unchanged, so the results must equal the contiguous run's bit
+for bit: the same scores, the top-k's positions mapped through the block table, the same
+attention outputs.  A small case is also checked against the oracle's paged layout.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_testlib as tl
+import deepseek_sparse_mla_amd as dsa
+import oracle
+from deepseek_sparse_mla_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def paged(case, page, seed=0):
+    """(layout, caches) of the case's caches scattered over shuffled pages of a pool."""
+    ctx = [int(c) for c in (case.kv_indptr[1:] - case.kv_indptr[:-1]).cpu()]
+    npages = [-(-c // page) for c in ctx]
+    total = sum(npages) + 5
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(total, generator=g)
+    width = max(max(npages), -(-case.max_ctx // page))
+    bt = torch.zeros((len(ctx), width), dtype=torch.int32)
+    src, dst = [], []
+    k0 = 0
+    kvp = case.kv_indptr.cpu()
+    for b, c in enumerate(ctx):
+        bt[b, :npages[b]] = perm[k0:k0 + npages[b]].to(torch.int32)
+        k0 += npages[b]
+        s = torch.arange(c)
+        src.append(int(kvp[b]) + s)
+        dst.append(bt[b, s // page].to(torch.int64) * page + s % page)
+    src, dst = torch.cat(src).to(DEV), torch.cat(dst).to(DEV)
+    rows = total * page
+
+    def scatter(x):
+        pool = torch.empty((rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=DEV)
+        if x.dtype == torch.uint8:
+            pool.copy_(torch.randint(0, 120, pool.shape, generator=torch.Generator(device=DEV).manual_seed(seed + 1),
+                                     device=DEV, dtype=torch.uint8))
+        else:
+            pool.copy_(torch.randn(pool.shape, generator=torch.Generator(device=DEV).manual_seed(seed + 2),
+                                   device=DEV).to(x.dtype).abs() + 0.5)
+        pool[dst] = x[src]
+        return pool
+
+    lay = dsa.Layout(case.kv_indptr, case.q_indptr, case.T, case.max_ctx, block_table=bt.to(DEV),
+                     page_size=page, cache_rows=rows)
+    caches = dict(ik=scatter(case.ik), ik_scale=scatter(case.ik_scale) if case.ik_scale is not None else None,
+                  kv=[scatter(L.kv) for L in case.layers])
+    return lay, caches, bt
+
+
+def run_path(case, layout, ik, ik_scale, kvs):
+    c = case
+    scores = torch.full((c.T, c.max_ctx), 7.0, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(layout, c.iq, c.iw, ik, k_scale=ik_scale, q_scale=c.iq_scale, scores=scores)
+    idx = dsa.dsa_topk(layout, scores, c.topk)
+    if len(c.layers) == 1:
+        L = c.layers[0]
+        fn = dsa.sparse_mla_prefill if c.q_indptr is not None else dsa.sparse_mla_decode
+        lse = torch.empty((c.T, c.H), dtype=torch.float32, device=DEV)
+        outs, lses = [fn(layout, L.q, kvs[0], idx, c.sm_scale, c.Dc, L.kv_scale, lse=lse)], [lse]
+    else:
+        lses = [torch.empty((c.T, c.H), dtype=torch.float32, device=DEV) for _ in c.layers]
+        outs = dsa.sparse_mla_decode_shared(layout, [L.q for L in c.layers], kvs, [L.kv_scale for L in c.layers],
+                                            idx, c.sm_scale, c.Dc, lses=lses)
+    torch.cuda.synchronize()
+    return scores, idx, outs, lses
+
+
+def check_equal(case, page, bt, contig, pg):
+    s_c, i_c, o_c, l_c = contig
+    s_p, i_p, o_p, l_p = pg
+    n = tl.visible(case)
+    sc, sp = s_c.cpu().numpy(), s_p.cpu().numpy()
+    for r in range(case.T):
+        assert np.array_equal(sc[r, :n[r]], sp[r, :n[r]]), "scores row %d" % r
+    mapped = oracle.to_physical(case.kv_indptr.cpu().numpy(), None if case.q_indptr is None
+                                else case.q_indptr.cpu().numpy(), i_c.cpu().numpy(), bt.numpy(), page)
+    assert np.array_equal(i_p.cpu().numpy(), mapped)
+    for a, b in zip(o_c + l_c, o_p + l_p):
+        assert torch.equal(a, b)
+
+
+CASES = {
+    "decode_bf16_page16": (dict(ctx=[3000, 8192, 5000, 700], kv_dt="bf16"), 16),
+    "decode_bf16_page64": (dict(ctx=[3000, 8192, 5000, 700], kv_dt="bf16"), 64),
+    "decode_fp8_long_rows_page64": (dict(ctx=[4096, 5000, 2049, 40000], kv_dt="fp8"), 64),
+    "shared_fp8_page32": (dict(ctx=[3000, 2100, 6000], kv_dt="fp8", n_layers=2), 32),
+    "prefill_page16": (dict(ctx=[5000, 3000], q_len=[300, 200], iq_dt="fp8", kv_dt="bf16"), 16),
+    "decode_page1": (dict(ctx=[700, 2500], kv_dt="bf16"), 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_paged_equals_contiguous(name):
+    kw, page = CASES[name]
+    case = synth.make_case(name, 2, sm_scale=1.0 / 16, device=DEV, **kw)
+    contig = run_path(case, dsa.Layout.of_case(case), case.ik, case.ik_scale, [L.kv for L in case.layers])
+    lay, caches, bt = paged(case, page, seed=len(name))
+    pg = run_path(case, lay, caches["ik"], caches["ik_scale"], caches["kv"])
+    check_equal(case, page, bt, contig, pg)
+
+
+def test_paged_generic_kernels_equal_contiguous():
+    """A page size that is not a power of two runs the generic indexer; the generic MLA is
+    forced for both runs; results still equal the contiguous ones bit for bit."""
+    case = synth.make_case("generic_paged", 2, ctx=[1000, 2300], kv_dt="bf16", sm_scale=1.0 / 16, device=DEV)
+    os.environ["DSA_KERNEL_VARIANT"] = "generic"
+    try:
+        contig = run_path(case, dsa.Layout.of_case(case), case.ik, case.ik_scale, [L.kv for L in case.layers])
+        lay, caches, bt = paged(case, 24, seed=5)
+        pg = run_path(case, lay, caches["ik"], caches["ik_scale"], caches["kv"])
+    finally:
+        del os.environ["DSA_KERNEL_VARIANT"]
+    check_equal(case, 24, bt, contig, pg)
+    # page 24 with the tuned MLA (only the indexer is generic then)
+    lay, caches, bt = paged(case, 24, seed=6)
+    pg = run_path(case, lay, caches["ik"], caches["ik_scale"], caches["kv"])
+    contig = run_path(case, dsa.Layout.of_case(case), case.ik, case.ik_scale, [L.kv for L in case.layers])
+    mapped = oracle.to_physical(case.kv_indptr.cpu().numpy(), None, contig[1].cpu().numpy(), bt.numpy(), 24)
+    assert np.array_equal(pg[1].cpu().numpy(), mapped)
+    assert torch.equal(pg[2][0], contig[2][0])
+
+
+def test_paged_small_case_against_the_oracle():
+    """Scores, selection and attention of a paged decode against the oracle's paged layout."""
+    case = synth.make_case("paged_oracle", 2, ctx=[900, 2100, 2049], kv_dt="fp8", sm_scale=1.0 / 16, device=DEV)
+    page = 32
+    lay, caches, bt = paged(case, page, seed=9)
+    s, idx, outs, _ = run_path(case, lay, caches["ik"], caches["ik_scale"], caches["kv"])
+    kvp = case.kv_indptr.cpu().numpy()
+    o_s = oracle.index_scores(kvp, None, synth.host(case.iq), synth.host(case.iw), synth.host(caches["ik"]),
+                              k_scale=synth.host(caches["ik_scale"]), ld=case.max_ctx, block_table=bt.numpy(),
+                              page_size=page)
+    n = tl.visible(case)
+    s_host = s.cpu().numpy()
+    i_host = idx.cpu().numpy()
+    for r in range(case.T):
+        tl.check_scores(s_host[r, :n[r]], o_s[r, :n[r]], "paged row %d" % r)
+    # selection: the GPU's positions (mapped) equal the oracle's top-k of the GPU's own scores
+    o_idx = oracle.topk(s_host.astype(np.float64), n, case.topk)
+    mapped = oracle.to_physical(kvp, None, o_idx, bt.numpy(), page)
+    for r in range(case.T):
+        assert np.array_equal(np.sort(i_host[r][i_host[r] >= 0]), np.sort(mapped[r][mapped[r] >= 0]))
+    L = case.layers[0]
+    o_o, _ = oracle.sparse_mla(kvp, None, synth.host(L.q), synth.host(caches["kv"][0]), i_host, case.sm_scale,
+                               case.Dc, L.kv_scale, physical=True)
+    tl.check_attention(tl.to_f64(outs[0]), o_o, tl.ATTN_ATOL_LOWP, "paged attention")
