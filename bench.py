@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="HBM bytes per stage call from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     p.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (MiB)")
+    p.add_argument("--paged", type=int, default=0, metavar="PAGE",
+                   help="run on paged caches: every cache scattered over shuffled pages of PAGE tokens")
     p.add_argument("--graph", action="store_true",
                    help="capture each input set's step once as a HIP graph and time graph replays")
     return p.parse_args()
@@ -105,15 +107,52 @@ def case_bytes(case):
     return tot
 
 
+def paged_caches(case, page, seed=0):
+    """The case's per-token caches scattered page by page over a pool in a shuffled order,
+    with the matching block table: (layout, index keys, key scales, latent caches)."""
+    import torch
+    import deepseek_sparse_mla_amd as dsa
+    dev = case.iq.device
+    kvp = case.kv_indptr.cpu()
+    ctx = [int(x) for x in (kvp[1:] - kvp[:-1])]
+    npages = [-(-c // page) for c in ctx]
+    total = sum(npages)
+    perm = torch.randperm(total, generator=torch.Generator().manual_seed(seed))
+    width = max(max(npages), -(-case.max_ctx // page))
+    bt = torch.zeros((len(ctx), width), dtype=torch.int32)
+    k0 = 0
+    for b, n in enumerate(npages):
+        bt[b, :n] = perm[k0:k0 + n].to(torch.int32)
+        k0 += n
+    # physical row of every cached token, in kv_indptr order
+    b_of = torch.repeat_interleave(torch.arange(len(ctx)), torch.tensor(ctx))
+    s_of = torch.arange(int(kvp[-1])) - kvp[:-1][b_of]
+    dst = (bt[b_of, s_of // page].to(torch.int64) * page + s_of % page).to(dev)
+    rows = total * page
+
+    def scatter(x):
+        pool = torch.zeros((rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+        pool[dst] = x
+        return pool
+
+    lay = dsa.Layout(case.kv_indptr, case.q_indptr, case.T, case.max_ctx, block_table=bt.to(dev),
+                     page_size=page, cache_rows=rows)
+    return (lay, scatter(case.ik), scatter(case.ik_scale) if case.ik_scale is not None else None,
+            [scatter(L.kv) for L in case.layers])
+
+
 class Runner:
     """Buffers and calls of one input set (all allocations happen before timing)."""
 
-    def __init__(self, case):
+    def __init__(self, case, paged=None):
         import torch
         import deepseek_sparse_mla_amd as dsa
         self.dsa = dsa
         self.case = case
         self.layout = dsa.Layout.of_case(case)
+        self.ik, self.ik_scale, self.kvs = case.ik, case.ik_scale, [L.kv for L in case.layers]
+        if paged:
+            self.layout, self.ik, self.ik_scale, self.kvs = paged
         dev = case.iq.device
         self.ld = case.max_ctx
         self.scores = torch.empty((case.T, self.ld), dtype=torch.float32, device=dev)
@@ -126,7 +165,7 @@ class Runner:
 
     def indexer(self):
         c = self.case
-        self.dsa.dsa_index_scores(self.layout, c.iq, c.iw, c.ik, k_scale=c.ik_scale, q_scale=c.iq_scale,
+        self.dsa.dsa_index_scores(self.layout, c.iq, c.iw, self.ik, k_scale=self.ik_scale, q_scale=c.iq_scale,
                                   scores=self.scores)
 
     def topk(self):
@@ -137,10 +176,10 @@ class Runner:
         if len(c.layers) == 1:
             L = c.layers[0]
             fn = self.dsa.sparse_mla_prefill if self.prefill else self.dsa.sparse_mla_decode
-            fn(self.layout, L.q, L.kv, self.idx, c.sm_scale, c.Dc, L.kv_scale, out=self.outs[0],
+            fn(self.layout, L.q, self.kvs[0], self.idx, c.sm_scale, c.Dc, L.kv_scale, out=self.outs[0],
                workspace=self.ws)
         else:
-            self.dsa.sparse_mla_decode_shared(self.layout, [L.q for L in c.layers], [L.kv for L in c.layers],
+            self.dsa.sparse_mla_decode_shared(self.layout, [L.q for L in c.layers], self.kvs,
                                               [L.kv_scale for L in c.layers], self.idx, c.sm_scale, c.Dc,
                                               outs=self.outs, workspace=self.ws)
 
@@ -433,7 +472,8 @@ def main():
     per_set = case_bytes(probe)
     nsets = args.sets or max(1, min(16, math.ceil(1.2e9 / per_set)))
     cases = [probe] + (make_sets(cfg, nsets, dev)[1:] if nsets > 1 else [])
-    runners = [Runner(c) for c in cases]
+    runners = [Runner(c, paged_caches(c, args.paged, seed=j) if args.paged else None)
+               for j, c in enumerate(cases)]
     model = algorithmic_model(probe)
     torch.cuda.synchronize()
 
@@ -528,7 +568,9 @@ def main():
                    "index_heads": probe.H_I, "index_dim": probe.D_I, "topk": probe.topk, "mla_heads": probe.H,
                    "latent": probe.Dc, "rope": probe.Dr, "kv_cache": probe.layers[0].kv_dt,
                    "layers": len(probe.layers), "input_sets_rotated": nsets,
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": "hip graph replay" if args.graph else "eager",
+                   "caches": "paged, %d tokens per page, shuffled pages" % args.paged if args.paged
+                   else "contiguous"},
         "path_hbm": {"algorithmic_bytes": model["path_bytes"], "achieved_GBps": round(path_gbs, 1),
                      "frac_of_peak": round(path_gbs / HBM_PEAK_GBS, 4)},
         "kernels_ms": {kernel_names[s]: round(dur[s], 5) for s in stages},

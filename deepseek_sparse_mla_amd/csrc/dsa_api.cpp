@@ -170,7 +170,13 @@ dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_
         return fail(DSA_ERR_INVALID_ARG, "n_layers=%d outside [1, %d]", n_layers, DSA_MAX_SHARED_LAYERS);
     if (!layers)
         return fail(DSA_ERR_INVALID_ARG, "layers is NULL");
-    const bool tuned = mla_tuned_shape(a) && !force_generic();
+    // the tuned kernels address one sequence's rows (or, paged, the whole cache) with unsigned
+    // 32-bit buffer offsets, keeping the top 1 MiB for the "no row" offset; larger ranges run
+    // the generic kernel
+    const int64_t rows_addressed = L->block_table ? L->cache_rows : L->max_ctx;
+    const bool fits32 = rows_addressed * (int64_t)(a.Dc + a.Dr) * elem_size(a.kv_dt) <=
+                        ((int64_t)1 << 32) - (1 << 20);
+    const bool tuned = mla_tuned_shape(a) && !force_generic() && fits32;
     if (!tuned) {
         if (a.H > 128 || a.Dc > 512 || a.Dc + a.Dr > 1024)
             return fail(DSA_ERR_UNSUPPORTED,
@@ -184,11 +190,6 @@ dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_
     }
     if (!aligned(indices, 4))
         return fail(DSA_ERR_INVALID_ARG, "indices must be 4-byte aligned");
-    const int64_t rows_addressed = L->block_table ? L->cache_rows : L->max_ctx;
-    if (tuned && rows_addressed * (int64_t)(a.Dc + a.Dr) * elem_size(a.kv_dt) > (int64_t)INT32_MAX)
-        return fail(DSA_ERR_UNSUPPORTED,
-                    "%s %lld too long for 32-bit row offsets of the tuned kernel",
-                    L->block_table ? "cache_rows" : "max_ctx", (long long)rows_addressed);
     const int64_t T = L->total_q;
     size_t need = tuned ? dsa::mla_workspace_bytes(T, n_layers, a.k) : 0;
     if (need > 0 && (!workspace || ws_bytes < need))

@@ -120,6 +120,7 @@ constexpr int IDX_PAGED_CHUNK = 2048;  // longest chunk with paged caches (its p
 // walks the concatenated token stream of all sequences, an equal share of it per block (a
 // block may finish one sequence and start the next), so no block waits on a longer one.
 // Otherwise: one block per (chunk, query row).
+template <bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
                                                          const float *__restrict__ w,
                                                          const uint8_t *__restrict__ k, int64_t kstride,
@@ -127,6 +128,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                                                          float *__restrict__ scores, int64_t ld, int chunk,
                                                          int stream)
 {
+    __shared__ int32_t s_pages[PAGED ? IDX_PAGED_CHUNK + 1 : 1];  // paged: a segment's table entries
+    const int lg = PAGED ? 31 - __builtin_clz((unsigned)L.page_size) : 0;  // power of two (host)
     if (!stream) {
         const int64_t i = blockIdx.y;
         const RowInfo r = row_info(L, i);
@@ -134,13 +137,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         if (s_begin >= r.n)
             return;
         const int64_t s_end = min(s_begin + (int64_t)chunk, r.n);
-        if (L.block_table == nullptr) {
+        if (!PAGED) {
             idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin, s_end);
             return;
         }
         // paged caches: this chunk's block-table entries to LDS (chunk <= IDX_PAGED_CHUNK)
-        __shared__ int32_t s_pages[IDX_PAGED_CHUNK + 1];
-        const int lg = 31 - __builtin_clz((unsigned)L.page_size);  // power of two (host)
         const int64_t p0 = s_begin >> lg, p1 = (s_end - 1) >> lg;
         for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
             s_pages[p - p0] = L.block_table[(int64_t)r.b * L.bt_stride + p];
@@ -169,8 +170,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         if (rb >= t1)
             break;
         const int64_t sb = max(t0, rb), se = min(t1, re);
-        if (se > sb)
+        if (se <= sb)
+            continue;
+        if (!PAGED) {
             idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, rb, sb - rb, se - rb);
+            continue;
+        }
+        // paged caches: the segment's block-table entries to LDS (a share is at most
+        // IDX_PAGED_CHUNK tokens), after every wave is done with the previous segment's
+        const int64_t s0 = sb - rb, s1 = se - rb, p0 = s0 >> lg, p1 = (s1 - 1) >> lg;
+        __syncthreads();
+        for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
+            s_pages[p - p0] = L.block_table[(int64_t)b * L.bt_stride + p];
+        __syncthreads();
+        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, 0, s0, s1, s_pages, lg, p0);
     }
 }
 
@@ -463,8 +476,7 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
     if (L.block_table && chunk > IDX_PAGED_CHUNK)
         chunk = IDX_PAGED_CHUNK;
     const int64_t nchunks = (max_ctx + chunk - 1) / chunk;
-    // rows are whole sequences (and their keys contiguous: paged caches take the other grid)
-    const bool as_stream = L.q_indptr == nullptr && L.block_table == nullptr;
+    const bool as_stream = L.q_indptr == nullptr;  // rows are whole sequences
     // stream: two blocks per CU for long streams (one round; four per CU measured no
     // better), fewer blocks (at least 256 tokens each) for short ones; the kernel divides
     // the actual token count
@@ -474,9 +486,15 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
         if (nb >= 1 && nb <= 65536)
             sblocks = min((int64_t)nb, T * max_ctx);
     }
+    if (L.block_table)  // a block's share must fit its LDS table of pages
+        sblocks = max(sblocks, (T * max_ctx + IDX_PAGED_CHUNK - 1) / IDX_PAGED_CHUNK);
     dim3 grid = as_stream ? dim3((unsigned)max((int64_t)1, sblocks)) : dim3((unsigned)nchunks, (unsigned)T);
-    hipLaunchKernelGGL(idx_decode_kernel, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
-                       (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
+    if (L.block_table)
+        hipLaunchKernelGGL(idx_decode_kernel<true>, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
+                           (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
+    else
+        hipLaunchKernelGGL(idx_decode_kernel<false>, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
+                           (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -66,64 +66,20 @@ struct StageRegs {
     u32x4 v[N];
 };
 
-// Issue the gathers of one tile (rows given by sidx) into registers, pieces U0 .. U1-1 of
-// this thread.  `seq` is a buffer resource over the sequence's rows, so offsets are 32-bit
-// and an index of -1 (or any row past the visible count) reads as zeros.
-template <bool KV_FP8, int U0 = 0, int U1 = StageRegs<KV_FP8>::N>
-__device__ __forceinline__ void stage_load(StageRegs<KV_FP8> &R, __amdgpu_buffer_rsrc_t seq,
-                                           const int32_t *sidx, int tid)
-{
-    typedef StageRegs<KV_FP8> SR;
-    constexpr int ROWB = KV_FP8 ? 576 : 1152;   // bytes per row in HBM
-#pragma unroll
-    for (int u = U0; u < U1; ++u) {
-        const int c = tid + M_THREADS * u;
-        if (SR::TOTAL % M_THREADS == 0 || c < SR::TOTAL) {
-            const int row = c / SR::PIECES, col = c % SR::PIECES;
-            const int32_t off = sidx[row] * ROWB + col * 16;
-            R.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, off, 0, 0));
-        } else {
-            R.v[u] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-}
-
-// Write the staged registers to the LDS tile (fp8 widened exactly to bf16).
-template <bool KV_FP8>
-__device__ __forceinline__ void stage_store(const StageRegs<KV_FP8> &R, char *tile, int tid)
-{
-    typedef StageRegs<KV_FP8> SR;
-#pragma unroll
-    for (int u = 0; u < SR::N; ++u) {
-        const int c = tid + M_THREADS * u;
-        if (SR::TOTAL % M_THREADS != 0 && c >= SR::TOTAL)
-            continue;
-        const int row = c / SR::PIECES, col = c % SR::PIECES;
-        if (KV_FP8) {
-            u32x4 lo, hi;
-            lo[0] = fp8x2_to_bf16x2<false>(R.v[u][0]);
-            lo[1] = fp8x2_to_bf16x2<true>(R.v[u][0]);
-            lo[2] = fp8x2_to_bf16x2<false>(R.v[u][1]);
-            lo[3] = fp8x2_to_bf16x2<true>(R.v[u][1]);
-            hi[0] = fp8x2_to_bf16x2<false>(R.v[u][2]);
-            hi[1] = fp8x2_to_bf16x2<true>(R.v[u][2]);
-            hi[2] = fp8x2_to_bf16x2<false>(R.v[u][3]);
-            hi[3] = fp8x2_to_bf16x2<true>(R.v[u][3]);
-            u32x4 *dst = (u32x4 *)(tile + row * M_ROWB + col * 32);
-            dst[0] = lo;
-            dst[1] = hi;
-        } else {
-            *(u32x4 *)(tile + row * M_ROWB + col * 16) = R.v[u];
-        }
-    }
-}
-
 // bf16 rows with a fixed lane -> row map: thread t gathers rows (t >> 3) and (t >> 3) + 32 of
 // the tile, 16-byte pieces (t & 7) + 8 v (v < 9) of each, so it needs only two indices per
 // tile and every load instruction reads whole 128-byte lines of 8 rows.  R.v[v] and
 // R.v[9 + v] hold piece v of the two rows.
 constexpr int SR_V = 9;
 static_assert(StageRegs<false>::N == 2 * SR_V && StageRegs<false>::PIECES == 8 * SR_V, "bf16 row map");
+
+// Byte offset of 16-byte piece `piece` of row `row` in a buffer of rows of `rowb` bytes, as
+// the unsigned 32-bit offset a buffer load takes (buffers up to 4 GB); a row of -1 (no
+// index) maps past every buffer's range, so its load returns zeros.
+__device__ __forceinline__ int row_offset(int32_t row, uint32_t rowb, int piece)
+{
+    return row >= 0 ? (int)((uint32_t)row * rowb + 16u * (uint32_t)piece) : (int)0xFFFFFFF0u;
+}
 
 template <int V0, int V1>
 __device__ __forceinline__ void stage_load_rows(StageRegs<false> &R, __amdgpu_buffer_rsrc_t seq,
@@ -132,9 +88,9 @@ __device__ __forceinline__ void stage_load_rows(StageRegs<false> &R, __amdgpu_bu
 #pragma unroll
     for (int v = V0; v < V1; ++v) {
         const int col = (tid & 7) + 8 * v;
-        R.v[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, r0 * 1152 + col * 16, 0, 0));
+        R.v[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, row_offset(r0, 1152, col), 0, 0));
         R.v[SR_V + v] =
-            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, r1 * 1152 + col * 16, 0, 0));
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, row_offset(r1, 1152, col), 0, 0));
     }
 }
 
@@ -578,7 +534,8 @@ __device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, co
     for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
         const int32_t idx = sidx[rc[q] & 0xFFu];
         const uint32_t col = rc[q] >> 8;
-        voff[q] = (col != 0xFFFFu && idx >= 0) ? idx * 576 + (int)col : (int)0x80000000;
+        // unsigned 32-bit offsets (buffers up to 4 GB); pads and missing rows read zeros
+        voff[q] = (col != 0xFFFFu && idx >= 0) ? (int)((uint32_t)idx * 576u + col) : (int)0xFFFFFFF0u;
     }
 #pragma unroll
     for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
@@ -958,7 +915,7 @@ __global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
         for (int u = 0; u < HH_N; ++u)
             R[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 seq, row_idx * (2 * M_DQK) + 16 * (hcol + 8 * u), 0, 0));
+                                                 seq, row_offset(row_idx, 2 * M_DQK, hcol + 8 * u), 0, 0));
     };
     auto stage = [&]() {
 #pragma unroll

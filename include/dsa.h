@@ -271,8 +271,9 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
  *                 split partials of the index list; none is needed when one
  *                 block covers a whole row).  No initial contents are needed.
  *                 Calls that overlap in time must not share a workspace.
- * The tuned kernel needs max_ctx * (D_c + D_r) * element size < 2^31
- * (cache_rows * (D_c + D_r) * element size with paged caches).
+ * The tuned kernels need max_ctx * (D_c + D_r) * element size <= 4 GiB - 1 MiB
+ * (cache_rows * (D_c + D_r) * element size with paged caches); beyond it the
+ * generic kernel runs.
  * The decode entry accepts any layout; prefill is the same computation with
  * a launch shape suited to many query rows per sequence.
  */
