@@ -34,12 +34,22 @@ struct LayoutDev {
 // Cache row of token s of sequence b: kv_base + s for contiguous caches, the page table's
 // physical row for paged ones.  With kv_base = 0 on contiguous caches it is the position
 // itself: the form top-k writes (positions, or physical rows when paged).
+// Positions are below 2^31 (the host checks max_ctx), so the page split runs in 32 bits: a
+// shift and a mask for power-of-two pages, else one unsigned division.
 __device__ __forceinline__ int64_t token_row(const LayoutDev &L, int b, int64_t kv_base, int64_t s)
 {
     if (L.block_table == nullptr)
         return kv_base + s;
-    const int64_t page = s / L.page_size;
-    return (int64_t)L.block_table[(int64_t)b * L.bt_stride + page] * L.page_size + (s - page * L.page_size);
+    const uint32_t ps = (uint32_t)L.page_size, si = (uint32_t)s;
+    uint32_t pg, off;
+    if ((ps & (ps - 1u)) == 0u) {
+        pg = si >> __builtin_ctz(ps);
+        off = si & (ps - 1u);
+    } else {
+        pg = si / ps;
+        off = si - pg * ps;
+    }
+    return (int64_t)L.block_table[(int64_t)b * L.bt_stride + pg] * ps + off;
 }
 
 struct RowInfo {

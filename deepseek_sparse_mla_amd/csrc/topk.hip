@@ -725,6 +725,16 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         }
     }
     __syncthreads();
+    // Paged caches list physical rows.  When the page size is a multiple of 4 the four
+    // positions of a group (which starts at a multiple of 4) share one page: one block-table
+    // lookup per group, all issued before the stores (clamped into the row, so always valid).
+    const bool quad_pages = L.block_table != nullptr && (L.page_size & 3) == 0;
+    int32_t qrow[NQ];
+    if (quad_pages) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            qrow[q] = (int32_t)token_row(L, r.b, 0, min(pos(q, 0), n32 - 1));
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const uint32_t m = (takes >> (4 * q)) & 15u, cnt = (uint32_t)__popc(m);
@@ -732,7 +742,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if ((m >> e) & 1u)
-                orow[slot++] = (int32_t)token_row(L, r.b, 0, pos(q, e));  // position, or physical row
+                orow[slot++] = quad_pages ? qrow[q] + e : (int32_t)token_row(L, r.b, 0, pos(q, e));
     }
     for (int t = (int)kk + tid; t < k; t += TK_THREADS)
         orow[t] = -1;
