@@ -114,7 +114,11 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     }
 }
 
-constexpr int IDX_PAGED_CHUNK = 2048;  // longest chunk with paged caches (its page table in LDS)
+// Paged caches: a block copies the block-table entries of the tokens it is about to read to
+// LDS (dynamic, sized by the host for the longest range a block covers, at most
+// IDX_PAGE_TABLE_MAX entries).
+constexpr int64_t IDX_PAGE_TABLE_MAX = 8192;
+constexpr int64_t IDX_PAGED_SHARE = IDX_PAGE_TABLE_MAX - 32;  // tokens per page of a block's share, at most
 
 // Two launch shapes.  Rows that are whole sequences (one query each, as in decode): the grid
 // walks the concatenated token stream of all sequences, an equal share of it per block (a
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                                                          float *__restrict__ scores, int64_t ld, int chunk,
                                                          int stream)
 {
-    __shared__ int32_t s_pages[PAGED ? IDX_PAGED_CHUNK + 1 : 1];  // paged: a segment's table entries
+    extern __shared__ int32_t s_pages[];  // paged: a segment's table entries (host-sized)
     const int lg = PAGED ? 31 - __builtin_clz((unsigned)L.page_size) : 0;  // power of two (host)
     if (!stream) {
         const int64_t i = blockIdx.y;
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
             idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin, s_end);
             return;
         }
-        // paged caches: this chunk's block-table entries to LDS (chunk <= IDX_PAGED_CHUNK)
+        // paged caches: this chunk's block-table entries to LDS
         const int64_t p0 = s_begin >> lg, p1 = (s_end - 1) >> lg;
         for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
             s_pages[p - p0] = L.block_table[(int64_t)r.b * L.bt_stride + p];
@@ -176,8 +180,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
             idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, rb, sb - rb, se - rb);
             continue;
         }
-        // paged caches: the segment's block-table entries to LDS (a share is at most
-        // IDX_PAGED_CHUNK tokens), after every wave is done with the previous segment's
+        // paged caches: the segment's block-table entries to LDS, after every wave is done
+        // with the previous segment's
         const int64_t s0 = sb - rb, s1 = se - rb, p0 = s0 >> lg, p1 = (s1 - 1) >> lg;
         __syncthreads();
         for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
@@ -473,8 +477,8 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
         if (c >= 128 && c <= 8192 && (c & (c - 1)) == 0)
             chunk = c;
     }
-    if (L.block_table && chunk > IDX_PAGED_CHUNK)
-        chunk = IDX_PAGED_CHUNK;
+    while (L.block_table && chunk / L.page_size + 2 > IDX_PAGE_TABLE_MAX)  // paged: table fits LDS
+        chunk >>= 1;
     const int64_t nchunks = (max_ctx + chunk - 1) / chunk;
     const bool as_stream = L.q_indptr == nullptr;  // rows are whole sequences
     // stream: two blocks per CU for long streams (one round; four per CU measured no
@@ -486,11 +490,22 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
         if (nb >= 1 && nb <= 65536)
             sblocks = min((int64_t)nb, T * max_ctx);
     }
-    if (L.block_table)  // a block's share must fit its LDS table of pages
-        sblocks = max(sblocks, (T * max_ctx + IDX_PAGED_CHUNK - 1) / IDX_PAGED_CHUNK);
+    // Paged: tokens [s0, s1) span at most (s1 - s0) / page + 2 pages.  A stream block's
+    // share is at most per_max tokens (the kernel divides N <= T * max_ctx tokens the same
+    // way); shares are kept to IDX_PAGED_SHARE pages' worth so the table stays in 32 KB.
+    size_t lds = 0;
+    if (L.block_table) {
+        const int64_t page = L.page_size;
+        int64_t span = chunk;
+        if (as_stream) {
+            sblocks = max(sblocks, (T * max_ctx + IDX_PAGED_SHARE * page - 1) / (IDX_PAGED_SHARE * page));
+            span = (((T * max_ctx + sblocks - 1) / sblocks) + 31) & ~(int64_t)31;
+        }
+        lds = (size_t)(span / page + 2) * sizeof(int32_t);  // <= IDX_PAGE_TABLE_MAX entries
+    }
     dim3 grid = as_stream ? dim3((unsigned)max((int64_t)1, sblocks)) : dim3((unsigned)nchunks, (unsigned)T);
     if (L.block_table)
-        hipLaunchKernelGGL(idx_decode_kernel<true>, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
+        hipLaunchKernelGGL(idx_decode_kernel<true>, grid, dim3(256), lds, stream, L, (const uint16_t *)q, w,
                            (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
     else
         hipLaunchKernelGGL(idx_decode_kernel<false>, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
