@@ -205,11 +205,15 @@ constexpr int PF_QPW = 2;                       // query rows per wave
 constexpr int PF_QPB = PF_WAVES * PF_QPW;       // query rows per block
 constexpr int PF_STAGE = 256;                   // tokens per LDS tile
 constexpr int PF_ROWB = 144;                    // LDS row stride in bytes (128 + pad)
-constexpr int PF_TILEB = PF_STAGE * PF_ROWB;    // 18432
+constexpr int PF_TILEB = PF_STAGE * PF_ROWB;    // 36864
 constexpr int PF_DMA = PF_TILEB / 1024;         // 36 wave-wide 1 KB loads per tile
 constexpr int PF_DMA_PER_WAVE = (PF_DMA + PF_WAVES - 1) / PF_WAVES;  // 5 (the last only on waves 0-3)
 constexpr int E8M0_ONE = 127;                   // block scale 2^0
-constexpr int PF_MAX_PAGES = 257;               // paged caches: block-table entries of one chunk
+// static LDS of the kernel (two tiles, their scales, row metadata, folded weights); paged
+// caches add a table of up to PF_MAX_PAGES block-table entries, which keeps two blocks per CU
+constexpr int PF_STATIC_LDS = 2 * PF_TILEB + 2 * PF_STAGE * 4 + PF_QPB * 3 * 8 + PF_QPB * 32 * 4;
+constexpr int PF_MAX_PAGES = (160 * 1024 / 2 - PF_STATIC_LDS) / 4;
+static_assert(PF_STAGE + 2 <= PF_MAX_PAGES, "a one-tile chunk of 1-token pages fits the table");
 
 __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 &a, const i32x8 &b, const f32x16 &c)
 {
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(4
     __shared__ float kscale[2][PF_STAGE];
     __shared__ int64_t s_meta[PF_QPB][3];  // b, kv_base, n per block query row (b = -1: none)
     __shared__ __attribute__((aligned(16))) float s_wq[PF_QPB][32];  // folded head weights w * qs
-    __shared__ int32_t s_pg[PAGED ? PF_MAX_PAGES : 1];  // paged: the segment's block-table entries
+    extern __shared__ int32_t s_pg[];  // paged: the segment's block-table entries (chunk / page + 2)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -529,12 +533,14 @@ hipError_t launch_index_fp8(const LayoutDev &L, int64_t T, int64_t max_ctx, cons
         if (c >= PF_STAGE && c <= 8192 && (c & (c - 1)) == 0)
             chunk = c;
     }
-    if (L.block_table)  // the chunk's block-table entries must fit the LDS table
-        while (chunk > PF_STAGE && (int64_t)chunk > (int64_t)(PF_MAX_PAGES - 1) * L.page_size)
+    // paged: a chunk spans at most chunk / page + 2 pages, whose table entries go to LDS
+    if (L.block_table)
+        while (chunk > PF_STAGE && chunk / L.page_size + 2 > PF_MAX_PAGES)
             chunk >>= 1;
+    const size_t lds = L.block_table ? (size_t)(chunk / L.page_size + 2) * sizeof(int32_t) : 0;
     dim3 grid((unsigned)((max_ctx + chunk - 1) / chunk), (unsigned)qblocks);
     if (L.block_table)
-        hipLaunchKernelGGL(idx_fp8_kernel<true>, grid, dim3(64 * PF_WAVES), 0, stream, L, T, (const uint8_t *)q, qs, w,
+        hipLaunchKernelGGL(idx_fp8_kernel<true>, grid, dim3(64 * PF_WAVES), lds, stream, L, T, (const uint8_t *)q, qs, w,
                            (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk);
     else
         hipLaunchKernelGGL(idx_fp8_kernel<false>, grid, dim3(64 * PF_WAVES), 0, stream, L, T, (const uint8_t *)q, qs, w,
