@@ -160,3 +160,51 @@ def check_attention(g: np.ndarray, o: np.ndarray, atol: float, what=""):
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def block_table(case, page, seed=0, spare=5):
+    """A block table that puts each sequence's pages at shuffled pages of a pool with `spare`
+    unused pages: (table int32 [B, width] on the CPU, physical row of every contiguous cache
+    row (int64, case device), rows of the pool)."""
+    kvp = case.kv_indptr.cpu()
+    ctx = [int(c) for c in (kvp[1:] - kvp[:-1])]
+    npages = [-(-c // page) for c in ctx]
+    total = sum(npages) + spare
+    perm = torch.randperm(total, generator=torch.Generator().manual_seed(seed))
+    width = max(max(npages), -(-case.max_ctx // page))
+    bt = torch.zeros((len(ctx), width), dtype=torch.int32)
+    k0 = 0
+    for b, n in enumerate(npages):
+        bt[b, :n] = perm[k0:k0 + n].to(torch.int32)
+        k0 += n
+    b_of = torch.repeat_interleave(torch.arange(len(ctx)), torch.tensor(ctx))
+    s_of = torch.arange(int(kvp[-1])) - kvp[:-1][b_of]
+    dst = bt[b_of, s_of // page].to(torch.int64) * page + s_of % page
+    return bt, dst.to(case.kv_indptr.device), total * page
+
+
+def paged_layout(case, page, bt, rows):
+    return dsa.Layout(case.kv_indptr, case.q_indptr, case.T, case.max_ctx, block_table=bt.to(case.kv_indptr.device),
+                      page_size=page, cache_rows=rows)
+
+
+def paged(case, page, seed=0):
+    """(layout, caches, table) of the case's caches scattered over shuffled pages of a pool whose
+    other rows hold unrelated values."""
+    bt, dst, rows = block_table(case, page, seed)
+    dev = case.kv_indptr.device
+
+    def scatter(x):
+        if x.dtype == torch.uint8:
+            pool = torch.randint(0, 120, (rows,) + tuple(x.shape[1:]), device=dev, dtype=torch.uint8,
+                                 generator=torch.Generator(device=dev).manual_seed(seed + 1))
+        else:
+            pool = (torch.randn((rows,) + tuple(x.shape[1:]), device=dev,
+                                generator=torch.Generator(device=dev).manual_seed(seed + 2)).abs() + 0.5).to(x.dtype)
+        pool[dst] = x
+        return pool
+
+    caches = dict(ik=scatter(case.ik), ik_scale=scatter(case.ik_scale) if case.ik_scale is not None else None,
+                  kv=[scatter(L.kv) for L in case.layers])
+    return paged_layout(case, page, bt, rows), caches, bt
+

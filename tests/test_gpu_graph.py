@@ -2,14 +2,15 @@
 
 Every entry point only enqueues kernels (no allocation, no memset, no host synchronisation,
 no other runtime call), so a whole step can be captured once and replayed.  Each test
-captures a step into a torch CUDA graph, replays it several times with eager work and
-synchronisations between the replays, and checks every replay bitwise against the eager
-step (the kernels are deterministic).  The top-k workspace of long rows must be left zero
+captures a step (contiguous or paged caches) into a torch CUDA graph, replays it several
+times with eager work and synchronisations between the replays, and checks every replay
+bitwise against the eager step (the kernels are deterministic).  The top-k workspace of long rows must be left zero
 by every call for the replays to stay correct; the second case exercises it.
 """
 import pytest
 import torch
 
+import dsa_testlib as tl
 import deepseek_sparse_mla_amd as dsa
 from deepseek_sparse_mla_amd import synth
 
@@ -21,9 +22,13 @@ DEV = "cuda"
 class Step:
     """Preallocated buffers and the three calls of one decode step."""
 
-    def __init__(self, case):
+    def __init__(self, case, page=0):
         self.case = case
         self.layout = dsa.Layout.of_case(case)
+        self.ik, self.ik_scale, self.kv = case.ik, case.ik_scale, case.layers[0].kv
+        if page:  # paged caches: the same step through a block table
+            self.layout, caches, _ = tl.paged(case, page, seed=1)
+            self.ik, self.ik_scale, self.kv = caches["ik"], caches["ik_scale"], caches["kv"][0]
         c = case
         self.scores = torch.empty((c.T, c.max_ctx), dtype=torch.float32, device=DEV)
         self.idx = torch.empty((c.T, c.topk), dtype=torch.int32, device=DEV)
@@ -34,19 +39,20 @@ class Step:
 
     def run(self):
         c, L = self.case, self.case.layers[0]
-        dsa.dsa_index_scores(self.layout, c.iq, c.iw, c.ik, k_scale=c.ik_scale, scores=self.scores)
+        dsa.dsa_index_scores(self.layout, c.iq, c.iw, self.ik, k_scale=self.ik_scale, scores=self.scores)
         dsa.dsa_topk(self.layout, self.scores, c.topk, indices=self.idx, workspace=self.tk_ws)
-        dsa.sparse_mla_decode(self.layout, L.q, L.kv, self.idx, c.sm_scale, c.Dc, L.kv_scale,
+        dsa.sparse_mla_decode(self.layout, L.q, self.kv, self.idx, c.sm_scale, c.Dc, L.kv_scale,
                               out=self.out, lse=self.lse, workspace=self.ws)
 
     def results(self):
         return self.idx.clone(), self.out.clone(), self.lse.clone()
 
 
-@pytest.mark.parametrize("ctx,kv_dt", [([3000, 8192, 5000, 700], "bf16"), ([40000, 70000], "fp8")])
-def test_decode_step_replays_equal_eager(ctx, kv_dt):
+@pytest.mark.parametrize("ctx,kv_dt,page", [([3000, 8192, 5000, 700], "bf16", 0), ([40000, 70000], "fp8", 0),
+                                          ([3000, 8192, 5000, 700], "bf16", 16), ([40000, 70000], "fp8", 64)])
+def test_decode_step_replays_equal_eager(ctx, kv_dt, page):
     case = synth.make_case("graph", 2, ctx=ctx, kv_dt=kv_dt, sm_scale=1.0 / 16, device=DEV)
-    st = Step(case)
+    st = Step(case, page)
     st.run()
     torch.cuda.synchronize()
     ref = st.results()

@@ -23,43 +23,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def paged(case, page, seed=0):
-    """(layout, caches) of the case's caches scattered over shuffled pages of a pool."""
-    ctx = [int(c) for c in (case.kv_indptr[1:] - case.kv_indptr[:-1]).cpu()]
-    npages = [-(-c // page) for c in ctx]
-    total = sum(npages) + 5
-    g = torch.Generator().manual_seed(seed)
-    perm = torch.randperm(total, generator=g)
-    width = max(max(npages), -(-case.max_ctx // page))
-    bt = torch.zeros((len(ctx), width), dtype=torch.int32)
-    src, dst = [], []
-    k0 = 0
-    kvp = case.kv_indptr.cpu()
-    for b, c in enumerate(ctx):
-        bt[b, :npages[b]] = perm[k0:k0 + npages[b]].to(torch.int32)
-        k0 += npages[b]
-        s = torch.arange(c)
-        src.append(int(kvp[b]) + s)
-        dst.append(bt[b, s // page].to(torch.int64) * page + s % page)
-    src, dst = torch.cat(src).to(DEV), torch.cat(dst).to(DEV)
-    rows = total * page
-
-    def scatter(x):
-        pool = torch.empty((rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=DEV)
-        if x.dtype == torch.uint8:
-            pool.copy_(torch.randint(0, 120, pool.shape, generator=torch.Generator(device=DEV).manual_seed(seed + 1),
-                                     device=DEV, dtype=torch.uint8))
-        else:
-            pool.copy_(torch.randn(pool.shape, generator=torch.Generator(device=DEV).manual_seed(seed + 2),
-                                   device=DEV).to(x.dtype).abs() + 0.5)
-        pool[dst] = x[src]
-        return pool
-
-    lay = dsa.Layout(case.kv_indptr, case.q_indptr, case.T, case.max_ctx, block_table=bt.to(DEV),
-                     page_size=page, cache_rows=rows)
-    caches = dict(ik=scatter(case.ik), ik_scale=scatter(case.ik_scale) if case.ik_scale is not None else None,
-                  kv=[scatter(L.kv) for L in case.layers])
-    return lay, caches, bt
+paged = tl.paged
 
 
 def run_path(case, layout, ik, ik_scale, kvs):
@@ -159,3 +123,53 @@ def test_paged_small_case_against_the_oracle():
     o_o, _ = oracle.sparse_mla(kvp, None, synth.host(L.q), synth.host(caches["kv"][0]), i_host, case.sm_scale,
                                case.Dc, L.kv_scale, physical=True)
     tl.check_attention(tl.to_f64(outs[0]), o_o, tl.ATTN_ATOL_LOWP, "paged attention")
+
+
+def test_writer_fills_the_paged_index_cache():
+    """Keys written with rope straight into the physical rows the block table gives (slots)
+    land byte for byte where the contiguous write puts them, and the paged indexer over that
+    pool (other rows junk) equals the contiguous indexer bit for bit, for the plane layout and
+    for 132-byte interleaved entries (generic indexer on both sides)."""
+    case = synth.make_case("paged_writer", 2, ctx=[700, 1300, 257], kv_dt="bf16", device=DEV)
+    page = 16
+    n = int(case.kv_indptr[-1])
+    kvp = case.kv_indptr.cpu()
+    b_of = torch.repeat_interleave(torch.arange(len(kvp) - 1), kvp[1:] - kvp[:-1])
+    pos = (torch.arange(n) - kvp[:-1][b_of]).to(DEV)
+    keys = torch.randn((n, 128), generator=torch.Generator(device=DEV).manual_seed(4), device=DEV).to(torch.bfloat16)
+    tab = dsa.rope_cos_sin_cache(case.max_ctx, device=DEV)
+    bt, dst, rows = tl.block_table(case, page, seed=3)
+    lay_p = tl.paged_layout(case, page, bt, rows)
+    vis = tl.visible(case)
+
+    cache_c = torch.zeros((n, 128), dtype=torch.uint8, device=DEV)
+    scale_c = torch.zeros(n, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_k_cache_write(keys, torch.arange(n, device=DEV), cache_c, scale_c, positions=pos, cos_sin=tab)
+    ref = dsa.dsa_index_scores(dsa.Layout.of_case(case), case.iq, case.iw, cache_c, k_scale=scale_c)
+
+    pool = torch.full((rows, 128), 0x3C, dtype=torch.uint8, device=DEV)
+    pscale = torch.full((rows,), 3.0, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_k_cache_write(keys, dst, pool, pscale, positions=pos, cos_sin=tab)
+    got = dsa.dsa_index_scores(lay_p, case.iq, case.iw, pool, k_scale=pscale)
+    torch.cuda.synchronize()
+    assert torch.equal(pool[dst], cache_c) and torch.equal(pscale[dst], scale_c)
+    for r in range(case.T):
+        assert torch.equal(got[r, :vis[r]], ref[r, :vis[r]]), "plane layout, row %d" % r
+
+    # 132-byte entries run the generic indexer (its own summation order): paged against
+    # contiguous entries, both written by the writer
+    def entries(n_rows, slots, layout):
+        ent = torch.full((n_rows, 132), 0x3C, dtype=torch.uint8, device=DEV)
+        dsa.dsa_index_k_cache_write(keys, slots, ent, ent.view(-1)[128:], positions=pos, cos_sin=tab,
+                                    cache_row_stride=132, cache_scale_stride=33, cache_rows=n_rows)
+        return ent, dsa.dsa_index_scores(layout, case.iq, case.iw, ent,
+                                         k_scale=ent.view(torch.float32).view(-1)[32:], k_row_stride=132,
+                                         k_scale_stride=33, k_dtype=dsa.DSA_FP8_E4M3FN)
+
+    ent_c, ref = entries(n, torch.arange(n, device=DEV), dsa.Layout.of_case(case))
+    ent_p, got = entries(rows, dst, lay_p)
+    torch.cuda.synchronize()
+    assert torch.equal(ent_p[dst], ent_c) and torch.equal(ent_c[:, :128], cache_c)
+    for r in range(case.T):
+        assert torch.equal(got[r, :vis[r]], ref[r, :vis[r]]), "132-byte entries, row %d" % r
+
