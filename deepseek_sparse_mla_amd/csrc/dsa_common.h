@@ -191,7 +191,7 @@ __device__ __forceinline__ i32x4 buffer_desc(const void *base, int64_t bytes)
     i32x4 d;
     d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
     d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
-    d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    d[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)bytes);  // unsigned range, up to 4 GiB - 1
     d[3] = 0x00020000;  // buffer descriptor word 3 for the gfx9 family
     return d;
 }

@@ -254,11 +254,11 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
     StageRegs<KV_FP8> R;
     constexpr int64_t ROWB = KV_FP8 ? 576 : 1152;
     // indices address the sequence's rows, or with paged caches the whole cache (physical
-    // rows); the host guarantees the range stays under 2^31 bytes
+    // rows); the host keeps the range at most 4 GiB - 1 MiB (unsigned 32-bit offsets)
     const bool paged = L.block_table != nullptr;
     const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * ROWB;
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * ROWB), (short)0, (int)seq_bytes, BUF_DWORD3);
+        (void *)((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * ROWB), (short)0, (int)(uint32_t)seq_bytes, BUF_DWORD3);
 
     // Pass 0 fixes each head's reference max at its first non-empty tile.  If a later
     // tile exceeds it by more than 2^100 (p would approach the fp32 range) the split is
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
     for (int mt = 0; mt < 8; ++mt)
         O[mt] = f32x16{};
 
-    // this sequence's rows, or with paged caches the whole cache (host: under 2^31 bytes)
+    // this sequence's rows, or with paged caches the whole cache (host: at most 4 GiB - 1 MiB)
     const bool paged = L.block_table != nullptr;
     const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * 576;
     const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * 576, seq_bytes);
@@ -900,11 +900,11 @@ __global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int mt = 0; mt < 4; ++mt)
         O[mt] = f32x16{};
 
-    // this sequence's rows, or with paged caches the whole cache (host: under 2^31 bytes)
+    // this sequence's rows, or with paged caches the whole cache (host: at most 4 GiB - 1 MiB)
     const bool paged = L.block_table != nullptr;
     const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * (2 * M_DQK);
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * (2 * M_DQK)), (short)0, (int)seq_bytes,
+        (void *)((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * (2 * M_DQK)), (short)0, (int)(uint32_t)seq_bytes,
         BUF_DWORD3);
     u32x4 R[HH_N];
     // thread t stages tile row t >> 3, 16-byte pieces (t & 7) + 8 u (u < 9): one index per
