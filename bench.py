@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (MiB)")
     p.add_argument("--paged", type=int, default=0, metavar="PAGE",
                    help="run on paged caches: every cache scattered over shuffled pages of PAGE tokens")
+    p.add_argument("--batch", type=int, default=0, metavar="B",
+                   help="decode workload only: B sequences of 8192 tokens instead of 8 (a sweep of "
+                        "the same layer shape; the headline line is the default)")
     p.add_argument("--graph", action="store_true",
                    help="capture each input set's step once as a HIP graph and time graph replays")
     return p.parse_args()
@@ -92,8 +95,11 @@ def algorithmic_model(case):
 
 # ------------------------------------------------------------------------------- GPU bench
 
-def make_sets(cfg, nsets, device):
+def make_sets(cfg, nsets, device, batch=0):
     from deepseek_sparse_mla_amd import synth
+    if batch:  # the decode layer at another batch size
+        return [synth.make_case("glm52_decode_b%d_ctx8192" % batch, cfg, ctx=[8192] * batch, sm_scale=1.0 / 16,
+                                kv_dt="bf16", seed=s, device=device) for s in range(nsets)]
     return [synth.config(cfg, device=device, seed=s) for s in range(nsets)]
 
 
@@ -468,10 +474,13 @@ def main():
     cfg = WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    probe = make_sets(cfg, 1, dev)[0]
+    if args.batch and args.workload != "decode":
+        print("--batch applies to the decode workload only", file=sys.stderr)
+        sys.exit(2)
+    probe = make_sets(cfg, 1, dev, args.batch)[0]
     per_set = case_bytes(probe)
     nsets = args.sets or max(1, min(16, math.ceil(1.2e9 / per_set)))
-    cases = [probe] + (make_sets(cfg, nsets, dev)[1:] if nsets > 1 else [])
+    cases = [probe] + (make_sets(cfg, nsets, dev, args.batch)[1:] if nsets > 1 else [])
     runners = [Runner(c, paged_caches(c, args.paged, seed=j) if args.paged else None)
                for j, c in enumerate(cases)]
     model = algorithmic_model(probe)
@@ -547,7 +556,7 @@ def main():
                                 "topk_hist_kernel + topk_select_kernel"),
         "mla": ("sparse_mla_prefill: " if prefill else "sparse_mla_decode%s: " % ("_shared" if len(probe.layers) > 1 else ""))
         + ("mla_fp8_kernel" if probe.layers[0].kv_dt == "fp8" else
-           "mla_hh_kernel" if probe.T * len(probe.layers) <= 512 else "mla_kernel")
+           "mla_hh_kernel" if probe.T * len(probe.layers) <= 64 else "mla_kernel")
         + (" + mla_combine_kernel" if split else ""),
     }
     path_gbs = model["path_bytes"] / (ms_per_step * 1e-3) / 1e9
@@ -577,7 +586,8 @@ def main():
         "roofline": {"kernel": kernel_names[dominant], "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic": st_model["bytes"] if bound == "hbm" else st_model["flops"],
-                     "traffic": measured_traffic(args.workload, dominant)},
+                     # counters are taken on the contiguous default shapes only
+                     "traffic": None if (args.paged or args.batch) else measured_traffic(args.workload, dominant)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(probe, args.cpu_seconds)

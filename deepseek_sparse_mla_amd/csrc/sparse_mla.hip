@@ -13,7 +13,7 @@
 //    and key half / output-dim half (w>>1); 64-row tiles staged through registers into one
 //    LDS tile [64][576 (+8 pad)], the next tile's rows in flight while the current one is
 //    computed;
-//  * mla_hh_kernel (bf16 rows, at most 512 (row, layer) pairs: decode): the same per
+//  * mla_hh_kernel (bf16 rows, at most 64 (row, layer) pairs: small decode): the same per
 //    (row, split, head half), 32-key tiles, small enough for two blocks per CU;
 //  * mla_fp8_kernel (fp8 rows): the mla_kernel wave roles over fp8 tiles gathered by DMA
 //    into three LDS buffers, two tiles in flight, widened to bf16 when read;
@@ -831,7 +831,10 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int6
 // from wave 2u + 1, in the key order of ds_read_b64_tr_b16).
 // ------------------------------------------------------------------------------------------
 constexpr int HH_TILE = 32;                          // keys per tile
-constexpr int64_t MLA_HH_MAX_ROWS = 512;             // bf16 rows up to this many use mla_hh_kernel
+// bf16 rows up to this many use mla_hh_kernel: measured on 8192-token decode, the half-head
+// blocks win at 8-32 rows, tie at 64 and lose from 128 rows on (96.1 against 91.2 us at 128,
+// 155 against 142 at 256), where the full-head kernel's single staging of each row pays
+constexpr int64_t MLA_HH_MAX_ROWS = 64;
 constexpr int HH_TILEB = HH_TILE * M_ROWB;           // 37376 B
 constexpr int HH_PIECES = HH_TILE * 72;              // 16-byte pieces per tile
 constexpr int HH_N = HH_PIECES / M_THREADS;          // 9 per thread

@@ -66,15 +66,17 @@ def test_decode_path(name):
     np.testing.assert_allclose(lses[0].cpu().numpy(), np.array(l_or), atol=1e-2, rtol=1e-3)
 
 
-def test_bf16_decode_many_rows_full_head_blocks():
-    """More than 512 bf16 rows take the full-head kernel (fewer rows take the half-head one):
-    sampled rows, including a short one and the last."""
+@pytest.mark.parametrize("n_rows", [100, 520])
+def test_bf16_decode_many_rows_full_head_blocks(n_rows):
+    """More than 64 bf16 rows take the full-head kernel (fewer rows take the half-head one),
+    with key splits and the combine at 100 rows, without at 520: sampled rows, including a
+    short one and the last."""
     rng = np.random.default_rng(31)
-    ctx = [int(c) for c in rng.integers(300, 2600, 520)]
+    ctx = [int(c) for c in rng.integers(300, 2600, n_rows)]
     ctx[7] = 40
     case = synth.make_case("many_rows_bf16", 2, ctx=ctx, sm_scale=1.0 / 16, kv_dt="bf16", device=DEV)
     scores, idx, outs, _ = tl.gpu_path(case)
-    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=[0, 7, 263, 519])
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=[0, 7, n_rows // 2, n_rows - 1])
 
 
 def test_prefill_single_sequence_sampled_rows():
