@@ -461,8 +461,11 @@ def main():
     if args.traffic_from:
         return traffic_from(*args.traffic_from, copy_bytes=args.copy_mib << 20, workload=args.workload)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.batch and args.workload != "decode":
+        print("--batch applies to the decode workload only", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, args.steps)
@@ -474,9 +477,6 @@ def main():
     cfg = WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    if args.batch and args.workload != "decode":
-        print("--batch applies to the decode workload only", file=sys.stderr)
-        sys.exit(2)
     probe = make_sets(cfg, 1, dev, args.batch)[0]
     per_set = case_bytes(probe)
     nsets = args.sets or max(1, min(16, math.ceil(1.2e9 / per_set)))
