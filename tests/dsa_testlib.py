@@ -188,10 +188,22 @@ def paged_layout(case, page, bt, rows):
                       page_size=page, cache_rows=rows)
 
 
-def paged(case, page, seed=0):
+def paged(case, page, seed=0, spare=5, top_page=False):
     """(layout, caches, table) of the case's caches scattered over shuffled pages of a pool whose
-    other rows hold unrelated values."""
-    bt, dst, rows = block_table(case, page, seed)
+    other rows hold unrelated values (`spare` unused pages; with top_page the first page of the
+    last sequence is moved to the pool's last page)."""
+    bt, dst, rows = block_table(case, page, seed, spare)
+    if top_page:
+        last = rows // page - 1
+        old = int(bt[-1, 0])
+        if old != last:
+            bt[bt == last] = old  # whichever page held the top id takes the old one
+            bt[-1, 0] = last
+        kvp = case.kv_indptr.cpu()
+        ctx = [int(c) for c in (kvp[1:] - kvp[:-1])]
+        b_of = torch.repeat_interleave(torch.arange(len(ctx)), torch.tensor(ctx))
+        s_of = torch.arange(int(kvp[-1])) - kvp[:-1][b_of]
+        dst = (bt[b_of, s_of // page].to(torch.int64) * page + s_of % page).to(case.kv_indptr.device)
     dev = case.kv_indptr.device
 
     def scatter(x):

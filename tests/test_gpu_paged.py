@@ -173,3 +173,53 @@ def test_writer_fills_the_paged_index_cache():
     for r in range(case.T):
         assert torch.equal(got[r, :vis[r]], ref[r, :vis[r]]), "132-byte entries, row %d" % r
 
+
+def test_paged_latent_pool_past_2gib():
+    """A bf16 latent pool of 2.2 GB with a sequence page at its top: the tuned kernels address
+    it with unsigned 32-bit offsets past 2^31 and still equal the contiguous run bit for bit."""
+    case = synth.make_case("pool_2g", 2, ctx=[3000, 5000], kv_dt="bf16", sm_scale=1.0 / 16, device=DEV)
+    page = 64
+    rows_needed = (1 << 31) // 1152 + 70000
+    used = sum(-(-c // page) for c in (3000, 5000))
+    lay, caches, bt = tl.paged(case, page, seed=11, spare=-(-rows_needed // page) - used, top_page=True)
+    assert int(bt[-1, 0]) * page * 1152 > (1 << 31)
+    contig = run_path(case, dsa.Layout.of_case(case), case.ik, case.ik_scale, [L.kv for L in case.layers])
+    pg = run_path(case, lay, caches["ik"], caches["ik_scale"], caches["kv"])
+    check_equal(case, page, bt, contig, pg)
+
+
+def test_paged_latent_pool_past_4gib_runs_the_generic_mla():
+    """Past 4 GiB - 1 MiB of latent rows the MLA falls back to the generic kernel (64-bit
+    addresses): on the same selected rows it equals the generic kernel on the contiguous cache,
+    bit for bit, including a row in the pool's top page."""
+    case = synth.make_case("pool_4g", 2, ctx=[2500, 4100], kv_dt="bf16", sm_scale=1.0 / 16, device=DEV)
+    page = 64
+    rows_needed = (1 << 32) // 1152 + 70000
+    used = sum(-(-c // page) for c in (2500, 4100))
+    bt, dst, rows = tl.block_table(case, page, seed=12, spare=-(-rows_needed // page) - used)
+    last = rows // page - 1
+    old = int(bt[-1, 0])
+    if old != last:
+        bt[bt == last] = old
+        bt[-1, 0] = last
+    kvp = case.kv_indptr.cpu()
+    b_of = torch.repeat_interleave(torch.arange(2), kvp[1:] - kvp[:-1])
+    s_of = torch.arange(int(kvp[-1])) - kvp[:-1][b_of]
+    dst = (bt[b_of, s_of // page].to(torch.int64) * page + s_of % page).to(DEV)
+    L = case.layers[0]
+    pool = torch.zeros((rows, 576), dtype=torch.bfloat16, device=DEV)
+    pool[dst] = L.kv
+    lay = tl.paged_layout(case, page, bt, rows)
+    scores = dsa.dsa_index_scores(dsa.Layout.of_case(case), case.iq, case.iw, case.ik, k_scale=case.ik_scale)
+    idx = dsa.dsa_topk(dsa.Layout.of_case(case), scores, case.topk)
+    idx_p = torch.from_numpy(oracle.to_physical(kvp.numpy(), None, idx.cpu().numpy(), bt.numpy(), page)).to(DEV)
+    assert int(idx_p.max()) >= last * page  # the top page is read
+    got = dsa.sparse_mla_decode(lay, L.q, pool, idx_p, case.sm_scale, case.Dc, L.kv_scale)
+    os.environ["DSA_KERNEL_VARIANT"] = "generic"
+    try:
+        ref = dsa.sparse_mla_decode(dsa.Layout.of_case(case), L.q, L.kv, idx, case.sm_scale, case.Dc, L.kv_scale)
+    finally:
+        del os.environ["DSA_KERNEL_VARIANT"]
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
