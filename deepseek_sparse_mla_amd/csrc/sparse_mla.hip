@@ -1287,8 +1287,10 @@ __global__ __launch_bounds__(G_THREADS) void mla_generic_kernel(LayoutDev L, int
 // ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
-// Splits depend on the query rows T only (not on the layer count), so a layer run through
-// the shared entry takes exactly the same reduction path as a single-layer call.
+// Key splits per (query row, layer).  They depend on the query rows T of one layer and on k
+// only, never on the layer count: a layer run through the shared entry then sums its keys in
+// exactly the same blocks and order as a single-layer call, and its output is the same bit
+// for bit.  The shared entry adds (row, layer) blocks instead of changing the split.
 int mla_num_splits(int64_t rows, int k)
 {
     const int ntiles = (k + M_TILE - 1) / M_TILE;
@@ -1317,7 +1319,7 @@ int mla_num_splits(int64_t rows, int k)
 size_t mla_workspace_bytes(int64_t T, int n_layers, int k)
 {
     const size_t rows = (size_t)T * n_layers;
-    const int ns = mla_num_splits((int64_t)rows, k);
+    const int ns = mla_num_splits(T, k);  // per layer: see mla_num_splits
     if (ns <= 1)
         return 0;
     size_t o = rows * ns * M_H * M_DC * sizeof(float);
@@ -1330,7 +1332,7 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
                             float sm_scale, void *workspace, hipStream_t stream)
 {
     const int64_t rows = T * n_layers;
-    const int ns = mla_num_splits(rows, k);
+    const int ns = mla_num_splits(T, k);  // from one layer's rows: layer-count independent
     const int ntiles = (k + M_TILE - 1) / M_TILE;
     const int tps = (ntiles + ns - 1) / ns;
     float *wo = nullptr, *wml = nullptr;
@@ -1351,7 +1353,7 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
         else
             hipLaunchKernelGGL((mla_fp8_kernel<false>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
                                indices, k, sm_scale, ns, tps, ppx, wo, wml);
-    } else if (rows <= MLA_HH_MAX_ROWS) {
+    } else if (T <= MLA_HH_MAX_ROWS) {
         // few rows (decode): half-head blocks, two per CU
         const int64_t hpairs = pairs * 2, hppx = (hpairs + 7) / 8;
         dim3 hgrid((unsigned)(8 * hppx));

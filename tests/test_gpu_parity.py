@@ -104,24 +104,35 @@ def test_prefill_ragged_sequences_share_blocks():
     _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=[0, 15, 16, 19, 20, 31, 32, 56, 57, 61])
 
 
-def test_shared_layers_match_oracle_and_single_layer_calls():
-    """Every shared layer meets the oracle bar, and agrees with a single-layer call on the same
-    indices up to the rounding of a different split of the 2048 keys (the split count
-    follows the number of (row, layer) pairs): the bf16 rounding of P and of the output
-    moves by a few 1e-4 at these magnitudes, so the two calls must agree to 4e-3 absolute,
-    five times tighter than the oracle bar."""
-    case = synth.make_case("shared_small", 5, ctx=[3000, 2100, 4096, 2500, 6000, 2048, 3333, 5000],
-                           sm_scale=1.0 / 16, kv_dt="fp8", n_layers=4, device=DEV)
-    scores, idx, outs, lses = tl.gpu_path(case)
-    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP)
+def _single_layer_calls_equal_shared(case, idx, outs, lses, layers=None):
+    """Layer l of the shared-index entry equals sparse_mla_decode on layer l alone, bit for
+    bit (outputs and lse): both sum each head's keys in the same splits and order."""
     layout = dsa.Layout.of_case(case)
-    for l, L in enumerate(case.layers):
+    for l in (range(len(case.layers)) if layers is None else layers):
+        L = case.layers[l]
         lse1 = torch.empty_like(lses[l])
-        o1 = dsa.sparse_mla_decode(layout, L.q, L.kv, idx, case.sm_scale, case.Dc, L.kv_scale, lse=lse1)
+        o1 = dsa.sparse_mla_decode(layout, L.q, L.kv, idx, case.sm_scale, case.Dc, L.kv_scale,
+                                   out_dtype=outs[l].dtype, lse=lse1)
         torch.cuda.synchronize()
-        d = (o1.float() - outs[l].float()).abs().max().item()
-        assert d <= 4e-3, "layer %d differs from its single-layer call by %.3g" % (l, d)
-        assert torch.allclose(lse1, lses[l], rtol=1e-5, atol=1e-5)
+        assert torch.equal(o1, outs[l]), "layer %d: shared and single-layer outputs differ (max %.3g)" % (
+            l, (o1.float() - outs[l].float()).abs().max().item())
+        assert torch.equal(lse1, lses[l]), "layer %d: shared and single-layer lse differ" % l
+
+
+@pytest.mark.parametrize("kv_dt,ctx", [
+    ("fp8", [3000, 2100, 4096, 2500, 6000, 2048, 3333, 5000]),   # fp8 kernel, key splits
+    ("bf16", [3000, 2100, 4096, 2500, 6000, 2048, 3333, 5000]),  # half-head kernel, key splits
+    ("bf16", [2100 + 37 * i for i in range(70)]),                # more than 64 rows: full-head kernel
+])
+def test_shared_layers_match_oracle_and_single_layer_calls(kv_dt, ctx):
+    """Every shared layer meets the oracle bar and equals, bit for bit, a single-layer call on
+    the same indices ([anatomy], layer scheduling: a shared layer reuses the full layer's
+    indices unchanged, so it must compute exactly what the full layer's own attention would)."""
+    case = synth.make_case("shared_small", 5, ctx=ctx, sm_scale=1.0 / 16, kv_dt=kv_dt, n_layers=4, device=DEV)
+    scores, idx, outs, lses = tl.gpu_path(case)
+    rows = None if len(ctx) <= 8 else [0, 1, 35, len(ctx) - 1]
+    _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=rows)
+    _single_layer_calls_equal_shared(case, idx, outs, lses)
     again = tl.gpu_path(case)
     for l in range(len(case.layers)):  # the shared call itself is deterministic
         assert torch.equal(again[2][l], outs[l]) and torch.equal(again[3][l], lses[l])
@@ -299,12 +310,15 @@ def test_topk_small_k_and_wide_ld():
 
 # ------------------------------------------------------------------------ full-size workloads
 
-@pytest.mark.parametrize("cfg,rows", [(2, [0, 7]), (3, [0, 33, 63]), (4, [0, 2047, 4095]), (5, [0, 31])])
+@pytest.mark.parametrize("cfg,rows", [(2, list(range(8))), (3, [0, 5, 17, 33, 40, 51, 63]),
+                                      (4, [0, 1, 511, 1024, 2047, 3001, 4094, 4095]), (5, [0, 9, 18, 31])])
 def test_full_size_workload_sampled_rows(cfg, rows):
     case = synth.config(cfg, DEV)
-    scores, idx, outs, _ = tl.gpu_path(case)
+    scores, idx, outs, lses = tl.gpu_path(case)
     _all_rows_check(case, scores, idx, outs, tl.ATTN_ATOL_LOWP, rows=rows)
-    del case, scores, idx, outs
+    if cfg == 5:  # the IndexShare workload: shared layers equal single-layer calls bit for bit
+        _single_layer_calls_equal_shared(case, idx, outs, lses, layers=[0, 3])
+    del case, scores, idx, outs, lses
     torch.cuda.empty_cache()
 
 
