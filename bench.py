@@ -1,23 +1,28 @@
 #!/usr/bin/env python3
 """Throughput of the DSA decode path (indexer -> top-2048 -> sparse MLA) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|ragged|prefill|share]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload share|decode|ragged|prefill]
     python bench.py --workload writer               # the index-cache writer at the prefill shape
     python bench.py --copy-calibration MIB          # a plain device copy, for counter scaling
     python bench.py --rocprof-summary CSV [CSV ..]  # per-kernel table of rocprofv3 output
     python bench.py --traffic-from FETCH WRITE COPY_FETCH COPY_WRITE [--workload W] [--copy-mib M]
 
 One step = one pass of the whole path over one batch of synthetic input.  The default
-workload is the GLM-5.2 layer decode (batch 8, context 8192, 32x128 fp8 index cache,
-top-2048, 64-head sparse MLA over bf16 latent rows).  Its working set fits in the 256 MB
-Infinity Cache, so the timed loop rotates over enough independent input sets (> 1 GB in
-total) that every step reads HBM.  Rank 0 prints one JSON line.
+workload is the largest decode workload, IndexShare decode: 32 sequences of 131072 tokens,
+one indexer pass over the fp8 index cache (32 heads x 128) and one top-2048 whose indices
+feed four sparse-MLA layers, each over its own fp8 latent cache (64 heads, 512 + 64).
+Smaller workloads fit in the 256 MB Infinity Cache, so the timed loop rotates over enough
+independent input sets (> 1 GB in total) that every step reads HBM.  The line prints one
+JSON object; after the headline workload the two other decode workloads (batch 8 x 8192
+bf16, ragged batch 64) are measured the same way and summarised under "other_workloads"
+(outside the headline's timed region; --no-others skips them).
 
 Timing: W untimed steps, then exactly K steps between two device synchronisations.  A
 second loop of K steps records HIP events around each stage on the stream the kernels run
-on (torch's current stream) to get every kernel's average duration; the roofline object is
-reported for the kernel with the largest share of the step.  The CPU baseline is the fp64
-oracle on the host cores, on the same input bytes.
+on (torch's current stream) to get every kernel's duration per step (mean, median, min,
+max); the roofline object is reported for the kernel with the largest share of the step,
+from its mean.  The CPU baseline is the fp64 oracle on the host cores, on the same input
+bytes.
 """
 from __future__ import annotations
 
@@ -43,7 +48,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="share", choices=sorted(WORKLOADS))
+    p.add_argument("--no-others", action="store_true",
+                   help="measure the headline workload only (no other_workloads summary)")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough for > 1 GB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
@@ -219,7 +226,7 @@ def cpu_baseline(case, target_s):
             break
     threads = oracle.num_threads()
     return {"value": rows_done / el, "unit": "query-tokens/s", "cores": int(min(threads, case.T)),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model_name(),
             "sample": "%d full passes of the %s batch (%d query rows each: indexer + top-%d + sparse MLA, "
                       "fp64) in %.1f s on %d host threads (%d usable: OpenMP over query rows)"
                       % (reps, case.name, case.T, case.topk, el, threads, min(threads, case.T))}
@@ -472,27 +479,72 @@ def main():
     if args.workload == "writer":
         return writer_main(args)
     import torch
+
+    torch.cuda.set_device(0)
+    line = measure(args.workload, args, args.steps, args.warmup, headline=True)
+    if not args.no_others and not (args.paged or args.batch or args.graph) and args.workload == "share":
+        others = {}
+        for wl in ("decode", "ragged"):
+            torch.cuda.empty_cache()
+            o = measure(wl, args, min(args.steps, 20), min(args.warmup, 3), headline=False)
+            others[o["config"]["workload"]] = {
+                "ms_per_step": o["ms_per_step"], "value": o["value"], "unit": o["unit"],
+                "step_ms_events": o["step_ms_events"], "path_hbm": o["path_hbm"],
+                "kernels_ms": o["kernels_ms"], "roofline": o["roofline"], "steps": o["steps"],
+                "dtype": o["dtype"]}
+        line["other_workloads"] = others
+    print(json.dumps(line), flush=True)
+
+
+def cpu_model_name():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def dtypes_of(case):
+    """What each stage computes in, for the line's "dtype" and "dtypes"."""
+    kv = case.layers[0].kv_dt
+    idx = ("fp8 keys x fp8 q (per-head scale), fp8 MFMA" if case.iq_dt == "fp8" else
+           "fp8 keys x %s q, keys widened exactly to bf16, bf16 MFMA" % case.iq_dt) + ", fp32 accumulate"
+    mla = ("fp8 latent x bf16 q, bf16 MFMA on exactly widened fp8" if kv == "fp8" else
+           "%s latent x %s q, %s MFMA" % (kv, kv, kv)) + ", fp32 softmax and accumulate"
+    d = {"indexer": idx, "topk": "fp32 scores, integer keys", "mla": mla}
+    short = "bf16" if kv == "bf16" else "fp8/bf16" if kv == "fp8" else kv
+    return short, d
+
+
+def measure(workload, args, steps, warmup, headline):
+    """One workload: build its input sets, warm up, time exactly `steps` steps, then time
+    each stage with HIP events.  Returns the JSON object of the line."""
+    import torch
     from deepseek_sparse_mla_amd import synth  # noqa: F401
 
-    cfg = WORKLOADS[args.workload]
+    cfg = WORKLOADS[workload]
     dev = "cuda:0"
-    torch.cuda.set_device(0)
-    probe = make_sets(cfg, 1, dev, args.batch)[0]
+    probe = make_sets(cfg, 1, dev, args.batch if headline else 0)[0]
     per_set = case_bytes(probe)
-    nsets = args.sets or max(1, min(16, math.ceil(1.2e9 / per_set)))
-    cases = [probe] + (make_sets(cfg, nsets, dev, args.batch)[1:] if nsets > 1 else [])
-    runners = [Runner(c, paged_caches(c, args.paged, seed=j) if args.paged else None)
+    nsets = (args.sets if headline else 0) or max(1, min(16, math.ceil(1.2e9 / per_set)))
+    cases = [probe] + (make_sets(cfg, nsets, dev, args.batch if headline else 0)[1:] if nsets > 1 else [])
+    paged = args.paged if headline else 0
+    runners = [Runner(c, paged_caches(c, paged, seed=j) if paged else None)
                for j, c in enumerate(cases)]
     model = algorithmic_model(probe)
     torch.cuda.synchronize()
 
     # warmup
-    for s in range(args.warmup):
+    for s in range(warmup):
         runners[s % nsets].step()
     torch.cuda.synchronize()
 
     steppers = [r.step for r in runners]
-    if args.graph:
+    graph = args.graph and headline
+    if graph:
         # one graph per input set, each holding one whole step (the library only enqueues
         # kernels: nothing in a step allocates, clears or synchronises)
         graphs = []
@@ -503,23 +555,23 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
         steppers = [g.replay for g in graphs]
-        for s in range(args.warmup):
+        for s in range(warmup):
             steppers[s % nsets]()
         torch.cuda.synchronize()
 
     # timed region: exactly K steps
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         steppers[s % nsets]()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = elapsed * 1e3 / steps
 
     # per-kernel durations with HIP events on the launch stream
     stream = torch.cuda.current_stream()
     stages = ("indexer", "topk", "mla")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for s in range(args.steps):
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(steps):
         r = runners[s % nsets]
         e = ev[s]
         e[0].record(stream)
@@ -530,11 +582,17 @@ def main():
         r.mla()
         e[3].record(stream)
     torch.cuda.synchronize()
-    dur = {st: sum(ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(args.steps)) / args.steps
-           for k, st in enumerate(stages)}  # ms
+    per = {st: [ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(steps)] for k, st in enumerate(stages)}
+    per_step = [ev[s][0].elapsed_time(ev[s][3]) for s in range(steps)]
+    dur = {st: sum(v) / steps for st, v in per.items()}  # ms
+
+    def spread(v):
+        a = sorted(v)
+        return {"median": round(a[len(a) // 2] if len(a) % 2 else 0.5 * (a[len(a) // 2 - 1] + a[len(a) // 2]), 5),
+                "min": round(a[0], 5), "max": round(a[-1], 5), "mean": round(sum(a) / len(a), 5)}
 
     T = probe.T
-    value = T * args.steps / elapsed
+    value = T * steps / elapsed
     dominant = max(stages, key=lambda st: dur[st])
     st_model = model[dominant]
     prefill = probe.q_indptr is not None
@@ -556,42 +614,47 @@ def main():
                                 "topk_hist_kernel + topk_select_kernel"),
         "mla": ("sparse_mla_prefill: " if prefill else "sparse_mla_decode%s: " % ("_shared" if len(probe.layers) > 1 else ""))
         + ("mla_fp8_kernel" if probe.layers[0].kv_dt == "fp8" else
-           "mla_hh_kernel" if probe.T * len(probe.layers) <= 64 else "mla_kernel")
+           "mla_hh_kernel" if probe.T <= 64 else "mla_kernel")
         + (" + mla_combine_kernel" if split else ""),
     }
     path_gbs = model["path_bytes"] / (ms_per_step * 1e-3) / 1e9
+    dshort, dstages = dtypes_of(probe)
     line = {
         "metric": "decode query-tokens/s (indexer+top-2048+sparse MLA) and % of peak HBM GB/s",
         "value": round(value, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dshort,
+        "dtypes": dstages,
         "data": "synthetic",
         "config": {"workload": probe.name, "batch": probe.B, "query_rows": T, "context": probe.ctx[0] if len(set(probe.ctx)) == 1 else "ragged",
                    "index_heads": probe.H_I, "index_dim": probe.D_I, "topk": probe.topk, "mla_heads": probe.H,
                    "latent": probe.Dc, "rope": probe.Dr, "kv_cache": probe.layers[0].kv_dt,
                    "layers": len(probe.layers), "input_sets_rotated": nsets,
-                   "launch": "hip graph replay" if args.graph else "eager",
-                   "caches": "paged, %d tokens per page, shuffled pages" % args.paged if args.paged
+                   "launch": "hip graph replay" if graph else "eager",
+                   "caches": "paged, %d tokens per page, shuffled pages" % paged if paged
                    else "contiguous"},
         "path_hbm": {"algorithmic_bytes": model["path_bytes"], "achieved_GBps": round(path_gbs, 1),
                      "frac_of_peak": round(path_gbs / HBM_PEAK_GBS, 4)},
+        "step_ms_events": spread(per_step),
         "kernels_ms": {kernel_names[s]: round(dur[s], 5) for s in stages},
+        "kernels_ms_spread": {kernel_names[s]: spread(per[s]) for s in stages},
         "roofline": {"kernel": kernel_names[dominant], "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic": st_model["bytes"] if bound == "hbm" else st_model["flops"],
                      # counters are taken on the contiguous default shapes only
-                     "traffic": None if (args.paged or args.batch) else measured_traffic(args.workload, dominant)},
+                     "traffic": None if (paged or (args.batch and headline)) else measured_traffic(workload, dominant)},
     }
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(probe, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    del runners, cases, probe
+    return line
 
 
 if __name__ == "__main__":

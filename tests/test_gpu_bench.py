@@ -29,7 +29,8 @@ def _bench(*args):
     ("--workload", "decode", "--sets", "1", "--no-cpu-baseline", "--graph"),
     ("--workload", "decode", "--sets", "1", "--no-cpu-baseline", "--batch", "16"),
     ("--workload", "writer", "--no-cpu-baseline"),
-], ids=["decode+cpu", "paged", "graph", "batch16", "writer"])
+    ("--no-cpu-baseline",),
+], ids=["decode+cpu", "paged", "graph", "batch16", "writer", "default"])
 def test_bench_line(args):
     d = _bench(*args)
     assert KEYS <= set(d)
@@ -46,3 +47,8 @@ def test_bench_line(args):
         assert d["config"]["batch"] == 16 and rf["traffic"] is None
     if "--graph" in args:
         assert d["config"]["launch"] == "hip graph replay"
+    if args == ("--no-cpu-baseline",):  # the headline: IndexShare decode, plus the other decode workloads
+        assert d["config"]["workload"] == "indexshare_b32_ctx131072_l4" and d["config"]["layers"] == 4
+        sp = d["step_ms_events"]
+        assert sp["min"] <= sp["median"] <= sp["max"]
+        assert set(d["other_workloads"]) == {"glm52_decode_b8_ctx8192", "ragged_decode_b64_ctx4k_64k"}
