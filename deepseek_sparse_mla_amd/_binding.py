@@ -24,7 +24,8 @@ DSA_TOPK_MAX = 2048
 DSA_MAX_SHARED_LAYERS = 8
 
 EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "sparse_mla_workspace_size",
-           "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "dsa_last_error",
+           "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "sparse_mla_decode_no_alloc",
+           "dsa_last_error",
            "dsa_abi_version")
 
 
@@ -74,11 +75,12 @@ def load_library(path: str = LIB_PATH):
         mla = [LP, I, I, I, F, I, P, I, P, F, P, I, I, P, P, P, S, P]
         lib.sparse_mla_decode.argtypes = mla
         lib.sparse_mla_prefill.argtypes = mla
+        lib.sparse_mla_decode_no_alloc.argtypes = mla[:15] + [P]
         lib.sparse_mla_decode_shared.argtypes = [LP, I, I, I, F, I, I, I, I,
                                                  ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
         for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_front_end,
                   lib.dsa_index_scores, lib.dsa_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
-                  lib.sparse_mla_decode_shared, lib.dsa_abi_version):
+                  lib.sparse_mla_decode_shared, lib.sparse_mla_decode_no_alloc, lib.dsa_abi_version):
             f.restype = I
         lib.dsa_last_error.restype = ctypes.c_char_p
         lib.dsa_last_error.argtypes = []
@@ -378,6 +380,25 @@ def sparse_mla_decode(layout: Layout, q, kv, indices, sm_scale, D_c, kv_scale=1.
     """Sparse MLA output [T, H, D_c]; q [T, H, D_c+D_r]; kv [rows, D_c+D_r]."""
     return _mla("sparse_mla_decode", layout, q, kv, indices, sm_scale, D_c, kv_scale, out, lse,
                 out_dtype, workspace, stream=stream)
+
+
+def sparse_mla_decode_no_alloc(layout: Layout, q, kv, indices, sm_scale, D_c, kv_scale=1.0, out=None, lse=None,
+                               out_dtype=None, stream=None) -> torch.Tensor:
+    """sparse_mla_decode with the split partials in the library's static scratch (no workspace);
+    with `out` given, the call allocates nothing."""
+    lib = load_library()
+    T, H, Dqk = q.shape
+    k = indices.shape[1]
+    if out_dtype is None:
+        out_dtype = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((T, H, D_c), dtype=out_dtype, device=q.device)
+    st = lib.sparse_mla_decode_no_alloc(ctypes.byref(layout.c), H, D_c, Dqk - D_c, float(sm_scale), _dt(q),
+                                        _dev(q, "q"), _dt(kv), _dev(kv, "kv"), float(kv_scale),
+                                        _dev(indices, "indices", torch.int32), k, _dt(out), _dev(out, "out"),
+                                        _dev(lse, "lse", torch.float32), _stream(stream))
+    _check(lib, st)
+    return out
 
 
 def sparse_mla_prefill(layout: Layout, q, kv, indices, sm_scale, D_c, kv_scale=1.0, out=None, lse=None,

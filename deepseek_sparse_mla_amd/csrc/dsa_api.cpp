@@ -7,10 +7,20 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "dsa_common.h"
 #include "dsa_kernels.h"
+
+// Scratch of the allocation-free entry point (sparse_mla_decode_no_alloc): one file-scope
+// device array per GPU, holding the split partials that sparse_mla_decode keeps in a caller
+// workspace.  Its size covers every single-layer call with k <= DSA_TOPK_MAX under the
+// library's split policy (at most 510 (row, split) partials of 64 x 512 fp32 plus their
+// (max, sum) pairs).  Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): the address comes from hipGetSymbolAddress, once per device
+// with that device current, and is kept per device.
+static __device__ __align__(256) unsigned char scratch[DSA_NO_ALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -157,9 +167,36 @@ dsa_status check_mla_layer(const MlaArgs &a, const dsa_mla_layer &l, int idx, bo
     return DSA_OK;
 }
 
+// The device address of `scratch` (declared above the namespace), kept per device.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+
+// Device address of the current device's scratch (looked up on the first call per device).
+dsa_status scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return fail(DSA_ERR_UNSUPPORTED, "device %d outside the %d devices the static scratch serves", dev,
+                    MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
 dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_layers,
                    const dsa_mla_layer *layers, const int32_t *indices, void *workspace,
-                   size_t ws_bytes, void *stream)
+                   size_t ws_bytes, void *stream, bool static_scratch = false)
 {
     dsa_status st = check_mla_common(L, a, indices);
     if (st != DSA_OK)
@@ -192,6 +229,20 @@ dsa_status run_mla(const dsa_layout *L, const MlaArgs &a, float sm_scale, int n_
         return fail(DSA_ERR_INVALID_ARG, "indices must be 4-byte aligned");
     const int64_t T = L->total_q;
     size_t need = tuned ? dsa::mla_workspace_bytes(T, n_layers, a.k) : 0;
+    if (static_scratch) {
+        if (need > DSA_NO_ALLOC_SCRATCH_BYTES)
+            return fail(DSA_ERR_WORKSPACE,
+                        "this call needs %zu bytes of split partials; the static scratch holds %zu "
+                        "(call sparse_mla_decode with a workspace instead)",
+                        need, (size_t)DSA_NO_ALLOC_SCRATCH_BYTES);
+        workspace = nullptr;
+        ws_bytes = DSA_NO_ALLOC_SCRATCH_BYTES;
+        if (need > 0 && T > 0) {
+            st = scratch_address(&workspace);
+            if (st != DSA_OK)
+                return st;
+        }
+    }
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need,
                     workspace ? ws_bytes : (size_t)0);
@@ -461,6 +512,16 @@ dsa_status sparse_mla_decode(const dsa_layout *layout, int H, int D_c, int D_r, 
     MlaArgs a{H, D_c, D_r, q_dt, kv_dt, out_dt, k};
     dsa_mla_layer l{q, kv, kv_scale, out, lse};
     return run_mla(layout, a, sm_scale, 1, &l, indices, workspace, workspace_bytes, stream);
+}
+
+dsa_status sparse_mla_decode_no_alloc(const dsa_layout *layout, int H, int D_c, int D_r, float sm_scale,
+                                      dsa_dtype q_dt, const void *q, dsa_dtype kv_dt, const void *kv,
+                                      float kv_scale, const int32_t *indices, int k, dsa_dtype out_dt,
+                                      void *out, float *lse, void *stream)
+{
+    MlaArgs a{H, D_c, D_r, q_dt, kv_dt, out_dt, k};
+    dsa_mla_layer l{q, kv, kv_scale, out, lse};
+    return run_mla(layout, a, sm_scale, 1, &l, indices, nullptr, 0, stream, true);
 }
 
 dsa_status sparse_mla_prefill(const dsa_layout *layout, int H, int D_c, int D_r, float sm_scale,

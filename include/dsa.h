@@ -294,6 +294,27 @@ dsa_status sparse_mla_prefill(const dsa_layout *layout, int H, int D_c, int D_r,
                               void *stream);
 
 /*
+ * sparse_mla_decode_no_alloc -- sparse_mla_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and result as
+ * sparse_mla_decode (bit for bit: the same kernels), without the workspace:
+ * the split partials live in a static device array of
+ * DSA_NO_ALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  The call allocates nothing and needs no initial
+ * contents of that array.  Every call on one GPU uses the same array, so calls
+ * that overlap in time on one GPU (several streams, several threads) race and
+ * must be serialised by the caller.  A call whose split partials would exceed
+ * the array (none with k <= DSA_TOPK_MAX under the library's split policy)
+ * returns DSA_ERR_WORKSPACE and launches nothing.
+ */
+#define DSA_NO_ALLOC_SCRATCH_BYTES (64u << 20)
+dsa_status sparse_mla_decode_no_alloc(const dsa_layout *layout, int H, int D_c, int D_r,
+                                      float sm_scale, dsa_dtype q_dt, const void *q,
+                                      dsa_dtype kv_dt, const void *kv, float kv_scale,
+                                      const int32_t *indices, int k, dsa_dtype out_dt, void *out,
+                                      float *lse, void *stream);
+
+/*
  * sparse_mla_decode_shared -- IndexShare ([anatomy], layer scheduling:
  * "shared" layers carry no indexer and reuse the indices the previous "full"
  * layer selected; full structure diagram: one int32 [tokens x 2048] buffer is

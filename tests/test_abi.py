@@ -246,3 +246,39 @@ def test_paged_layout_rejects(lib):
         assert lib.dsa_last_error()
     L = ctypes.byref(_layout(**ok))
     assert lib.dsa_topk(L, FAKE, 4096, 0, FAKE, None, 0, None) == B.DSA_ERR_INVALID_ARG  # k still checked
+
+
+# ------------------------------------------------------------------ allocation-free entry point
+
+NO_ALLOC_MAX = 64 << 20  # DSA_NO_ALLOC_SCRATCH_BYTES
+
+
+def test_no_alloc_scratch_holds_every_single_layer_call(lib):
+    """The static scratch covers the split partials of every single-layer call with k <= 2048
+    (only calls with fewer than 256 rows split their keys)."""
+    worst = 0
+    for T in list(range(1, 300)) + [511, 512, 4096]:
+        for k in (1, 63, 64, 65, 128, 500, 1024, 2047, 2048):
+            lay = _layout(batch=T, total_q=T)
+            worst = max(worst, lib.sparse_mla_workspace_size(ctypes.byref(lay), 64, 512, 64, k, 1))
+    assert 0 < worst <= NO_ALLOC_MAX, worst
+
+
+def _mla_na(lib, layout, k=2048):
+    return lib.sparse_mla_decode_no_alloc(ctypes.byref(layout), 64, 512, 64, 0.0625, B.DSA_BF16, FAKE,
+                                          B.DSA_FP8_E4M3FN, FAKE, 1.0, FAKE, k, B.DSA_BF16, FAKE, None, None)
+
+
+def test_no_alloc_rejects_partials_beyond_the_scratch(lib, monkeypatch):
+    """A split count forced past the policy (tuning override) needs more partials than the
+    static scratch holds: the call is refused on the host, before any HIP call."""
+    monkeypatch.setenv("DSA_MLA_SPLITS", "32")
+    st = _mla_na(lib, _layout(batch=255, total_q=255))
+    assert st == B.DSA_ERR_WORKSPACE
+    assert b"static scratch" in lib.dsa_last_error()
+
+
+def test_no_alloc_checks_arguments_like_the_workspace_entry(lib):
+    assert _mla_na(lib, _layout(), k=0) == B.DSA_ERR_INVALID_ARG
+    assert lib.sparse_mla_decode_no_alloc(None, 64, 512, 64, 0.0625, B.DSA_BF16, FAKE, B.DSA_FP8_E4M3FN, FAKE,
+                                          1.0, FAKE, 2048, B.DSA_BF16, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
