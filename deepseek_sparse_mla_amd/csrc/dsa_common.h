@@ -206,9 +206,11 @@ __device__ __forceinline__ i32x4 buffer_desc(const void *base, int64_t bytes)
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const i32x4 &desc, uint32_t lds_addr, int voff)
 {
+    // the LDS address is wave-uniform; readfirstlane keeps it in an SGPR whatever the compiler's
+    // uniformity analysis concluded
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(lds_addr), "v"(voff), "s"(desc)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(desc)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop

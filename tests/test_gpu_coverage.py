@@ -161,3 +161,31 @@ def test_tuned_mla_fp32_output(name):
     bound = outs[0].abs() * 2.0 ** -7 + 1e-3
     assert bool((d <= bound).all()), "bf16 and fp32 outputs differ by more than a bf16 rounding: %.3g" % (
         d.max().item())
+
+
+def test_fp8_extreme_logit_spread_takes_exact_rerun():
+    """fp8 latent rows: a late tile whose logit exceeds the first tile's maximum by far more
+    than 2^100 (in exp2 units) makes the fp8 kernel rerun its split with the exact maximum; the
+    output must still meet the oracle.  256 one-query sequences give one split per row, so all
+    32 tiles of the index list run in one block."""
+    B, ctx, H, Dc, Dr = 256, 2048, 64, 512, 64
+    g = torch.Generator(device=DEV).manual_seed(321)
+    x = torch.randn((B * ctx, Dc + Dr), generator=g, device=DEV)
+    codes = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    q = torch.randn((B, H, Dc + Dr), generator=g, device=DEV)
+    for b in (0, 1):
+        codes[b * ctx:(b + 1) * ctx, 0] = 0
+        codes[b * ctx + 1500, 0] = 0x7E  # 448
+        q[b, :, 0] = 64.0
+    q = q.to(torch.bfloat16)
+    kvp = torch.arange(0, (B + 1) * ctx, ctx, dtype=torch.int64, device=DEV)
+    layout = dsa.Layout(kvp, None, B, ctx)
+    idx = torch.arange(ctx, dtype=torch.int32, device=DEV).repeat(B, 1).contiguous()
+    lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    out = dsa.sparse_mla_decode(layout, q, codes, idx, 1.0 / 16, Dc, 1.0, lse=lse)
+    torch.cuda.synchronize()
+    for b in (0, 1, 2):
+        o, l = oracle.sparse_mla([0, ctx], None, synth.host(q[b:b + 1]), synth.host(codes[b * ctx:(b + 1) * ctx]),
+                                 idx[b:b + 1].cpu().numpy(), 1.0 / 16, Dc, 1.0)
+        tl.check_attention(tl.to_f64(out[b]), o[0], tl.ATTN_ATOL_LOWP, "row %d" % b)
+        np.testing.assert_allclose(lse[b].cpu().numpy(), l[0], rtol=1e-4, atol=1e-3)
