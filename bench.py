@@ -389,7 +389,7 @@ def writer_main(args):
     torch.cuda.set_device(0)
     probe = synth.writer_case(0, dev)
     T, H_I = probe.q.shape[:2]
-    tab = dsa.rope_cos_sin_cache(probe.cache_rows, device=dev)
+    tab = synth.rope_table(probe.cache_rows, device=dev)
     per_set = T * H_I * (256 + 132) + T * (256 + 132)
     nsets = args.sets or max(1, min(32, math.ceil(1.2e9 / per_set)))
     sets = []

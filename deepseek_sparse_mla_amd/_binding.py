@@ -154,19 +154,6 @@ class Layout:
         return Layout(case.kv_indptr, case.q_indptr, case.T, case.max_ctx)
 
 
-def rope_cos_sin_cache(max_pos: int, rope_dim: int = 64, theta: float = 8e6,
-                       device="cuda") -> torch.Tensor:
-    """Rope table fp32 [max_pos, rope_dim]: cos of the rope_dim/2 frequencies theta^(-2i/rope_dim)
-    at each position, then their sin.  Angles and their cos/sin are taken in fp64 on the host and
-    rounded once to fp32.  theta 8e6 is GLM-5.2's rope base (anatomy page, configuration table
-    and structure diagram), which the pages give without YaRN scaling."""
-    import numpy as np
-    inv = theta ** (-np.arange(0, rope_dim, 2, dtype=np.float64) / rope_dim)
-    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
-    tab = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
-    return torch.from_numpy(tab).to(device)
-
-
 def _rope_args(positions, cos_sin, n):
     if cos_sin is None:
         return None, None, 0

@@ -524,15 +524,15 @@ dsa_status sparse_mla_decode_no_alloc(const dsa_layout *layout, int H, int D_c, 
     return run_mla(layout, a, sm_scale, 1, &l, indices, nullptr, 0, stream, true);
 }
 
+// The same computation and launch choice as the decode entry (both follow T): one code path.
 dsa_status sparse_mla_prefill(const dsa_layout *layout, int H, int D_c, int D_r, float sm_scale,
                               dsa_dtype q_dt, const void *q, dsa_dtype kv_dt, const void *kv,
                               float kv_scale, const int32_t *indices, int k, dsa_dtype out_dt,
                               void *out, float *lse, void *workspace, size_t workspace_bytes,
                               void *stream)
 {
-    MlaArgs a{H, D_c, D_r, q_dt, kv_dt, out_dt, k};
-    dsa_mla_layer l{q, kv, kv_scale, out, lse};
-    return run_mla(layout, a, sm_scale, 1, &l, indices, workspace, workspace_bytes, stream);
+    return sparse_mla_decode(layout, H, D_c, D_r, sm_scale, q_dt, q, kv_dt, kv, kv_scale, indices, k, out_dt,
+                             out, lse, workspace, workspace_bytes, stream);
 }
 
 dsa_status sparse_mla_decode_shared(const dsa_layout *layout, int H, int D_c, int D_r,

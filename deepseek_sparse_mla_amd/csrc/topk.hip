@@ -22,8 +22,8 @@
 //  4. a block scan over per-thread popcounts of consecutive bitmap words gives every marked
 //     position its output slot.
 // Three ways to run it:
-//  DIRECT  rows of at most 8192 scores: one 1024-thread block per row holds its row in
-//          registers and does everything; its histogram bins are equal-width value bins
+//  DIRECT  rows of at most 32768 scores: one 1024-thread block per row holds its row in
+//          registers and LDS and does everything; its histogram bins are equal-width value bins
 //          over the row's range (see topk_direct_kernel), and it writes the output slots
 //          from a block scan over the positions themselves, without a bitmap;
 //  ROW     many rows (prefill): topk_hist_kernel builds the histogram with many blocks per

@@ -262,6 +262,18 @@ def writer_case(seed=0, device="cpu", T=4096, H_I=32, prefix=28672) -> WriterCas
 # ----------------------------------------------------------------------------------------------
 # host views for the oracle (raw storage as numpy: float32, uint16 bf16 bits, uint8 fp8 codes)
 
+def rope_table(max_pos: int, rope_dim: int = 64, theta: float = 8e6, device="cpu") -> torch.Tensor:
+    """Rope table fp32 [max_pos, rope_dim], the writer's caller-supplied input: cos of the
+    rope_dim/2 frequencies theta^(-2i/rope_dim) at each position, then their sin.  Angles and
+    their cos/sin are taken in fp64 and rounded once to fp32.  theta 8e6 is GLM-5.2's rope base
+    ("GLM-5.2 架构解剖", configuration table), given there without YaRN scaling."""
+    import numpy as np
+    inv = theta ** (-np.arange(0, rope_dim, 2, dtype=np.float64) / rope_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    tab = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    return torch.from_numpy(tab).to(device)
+
+
 def host(t: Optional[torch.Tensor]):
     """Copy a tensor to host numpy, keeping raw bits of bf16 tensors."""
     if t is None:

@@ -234,7 +234,7 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
  * rows (see dsa_layout).  1 <= k <= DSA_TOPK_MAX.  NaN scores are outside the
  * contract.
  *   workspace     device scratch of dsa_topk_workspace_size() bytes, needed
- *                 when max_ctx exceeds what one block holds in LDS (8192): a
+ *                 when max_ctx exceeds what one block holds (32768): a
  *                 score histogram per row and, for up to 512 long rows, each
  *                 row's bitmap of selected positions and its threshold-bin
  *                 candidates; may be NULL when the size is 0.  It must be
@@ -277,8 +277,12 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
  * The tuned kernels need max_ctx * (D_c + D_r) * element size <= 4 GiB - 1 MiB
  * (cache_rows * (D_c + D_r) * element size with paged caches); beyond it the
  * generic kernel runs.
- * The decode entry accepts any layout; prefill is the same computation with
- * a launch shape suited to many query rows per sequence.
+ * The two entries run the same code: the kernel and the split of each row's
+ * index list follow the number of query rows T (half-head blocks for bf16 KV
+ * up to 64 rows, full-head blocks beyond; key splits while T < 256), whatever
+ * the entry, so a prefill chunk and a decode batch of the same T and dtypes
+ * take the same path.  Both accept any layout; the two names mark the two
+ * call sites of a model (a prefill chunk with q_len_b > 1, a decode step).
  */
 size_t sparse_mla_workspace_size(const dsa_layout *layout, int H, int D_c, int D_r, int k,
                                  int n_layers);

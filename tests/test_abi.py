@@ -201,18 +201,6 @@ def test_index_q_quant_rejects(lib):
     assert q(T=0) == B.DSA_OK
 
 
-def test_rope_table_follows_its_definition():
-    """Row p holds cos(p * theta^(-2i/64)) then sin of the same angles; row 0 is (1, 0)."""
-    import numpy as np
-    tab = dsa.rope_cos_sin_cache(300, device="cpu").numpy()
-    assert tab.shape == (300, 64) and tab.dtype == np.float32
-    assert np.all(tab[0, :32] == 1) and np.all(tab[0, 32:] == 0)
-    p, i = 257, 5
-    ang = p * 8e6 ** (-2 * i / 64)
-    assert tab[p, i] == np.float32(np.cos(ang)) and tab[p, 32 + i] == np.float32(np.sin(ang))
-    assert np.allclose(tab[:, :32] ** 2 + tab[:, 32:] ** 2, 1, atol=1e-6)
-
-
 def test_writer_empty_calls_accept_null_pointers(lib):
     """An empty batch is a no-op; empty device tensors carry NULL data pointers."""
     assert _kw(lib, n=0, k=None, slots=None, cache=None, cscale=None) == B.DSA_OK

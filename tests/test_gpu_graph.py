@@ -90,7 +90,7 @@ def test_writer_front_end_replays_equal_eager():
     k = torch.randn((T, 128), generator=g0, device=DEV).to(torch.bfloat16)
     pos = torch.arange(100, 100 + T, dtype=torch.int64, device=DEV)
     slots = torch.randperm(rows, device=DEV)[:T].to(torch.int64)
-    tab = dsa.rope_cos_sin_cache(1024, device=DEV)
+    tab = synth.rope_table(1024, device=DEV)
     cache = torch.zeros((rows, 128), dtype=torch.uint8, device=DEV)
     scale = torch.zeros(rows, dtype=torch.float32, device=DEV)
     q8 = torch.empty((T, H, 128), dtype=torch.uint8, device=DEV)

@@ -137,7 +137,7 @@ def test_writer_fills_the_paged_index_cache():
     b_of = torch.repeat_interleave(torch.arange(len(kvp) - 1), kvp[1:] - kvp[:-1])
     pos = (torch.arange(n) - kvp[:-1][b_of]).to(DEV)
     keys = torch.randn((n, 128), generator=torch.Generator(device=DEV).manual_seed(4), device=DEV).to(torch.bfloat16)
-    tab = dsa.rope_cos_sin_cache(case.max_ctx, device=DEV)
+    tab = synth.rope_table(case.max_ctx, device=DEV)
     bt, dst, rows = tl.block_table(case, page, seed=3)
     lay_p = tl.paged_layout(case, page, bt, rows)
     vis = tl.visible(case)

@@ -45,7 +45,7 @@ def test_k_cache_write_planes(dtype, rope_off):
     slots = rng.permutation(rows)[:n].astype(np.int64)
     slots[rng.choice(n, 37, replace=False)] = -1
     pos = rng.integers(0, 4096, n).astype(np.int64)
-    tab = dsa.rope_cos_sin_cache(4096, device="cpu")
+    tab = synth.rope_table(4096, device="cpu")
     init_c = rng.integers(0, 256, (rows, 128)).astype(np.uint8)
     init_s = rng.standard_normal(rows).astype(np.float32)
 
@@ -76,7 +76,7 @@ def test_k_cache_write_interleaved_132_byte_entries_and_strided_keys():
     rng = np.random.default_rng(4)
     slots = rng.permutation(rows)[:n].astype(np.int64)
     pos = rng.integers(0, 1000, n).astype(np.int64)
-    tab = dsa.rope_cos_sin_cache(1000, device="cpu")
+    tab = synth.rope_table(1000, device="cpu")
     init = rng.integers(0, 256, (rows, 132)).astype(np.uint8)
     init[:, 128:] = np.frombuffer(np.full(rows, 7.0, np.float32).tobytes(), np.uint8).reshape(rows, 4)
 
@@ -106,7 +106,7 @@ def test_q_quant_prefill_rows(dtype):
     T, H = 300, 32
     q = _randn((T, H, 128), 5).to(dtype)
     pos = np.arange(28672 - 7, 28672 - 7 + T, dtype=np.int64)
-    tab = dsa.rope_cos_sin_cache(32768, device="cpu")
+    tab = synth.rope_table(32768, device="cpu")
     codes, scales = dsa.dsa_index_q_quant(q.to(DEV), positions=torch.from_numpy(pos).to(DEV),
                                           cos_sin=tab.to(DEV))
     oc, os_ = oracle.index_quant(_oracle_in(q), positions=pos, cos_sin=tab.numpy())
@@ -121,7 +121,7 @@ def test_q_quant_four_groups_per_team(dtype):
     T, H = 517, 32
     q = _randn((T, H, 128), 12).to(dtype)
     pos = np.random.default_rng(13).integers(0, 32768, T).astype(np.int64)
-    tab = dsa.rope_cos_sin_cache(32768, device="cpu")
+    tab = synth.rope_table(32768, device="cpu")
     codes, scales = dsa.dsa_index_q_quant(q.to(DEV), positions=torch.from_numpy(pos).to(DEV),
                                           cos_sin=tab.to(DEV), rope_off=64)
     oc, os_ = oracle.index_quant(_oracle_in(q), positions=pos, cos_sin=tab.numpy(), rope_off=64)
@@ -135,7 +135,7 @@ def test_q_quant_other_head_counts(T, H):
     into fours) and 8 heads over 16800 groups (four per team); every row checked."""
     q = _randn((T, H, 128), 18).to(torch.bfloat16)
     pos = np.random.default_rng(19).integers(0, 4096, T).astype(np.int64)
-    tab = dsa.rope_cos_sin_cache(4096, device="cpu")
+    tab = synth.rope_table(4096, device="cpu")
     codes, scales = dsa.dsa_index_q_quant(q.to(DEV), positions=torch.from_numpy(pos).to(DEV),
                                           cos_sin=tab.to(DEV))
     oc, os_ = oracle.index_quant(_oracle_in(q), positions=pos, cos_sin=tab.numpy())
@@ -221,7 +221,7 @@ def test_decode_step_into_full_size_index_cache():
     k = _randn((B, 128), 9).to(torch.bfloat16)
     slots = torch.arange(1, B + 1, dtype=torch.int64) * ctx - 1
     pos = torch.full((B,), ctx - 1, dtype=torch.int64)
-    tab = dsa.rope_cos_sin_cache(ctx, device="cpu")
+    tab = synth.rope_table(ctx, device="cpu")
     dsa.dsa_index_k_cache_write(k.to(DEV), slots.to(DEV), buf, buf.view(-1)[128:],
                                 positions=pos.to(DEV), cos_sin=tab.to(DEV), cache_row_stride=132,
                                 cache_scale_stride=33, cache_rows=rows)
@@ -243,7 +243,7 @@ def test_prefill_queries_at_full_size_sampled_rows():
     g = torch.Generator(device=DEV).manual_seed(10)
     q = torch.randn((T, H, 128), generator=g, device=DEV).to(torch.bfloat16)
     pos = torch.arange(28672, 28672 + T, dtype=torch.int64, device=DEV)
-    tab = dsa.rope_cos_sin_cache(32768, device=DEV)
+    tab = synth.rope_table(32768, device=DEV)
     codes, scales = dsa.dsa_index_q_quant(q, positions=pos, cos_sin=tab)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(11).integers(0, T, 61)]))
@@ -263,7 +263,7 @@ def test_front_end_equals_the_two_calls(T, dtype):
     k = _randn((T, 128), 15).to(dtype).to(DEV)
     pos = torch.arange(28672, 28672 + T, dtype=torch.int64, device=DEV)
     slots = torch.from_numpy(np.random.default_rng(16).permutation(rows)[:T].astype(np.int64)).to(DEV)
-    tab = dsa.rope_cos_sin_cache(32768, device=DEV)
+    tab = synth.rope_table(32768, device=DEV)
     bufs = [torch.full((rows, 132), 5, dtype=torch.uint8, device=DEV) for _ in range(2)]
     kw = dict(cache_row_stride=132, cache_scale_stride=33, cache_rows=rows)
     c1, s1 = dsa.dsa_index_front_end(q, k, slots, bufs[0], bufs[0].view(-1)[128:], positions=pos,

@@ -227,3 +227,27 @@ def test_bad_positions_are_rejected():
     x = np.zeros((2, 1, 128), np.float32)
     with pytest.raises(ValueError):
         oracle.index_quant(x, positions=np.array([0, 5]), cos_sin=_table(5))
+
+
+# ------------------------------------------------------------------------- rope table (input)
+
+def test_rope_table_angles_add_and_first_frequency_is_one_radian():
+    """The generator's rope table (the writer's caller-supplied input): row p holds cos then sin
+    of p * theta^(-2i/64).  Pinned by properties, not by retyping it: the first frequency is 1,
+    so row p, column 0 is cos(p rad) (textbook values); angles add, so row p + q is the complex
+    product of rows p and q; every pair lies on the unit circle; adjacent frequencies keep the
+    ratio theta^(-2/64), seen in the phase of row 1; and row 0 is the identity."""
+    import math
+    from deepseek_sparse_mla_amd import synth
+    tab = synth.rope_table(4096).numpy().astype(np.float64)
+    c, s = tab[:, :32], tab[:, 32:]
+    assert np.array_equal(tab[0], np.concatenate([np.ones(32), np.zeros(32)]))
+    assert abs(c[1, 0] - 0.5403023058681398) < 1e-7 and abs(s[1, 0] - 0.8414709848078965) < 1e-7  # cos 1, sin 1
+    assert abs(c[3, 0] - (-0.9899924966004454)) < 1e-7                                              # cos 3
+    np.testing.assert_allclose(c * c + s * s, 1.0, atol=2e-7)
+    for p, q in ((1, 1), (17, 250), (1000, 3000), (2047, 2048)):
+        zp, zq, zpq = c[p] + 1j * s[p], c[q] + 1j * s[q], c[p + q] + 1j * s[p + q]
+        np.testing.assert_allclose(zp * zq, zpq, atol=1e-6)
+    w = np.angle(c[1] + 1j * s[1])  # the 32 frequencies themselves (all below pi)
+    np.testing.assert_allclose(w[1:] / w[:-1], 8e6 ** (-2.0 / 64), rtol=1e-6)
+    assert math.isclose(w[0], 1.0, rel_tol=1e-7)
