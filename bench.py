@@ -184,6 +184,12 @@ class Runner:
     def topk(self):
         self.dsa.dsa_topk(self.layout, self.scores, self.case.topk, indices=self.idx, workspace=self.tk_ws)
 
+    def index_topk(self):
+        """Indexer and top-k as the one fused call (the top-k's histogram built by the indexer)."""
+        c = self.case
+        self.dsa.dsa_index_topk(self.layout, c.iq, c.iw, self.ik, c.topk, k_scale=self.ik_scale, q_scale=c.iq_scale,
+                                scores=self.scores, indices=self.idx, workspace=self.tk_ws)
+
     def mla(self):
         c = self.case
         if len(c.layers) == 1:
@@ -491,7 +497,7 @@ def main():
                 "ms_per_step": o["ms_per_step"], "value": o["value"], "unit": o["unit"],
                 "step_ms_events": o["step_ms_events"], "path_hbm": o["path_hbm"],
                 "kernels_ms": o["kernels_ms"], "roofline": o["roofline"], "steps": o["steps"],
-                "dtype": o["dtype"]}
+                "dtype": o["dtype"], "fused_index_topk": o["fused_index_topk"]}
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
@@ -591,6 +597,20 @@ def measure(workload, args, steps, warmup, headline):
         return {"median": round(a[len(a) // 2] if len(a) % 2 else 0.5 * (a[len(a) // 2 - 1] + a[len(a) // 2]), 5),
                 "min": round(a[0], 5), "max": round(a[-1], 5), "mean": round(sum(a) / len(a), 5)}
 
+    # the same steps with indexer and top-k as the fused call (reported beside the headline)
+    fz = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s in range(steps):
+        r = runners[s % nsets]
+        e = fz[s]
+        e[0].record(stream)
+        r.index_topk()
+        e[1].record(stream)
+        r.mla()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    fused_it = [fz[s][0].elapsed_time(fz[s][1]) for s in range(steps)]
+    fused_step = [fz[s][0].elapsed_time(fz[s][2]) for s in range(steps)]
+
     T = probe.T
     value = T * steps / elapsed
     dominant = max(stages, key=lambda st: dur[st])
@@ -645,6 +665,9 @@ def measure(workload, args, steps, warmup, headline):
         "step_ms_events": spread(per_step),
         "kernels_ms": {kernel_names[s]: round(dur[s], 5) for s in stages},
         "kernels_ms_spread": {kernel_names[s]: spread(per[s]) for s in stages},
+        "fused_index_topk": {"call": "dsa_index_topk (indexer with the top-k histogram, then the selection)",
+                             "stage_ms": spread(fused_it), "step_ms_events": spread(fused_step),
+                             "separate_stage_ms": round(dur["indexer"] + dur["topk"], 5)},
         "roofline": {"kernel": kernel_names[dominant], "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic": st_model["bytes"] if bound == "hbm" else st_model["flops"],

@@ -23,7 +23,7 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
 DSA_TOPK_MAX = 2048
 DSA_MAX_SHARED_LAYERS = 8
 
-EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "sparse_mla_workspace_size",
+EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_index_topk", "sparse_mla_workspace_size",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "sparse_mla_decode_no_alloc",
            "dsa_last_error",
            "dsa_abi_version")
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH):
         lib.dsa_topk_workspace_size.argtypes = [LP, L, I]
         lib.dsa_topk_workspace_size.restype = S
         lib.dsa_topk.argtypes = [LP, P, L, I, P, P, S, P]
+        lib.dsa_index_topk.argtypes = [LP, I, I, I, P, P, P, I, P, L, P, L, P, L, I, P, P, S, P]
         lib.sparse_mla_workspace_size.argtypes = [LP, I, I, I, I, I]
         lib.sparse_mla_workspace_size.restype = S
         mla = [LP, I, I, I, F, I, P, I, P, F, P, I, I, P, P, P, S, P]
@@ -79,7 +80,7 @@ def load_library(path: str = LIB_PATH):
         lib.sparse_mla_decode_shared.argtypes = [LP, I, I, I, F, I, I, I, I,
                                                  ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
         for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_front_end,
-                  lib.dsa_index_scores, lib.dsa_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
+                  lib.dsa_index_scores, lib.dsa_topk, lib.dsa_index_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
                   lib.sparse_mla_decode_shared, lib.sparse_mla_decode_no_alloc, lib.dsa_abi_version):
             f.restype = I
         lib.dsa_last_error.restype = ctypes.c_char_p
@@ -328,6 +329,38 @@ def dsa_topk(layout: Layout, scores: torch.Tensor, k: int, indices: Optional[tor
                       workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(lib, st)
     return indices
+
+
+def dsa_index_topk(layout: Layout, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, k_top: int,
+                   k_scale: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
+                   scores: Optional[torch.Tensor] = None, indices: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, ld: Optional[int] = None,
+                   k_row_stride: Optional[int] = None, k_scale_stride: int = 1,
+                   k_dtype: Optional[int] = None, stream=None):
+    """Indexer scores and top-k in one call (the top-k's histogram built by the indexer where
+    the kernels allow): returns (scores [T, ld] fp32, indices [T, k_top] int32)."""
+    lib = load_library()
+    T, H_I, D_I = q.shape
+    kd = _dt(k) if k_dtype is None else k_dtype
+    if k_row_stride is None:
+        k_row_stride = k.shape[-1] * k.element_size()
+    if ld is None:
+        ld = scores.shape[1] if scores is not None else layout.max_ctx
+    if scores is None:
+        scores = torch.empty((T, ld), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((T, k_top), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = topk_workspace(layout, ld, k_top, q.device)
+    st = lib.dsa_index_topk(ctypes.byref(layout.c), H_I, D_I, _dt(q), _dev(q, "q"),
+                            _dev(q_scale, "q_scale", torch.float32), _dev(w, "w", torch.float32),
+                            kd, _dev(k, "k", contiguous=False), int(k_row_stride),
+                            _dev(k_scale, "k_scale", torch.float32, contiguous=False), int(k_scale_stride),
+                            _dev(scores, "scores", torch.float32), int(ld), int(k_top),
+                            _dev(indices, "indices", torch.int32), _dev(workspace, "workspace"),
+                            workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(lib, st)
+    return scores, indices
 
 
 def sparse_mla_workspace_size(layout: Layout, H: int, D_c: int, D_r: int, k: int, n_layers: int = 1) -> int:

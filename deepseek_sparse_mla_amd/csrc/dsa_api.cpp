@@ -313,23 +313,42 @@ dsa_status check_index_quant(int64_t rows, int H, dsa_dtype x_dt, const void *x,
 
 }  // namespace
 
-extern "C" {
-
-const char *dsa_last_error(void)
+// Checks of the top-k arguments (dsa_topk and the fused entry).
+static dsa_status check_topk(const dsa_layout *layout, const float *scores, int64_t ld, int k,
+                             int32_t *indices, void *workspace, size_t workspace_bytes)
 {
-    return g_err.c_str();
+    dsa_status st = check_layout(layout);
+    if (st != DSA_OK)
+        return st;
+    if (k < 1 || k > DSA_TOPK_MAX)
+        return fail(DSA_ERR_INVALID_ARG, "k=%d outside [1, %d]", k, DSA_TOPK_MAX);
+    if (!scores || !indices)
+        return fail(DSA_ERR_INVALID_ARG, "scores and indices must be non-NULL");
+    if (ld < layout->max_ctx)
+        return fail(DSA_ERR_INVALID_ARG, "ld %lld < max_ctx %lld", (long long)ld,
+                    (long long)layout->max_ctx);
+    if (!aligned(scores, 4) || !aligned(indices, 4))
+        return fail(DSA_ERR_INVALID_ARG, "scores and indices must be 4-byte aligned");
+    const size_t need = dsa::topk_workspace_bytes(layout->total_q, layout->max_ctx);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(DSA_ERR_WORKSPACE, "top-k workspace of %zu bytes required, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 256))
+        return fail(DSA_ERR_WORKSPACE, "top-k workspace must be 256-byte aligned");
+    return DSA_OK;
 }
 
-int dsa_abi_version(void)
+// The indexer entry; with hist != nullptr and the tuned decode kernel, the kernel also adds
+// every row's score histogram to hist (*hist_used says whether it did).  Every check runs
+// before the launch.
+static dsa_status index_scores_impl(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
+                                    const void *q, const float *q_scale, const float *w, dsa_dtype k_dt,
+                                    const void *k, int64_t k_row_stride, const float *k_scale,
+                                    int64_t k_scale_stride, float *scores, int64_t ld, void *stream,
+                                    uint32_t *hist, bool *hist_used)
 {
-    return DSA_ABI_VERSION;
-}
-
-dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
-                            const void *q, const float *q_scale, const float *w, dsa_dtype k_dt,
-                            const void *k, int64_t k_row_stride, const float *k_scale,
-                            int64_t k_scale_stride, float *scores, int64_t ld, void *stream)
-{
+    if (hist_used)
+        *hist_used = false;
     dsa_status st = check_layout(layout);
     if (st != DSA_OK)
         return st;
@@ -375,9 +394,12 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
     const dsa::LayoutDev dl = to_dev(layout);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (tuned_decode)
+    if (tuned_decode) {
         e = dsa::launch_index_decode(dl, T, layout->max_ctx, q, w, k, k_row_stride, k_scale,
-                                     k_scale_stride, scores, ld, s);
+                                     k_scale_stride, scores, ld, s, hist);
+        if (hist_used)
+            *hist_used = hist != nullptr;
+    }
     else if (tuned_fp8)
         e = dsa::launch_index_fp8(dl, T, layout->max_ctx, q, q_scale, w, k, k_row_stride, k_scale,
                                   k_scale_stride, scores, ld, s);
@@ -385,6 +407,27 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
         e = dsa::launch_index_generic(dl, T, layout->max_ctx, H_I, D_I, q_dt, q, q_scale, w, k_dt, k,
                                       k_row_stride, k_scale, k_scale_stride, scores, ld, s);
     return hip_status(e, "indexer launch");
+}
+
+extern "C" {
+
+const char *dsa_last_error(void)
+{
+    return g_err.c_str();
+}
+
+int dsa_abi_version(void)
+{
+    return DSA_ABI_VERSION;
+}
+
+dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
+                            const void *q, const float *q_scale, const float *w, dsa_dtype k_dt,
+                            const void *k, int64_t k_row_stride, const float *k_scale,
+                            int64_t k_scale_stride, float *scores, int64_t ld, void *stream)
+{
+    return index_scores_impl(layout, H_I, D_I, q_dt, q, q_scale, w, k_dt, k, k_row_stride, k_scale,
+                             k_scale_stride, scores, ld, stream, nullptr, nullptr);
 }
 
 dsa_status dsa_index_k_cache_write(int64_t n, dsa_dtype k_dt, const void *k, int64_t k_row_stride,
@@ -467,29 +510,36 @@ size_t dsa_topk_workspace_size(const dsa_layout *layout, int64_t ld, int k)
 dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, int k,
                     int32_t *indices, void *workspace, size_t workspace_bytes, void *stream)
 {
-    dsa_status st = check_layout(layout);
+    dsa_status st = check_topk(layout, scores, ld, k, indices, workspace, workspace_bytes);
     if (st != DSA_OK)
         return st;
-    if (k < 1 || k > DSA_TOPK_MAX)
-        return fail(DSA_ERR_INVALID_ARG, "k=%d outside [1, %d]", k, DSA_TOPK_MAX);
-    if (!scores || !indices)
-        return fail(DSA_ERR_INVALID_ARG, "scores and indices must be non-NULL");
-    if (ld < layout->max_ctx)
-        return fail(DSA_ERR_INVALID_ARG, "ld %lld < max_ctx %lld", (long long)ld,
-                    (long long)layout->max_ctx);
-    if (!aligned(scores, 4) || !aligned(indices, 4))
-        return fail(DSA_ERR_INVALID_ARG, "scores and indices must be 4-byte aligned");
-    const size_t need = dsa::topk_workspace_bytes(layout->total_q, layout->max_ctx);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(DSA_ERR_WORKSPACE, "top-k workspace of %zu bytes required, got %zu", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (need > 0 && !aligned(workspace, 256))
-        return fail(DSA_ERR_WORKSPACE, "top-k workspace must be 256-byte aligned");
     const int64_t T = layout->total_q;
     if (T == 0)
         return ok();
     return hip_status(dsa::launch_topk(to_dev(layout), T, layout->max_ctx, scores, ld, k, indices, workspace,
                                        (hipStream_t)stream),
+                      "top-k launch");
+}
+
+dsa_status dsa_index_topk(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt, const void *q,
+                          const float *q_scale, const float *w, dsa_dtype k_dt, const void *k,
+                          int64_t k_row_stride, const float *k_scale, int64_t k_scale_stride,
+                          float *scores, int64_t ld, int k_top, int32_t *indices, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    // the top-k's own checks first: the indexer launch below is the first thing that runs
+    dsa_status st = check_topk(layout, scores, ld, k_top, indices, workspace, workspace_bytes);
+    if (st != DSA_OK)
+        return st;
+    const int64_t T = layout->total_q;
+    uint32_t *hist = T > 0 ? dsa::topk_hist_of(workspace, T, layout->max_ctx) : nullptr;
+    bool fused = false;
+    st = index_scores_impl(layout, H_I, D_I, q_dt, q, q_scale, w, k_dt, k, k_row_stride, k_scale,
+                           k_scale_stride, scores, ld, stream, hist, &fused);
+    if (st != DSA_OK || T == 0)
+        return st;
+    return hip_status(dsa::launch_topk(to_dev(layout), T, layout->max_ctx, scores, ld, k_top, indices,
+                                       workspace, (hipStream_t)stream, fused),
                       "top-k launch");
 }
 

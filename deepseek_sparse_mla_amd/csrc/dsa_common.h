@@ -149,6 +149,18 @@ template <> __device__ __forceinline__ float load_elem<2>(const void *base, int6
     return fp8_to_f32(((const uint8_t *)base)[idx]);
 }
 
+// Monotone 32-bit key of a score (sign-flipped IEEE bits, -0 folded into +0): a > b as floats
+// iff key(a) > key(b), and -0 == +0 share a key.  The top 11 bits are the top-k's histogram bin.
+__device__ __forceinline__ uint32_t score_key(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr int SCORE_BINS = 2048;  // 11-bit key digits
+constexpr int SCORE_BIN_SHIFT = 21;
+
 // ---- wave / block reductions (wave64) -----------------------------------------------------
 
 __device__ __forceinline__ float wave_max(float v)

@@ -25,9 +25,12 @@ struct MlaLayersDev {
 // Sparse-MLA split heuristic: enough (query row, split) blocks to give every CU one block.
 constexpr int MLA_TARGET_BLOCKS = 256;
 
+// hist: nullptr, or per-row histograms of the top 11 key bits of the scores to add to
+// (the top-k workspace's, see topk_hist_of)
 hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
                                const float *w, const void *k, int64_t kstride, const float *ks,
-                               int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream);
+                               int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream,
+                               uint32_t *hist = nullptr);
 hipError_t launch_index_fp8(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
                             const float *qs, const float *w, const void *k, int64_t kstride,
                             const float *ks, int64_t ks_stride, float *scores, int64_t ld,
@@ -37,8 +40,13 @@ hipError_t launch_index_generic(const LayoutDev &L, int64_t T, int64_t max_ctx, 
                                 const void *k, int64_t kstride, const float *ks, int64_t ks_stride,
                                 float *scores, int64_t ld, hipStream_t stream);
 size_t topk_workspace_bytes(int64_t T, int64_t max_ctx);
+// The per-row score histograms inside a top-k workspace (nullptr when the layout's rows take
+// the single-block mode, which needs none).
+uint32_t *topk_hist_of(void *workspace, int64_t T, int64_t max_ctx);
+// hist_ready: the workspace's histograms already hold every row's scores (built by the
+// indexer), so the histogram pass is skipped.
 hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const float *scores, int64_t ld,
-                       int k, int32_t *indices, void *workspace, hipStream_t stream);
+                       int k, int32_t *indices, void *workspace, hipStream_t stream, bool hist_ready = false);
 
 hipError_t launch_index_quant(int64_t rows, int H, bool in_f32, const void *x, int64_t x_row_bytes,
                               const int64_t *positions, const float *cos_sin, int64_t rope_rows,

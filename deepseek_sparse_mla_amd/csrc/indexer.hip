@@ -42,7 +42,8 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
                                                    const float *__restrict__ ks, int64_t ks_stride,
                                                    float *__restrict__ scores, int64_t ld, int64_t i,
                                                    int64_t kv_base, int64_t s_begin, int64_t s_end,
-                                                   const int32_t *pages = nullptr, int lg = 0, int64_t p0 = 0)
+                                                   const int32_t *pages = nullptr, int lg = 0, int64_t p0 = 0,
+                                                   uint32_t *wh = nullptr)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform loop bounds
@@ -89,8 +90,12 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
             part = fmaf(wr[rr], relu(acc[rr]), part);
         part += __shfl_xor(part, 32, 64);
         const int64_t s = s0 + j;
-        if (g == 0 && s < s_end)
-            out[s] = part * ksv;
+        const float v = part * ksv;
+        if (g == 0 && s < s_end) {
+            out[s] = v;
+            if (wh)  // the top-k's histogram bin of exactly the stored score (this wave's LDS copy)
+                atomicAdd(&wh[score_key(v) >> SCORE_BIN_SHIFT], 1u);
+        }
     };
     // Ping-pong over two register buffers (no copies, so only the tile being computed is
     // waited for while the other one is in flight).
@@ -124,15 +129,44 @@ constexpr int64_t IDX_PAGED_SHARE = IDX_PAGE_TABLE_MAX - 32;  // tokens per page
 // walks the concatenated token stream of all sequences, an equal share of it per block (a
 // block may finish one sequence and start the next), so no block waits on a longer one.
 // Otherwise: one block per (chunk, query row).
-template <bool PAGED>
+// With HIST the kernel also builds, for the top-k, each row's histogram of the top 11 key bits
+// of its scores (SCORE_BINS bins, added to hist[row][bin] with integer atomics): per-wave
+// histograms in LDS, summed and flushed once per (block, sequence segment).
+constexpr int IDX_HIST_LDS = 4 * SCORE_BINS * (int)sizeof(uint32_t);  // 32 KB
+
+template <bool HIST>
+__device__ __forceinline__ void idx_hist_flush(uint32_t *lh, uint32_t *__restrict__ hist, int64_t row)
+{
+    if (!HIST)
+        return;
+    __syncthreads();  // every wave has added this segment's scores
+    for (int b = threadIdx.x; b < SCORE_BINS; b += 256) {
+        const uint32_t c = lh[b] + lh[SCORE_BINS + b] + lh[2 * SCORE_BINS + b] + lh[3 * SCORE_BINS + b];
+        if (c)
+            atomicAdd(&hist[row * SCORE_BINS + b], c);
+        lh[b] = lh[SCORE_BINS + b] = lh[2 * SCORE_BINS + b] = lh[3 * SCORE_BINS + b] = 0u;
+    }
+    __syncthreads();
+}
+
+template <bool PAGED, bool HIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
                                                          const float *__restrict__ w,
                                                          const uint8_t *__restrict__ k, int64_t kstride,
                                                          const float *__restrict__ ks, int64_t ks_stride,
                                                          float *__restrict__ scores, int64_t ld, int chunk,
-                                                         int stream)
+                                                         int stream, uint32_t *__restrict__ hist)
 {
-    extern __shared__ int32_t s_pages[];  // paged: a segment's table entries (host-sized)
+    // dynamic LDS: with HIST the four waves' histograms, then (paged) a segment's table entries
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
+    uint32_t *lh = s_dyn;
+    int32_t *s_pages = (int32_t *)(s_dyn + (HIST ? 4 * SCORE_BINS : 0));
+    uint32_t *wh = HIST ? lh + SCORE_BINS * (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : nullptr;
+    if (HIST) {
+        for (int b = threadIdx.x; b < 4 * SCORE_BINS; b += 256)
+            lh[b] = 0u;
+        __syncthreads();
+    }
     const int lg = PAGED ? 31 - __builtin_clz((unsigned)L.page_size) : 0;  // power of two (host)
     if (!stream) {
         const int64_t i = blockIdx.y;
@@ -142,7 +176,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
             return;
         const int64_t s_end = min(s_begin + (int64_t)chunk, r.n);
         if (!PAGED) {
-            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin, s_end);
+            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin, s_end,
+                               nullptr, 0, 0, wh);
+            idx_hist_flush<HIST>(lh, hist, i);
             return;
         }
         // paged caches: this chunk's block-table entries to LDS
@@ -150,7 +186,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
             s_pages[p - p0] = L.block_table[(int64_t)r.b * L.bt_stride + p];
         __syncthreads();
-        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, 0, s_begin, s_end, s_pages, lg, p0);
+        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, 0, s_begin, s_end, s_pages, lg, p0, wh);
+        idx_hist_flush<HIST>(lh, hist, i);
         return;
     }
     // stream: the grid's blocks split the N cached tokens evenly (N is known only here), in
@@ -177,7 +214,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         if (se <= sb)
             continue;
         if (!PAGED) {
-            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, rb, sb - rb, se - rb);
+            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, rb, sb - rb, se - rb,
+                               nullptr, 0, 0, wh);
+            idx_hist_flush<HIST>(lh, hist, b);
             continue;
         }
         // paged caches: the segment's block-table entries to LDS, after every wave is done
@@ -187,7 +226,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
             s_pages[p - p0] = L.block_table[(int64_t)b * L.bt_stride + p];
         __syncthreads();
-        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, 0, s0, s1, s_pages, lg, p0);
+        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, 0, s0, s1, s_pages, lg, p0, wh);
+        idx_hist_flush<HIST>(lh, hist, b);
     }
 }
 
@@ -466,7 +506,8 @@ constexpr int IDX_STREAM_BLOCKS = 512;  // two blocks per CU: measured as good a
 
 hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, const void *q,
                                const float *w, const void *k, int64_t kstride, const float *ks,
-                               int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream)
+                               int64_t ks_stride, float *scores, int64_t ld, hipStream_t stream,
+                               uint32_t *hist)
 {
     // Per (chunk, query row) blocks: waves of at most 16 tiles and enough blocks to cover the
     // chip several times, at least two 32-token tiles per wave (one tile per wave re-reads q
@@ -508,12 +549,23 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
         lds = (size_t)(span / page + 2) * sizeof(int32_t);  // <= IDX_PAGE_TABLE_MAX entries
     }
     dim3 grid = as_stream ? dim3((unsigned)max((int64_t)1, sblocks)) : dim3((unsigned)nchunks, (unsigned)T);
-    if (L.block_table)
-        hipLaunchKernelGGL(idx_decode_kernel<true>, grid, dim3(256), lds, stream, L, (const uint16_t *)q, w,
-                           (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
+    const int st = as_stream ? 1 : 0;
+    const uint16_t *qh = (const uint16_t *)q;
+    const uint8_t *kk = (const uint8_t *)k;
+    if (hist) {
+        lds += IDX_HIST_LDS;
+        if (L.block_table)
+            hipLaunchKernelGGL((idx_decode_kernel<true, true>), grid, dim3(256), lds, stream, L, qh, w, kk, kstride, ks,
+                               ks_stride, scores, ld, chunk, st, hist);
+        else
+            hipLaunchKernelGGL((idx_decode_kernel<false, true>), grid, dim3(256), lds, stream, L, qh, w, kk, kstride, ks,
+                               ks_stride, scores, ld, chunk, st, hist);
+    } else if (L.block_table)
+        hipLaunchKernelGGL((idx_decode_kernel<true, false>), grid, dim3(256), lds, stream, L, qh, w, kk, kstride, ks,
+                           ks_stride, scores, ld, chunk, st, nullptr);
     else
-        hipLaunchKernelGGL(idx_decode_kernel<false>, grid, dim3(256), 0, stream, L, (const uint16_t *)q, w,
-                           (const uint8_t *)k, kstride, ks, ks_stride, scores, ld, chunk, as_stream ? 1 : 0);
+        hipLaunchKernelGGL((idx_decode_kernel<false, false>), grid, dim3(256), 0, stream, L, qh, w, kk, kstride, ks,
+                           ks_stride, scores, ld, chunk, st, nullptr);
     return hipGetLastError();
 }
 

@@ -103,13 +103,6 @@ static TkWs carve(void *ws, int64_t T, int64_t max_ctx)
     return w;
 }
 
-__device__ __forceinline__ uint32_t score_key(float x)
-{
-    uint32_t u = __float_as_uint(x);
-    if (u == 0x80000000u)
-        u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int64_t s)
 {
@@ -955,13 +948,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
 }
 
 // ------------------------------------------------------------------------------------------
+uint32_t *topk_hist_of(void *workspace, int64_t T, int64_t max_ctx)
+{
+    return topk_mode(T, max_ctx) == TK_DIRECT ? nullptr : carve(workspace, T, max_ctx).hist;
+}
+
 hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const float *scores, int64_t ld,
-                       int k, int32_t *indices, void *workspace, hipStream_t stream)
+                       int k, int32_t *indices, void *workspace, hipStream_t stream, bool hist_ready)
 {
     const int mode = topk_mode(T, max_ctx);
     const TkWs ws = mode == TK_DIRECT ? TkWs{} : carve(workspace, T, max_ctx);
     const dim3 hgrid((unsigned)((max_ctx + H_CHUNK - 1) / H_CHUNK), (unsigned)T);
-    if (mode != TK_DIRECT) {
+    if (mode != TK_DIRECT && !hist_ready) {
         hipLaunchKernelGGL(topk_hist_kernel, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, ws.hist);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)

@@ -247,6 +247,28 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
                     int32_t *indices, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * dsa_index_topk -- dsa_index_scores followed by dsa_topk as one call, with
+ * the top-k's histogram pass folded into the indexer ([anatomy], ATOM's
+ * GLM-5.2 optimisations: the indexer's steps fused into one kernel; stable
+ * top-k).  Arguments: those of dsa_index_scores (scores is still written:
+ * the selection reads it), then k, indices and workspace as for dsa_topk
+ * (workspace of dsa_topk_workspace_size() bytes, zero before its first use,
+ * left zero by every completed call).  Results: the same scores and indices,
+ * bit for bit, as the two separate calls.  For bf16 index queries (the decode
+ * indexer) and rows longer than 32768 scores, the indexer adds every row's
+ * histogram of the top 11 bits of its score keys to the workspace while it
+ * writes the scores, and the selection skips its own histogram pass; every
+ * other shape runs the two separate launches.  Every check of both calls
+ * runs before anything is launched.
+ */
+dsa_status dsa_index_topk(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
+                          const void *q, const float *q_scale, const float *w, dsa_dtype k_dt,
+                          const void *k, int64_t k_row_stride_bytes, const float *k_scale,
+                          int64_t k_scale_stride, float *scores, int64_t ld_scores, int k_top,
+                          int32_t *indices, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
  * sparse_mla_decode / sparse_mla_prefill -- attention over the selected
  * latent rows ([anatomy], full structure diagram, sparse MLA box: 64 heads
  * computed only on the 2048 selected rows of the latent KV cache, 576 = 512

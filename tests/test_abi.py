@@ -270,3 +270,26 @@ def test_no_alloc_checks_arguments_like_the_workspace_entry(lib):
     assert _mla_na(lib, _layout(), k=0) == B.DSA_ERR_INVALID_ARG
     assert lib.sparse_mla_decode_no_alloc(None, 64, 512, 64, 0.0625, B.DSA_BF16, FAKE, B.DSA_FP8_E4M3FN, FAKE,
                                           1.0, FAKE, 2048, B.DSA_BF16, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
+
+
+def _it(lib, layout, **kw):
+    a = dict(H=32, D=128, q_dt=B.DSA_BF16, q=FAKE, qs=None, w=FAKE, k_dt=B.DSA_FP8_E4M3FN, k=FAKE,
+             kstride=128, ks=FAKE, ks_stride=1, scores=FAKE, ld=4096, k_top=2048, idx=FAKE, ws=None, wsb=0)
+    a.update(kw)
+    return lib.dsa_index_topk(ctypes.byref(layout), a["H"], a["D"], a["q_dt"], a["q"], a["qs"], a["w"], a["k_dt"],
+                              a["k"], a["kstride"], a["ks"], a["ks_stride"], a["scores"], a["ld"], a["k_top"],
+                              a["idx"], a["ws"], a["wsb"], None)
+
+
+def test_index_topk_checks_both_calls_before_launching(lib):
+    """The fused entry refuses, on the host, whatever either separate call would refuse."""
+    assert _it(lib, _layout(), k_top=0) == B.DSA_ERR_INVALID_ARG            # top-k: k out of range
+    assert _it(lib, _layout(), idx=None) == B.DSA_ERR_INVALID_ARG           # top-k: no indices
+    assert _it(lib, _layout(), H=0) == B.DSA_ERR_INVALID_ARG                # indexer: bad shape
+    assert _it(lib, _layout(), ks=None) == B.DSA_ERR_INVALID_ARG            # indexer: fp8 keys need a scale
+    assert _it(lib, _layout(), ld=100) == B.DSA_ERR_INVALID_ARG             # ld < max_ctx
+    long_rows = _layout(batch=4, total_q=4, max_ctx=70000)
+    assert _it(lib, long_rows, ld=70000) == B.DSA_ERR_WORKSPACE             # long rows need the workspace
+    need = lib.dsa_topk_workspace_size(ctypes.byref(long_rows), 70000, 2048)
+    assert _it(lib, long_rows, ld=70000, ws=FAKE, wsb=need - 1) == B.DSA_ERR_WORKSPACE
+    assert _it(lib, _layout(batch=0, total_q=0)) == B.DSA_ERR_INVALID_ARG   # a layout needs a sequence
