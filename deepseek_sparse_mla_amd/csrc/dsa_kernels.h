@@ -61,7 +61,7 @@ hipError_t launch_index_front(int64_t T, int H, bool in_f32, const void *q, int6
                               int64_t cache_row_bytes, float *cache_scale, int64_t cache_scale_stride,
                               uint8_t *q_fp8, float *q_scale, hipStream_t stream);
 
-int mla_num_splits(int64_t T, int k);
+int mla_num_splits(int64_t T, int k, int min_tiles);
 size_t mla_workspace_bytes(int64_t T, int n_layers, int k);
 hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &layers, int n_layers,
                             bool kv_fp8, bool out_f32, const int32_t *indices, int k,

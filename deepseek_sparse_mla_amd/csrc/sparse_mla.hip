@@ -1129,6 +1129,8 @@ __global__ __launch_bounds__(M_THREADS) __attribute__((amdgpu_waves_per_eu(2))) 
 }
 
 constexpr int MLA_MAX_SPLITS = 32;  // the split count never exceeds this (mla_num_splits)
+constexpr int MLA_MIN_TILES_BF16 = 2;  // fewest tiles per split (see mla_num_splits)
+constexpr int MLA_MIN_TILES_FP8 = 8;
 
 // Combine the split partials of every (output row, head), in split order.  One 128-thread
 // block per (row, head); thread t owns dims 4t .. 4t + 3.  Partial s holds O_s / l_s, so
@@ -1291,16 +1293,21 @@ __global__ __launch_bounds__(G_THREADS) void mla_generic_kernel(LayoutDev L, int
 // only, never on the layer count: a layer run through the shared entry then sums its keys in
 // exactly the same blocks and order as a single-layer call, and its output is the same bit
 // for bit.  The shared entry adds (row, layer) blocks instead of changing the split.
-int mla_num_splits(int64_t rows, int k)
+//
+// min_tiles: the fewest 64-key tiles a split may hold.  bf16 latent (half-head decode kernel):
+// 2 -- a second tile hides the first one's fixed costs better than a second wave of split
+// partials does (measured on 8-row decode).  fp8 latent: 8 -- a block's fixed costs (index
+// list, Q, the first gathers' latency, the partial's store) are ~20K cycles against ~7.5K per
+// tile, so 4-tile splits lose even with twice the blocks (64-row ragged decode: 512 blocks of 4
+// tiles 59 us, 256 blocks of 8 tiles 48 us).
+int mla_num_splits(int64_t rows, int k, int min_tiles)
 {
     const int ntiles = (k + M_TILE - 1) / M_TILE;
     if (rows <= 0)
         return 1;
     int64_t ns = (MLA_TARGET_BLOCKS + rows - 1) / rows;
-    // at least two tiles per split: a second tile hides the first one's fixed costs better
-    // than a second wave of split partials does (measured on 8-row decode)
-    if (ns > ntiles / 2)
-        ns = ntiles / 2;
+    if (ns > ntiles / min_tiles)
+        ns = ntiles / min_tiles;
     if (const char *env = getenv("DSA_MLA_SPLITS")) {  // tuning sweeps: a fixed split count
         const long v = strtol(env, nullptr, 10);
         if (v >= 1 && v <= MLA_MAX_SPLITS)
@@ -1319,7 +1326,8 @@ int mla_num_splits(int64_t rows, int k)
 size_t mla_workspace_bytes(int64_t T, int n_layers, int k)
 {
     const size_t rows = (size_t)T * n_layers;
-    const int ns = mla_num_splits(T, k);  // per layer: see mla_num_splits
+    // the most splits any tuned kernel takes (the bf16 policy), so one size serves both dtypes
+    const int ns = mla_num_splits(T, k, MLA_MIN_TILES_BF16);
     if (ns <= 1)
         return 0;
     size_t o = rows * ns * M_H * M_DC * sizeof(float);
@@ -1332,7 +1340,8 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
                             float sm_scale, void *workspace, hipStream_t stream)
 {
     const int64_t rows = T * n_layers;
-    const int ns = mla_num_splits(T, k);  // from one layer's rows: layer-count independent
+    // from one layer's rows and the latent dtype: layer-count independent
+    const int ns = mla_num_splits(T, k, kv_fp8 ? MLA_MIN_TILES_FP8 : MLA_MIN_TILES_BF16);
     const int ntiles = (k + M_TILE - 1) / M_TILE;
     const int tps = (ntiles + ns - 1) / ns;
     float *wo = nullptr, *wml = nullptr;
