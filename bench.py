@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--workload", default="share", choices=sorted(WORKLOADS))
     p.add_argument("--no-others", action="store_true",
                    help="measure the headline workload only (no other_workloads summary)")
+    p.add_argument("--no-fused", action="store_true",
+                   help="skip the fused indexer + top-k timing (profiler runs: only the headline's kernels)")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough for > 1 GB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
@@ -599,7 +601,7 @@ def measure(workload, args, steps, warmup, headline):
 
     # the same steps with indexer and top-k as the fused call (reported beside the headline)
     fz = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for s in range(steps):
+    for s in range(0 if args.no_fused else steps):
         r = runners[s % nsets]
         e = fz[s]
         e[0].record(stream)
@@ -608,8 +610,8 @@ def measure(workload, args, steps, warmup, headline):
         r.mla()
         e[2].record(stream)
     torch.cuda.synchronize()
-    fused_it = [fz[s][0].elapsed_time(fz[s][1]) for s in range(steps)]
-    fused_step = [fz[s][0].elapsed_time(fz[s][2]) for s in range(steps)]
+    fused_it = [fz[s][0].elapsed_time(fz[s][1]) for s in range(0 if args.no_fused else steps)]
+    fused_step = [fz[s][0].elapsed_time(fz[s][2]) for s in range(0 if args.no_fused else steps)]
 
     T = probe.T
     value = T * steps / elapsed
@@ -665,9 +667,10 @@ def measure(workload, args, steps, warmup, headline):
         "step_ms_events": spread(per_step),
         "kernels_ms": {kernel_names[s]: round(dur[s], 5) for s in stages},
         "kernels_ms_spread": {kernel_names[s]: spread(per[s]) for s in stages},
-        "fused_index_topk": {"call": "dsa_index_topk (indexer with the top-k histogram, then the selection)",
-                             "stage_ms": spread(fused_it), "step_ms_events": spread(fused_step),
-                             "separate_stage_ms": round(dur["indexer"] + dur["topk"], 5)},
+        "fused_index_topk": None if args.no_fused else {
+            "call": "dsa_index_topk (indexer with the top-k histogram, then the selection)",
+            "stage_ms": spread(fused_it), "step_ms_events": spread(fused_step),
+            "separate_stage_ms": round(dur["indexer"] + dur["topk"], 5)},
         "roofline": {"kernel": kernel_names[dominant], "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic": st_model["bytes"] if bound == "hbm" else st_model["flops"],
