@@ -129,7 +129,23 @@ constexpr int E_ROWB = 1040;
 constexpr int E_STAGE_BYTES = M_H * E_ROWB;  // 66560
 static_assert(E_STAGE_BYTES <= M_TILEB, "output staging must fit in a tile buffer");
 
-template <bool OUT_F32>
+// The staged copy of a bf16 block result to the output or partial buffer by NT threads.
+template <int NT>
+__device__ __forceinline__ void mla_store_copy(const MlaLayerDev &Ld, int64_t i, int64_t orow, int split, int nsplit,
+                                               float *__restrict__ ws_o, const char *stage, int tid)
+{
+    char *dst = (nsplit == 1) ? (char *)((uint16_t *)Ld.out + i * M_H * M_DC)
+                              : (char *)((uint16_t *)ws_o + (orow * nsplit + split) * M_H * M_DC);
+#pragma unroll
+    for (int u = 0; u < M_H * M_DC * 2 / (16 * NT); ++u) {
+        const int c = tid + NT * u, h = c >> 6, c16 = c & 63;
+        *(u32x4 *)(dst + h * (M_DC * 2) + 16 * c16) = *(const u32x4 *)(stage + h * E_ROWB + 16 * c16);
+    }
+}
+
+// Called by the waves that hold O; with NT > 256 the other threads of the block call
+// mla_store_copy<NT> (after the same barrier) for their share of the staged copy.
+template <bool OUT_F32, int NT = M_THREADS>
 __device__ __forceinline__ void mla_store(const f32x16 (&O)[8], float l_run, float m_ref, const MlaLayerDev &Ld,
                                           int64_t i, int64_t orow, int split, int nsplit, int dq, int g, int head,
                                           float *__restrict__ ws_o, float *__restrict__ ws_ml, char *stage,
@@ -158,13 +174,7 @@ __device__ __forceinline__ void mla_store(const f32x16 (&O)[8], float l_run, flo
                                                  pack_bf16x2(O[mt][4 * q4 + 2] * inv, O[mt][4 * q4 + 3] * inv)};
             }
         __syncthreads();
-        char *dst = (nsplit == 1) ? (char *)((uint16_t *)Ld.out + i * M_H * M_DC)
-                                  : (char *)((uint16_t *)ws_o + (orow * nsplit + split) * M_H * M_DC);
-#pragma unroll
-        for (int u = 0; u < M_H * M_DC * 2 / (16 * M_THREADS); ++u) {
-            const int c = tid + M_THREADS * u, h = c >> 6, c16 = c & 63;
-            *(u32x4 *)(dst + h * (M_DC * 2) + 16 * c16) = *(const u32x4 *)(stage + h * E_ROWB + 16 * c16);
-        }
+        mla_store_copy<NT>(Ld, i, orow, split, nsplit, ws_o, stage, tid);
     }
     if (nsplit == 1) {
         if (Ld.lse && dq == 0 && g == 0)
@@ -469,14 +479,50 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
 }
 
 // ------------------------------------------------------------------------------------------
-// fp8 latent rows: gathered straight into double-buffered LDS with the buffer DMA path and
-// kept as fp8 there (2 x 37 KB); operands are widened to bf16 in registers when read.
+// fp8 latent rows: one 8-wave block per group of consecutive splits of a row, two wave teams
+// a tile apart.
+//
+// A 4-wave block that runs S, softmax and PV of a tile in sequence keeps each SIMD's matrix
+// core idle through the softmax, the exchanges and the barriers.  Here each SIMD holds one
+// wave of each team, and between two barriers the teams work on different tiles:
+//   * the S team (waves 0-3, wave a: heads 32*(a & 1) .., keys 32*(a >> 1) .. of each tile)
+//     computes S^T [32 keys x 32 heads] over all 576 dims (36 MFMA; the wave holds its heads'
+//     Q^T), the softmax numerators against the split's fixed reference maximum and writes P^T
+//     (bf16) to LDS: tile t in step t;
+//   * the PV team (waves 4-7, wave b: dims 128*b .. +127 of all 64 heads) issues the gathers
+//     and accumulates O^T [128 dims x 64 heads] += V^T . P^T (32 MFMA, each V element widened
+//     once): tile t in step t + 1.
+// One team's softmax and widening then run beside the other's MFMAs.  With all 576 dims in
+// one wave the logits need no cross-wave sum; only the reference maximum (fixed at each
+// split's first non-empty tile) is exchanged, once per split.
+//
+// Splits: the split count and boundaries come from the split policy alone; a block runs
+// `group` consecutive splits of one row as one tile sequence (the S team restarts its softmax
+// state and hands (row sum, reference maximum) over at each split boundary, the PV team
+// stores the split's result and clears O), so grouping changes scheduling, not a bit of any
+// result.  Q is loaded once per block: staged through LDS by all 512 threads.
+//
+// Gathers: rows land by buffer-to-LDS DMA in a ring of seven 32-row slots (half tiles), kept
+// fp8 there and widened to bf16 in registers when read.  In step s the S team reads tile s,
+// the PV team tile s - 1, and the half tiles 2s+2 .. 2s+4 are in flight: half tiles 2s+3 and
+// 2s+4 are issued at the start of step s, into the slots tile s - 2 left, and the step ends
+// once 2s+2 and 2s+3 have landed.
+//
+// Softmax without rescaling, as in mla_kernel: the reference maximum is fixed at the split's
+// first non-empty tile; a later logit above it by more than 2^100 makes that split run again
+// (a cold second pass) with the exact maximum of the first pass.
 // ------------------------------------------------------------------------------------------
-constexpr int F_ROWB = 592;                   // fp8 LDS row stride (576 + 16 pad)
-constexpr int F_TILEB = M_TILE * F_ROWB;      // 37888 B per tile buffer
-constexpr int F_DMA = F_TILEB / 1024;         // 37 wave-wide 1 KB loads per tile
-static_assert(E_STAGE_BYTES <= 3 * F_TILEB, "output staging must fit in the tile buffers");
-
+constexpr int F_ROWB = 592;                      // fp8 LDS row stride (576 + 16 pad)
+constexpr int TM_THREADS = 512;
+constexpr int TM_HALF = 32;                      // gathered rows per ring slot (half a tile)
+constexpr int TM_SLOTB = TM_HALF * F_ROWB;       // 18944 B
+constexpr int TM_SLOTS = 7;
+constexpr int TM_DMA = (TM_SLOTB + 1023) / 1024;     // 19 wave-wide loads per slot, the last half wide
+constexpr int TM_DMA_PER_WAVE = (TM_DMA + 3) / 4;    // 5 (4 on the last PV wave)
+constexpr int TM_PROWB = 144;                    // P^T row of one head: 64 keys bf16 + 16 pad
+constexpr int TM_PBUFB = M_H * TM_PROWB;         // 9216 B
+static_assert(TM_DMA == 19 && TM_SLOTB - 18 * 1024 == 512, "the last load of a slot is 32 lanes wide");
+static_assert(E_STAGE_BYTES <= TM_SLOTS * TM_SLOTB, "output staging must fit in the ring");
 
 // Value of lane l ^ 32 (g = lane >> 5), through one v_permlane32_swap (no LDS round trip).
 __device__ __forceinline__ float other_half(float x, int g)
@@ -491,331 +537,457 @@ __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
         (i32x2 __attribute__((address_space(3))) *)((__attribute__((address_space(3))) char *)(lds_generic_ptr)));
 }
 
-// Gather one 64-row tile (rows given by sidx) into an LDS buffer: 37 wave-wide 1 KB DMA
-// loads shared by the 4 waves; the 16 pad bytes of each row and rows with index -1 get an
-// out-of-range offset, which reads zeros.  The row indices are read first so that the LDS
-// reads are waited for once.
-constexpr int F_DMA_PER_WAVE = (F_DMA + 3) / 4;  // 10 (the last only on wave 0)
-
 constexpr int F_IDX = 2048;  // index slots of one split (32 tiles) held in LDS
 static_assert(F_IDX >= DSA_TOPK_MAX, "a split never holds more than k index slots");
 
-// Wait until only the DMA steps of the most recent tile (10 on wave 0, 9 on the others) may
-// still be outstanding: every earlier tile has landed.
-__device__ __forceinline__ void wait_but_last_tile8(int w)
-{
-    static_assert(F_DMA == 37 && F_DMA_PER_WAVE == 10, "DMA steps per wave");
-    if (w == 0)
-        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-}
-
-// Lane geometry of the gather, fixed per lane: DMA instruction q of wave w covers bytes
-// 1024*(4q + w) + 16*lane of the tile, i.e. row rc & 0xFF, column rc >> 8 (0xFFFF: the
-// pad bytes, or an instruction past the tile, which reads zeros).
-__device__ __forceinline__ void dma_geometry(int w, int lane, uint32_t (&rc)[F_DMA_PER_WAVE])
+// Lane geometry of a slot's gather, fixed per lane: load q of PV wave b covers bytes
+// 1024*(4q + b) + 16*lane of the slot, i.e. row rc & 0xFF, column rc >> 8 (0xFFFF: the pad
+// bytes, which read zeros).  Load 18 exists on wave 2 only, for lanes 0-31.
+__device__ __forceinline__ void slot_geometry(int b, int lane, uint32_t (&rc)[TM_DMA_PER_WAVE])
 {
 #pragma unroll
-    for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
-        const int o = 1024 * (4 * q + w) + 16 * lane;
-        const int row = min(o / F_ROWB, M_TILE - 1);
+    for (int q = 0; q < TM_DMA_PER_WAVE; ++q) {
+        const int o = 1024 * (4 * q + b) + 16 * lane;
+        const int row = min(o / F_ROWB, TM_HALF - 1);
         const int col = o - (o / F_ROWB) * F_ROWB;
-        const bool real = o < F_TILEB && col < 576;
+        const bool real = o < TM_SLOTB && col < 576;
         rc[q] = (uint32_t)row | ((real ? (uint32_t)col : 0xFFFFu) << 8);
     }
 }
 
-__device__ __forceinline__ void dma_tile(const i32x4 &seq, uint32_t lds_base, const int32_t *sidx, int w,
-                                         const uint32_t (&rc)[F_DMA_PER_WAVE])
+// Gather the 32 rows given by sidx (index -1: zeros) into the slot at lds_base.
+__device__ __forceinline__ void dma_slot(const i32x4 &seq, uint32_t lds_base, const int32_t *sidx, int b, int lane,
+                                         const uint32_t (&rc)[TM_DMA_PER_WAVE])
 {
-    int voff[F_DMA_PER_WAVE];
+    int voff[TM_DMA_PER_WAVE];
 #pragma unroll
-    for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
+    for (int q = 0; q < TM_DMA_PER_WAVE; ++q) {
         const int32_t idx = sidx[rc[q] & 0xFFu];
         const uint32_t col = rc[q] >> 8;
         // unsigned 32-bit offsets (buffers up to 4 GB); pads and missing rows read zeros
         voff[q] = (col != 0xFFFFu && idx >= 0) ? (int)((uint32_t)idx * 576u + col) : (int)0xFFFFFFF0u;
     }
 #pragma unroll
-    for (int q = 0; q < F_DMA_PER_WAVE; ++q) {
-        const int u = 4 * q + w;
-        if (q + 1 < F_DMA_PER_WAVE || u < F_DMA)
+    for (int q = 0; q < TM_DMA_PER_WAVE; ++q) {
+        const int u = 4 * q + b;
+        if (u < TM_DMA - 1)
+            dma16(seq, lds_base + 1024u * (uint32_t)u, voff[q]);
+        else if (u == TM_DMA - 1 && lane < 32)
             dma16(seq, lds_base + 1024u * (uint32_t)u, voff[q]);
     }
 }
 
-
-//
-// Same wave roles and math as mla_kernel (see above), software-pipelined over tiles:
-//  * the split's whole index list is loaded into LDS up front; tiles are gathered by DMA into
-//    three LDS buffers, kept fp8 there and widened to bf16 in registers when read.  While
-//    tile t is computed (S partials, softmax, PV) tiles t+1 and t+2 are in flight, and the end
-//    of the step waits only for tile t+1 (a count-based wait: the newest tile's DMA steps may
-//    stay outstanding);
-//  * S operands: 16 fp8 bytes per lane (two k-steps) widened to bf16; Q^T is loaded in the
-//    same permuted dim order (k-step 2p + h of lane half g covers dims 288dq + 32p + 16g +
-//    8h .. +7), which leaves the contraction unchanged;
-//  * V^T operands: ds_read_b64_tr_b8 gives a lane 8 consecutive keys of one dim; P is put
-//    in the same consecutive-key order by one v_permlane32_swap per dword;
-//  * softmax without rescaling, as in mla_kernel: each head fixes its reference maximum at
-//    its first non-empty tile; if a later logit exceeds it by more than 2^100 the split is
-//    run again (a separate, cold copy of the tile loop) with the exact maximum of the first
-//    run, so the hot loop never touches O outside its MFMAs.
-//
-template <bool OUT_F32>
-__global__ __launch_bounds__(M_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int64_t T, int64_t n_rows,
-                                                               MlaLayersDev layers,
-                                                               const int32_t *__restrict__ indices, int k,
-                                                               float sm_scale, int nsplit, int tiles_per_split,
-                                                               int64_t pairs_per_xcd, float *__restrict__ ws_o,
-                                                               float *__restrict__ ws_ml)
+// Wait until only the most recent slot's loads (5 on PV waves 0-2, 4 on wave 3) may still be
+// outstanding: every earlier slot has landed.
+__device__ __forceinline__ void wait_but_last_slot(int b)
 {
-    __shared__ __attribute__((aligned(16))) char kt8[3][F_TILEB];
-    __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
-    __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
-    __shared__ float xm[4][32];                                    // per-head maxima swap
-    __shared__ int32_t sidx[F_IDX];                                // this split's index slots
-    __shared__ int sh_flag;
+    static_assert(TM_DMA_PER_WAVE == 5, "loads per wave and slot");
+    if (b == 3)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+}
 
+// Partial (or, with one split, final) result of one split from the PV team's registers:
+// wave b holds dims 128 b + 32 mt + 8 q4 + 4 g + 0..3 of heads j (nh = 0) and 32 + j (nh = 1).
+// bf16 results are staged through LDS in the wave's own columns 128 b .. +127 of the 64 rows
+// the split's last tile left in slots sa, sb (no other wave reads those bytes): 32 heads at a
+// time, each head's 256 bytes in two stage rows, then stored as whole 256-byte pieces, four
+// heads per instruction.  fp32 results are stored straight from the MFMA layout.
+template <bool OUT_F32>
+__device__ __forceinline__ void mla_fp8_store(const f32x16 (&O)[4][2], const float (&l)[2], const float (&m)[2],
+                                              const MlaLayerDev &Ld, int64_t i, int64_t orow, int split, int nsplit,
+                                              int b, int g, int j, int lane, char *slot_a, char *slot_b,
+                                              float *__restrict__ ws_o, float *__restrict__ ws_ml)
+{
+    const int64_t base = (nsplit == 1) ? i * M_H * M_DC : (orow * nsplit + split) * M_H * M_DC;
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh) {
+        const float inv = (l[nh] > 0.f) ? (nsplit == 1 ? Ld.kv_scale / l[nh] : 1.f / l[nh]) : 0.f;
+        if (OUT_F32) {
+            float *dst = ((nsplit == 1) ? (float *)Ld.out : ws_o) + base + (32 * nh + j) * M_DC;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x16 &o = O[mt][nh];
+                    *(f32x4 *)(dst + 128 * b + 32 * mt + 8 * q4 + 4 * g) =
+                        f32x4{o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv};
+                }
+        } else {
+            // stage row R: row R & 31 of slot_a (R < 32) or slot_b, bytes 128 b .. +127
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int c = 2 * (32 * mt + 8 * q4 + 4 * g);  // byte of the head's 256
+                    const int R = 2 * j + (c >> 7);
+                    char *sp = (R < 32 ? slot_a : slot_b) + (R & 31) * F_ROWB + 128 * b + (c & 127);
+                    const f32x16 &o = O[mt][nh];
+                    *(u32x2 *)sp = u32x2{pack_bf16x2(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
+                                         pack_bf16x2(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv)};
+                }
+            uint16_t *dst = ((nsplit == 1) ? (uint16_t *)Ld.out : (uint16_t *)ws_o) + base + 128 * b;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = 4 * u + (lane >> 4), c = 16 * (lane & 15);
+                const int R = 2 * r + (c >> 7);
+                const u32x4 v = *(const u32x4 *)((R < 32 ? slot_a : slot_b) + (R & 31) * F_ROWB + 128 * b + (c & 127));
+                *(u32x4 *)((char *)(dst + (32 * nh + r) * M_DC) + c) = v;
+            }
+        }
+        if (b == 0 && g == 0) {
+            const int head = 32 * nh + j;
+            if (nsplit == 1) {
+                if (Ld.lse)
+                    Ld.lse[i * M_H + head] = (l[nh] > 0.f) ? (m[nh] + __log2f(l[nh])) * LN2 : -INFINITY;
+            } else {
+                float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
+                pml[0] = m[nh];
+                pml[1] = l[nh];
+            }
+        }
+    }
+}
+
+constexpr int TM_MAX_GROUP = 4;       // consecutive splits of one row run by one block, at most
+constexpr int TM_QROWB = 1168;        // Q staging row in LDS: 576 bf16 + 16 pad
+constexpr int TM_QOFF = 3 * TM_SLOTB; // Q staged in slots 3..6 before the first gathers
+static_assert(M_H * TM_QROWB <= 4 * TM_SLOTB, "Q staging fits slots 3..6");
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(TM_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int64_t T, int64_t n_rows,
+                                                                MlaLayersDev layers,
+                                                                const int32_t *__restrict__ indices, int k,
+                                                                float sm_scale, int nsplit, int tiles_per_split,
+                                                                int group, int64_t pairs_per_xcd,
+                                                                float *__restrict__ ws_o, float *__restrict__ ws_ml)
+{
+    __shared__ __attribute__((aligned(16))) char ring[TM_SLOTS][TM_SLOTB];
+    __shared__ __attribute__((aligned(16))) char pbuf[2][TM_PBUFB];  // P^T of tiles s, s - 1
+    __shared__ int32_t sidx[F_IDX];                                   // the group's index slots
+    __shared__ float xm[2][M_H];                  // reference-maximum exchange (key halves)
+    __shared__ float xl[2][2][M_H];               // row sums of the key halves, by split parity
+    __shared__ float xr[2][M_H];                  // reference maximum, by split parity
+    __shared__ float xs[TM_MAX_GROUP][2][M_H];    // largest logit per split and key half (reruns)
+    __shared__ uint32_t sh_ne, sh_ovf;            // non-empty tiles; splits to run again
+
+    const int ngroups = nsplit / group;
     const int64_t pair = xcd_pair(pairs_per_xcd);
-    if (pair >= n_rows * nsplit)
+    if (pair >= n_rows * ngroups)
         return;
-    const int64_t orow = pair / nsplit;
-    const int split = (int)(pair % nsplit);
+    const int64_t orow = pair / ngroups;
+    const int split0 = (int)(pair % ngroups) * group;
     const int layer = (int)(orow / T);
     const int64_t i = orow % T;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tw = w & 3;  // wave within its team
     const int g = lane >> 5, j = lane & 31;
-    const int hh = w & 1, dq = w >> 1, wp = w ^ 2;
     const MlaLayerDev Ld = layers.l[layer];
     const RowInfo r = row_info(L, i);
     const float c2 = sm_scale * Ld.kv_scale * LOG2E;
 
+    // the group's tiles: split split0 + gs covers tiles [gs tps, min(nt, (gs + 1) tps))
+    const int tps = tiles_per_split;
     const int ntiles_all = (k + M_TILE - 1) / M_TILE;
-    const int t_begin = split * tiles_per_split;
-    const int ntiles = max(0, min(ntiles_all, t_begin + tiles_per_split) - t_begin);
-    const int32_t *irow = indices + i * k;
+    const int g_begin = split0 * tps;
+    const int nt = max(0, min(ntiles_all, (split0 + group) * tps) - g_begin);
+    const int32_t *irow = indices + i * k + (int64_t)g_begin * M_TILE;
+    const int nidx = min(k - g_begin * M_TILE, nt * M_TILE);
 
-    // the split's whole index list goes to LDS up front (its latency overlaps Q's), so the
-    // tile loop issues no loads the compiler would wait on together with the tile DMAs
+    // ---- prologue (all 512 threads): the group's index list and the row's Q to LDS, slots
+    //      0..2 cleared; the non-empty tiles noted
     {
-        const int s0 = t_begin * M_TILE, nsl = min(k - s0, ntiles * M_TILE);
-        for (int e = tid; e < ntiles * M_TILE; e += M_THREADS)
-            sidx[e] = e < nsl ? irow[s0 + e] : -1;
+        int32_t v[F_IDX / TM_THREADS];
+#pragma unroll
+        for (int u = 0; u < F_IDX / TM_THREADS; ++u) {
+            const int e = tid + TM_THREADS * u;
+            v[u] = e < nidx ? irow[e] : -1;
+        }
+        u32x4 qv[(M_H * 72 + TM_THREADS - 1) / TM_THREADS];
+        const u32x4 *qsrc = (const u32x4 *)((const uint16_t *)Ld.q + i * M_H * M_DQK);
+#pragma unroll
+        for (int u = 0; u < (M_H * 72 + TM_THREADS - 1) / TM_THREADS; ++u) {
+            const int c = tid + TM_THREADS * u;
+            if (c < M_H * 72)
+                qv[u] = qsrc[c];
+        }
+        for (int e = tid; e < 3 * TM_SLOTB / 16; e += TM_THREADS)
+            ((u32x4 *)&ring[0][0])[e] = u32x4{0u, 0u, 0u, 0u};
+        if (tid == 0) {
+            sh_ne = 0u;
+            sh_ovf = 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < F_IDX / TM_THREADS; ++u) {
+            const int e = tid + TM_THREADS * u;  // a wave covers one tile: e >> 6 is wave-uniform
+            if (e < nt * M_TILE) {
+                sidx[e] = v[u];
+                if (__ballot(v[u] >= 0) != 0ull && lane == 0)
+                    atomicOr(&sh_ne, 1u << (e >> 6));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < (M_H * 72 + TM_THREADS - 1) / TM_THREADS; ++u) {
+            const int c = tid + TM_THREADS * u;
+            if (c < M_H * 72)
+                *(u32x4 *)(&ring[0][0] + TM_QOFF + (c / 72) * TM_QROWB + 16 * (c % 72)) = qv[u];
+        }
+        __syncthreads();
     }
-
-    // Q^T operand in the permuted dim order (see above)
-    bf16x8 qT[18];
-    {
-        const uint16_t *qp = (const uint16_t *)Ld.q + ((i * M_H + 32 * hh + j) * M_DQK + 288 * dq + 16 * g);
-#pragma unroll
-        for (int t = 0; t < 18; ++t)
-            qT[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 32 * (t >> 1) + 8 * (t & 1)));
-    }
-
-    f32x16 O[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-        O[mt] = f32x16{};
-
-    // this sequence's rows, or with paged caches the whole cache (host: at most 4 GiB - 1 MiB)
-    const bool paged = L.block_table != nullptr;
-    const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * 576;
-    const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * 576, seq_bytes);
-    const uint32_t lds0 = lds_addr_of(&kt8[0][0]);
-    uint32_t rc[F_DMA_PER_WAVE];
-    dma_geometry(w, lane, rc);
-
-    // rows with index -1 may be skipped by the DMA: start from finite (zero) data
-    for (int e = tid; e < 3 * F_TILEB / 16; e += M_THREADS)
-        ((u32x4 *)&kt8[0][0])[e] = u32x4{0u, 0u, 0u, 0u};
-    if (tid == 0)
-        sh_flag = 0;
-
-    // V^T read geometry: 16-lane group G covers dims +16 * (G & 1), keys +8 * (G >> 1)
-    const int mq = lane & 15;
-    const int voffs = (8 * (lane >> 5) + (mq >> 1)) * F_ROWB + 256 * dq + 16 * ((lane >> 4) & 1) + 8 * (mq & 1);
-    const char *arow0 = &kt8[0][0] + j * F_ROWB + 288 * dq + 16 * g;  // S operand row of buffer 0
-
-    float m_ref = -INFINITY, m_seen = -INFINITY, l_own = 0.f;
-    bool ovf = false;
-    f32x16 S[2];
-    bf16x8 bop[4];  // P^T operands of the tile whose PV runs next (4 steps of 16 keys)
-
-    // ---- S^T partial step p (k-steps 2p, 2p+1) of the tile in buffer kb
-    auto s_load = [&](int kb, int p, u32x4 (&A)[2]) {
-        const char *a = arow0 + kb * F_TILEB + 32 * p;
-        A[0] = *(const u32x4 *)a;
-        A[1] = *(const u32x4 *)(a + 32 * F_ROWB);
+    const uint32_t ne = sh_ne;
+    // tile s is the first non-empty tile of its split
+    auto first_of_split = [&](int s) __attribute__((always_inline)) {
+        const int st = (s / tps) * tps;
+        const uint32_t below = ((1u << s) - 1u) & ~((1u << st) - 1u);
+        return ((ne >> s) & 1u) != 0u && (ne & below) == 0u;
     };
-    auto s_mfma = [&](const u32x4 (&A)[2], int p) {
-        const bf16x8 a00 = fp8x8_to_bf16x8(A[0][0], A[0][1]), a10 = fp8x8_to_bf16x8(A[1][0], A[1][1]);
-        const bf16x8 a01 = fp8x8_to_bf16x8(A[0][2], A[0][3]), a11 = fp8x8_to_bf16x8(A[1][2], A[1][3]);
-        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a00, qT[2 * p], S[0], 0, 0, 0);
-        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a10, qT[2 * p], S[1], 0, 0, 0);
-        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a01, qT[2 * p + 1], S[0], 0, 0, 0);
-        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a11, qT[2 * p + 1], S[1], 0, 0, 0);
-    };
-    // ---- PV step u (keys 16u .. 16u+15) of the tile in buffer vb, dims 256dq + 32mt + ..
-    auto v_load = [&](int vb, int u, i32x2 (&V)[8]) {
-        const char *v = &kt8[0][0] + vb * F_TILEB + voffs + (32 * (u >> 1) + 16 * (u & 1)) * F_ROWB;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            V[mt] = lds_tr8(v + 32 * mt);
-    };
-    auto pv_mfma = [&](const i32x2 (&V)[8], const bf16x8 &b, int mt0) {
-#pragma unroll
-        for (int mt = mt0; mt < mt0 + 4; ++mt)
-            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                fp8x8_to_bf16x8((uint32_t)V[mt][0], (uint32_t)V[mt][1]), b, O[mt], 0, 0, 0);
+    auto last_of_split = [&](int s) __attribute__((always_inline)) {
+        return s + 1 == nt || (s + 1) % tps == 0;
     };
 
-    // ---- softmax of the tile whose S^T partials are in S (indices sx): fixes bop
-    auto softmax = [&](const int32_t *sx) {
-        const uint64_t valid = __ballot(sx[lane] >= 0);
-        {  // swap the half partials; s = full S^T for keys 32*dq + .. (this wave's)
-            const f32x16 give = dq ? S[0] : S[1];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                xs[w][q4][lane] = f32x4{give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]};
-        }
-        lds_barrier();
-        f32x16 s = dq ? S[1] : S[0];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 o = xs[wp][q4][lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                s[4 * q4 + e] = dq ? (o[e] + s[4 * q4 + e]) : (s[4 * q4 + e] + o[e]);
-        }
-        const uint32_t vkeys = (uint32_t)(valid >> (32 * dq)) >> (4 * g);
-        const bool full = valid == ~0ull;
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const bool ok = full || ((vkeys >> (8 * (rr >> 2) + (rr & 3))) & 1u);
-            s[rr] = ok ? s[rr] * c2 : -INFINITY;
-            mloc = fmaxf(mloc, s[rr]);
-        }
-        mloc = fmaxf(mloc, other_half(mloc, g));
-        if (m_ref == -INFINITY && valid != 0ull) {  // first non-empty tile (block-uniform)
-            if (g == 0)
-                xm[w][j] = mloc;
-            lds_barrier();
-            m_ref = fmaxf(mloc, xm[wp][j]);
-            lds_barrier();
-        }
-        m_seen = fmaxf(m_seen, mloc);
-        ovf |= mloc > m_ref + 100.f;
-        uint32_t pk[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float p0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q] - m_ref);
-            const float p1 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q + 1] - m_ref);
-            l_own += p0 + p1;
-            pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
-        }
-        xp[w][0][lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        xp[w][1][lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-        lds_barrier();
-        const u32x4 pp0 = xp[wp][0][lane], pp1 = xp[wp][1][lane];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int khu = u >> 1, jj = u & 1;
-            const u32x4 own = jj ? u32x4{pk[4], pk[5], pk[6], pk[7]} : u32x4{pk[0], pk[1], pk[2], pk[3]};
-            const u32x4 pw = (khu == dq) ? own : (jj ? pp1 : pp0);
-            // keys 4g..4g+3 (dwords 0,1) and 8+4g..8+4g+3 (dwords 2,3) -> 8g'..8g'+7
-            const auto s0 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-            bop[u] = __builtin_bit_cast(bf16x8, u32x4{s0[0], s1[0], s0[1], s1[1]});
-        }
-    };
+    // The two teams run separate code (so that Q^T and O share registers) with the same
+    // sequence of barriers: per pass two after the first gathers, one per step, two more in
+    // the step of each split's first non-empty tile in the first pass; the rerun flag; per
+    // rerun split a pass of its own.
+    if (w < 4) {
+        // ================================ S team ================================
+        // wave a: heads 32 hh .. +31, keys 32 hi .. +31 of each tile
+        const int hh = tw & 1, hi = tw >> 1, head = 32 * hh + j;
+        // Q^T of its 32 heads over all 576 dims; k-step 2p + h of lane half g covers dims
+        // 32p + 16g + 8h .. +7 (the K rows are read 16 bytes per lane in the same order)
+        bf16x8 qT[36];
+        const char *srow = &ring[0][0] + j * F_ROWB + 16 * g;  // S operand row j of slot 0
+        float m_ref = -INFINITY, m_seen = -INFINITY, l_own = 0.f;
+        bool ovf = false;
 
-    auto run = [&]() {
-        __builtin_amdgcn_s_waitcnt(0x0070);  // indices and Q have landed: nothing else in flight
-        lds_barrier();
-        if (ntiles > 0)
-            dma_tile(seq, lds0, sidx, w, rc);
-        if (ntiles > 1) {
-            dma_tile(seq, lds0 + F_TILEB, sidx + M_TILE, w, rc);
-            wait_but_last_tile8(w);  // tile 0 has landed
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        lds_barrier();
-
-        for (int tt = 0; tt < ntiles; ++tt) {
-            const int b0 = tt % 3;
-            if (tt + 2 < ntiles)  // into the buffer of tile tt - 1, consumed before the last barrier
-                dma_tile(seq, lds0 + (uint32_t)((tt + 2) % 3) * F_TILEB, sidx + (tt + 2) * M_TILE, w, rc);
-
-            // ---- S^T partials of tile tt (two key halves over this wave's 288 dims)
-            S[0] = f32x16{};
-            S[1] = f32x16{};
-            {
-                u32x4 A[2][2];
-                s_load(b0, 0, A[0]);
+        // step s (tile s of the pass starting at tile t0): logits of this wave's key half,
+        // softmax numerators against the split's reference maximum, P^T to LDS
+        auto s_step = [&](int s, int t0, bool need_ref) __attribute__((always_inline)) {
+            const int gs = s / tps;
+            if (s % tps == 0 || s == t0) {  // a split starts
+                m_ref = need_ref ? -INFINITY : fmaxf(xs[gs][0][head], xs[gs][1][head]);
+                m_seen = -INFINITY;
+                l_own = 0.f;
+                ovf = false;
+            }
+            const int sl = (2 * (s - t0) + hi) % TM_SLOTS;
+            const char *a = srow + sl * TM_SLOTB;
+            char *prow = &pbuf[(s - t0) & 1][0] + head * TM_PROWB + 2 * (32 * hi + 4 * g);
+            const uint64_t valid = __ballot(sidx[s * M_TILE + lane] >= 0);
+            if (valid == 0ull) {  // no key of the tile: P = 0 (also before the reference is fixed)
 #pragma unroll
-                for (int p = 0; p < 9; ++p) {
-                    if (p + 1 < 9)
-                        s_load(b0, p + 1, A[(p + 1) & 1]);
-                    s_mfma(A[p & 1], p);
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int q = 0; q < 4; ++q)
+                    *(u32x2 *)(prow + 16 * q) = u32x2{0u, 0u};
+            } else {
+                f32x16 S = f32x16{};
+                u32x4 A[2];
+                A[0] = *(const u32x4 *)a;
+#pragma unroll
+                for (int p = 0; p < 18; ++p) {
+                    if (p + 1 < 18)
+                        A[(p + 1) & 1] = *(const u32x4 *)(a + 32 * (p + 1));
+                    const u32x4 x = A[p & 1];
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(x[0], x[1]), qT[2 * p], S, 0, 0, 0);
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(x[2], x[3]), qT[2 * p + 1], S, 0, 0,
+                                                                0);
+                }
+                // lane (g, j) holds keys 32 hi + 8 (rr >> 2) + 4 g + (rr & 3) of head 32 hh + j
+                const uint32_t vkeys = (uint32_t)(valid >> (32 * hi)) >> (4 * g);
+                const bool full = valid == ~0ull;
+                float mloc = -INFINITY;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const bool ok = full || ((vkeys >> (8 * (rr >> 2) + (rr & 3))) & 1u);
+                    S[rr] = ok ? S[rr] * c2 : -INFINITY;
+                    mloc = fmaxf(mloc, S[rr]);
+                }
+                mloc = fmaxf(mloc, other_half(mloc, g));
+                if (need_ref && first_of_split(s)) {  // the maximum over both key halves
+                    if (g == 0)
+                        xm[hi][head] = mloc;
+                    lds_barrier();
+                    m_ref = fmaxf(xm[0][head], xm[1][head]);
+                    lds_barrier();
+                }
+                m_seen = fmaxf(m_seen, mloc);
+                ovf |= mloc > m_ref + 100.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float p4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        p4[e] = __builtin_amdgcn_exp2f(S[4 * q + e] - m_ref);  // masked: exp2(-inf) = 0
+                    l_own += p4[0] + p4[1];
+                    l_own += p4[2] + p4[3];
+                    *(u32x2 *)(prow + 16 * q) = u32x2{pack_bf16x2(p4[0], p4[1]), pack_bf16x2(p4[2], p4[3])};
                 }
             }
-            softmax(sidx + tt * M_TILE);
-
-            // ---- O^T += V^T . P^T over the tile's 64 keys
-            {
-                i32x2 V[2][8];
-                v_load(b0, 0, V[0]);
+            if (last_of_split(s)) {  // (row sum, reference maximum) to the PV team
+                const float l_pair = l_own + other_half(l_own, g);
+                if (g == 0) {
+                    xl[gs & 1][hi][head] = l_pair;
+                    if (hi == 0)
+                        xr[gs & 1][head] = m_ref;
+                    if (need_ref)
+                        xs[gs][hi][head] = m_seen;
+                }
+                if (ovf)
+                    atomicOr(&sh_ovf, 1u << gs);
+            }
+        };
+        // Q^T from LDS; the staging slots are cleared once every S wave has its copy
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    if (u + 1 < 4)
-                        v_load(b0, u + 1, V[(u + 1) & 1]);
-                    pv_mfma(V[u & 1], bop[u], 0);
-                    pv_mfma(V[u & 1], bop[u], 4);
-                    __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < 36; ++t)
+            qT[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(&ring[0][0] + TM_QOFF + head * TM_QROWB +
+                                                                64 * (t >> 1) + 32 * g + 16 * (t & 1)));
+        // pass 0: every tile of the group; pass 1 + gs: split gs again, if it overflowed
+        uint32_t rerun = 0u;
+        for (int pass = 0; pass <= group; ++pass) {
+            const int t0 = pass == 0 ? 0 : (pass - 1) * tps;
+            const int t1 = pass == 0 ? nt : min(nt, pass * tps);
+            if ((pass == 0 && nt > 0) || (pass > 0 && ((rerun >> (pass - 1)) & 1u))) {
+                lds_barrier();
+                if (pass == 0)
+                    for (int e = tid; e < 4 * TM_SLOTB / 16; e += 256)
+                        ((u32x4 *)(&ring[0][0] + TM_QOFF))[e] = u32x4{0u, 0u, 0u, 0u};
+                lds_barrier();  // tile t0 has landed
+                for (int s = t0; s <= t1; ++s) {
+                    if (s < t1)
+                        s_step(s, t0, pass == 0);
+                    lds_barrier();
                 }
             }
-
-            // ---- tile tt + 1 must have landed (tile tt + 2 may stay in flight)
-            if (tt + 1 < ntiles) {
-                if (tt + 2 < ntiles)
-                    wait_but_last_tile8(w);
-                else
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (pass == 0) {
+                __syncthreads();
+                rerun = sh_ovf;
             }
-            lds_barrier();  // tile tt, S partials and P consumed; tile tt + 1 visible to all
         }
-    };
-    run();
-    if (ovf)
-        sh_flag = 1;
-    __syncthreads();
-    if (sh_flag) {  // rare: rerun with the exact maximum of the first run as the reference
-        if (g == 0)
-            xm[w][j] = m_seen;
-        __syncthreads();
-        m_ref = fmaxf(m_seen, xm[wp][j]);
-        l_own = 0.f;
+    } else {
+        // ================================ PV team ================================
+        // wave b: dims 128 b .. +127 of all 64 heads
+        const int b = tw;
+        f32x16 O[4][2];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            O[mt] = f32x16{};
-        __syncthreads();
-        run();
-    }
+        for (int mt = 0; mt < 4; ++mt)
+            O[mt][0] = O[mt][1] = f32x16{};
 
-    float l_run = l_own + other_half(l_own, g);
-    __syncthreads();
-    if (g == 0)
-        xm[w][j] = l_run;
-    __syncthreads();
-    l_run = dq ? (xm[wp][j] + l_run) : (l_run + xm[wp][j]);
-    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml, &kt8[0][0], tid);
+        // this sequence's rows, or with paged caches the whole cache (host: at most 4 GiB - 1 MiB)
+        const bool paged = L.block_table != nullptr;
+        const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * 576;
+        const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * 576, seq_bytes);
+        const uint32_t lds0 = lds_addr_of(&ring[0][0]);
+        uint32_t rc[TM_DMA_PER_WAVE];
+        slot_geometry(b, lane, rc);
+        // V^T read geometry: 16-lane group G covers dims +16 (G & 1), keys +8 (G >> 1)
+        const int mq = lane & 15;
+        const int voffs = (8 * g + (mq >> 1)) * F_ROWB + 128 * b + 16 * ((lane >> 4) & 1) + 8 * (mq & 1);
+
+        // O^T += V^T . P^T over the 64 keys of tile t (pass starting at t0)
+        auto pv_tile = [&](int t, int t0) __attribute__((always_inline)) {
+            const int h0 = 2 * (t - t0);
+            const char *v0 = &ring[0][0] + (h0 % TM_SLOTS) * TM_SLOTB + voffs;
+            const char *v1 = &ring[0][0] + ((h0 + 1) % TM_SLOTS) * TM_SLOTB + voffs;
+            const char *pb = &pbuf[(t - t0) & 1][0] + j * TM_PROWB + 16 * g;
+            i32x2 V[2][4];
+            auto v_load = [&](int u, i32x2 (&Vd)[4]) __attribute__((always_inline)) {
+                const char *v = ((u >> 1) ? v1 : v0) + 16 * (u & 1) * F_ROWB;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    Vd[mt] = lds_tr8(v + 32 * mt);
+            };
+            v_load(0, V[0]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (u + 1 < 4)
+                    v_load(u + 1, V[(u + 1) & 1]);
+                // keys 16u + 8g .. +7 of heads j, 32 + j: the key order of the V^T operand
+                const bf16x8 p0 = __builtin_bit_cast(bf16x8, *(const u32x4 *)(pb + 32 * u));
+                const bf16x8 p1 = __builtin_bit_cast(bf16x8, *(const u32x4 *)(pb + 32 * TM_PROWB + 32 * u));
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const bf16x8 va = fp8x8_to_bf16x8((uint32_t)V[u & 1][mt][0], (uint32_t)V[u & 1][mt][1]);
+                    O[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p0, O[mt][0], 0, 0, 0);
+                    O[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1, O[mt][1], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // the split of tile t (pass starting at t0) is complete: its result out, O cleared
+        auto finish_split = [&](int t, int t0) __attribute__((always_inline)) {
+            const int gs = t / tps;
+            const int h0 = 2 * (t - t0);
+            char *sa = &ring[0][0] + (h0 % TM_SLOTS) * TM_SLOTB, *sb = &ring[0][0] + ((h0 + 1) % TM_SLOTS) * TM_SLOTB;
+            float l[2], m[2];
+#pragma unroll
+            for (int nh = 0; nh < 2; ++nh) {
+                l[nh] = xl[gs & 1][0][32 * nh + j] + xl[gs & 1][1][32 * nh + j];
+                m[nh] = xr[gs & 1][32 * nh + j];
+            }
+            mla_fp8_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, sa, sb, ws_o, ws_ml);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                O[mt][0] = O[mt][1] = f32x16{};
+        };
+        auto run = [&](int t0, int t1, bool need_ref) __attribute__((always_inline)) {
+            const int nslots = 2 * (t1 - t0);
+            for (int h = 0; h < min(3, nslots); ++h)
+                dma_slot(seq, lds0 + (uint32_t)h * TM_SLOTB, sidx + (2 * t0 + h) * TM_HALF, b, lane, rc);
+            lds_barrier();  // (first pass: the S team has its copy of Q and clears slots 3..6)
+            if (nslots > 2)
+                wait_but_last_slot(b);  // tile t0 has landed
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            for (int s = t0; s <= t1; ++s) {
+                const int hs = 2 * (s - t0);
+                // half tiles hs+3, hs+4 into the slots of tile s - 2 (consumed in step s - 1)
+                for (int h = hs + 3; h <= hs + 4; ++h)
+                    if (h < nslots)
+                        dma_slot(seq, lds0 + (uint32_t)(h % TM_SLOTS) * TM_SLOTB, sidx + (2 * t0 + h) * TM_HALF,
+                                 b, lane, rc);
+                if (need_ref && s < t1 && first_of_split(s)) {
+                    lds_barrier();  // the S team's two exchange barriers
+                    lds_barrier();
+                }
+                if (s > t0)
+                    pv_tile(s - 1, t0);
+                // tile s + 1 (half tiles hs+2, hs+3) must have landed; hs+4 may stay in flight
+                if (s + 1 < t1) {
+                    if (hs + 4 < nslots)
+                        wait_but_last_slot(b);
+                    else
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                // after the wait, so that the result's stores are the newest memory operations
+                // and the count-based waits of the next step do not wait for them
+                if (s > t0 && last_of_split(s - 1))
+                    finish_split(s - 1, t0);
+                lds_barrier();
+            }
+        };
+        uint32_t rerun = 0u;
+        for (int pass = 0; pass <= group; ++pass) {
+            const int t0 = pass == 0 ? 0 : (pass - 1) * tps;
+            const int t1 = pass == 0 ? nt : min(nt, pass * tps);
+            if ((pass == 0 && nt > 0) || (pass > 0 && ((rerun >> (pass - 1)) & 1u)))
+                run(t0, t1, pass == 0);
+            if (pass == 0) {
+                __syncthreads();
+                rerun = sh_ovf;
+            }
+        }
+        // splits past the end of the index list (none under the split policy): empty results
+        for (int gs = 0; gs < group; ++gs)
+            if (gs * tps >= nt) {
+                const float l[2] = {0.f, 0.f}, m[2] = {-INFINITY, -INFINITY};
+                mla_fp8_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, &ring[0][0],
+                                       &ring[1][0], ws_o, ws_ml);
+            }
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1356,12 +1528,20 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
     hipLaunchKernelGGL((mla_kernel<F8, OF>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,  \
                        indices, k, sm_scale, ns, tps, ppx, wo, wml)
     if (kv_fp8) {
+        // consecutive splits of a row share a block while that leaves a block per CU: the
+        // splits (and so every result bit) stay those of the policy above, only their
+        // scheduling changes
+        int group = 1;
+        while (group * 2 <= TM_MAX_GROUP && ns % (group * 2) == 0 && pairs / (group * 2) >= MLA_TARGET_BLOCKS)
+            group *= 2;
+        const int64_t gpx = (pairs / group + 7) / 8;
+        dim3 fgrid((unsigned)(8 * gpx));
         if (out_f32)
-            hipLaunchKernelGGL((mla_fp8_kernel<true>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
-                               indices, k, sm_scale, ns, tps, ppx, wo, wml);
+            hipLaunchKernelGGL((mla_fp8_kernel<true>), fgrid, dim3(TM_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, tps, group, gpx, wo, wml);
         else
-            hipLaunchKernelGGL((mla_fp8_kernel<false>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
-                               indices, k, sm_scale, ns, tps, ppx, wo, wml);
+            hipLaunchKernelGGL((mla_fp8_kernel<false>), fgrid, dim3(TM_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, tps, group, gpx, wo, wml);
     } else if (T <= MLA_HH_MAX_ROWS) {
         // few rows (decode): half-head blocks, two per CU
         const int64_t hpairs = pairs * 2, hppx = (hpairs + 7) / 8;
