@@ -35,6 +35,8 @@
 // the workspace they wrote zero again, so it can be reused as is for any layout.  If a
 // row's bin d holds more than 8192 keys (heavily tied scores), two more radix passes over
 // the row find the exact kk-th key and its ties are taken in position order.
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -208,11 +210,16 @@ __device__ __forceinline__ f32x4 load4(const float *row, int64_t s, int64_t n)
 
 // One wave over positions base .. base+255 (base a multiple of 256; lane l holds base+4l ..
 // +3): the bitmap words of the positions whose bin is above d (lanes 8w'.. 8w'+7 build word
-// w' with three xor-shuffles; no atomics), and the keys of bin d appended to `mem` through
-// one counter atomic per wave and element.
-template <typename WordStore, typename MemberStore>
+// w' with three DPP moves; no atomics), and the keys of bin d either handed to store_member
+// per element (a ballot and the lane's rank among the wave's members) or, with note_member
+// given, only flagged per lane and element, for the caller to reserve once per wave.
+struct NoNote {
+    __device__ void operator()(int, bool) const {}
+};
+template <typename WordStore, typename MemberStore, typename MemberNote = NoNote>
 __device__ __forceinline__ void take_wave(int64_t base, const f32x4 &x, int64_t n, uint32_t d, int lane,
-                                          WordStore store_word, MemberStore store_member)
+                                          WordStore store_word, MemberStore store_member,
+                                          MemberNote note_member = NoNote())
 {
     const int64_t s0 = base + 4 * lane;
     uint32_t key[4], nib = 0;
@@ -222,19 +229,25 @@ __device__ __forceinline__ void take_wave(int64_t base, const f32x4 &x, int64_t 
         if (s0 + e < n && (key[e] >> 21) > d)
             nib |= 1u << e;
     }
+    // OR over each group of 8 lanes with DPP moves: the quad, then row_shr:4 (lanes 4-7 and
+    // 12-15 of each 16-lane row then hold their 8-lane group's word)
     uint32_t word = nib << (4 * (lane & 7));
-    word |= __shfl_xor(word, 1, 64);
-    word |= __shfl_xor(word, 2, 64);
-    word |= __shfl_xor(word, 4, 64);
-    if ((lane & 7) == 0 && base + 32 * (lane >> 3) < n)
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xf, 0xf, false);  // quad_perm 1,0,3,2
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xf, 0xf, false);  // quad_perm 2,3,0,1
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x114, 0xf, 0xf, true);  // row_shr:4
+    if ((lane & 7) == 7 && base + 32 * (lane >> 3) < n)
         store_word((base >> 5) + (lane >> 3), word);
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const bool m = s0 + e < n && (key[e] >> 21) == d;
-        const uint64_t mb = __ballot(m);
-        if (mb)
-            store_member(mb, (uint32_t)__popcll(mb & below), m, composite(key[e], s0 + e));
+        if constexpr (std::is_same<MemberNote, NoNote>::value) {
+            const uint64_t mb = __ballot(m);
+            if (mb)
+                store_member(mb, (uint32_t)__popcll(mb & below), m, composite(key[e], s0 + e));
+        } else {
+            note_member(e, m);
+        }
     }
 }
 
@@ -321,21 +334,30 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     lds_sync();
     const uint32_t d = pick_digit<TK_BINS>(hist, kk, sh).digit;
 
+    // bitmap words of this chunk; the members of bin d are noted per lane (bit 4u + e) and
+    // appended to lmem with one LDS reservation per wave, in (lane, u, e) order
+    uint32_t mflag = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t base = s0 + (int64_t)u * 4 * H_THREADS + 256 * wave;
         if (base < n)
             take_wave(
                 base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bits[w] = word; },
-                [&](uint64_t mb, uint32_t rank, bool m, uint64_t comp) {
-                    uint32_t at = 0;
-                    if (lane == 0)
-                        at = atomicAdd(&lcnt, (uint32_t)__popcll(mb));
-                    at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at) + rank;
-                    if (m)
-                        lmem[at] = comp;  // at < H_CHUNK: one slot per position
-                });
+                [&](uint64_t, uint32_t, bool m, uint64_t) {},
+                [&](int e, bool m) { mflag |= (m ? 1u : 0u) << (4 * u + e); });
     }
+    const uint32_t mc = (uint32_t)__popc(mflag);
+    const uint32_t incl = wave_incl_scan(mc, lane);
+    uint32_t wbase = 0;
+    if (lane == 63 && incl != 0u)
+        wbase = atomicAdd(&lcnt, incl);
+    uint32_t at = (uint32_t)__shfl((int)wbase, 63, 64) + incl - mc;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if ((mflag >> (4 * u + e)) & 1u)  // at < H_CHUNK: one slot per position
+                lmem[at++] = composite(score_key(v[u][e]), s0 + (int64_t)u * 4 * H_THREADS + 256 * wave + 4 * lane + e);
     __syncthreads();
     // one reservation per block in the row's member list, then a coalesced copy
     const uint32_t m = lcnt;
@@ -771,7 +793,40 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
     const int nw = (int)((n + 31) >> 5);
     // MB rows keep their bitmap in global memory unless it fits the LDS one
     const bool gbm = MODE == TK_MB && ws.W > TK_ROW_BITS / 32;
-    uint32_t *bm = gbm ? ws.bits + i * ws.W : bmap_lds;
+    uint32_t *gbits = ws.bits + i * ws.W;
+    // bitmap access through typed pointers (a generic one would turn every LDS access into a
+    // flat access waited for on its own)
+    auto bm_or = [&](int64_t w, uint32_t bit) {
+        if (gbm)
+            atomicOr(&gbits[w], bit);
+        else
+            atomicOr(&bmap_lds[w], bit);
+    };
+
+    // MB: the member count, the bitmap words and the members (written by topk_mark_kernel) are
+    // requested first, so their latency overlaps the histogram's and the digit pick
+    constexpr int PB = TK_ROW_BITS / 32 / TK_THREADS, PM = TK_CAP / TK_THREADS;
+    uint32_t bw[PB];
+    uint64_t mv[PM];
+    uint32_t c = 0;  // members of bin d
+    if (MODE == TK_MB) {
+        c = ws.cnt[i];
+        if (!gbm) {
+            const uint32_t *g = ws.bits + i * ws.W;
+#pragma unroll
+            for (int q = 0; q < PB; ++q) {
+                const int w = tid + TK_THREADS * q;
+                bw[q] = w < nw ? g[w] : 0u;
+            }
+        }
+        const uint64_t *memb = ws.memb + i * TK_CAP;
+        const uint32_t cm = min(c, (uint32_t)TK_CAP);
+#pragma unroll
+        for (int q = 0; q < PM; ++q) {
+            const uint32_t e = tid + TK_THREADS * q;
+            mv[q] = e < cm ? memb[e] : 0ull;
+        }
+    }
 
     // ---- 1. threshold bin d from the histogram of the top 11 key bits
     if (tid == 0)
@@ -787,7 +842,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
     const uint32_t need = kk - p0.above;  // 1 .. p0.count members of bin d are taken
 
     // ---- 2. bitmap of the positions above bin d; members of bin d into cand
-    uint32_t c;  // members of bin d
     if (MODE == TK_ROW) {
         constexpr int U = 4;  // 4 vectors per thread: 16384 positions per round
 #pragma unroll 1
@@ -801,7 +855,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
                 const int64_t base = b0 + (int64_t)u * 4 * TK_THREADS + 256 * wave;
                 if (base < n)
                     take_wave(
-                        base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bm[w] = word; },
+                        base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bmap_lds[w] = word; },
                         [&](uint64_t mb, uint32_t rank, bool m, uint64_t comp) {
                             uint32_t at = 0;
                             if (lane == 0)
@@ -815,19 +869,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
         __syncthreads();
         c = sh_cnt;
     } else {
-        if (!gbm) {  // copy the bitmap into LDS, leaving the global words zero
+        if (!gbm) {  // the bitmap into LDS, the global words left zero
             uint32_t *g = ws.bits + i * ws.W;
-            for (int w = tid; w < nw; w += TK_THREADS) {
-                bmap_lds[w] = g[w];
-                g[w] = 0u;
+#pragma unroll
+            for (int q = 0; q < PB; ++q) {
+                const int w = tid + TK_THREADS * q;
+                if (w < nw) {
+                    bmap_lds[w] = bw[q];
+                    g[w] = 0u;
+                }
             }
         }
-        c = ws.cnt[i];  // written by topk_mark_kernel
         uint64_t *memb = ws.memb + i * TK_CAP;
-        for (uint32_t e = tid; e < min(c, (uint32_t)TK_CAP); e += TK_THREADS) {
-            if (c <= (uint32_t)TK_CAP)
-                cand[e] = memb[e];
-            memb[e] = 0ull;  // everything this call wrote is left zero for the next one
+#pragma unroll
+        for (int q = 0; q < PM; ++q) {
+            const uint32_t e = tid + TK_THREADS * q;
+            if (e < min(c, (uint32_t)TK_CAP)) {
+                if (c <= (uint32_t)TK_CAP)
+                    cand[e] = mv[q];
+                memb[e] = 0ull;  // everything this call wrote is left zero for the next one
+            }
         }
         __syncthreads();
         if (tid == 0)
@@ -868,7 +929,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
             const uint64_t v = cand[e];
             if (v >= lo) {
                 const uint32_t pos = comp_pos(v);
-                atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+                bm_or(pos >> 5, 1u << (pos & 31));
             }
         }
     } else {
@@ -899,7 +960,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
         for (int64_t s = tid; s < n; s += TK_THREADS) {
             const uint32_t key = score_key(row[s]);
             if ((key >> 21) == d && key > tau)
-                atomicOr(&bm[s >> 5], 1u << (s & 31));
+                bm_or(s >> 5, 1u << (s & 31));
         }
         uint32_t taken = 0;
         for (int64_t b0 = 0; b0 < n && taken < nd; b0 += TK_THREADS) {
@@ -908,7 +969,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
             uint32_t tot;
             const uint32_t rank = block_excl_scan(flag, wsum, &tot);
             if (flag && taken + rank < nd)
-                atomicOr(&bm[s >> 5], 1u << (s & 31));
+                bm_or(s >> 5, 1u << (s & 31));
             taken += tot;
         }
     }
@@ -922,24 +983,49 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
     const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
     auto word = [&](int w) -> uint32_t {
         if (gbm)  // written by other CUs and by atomics: read past the L1
-            return __hip_atomic_load(&bm[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return bm[w];
+            return __hip_atomic_load(&gbits[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return bmap_lds[w];
     };
     uint32_t cnt_mine = 0;
-    for (int w = w0; w < w1; ++w)
-        cnt_mine += __popc(word(w));
-    uint32_t tot;
-    uint32_t slot = block_excl_scan(cnt_mine, wsum, &tot);
-    for (int w = w0; w < w1; ++w) {
-        uint32_t b = word(w);
-        if (gbm)
-            bm[w] = 0u;  // left zero for the next call
-        while (b) {
-            const int bit = __ffs(b) - 1;
-            if (slot < (uint32_t)TK_BINS)
-                slots[slot] = (uint32_t)(32 * w + bit);
-            ++slot;
-            b &= b - 1u;
+    if (!gbm) {
+        // LDS bitmap (at most 8192 words): this thread's words read once into registers, so
+        // that neither pass waits on memory per word
+        constexpr int WPT = TK_ROW_BITS / 32 / TK_THREADS;
+        uint32_t wv[WPT];
+#pragma unroll
+        for (int q = 0; q < WPT; ++q)
+            wv[q] = w0 + q < w1 ? bmap_lds[w0 + q] : 0u;
+#pragma unroll
+        for (int q = 0; q < WPT; ++q)
+            cnt_mine += __popc(wv[q]);
+        uint32_t tot;
+        uint32_t slot = block_excl_scan(cnt_mine, wsum, &tot);
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            uint32_t b = wv[q];
+            while (b) {
+                const int bit = __ffs(b) - 1;
+                if (slot < (uint32_t)TK_BINS)
+                    slots[slot] = (uint32_t)(32 * (w0 + q) + bit);
+                ++slot;
+                b &= b - 1u;
+            }
+        }
+    } else {
+        for (int w = w0; w < w1; ++w)
+            cnt_mine += __popc(word(w));
+        uint32_t tot;
+        uint32_t slot = block_excl_scan(cnt_mine, wsum, &tot);
+        for (int w = w0; w < w1; ++w) {
+            uint32_t b = word(w);
+            gbits[w] = 0u;  // left zero for the next call
+            while (b) {
+                const int bit = __ffs(b) - 1;
+                if (slot < (uint32_t)TK_BINS)
+                    slots[slot] = (uint32_t)(32 * w + bit);
+                ++slot;
+                b &= b - 1u;
+            }
         }
     }
     __syncthreads();
