@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload share|decode|ragged|prefill]
     python bench.py --workload writer               # the index-cache writer at the prefill shape
     python bench.py --copy-calibration MIB          # a plain device copy, for counter scaling
+    python bench.py --gather-ceiling [--workload W] # the sparse-MLA row gathers alone (a bound)
     python bench.py --rocprof-summary CSV [CSV ..]  # per-kernel table of rocprofv3 output
     python bench.py --traffic-from FETCH WRITE COPY_FETCH COPY_WRITE [--workload W] [--copy-mib M]
 
@@ -58,6 +59,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run --steps device-to-device copies of MIB MiB (counter calibration)")
+    p.add_argument("--gather-ceiling", action="store_true",
+                   help="time the workload's sparse-MLA row gathers alone (dsa_gather_ceiling) beside the stage")
     p.add_argument("--rocprof-summary", nargs="+", metavar="CSV", help="summarise rocprofv3 CSV files")
     p.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="HBM bytes per stage call from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
@@ -344,6 +347,59 @@ def measured_traffic(workload, stage):
     return st["hbm_bytes_per_call"]
 
 
+def gather_ceiling(workload, steps, warmup):
+    """The workload's own top-k rows gathered with no arithmetic (dsa_gather_ceiling, the
+    sparse-MLA kernels' load path), timed beside the sparse-MLA stage on the same indices."""
+    import torch
+    from deepseek_sparse_mla_amd import synth
+    torch.cuda.set_device(0)
+    case = synth.config(WORKLOADS[workload], "cuda:0")
+    run = Runner(case)
+    run.indexer()
+    run.topk()
+    # positions -> absolute cache rows (contiguous caches: the sequence's first row added)
+    kv_base = case.kv_indptr[:-1]
+    if case.q_indptr is None:
+        seq_of_row = torch.arange(case.T, device="cuda:0")
+    else:
+        seq_of_row = torch.repeat_interleave(torch.arange(case.B, device="cuda:0"),
+                                             (case.q_indptr[1:] - case.q_indptr[:-1]).long())
+    absidx = torch.where(run.idx >= 0, run.idx + kv_base[seq_of_row].unsqueeze(1).to(torch.int32),
+                         torch.full_like(run.idx, -1)).contiguous()
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda:0")
+    tables = [kv.view(torch.uint8) if kv.dtype != torch.bfloat16 else kv for kv in run.kvs]
+
+    def gather():
+        for tab in tables:
+            run.dsa.dsa_gather_ceiling(tab, absidx, sink)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for i in range(steps):
+            ev[i].record()
+            fn()
+        ev[steps].record()
+        torch.cuda.synchronize()
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        return {"median": round(t[steps // 2], 5), "min": round(t[0], 5), "max": round(t[-1], 5)}
+
+    g = timed(gather)
+    m = timed(run.mla)
+    row_bytes = tables[0].shape[1] * tables[0].element_size()
+    nrows = int((absidx >= 0).sum().item()) * len(tables)
+    gbytes = nrows * row_bytes
+    print(json.dumps({
+        "workload": case.name,
+        "gathered_rows": nrows, "row_bytes": row_bytes, "gathered_bytes": gbytes,
+        "gather_only_ms": g, "gather_only_GBps": round(gbytes / (g["median"] * 1e-3) / 1e9, 1),
+        "sparse_mla_stage_ms": m, "stage_GBps_of_gathers": round(gbytes / (m["median"] * 1e-3) / 1e9, 1),
+        "stage_over_gather_only": round(m["median"] / g["median"], 3),
+        "steps": steps, "warmup": warmup}))
+
+
 def copy_calibration(mib, copies):
     import torch
     n = mib << 20
@@ -484,6 +540,8 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, args.steps)
+    if args.gather_ceiling:
+        return gather_ceiling(args.workload, min(args.steps, 20), min(args.warmup, 3))
     if args.workload == "writer":
         return writer_main(args)
     import torch
@@ -636,7 +694,7 @@ def measure(workload, args, steps, warmup, headline):
                                 "topk_hist_kernel + topk_select_kernel"),
         "mla": ("sparse_mla_prefill: " if prefill else "sparse_mla_decode%s: " % ("_shared" if len(probe.layers) > 1 else ""))
         + ("mla_fp8_kernel" if probe.layers[0].kv_dt == "fp8" else
-           "mla_hh_kernel" if probe.T <= 64 else "mla_kernel")
+           "mla_hh_kernel" if probe.T <= 64 else "mla_bf16_team_kernel")
         + (" + mla_combine_kernel" if split else ""),
     }
     path_gbs = model["path_bytes"] / (ms_per_step * 1e-3) / 1e9

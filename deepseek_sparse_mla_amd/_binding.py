@@ -25,7 +25,7 @@ DSA_MAX_SHARED_LAYERS = 8
 
 EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_index_topk", "sparse_mla_workspace_size",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "sparse_mla_decode_no_alloc",
-           "dsa_last_error",
+           "dsa_gather_ceiling", "dsa_last_error",
            "dsa_abi_version")
 
 
@@ -79,9 +79,11 @@ def load_library(path: str = LIB_PATH):
         lib.sparse_mla_decode_no_alloc.argtypes = mla[:15] + [P]
         lib.sparse_mla_decode_shared.argtypes = [LP, I, I, I, F, I, I, I, I,
                                                  ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
+        lib.dsa_gather_ceiling.argtypes = [P, L, I, P, L, I, P, P]
         for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_front_end,
                   lib.dsa_index_scores, lib.dsa_topk, lib.dsa_index_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
-                  lib.sparse_mla_decode_shared, lib.sparse_mla_decode_no_alloc, lib.dsa_abi_version):
+                  lib.sparse_mla_decode_shared, lib.sparse_mla_decode_no_alloc, lib.dsa_gather_ceiling,
+                  lib.dsa_abi_version):
             f.restype = I
         lib.dsa_last_error.restype = ctypes.c_char_p
         lib.dsa_last_error.argtypes = []
@@ -419,6 +421,18 @@ def sparse_mla_decode_no_alloc(layout: Layout, q, kv, indices, sm_scale, D_c, kv
                                         _dev(lse, "lse", torch.float32), _stream(stream))
     _check(lib, st)
     return out
+
+
+def dsa_gather_ceiling(rows: torch.Tensor, indices: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement aid: gather the rows of `rows` ([n, 576] fp8 bytes or [n, 576] bf16) that
+    `indices` ([T, k] int32, absolute rows, -1 = none) select, with no arithmetic."""
+    lib = load_library()
+    n = rows.shape[0]
+    rb = rows.shape[1] * rows.element_size()
+    T, k = indices.shape
+    st = lib.dsa_gather_ceiling(_dev(rows, "rows"), n, rb, _dev(indices, "indices", torch.int32), T, k,
+                                _dev(sink, "sink"), _stream(stream))
+    _check(lib, st)
 
 
 def sparse_mla_prefill(layout: Layout, q, kv, indices, sm_scale, D_c, kv_scale=1.0, out=None, lse=None,

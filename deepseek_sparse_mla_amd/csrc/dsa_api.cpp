@@ -596,4 +596,19 @@ dsa_status sparse_mla_decode_shared(const dsa_layout *layout, int H, int D_c, in
                    stream);
 }
 
+dsa_status dsa_gather_ceiling(const void *rows, int64_t n_rows, int row_bytes, const int32_t *indices, int64_t T,
+                              int k, uint32_t *sink, void *stream)
+{
+    if (!rows || !indices || !sink)
+        return fail(DSA_ERR_INVALID_ARG, "rows, indices and sink must not be NULL");
+    if (row_bytes != 576 && row_bytes != 1152)
+        return fail(DSA_ERR_INVALID_ARG, "row_bytes must be 576 (fp8 rows) or 1152 (bf16 rows)");
+    if (T < 1 || k < 1 || k > DSA_TOPK_MAX || n_rows < 1)
+        return fail(DSA_ERR_INVALID_ARG, "need T >= 1, 1 <= k <= %d and n_rows >= 1", DSA_TOPK_MAX);
+    if (n_rows > (int64_t)(0xFFFFFFFFu - (1u << 20)) / row_bytes)
+        return fail(DSA_ERR_INVALID_ARG, "the row table must stay below 4 GiB - 1 MiB");
+    return hip_status(dsa::launch_gather_ceiling(rows, n_rows, row_bytes, indices, T, k, sink, (hipStream_t)stream),
+                      "gather ceiling launch");
+}
+
 }  // extern "C"

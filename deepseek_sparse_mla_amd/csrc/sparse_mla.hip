@@ -8,18 +8,13 @@
 //   z_j = sm_scale * kv_scale * q_h . c_j ;  o_h = kv_scale * sum_j softmax(z)_j c_j[0:512]
 //
 // Tuned kernels (H = 64, Dc = 512, Dr = 64, bf16 q, bf16 or fp8 latent rows):
-//  * mla_kernel (bf16 rows, many query rows, e.g. prefill): one 256-thread block per
-//    (layer, query row, split of the index list); 4 waves, wave w owns heads 32*(w&1) .. +31
-//    and key half / output-dim half (w>>1); 64-row tiles staged through registers into one
-//    LDS tile [64][576 (+8 pad)], the next tile's rows in flight while the current one is
-//    computed;
-//  * mla_hh_kernel (bf16 rows, at most 64 (row, layer) pairs: small decode): the same per
-//    (row, split, head half), 32-key tiles, small enough for two blocks per CU;
-//  * mla_fp8_kernel (fp8 rows): the mla_kernel wave roles over fp8 tiles gathered by DMA
-//    into three LDS buffers, two tiles in flight, widened to bf16 when read;
-//  * S^T[keys x heads] = K . Q^T on v_mfma_f32_32x32x16_bf16 with Q^T held in registers,
-//    so each lane owns one head column: the online-softmax max/sum need one cross-half
-//    swap and LDS exchanges between the waves that split the contraction;
+//  * mla_fp8_kernel (fp8 rows) and mla_bf16_team_kernel (bf16 rows, more than 64 (row, layer)
+//    pairs, e.g. prefill): 8-wave blocks of two wave teams a tile apart -- an S team (logits
+//    over all 576 dims with Q^T in registers, softmax, P^T to LDS) and a PV team (gathers,
+//    O^T for 128 dims of all 64 heads) -- rows gathered by buffer-to-LDS DMA into a ring of
+//    32-row slots;
+//  * mla_hh_kernel (bf16 rows, at most 64 (row, layer) pairs: small decode): one 4-wave block
+//    per (row, split, head half), 32-key tiles, small enough for two blocks per CU;
 //  * O^T[dims x heads] += V^T . P^T, V^T read straight from the row-major tile with
 //    ds_read_b64_tr_b16 (4 consecutive keys of one dim per lane; _b8 for fp8 tiles);
 //  * softmax reference: each head's reference max is fixed at its first non-empty tile and
@@ -42,7 +37,6 @@ constexpr int M_DC = 512;
 constexpr int M_DQK = 576;
 constexpr int M_TILE = 64;                 // gathered rows per tile
 constexpr int M_ROWB = 1168;               // LDS row stride in bytes (1152 + 16 pad)
-constexpr int M_TILEB = M_TILE * M_ROWB;   // 74752 B per tile buffer
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int BUF_DWORD3 = 0x00020000;     // buffer descriptor word 3 for the gfx9 family
@@ -58,51 +52,12 @@ __device__ __forceinline__ s16x4 lds_tr16(const char *lds_generic_ptr)
 
 constexpr int M_THREADS = 256;             // 4 waves, one per SIMD (512 registers each)
 
-template <bool KV_FP8>
-struct StageRegs {
-    static constexpr int PIECES = KV_FP8 ? 36 : 72;           // 16-byte pieces per row in HBM
-    static constexpr int TOTAL = M_TILE * PIECES;            // per tile
-    static constexpr int N = (TOTAL + M_THREADS - 1) / M_THREADS;
-    u32x4 v[N];
-};
-
-// bf16 rows with a fixed lane -> row map: thread t gathers rows (t >> 3) and (t >> 3) + 32 of
-// the tile, 16-byte pieces (t & 7) + 8 v (v < 9) of each, so it needs only two indices per
-// tile and every load instruction reads whole 128-byte lines of 8 rows.  R.v[v] and
-// R.v[9 + v] hold piece v of the two rows.
-constexpr int SR_V = 9;
-static_assert(StageRegs<false>::N == 2 * SR_V && StageRegs<false>::PIECES == 8 * SR_V, "bf16 row map");
-
 // Byte offset of 16-byte piece `piece` of row `row` in a buffer of rows of `rowb` bytes, as
 // the unsigned 32-bit offset a buffer load takes (buffers up to 4 GB); a row of -1 (no
 // index) maps past every buffer's range, so its load returns zeros.
 __device__ __forceinline__ int row_offset(int32_t row, uint32_t rowb, int piece)
 {
     return row >= 0 ? (int)((uint32_t)row * rowb + 16u * (uint32_t)piece) : (int)0xFFFFFFF0u;
-}
-
-template <int V0, int V1>
-__device__ __forceinline__ void stage_load_rows(StageRegs<false> &R, __amdgpu_buffer_rsrc_t seq,
-                                                int32_t r0, int32_t r1, int tid)
-{
-#pragma unroll
-    for (int v = V0; v < V1; ++v) {
-        const int col = (tid & 7) + 8 * v;
-        R.v[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, row_offset(r0, 1152, col), 0, 0));
-        R.v[SR_V + v] =
-            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seq, row_offset(r1, 1152, col), 0, 0));
-    }
-}
-
-__device__ __forceinline__ void stage_store_rows(const StageRegs<false> &R, char *tile, int tid)
-{
-    const int row = tid >> 3;
-#pragma unroll
-    for (int v = 0; v < SR_V; ++v) {
-        const int col = (tid & 7) + 8 * v;
-        *(u32x4 *)(tile + row * M_ROWB + col * 16) = R.v[v];
-        *(u32x4 *)(tile + (row + 32) * M_ROWB + col * 16) = R.v[SR_V + v];
-    }
 }
 
 // Block -> (output row, split).  The (row, split) pairs are cut into 8 contiguous ranges,
@@ -113,369 +68,6 @@ __device__ __forceinline__ int64_t xcd_pair(int64_t pairs_per_xcd)
 {
     const int64_t b = blockIdx.x;
     return (b & 7) * pairs_per_xcd + (b >> 3);
-}
-
-// Epilogue shared by the sparse-MLA kernels: the normalised output (one split), or this
-// split's partial: O / l in the output's precision (fp32, or bf16 for a bf16 output, like the
-// output itself) plus (reference max, l) in fp32 for the combine.  Wave (hh, dq) owns dims
-// 256*dq + 32*mt + 8*q4 + 4*g + 0..3 of head 32*hh + j.
-//
-// A bf16 block result (64 heads x 512 dims) is one contiguous 64 KB range of the output or of
-// the partial buffer.  It is staged through LDS (`stage`, free once the tiles are consumed;
-// rows padded to 1040 B so that the 32 heads of one write fall on distinct banks) and then
-// stored as whole 1 KB head rows, 16 B per lane: the direct stores from the MFMA layout would
-// write 16-byte pieces of 32 different rows per instruction.  fp32 results are stored directly.
-constexpr int E_ROWB = 1040;
-constexpr int E_STAGE_BYTES = M_H * E_ROWB;  // 66560
-static_assert(E_STAGE_BYTES <= M_TILEB, "output staging must fit in a tile buffer");
-
-// The staged copy of a bf16 block result to the output or partial buffer by NT threads.
-template <int NT>
-__device__ __forceinline__ void mla_store_copy(const MlaLayerDev &Ld, int64_t i, int64_t orow, int split, int nsplit,
-                                               float *__restrict__ ws_o, const char *stage, int tid)
-{
-    char *dst = (nsplit == 1) ? (char *)((uint16_t *)Ld.out + i * M_H * M_DC)
-                              : (char *)((uint16_t *)ws_o + (orow * nsplit + split) * M_H * M_DC);
-#pragma unroll
-    for (int u = 0; u < M_H * M_DC * 2 / (16 * NT); ++u) {
-        const int c = tid + NT * u, h = c >> 6, c16 = c & 63;
-        *(u32x4 *)(dst + h * (M_DC * 2) + 16 * c16) = *(const u32x4 *)(stage + h * E_ROWB + 16 * c16);
-    }
-}
-
-// Called by the waves that hold O; with NT > 256 the other threads of the block call
-// mla_store_copy<NT> (after the same barrier) for their share of the staged copy.
-template <bool OUT_F32, int NT = M_THREADS>
-__device__ __forceinline__ void mla_store(const f32x16 (&O)[8], float l_run, float m_ref, const MlaLayerDev &Ld,
-                                          int64_t i, int64_t orow, int split, int nsplit, int dq, int g, int head,
-                                          float *__restrict__ ws_o, float *__restrict__ ws_ml, char *stage,
-                                          int tid)
-{
-    const float inv = (l_run > 0.f) ? (nsplit == 1 ? Ld.kv_scale / l_run : 1.f / l_run) : 0.f;
-    if (OUT_F32) {
-        float *dst = (nsplit == 1) ? (float *)Ld.out + (i * M_H + head) * M_DC
-                                   : ws_o + ((orow * nsplit + split) * M_H + head) * M_DC;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-                *(f32x4 *)(dst + d) = f32x4{O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv,
-                                            O[mt][4 * q4 + 2] * inv, O[mt][4 * q4 + 3] * inv};
-            }
-    } else {
-        char *srow = stage + head * E_ROWB;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 256 * dq + 32 * mt + 8 * q4 + 4 * g;
-                *(u32x2 *)(srow + 2 * d) = u32x2{pack_bf16x2(O[mt][4 * q4] * inv, O[mt][4 * q4 + 1] * inv),
-                                                 pack_bf16x2(O[mt][4 * q4 + 2] * inv, O[mt][4 * q4 + 3] * inv)};
-            }
-        __syncthreads();
-        mla_store_copy<NT>(Ld, i, orow, split, nsplit, ws_o, stage, tid);
-    }
-    if (nsplit == 1) {
-        if (Ld.lse && dq == 0 && g == 0)
-            Ld.lse[i * M_H + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * LN2 : -INFINITY;
-    } else if (dq == 0 && g == 0) {
-        float *pml = ws_ml + ((orow * nsplit + split) * M_H + head) * 2;
-        pml[0] = m_ref;
-        pml[1] = l_run;
-    }
-}
-
-//
-// Wave w of the block: hh = w & 1 owns heads 32*hh .. +31 and dq = w >> 1 owns half of the
-// 576-long contraction for S, the keys 32*dq .. +31 of each tile for the softmax, and half
-// of the 512 output dims for O.  Per 64-row tile:
-//   1. S^T partials [64 keys x 32 heads] = K . Q^T over the wave's 288 dims (2 x 18 MFMA);
-//   2. the two waves of a head half swap the partial of each other's key half through LDS
-//      and add it (dq 0 + dq 1, in that order) -> full S^T for the wave's own 32 keys;
-//   3. online softmax on those 32 keys against the fixed reference, P packed to bf16 and
-//      swapped with the partner so both hold P^T for all 64 keys;
-//   4. O^T [256 dims x 32 heads] += V^T . P^T (32 MFMA), V^T read with ds_read_b64_tr_b16.
-// Each wave keeps the row sum l of its own keys; the pair adds theirs once at the end.
-//
-template <bool KV_FP8, bool OUT_F32>
-__global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t T, int64_t n_rows,
-                                                           MlaLayersDev layers,
-                                                           const int32_t *__restrict__ indices, int k,
-                                                           float sm_scale, int nsplit, int tiles_per_split,
-                                                           int64_t pairs_per_xcd, float *__restrict__ ws_o,
-                                                           float *__restrict__ ws_ml)
-{
-    static_assert(!KV_FP8, "fp8 latent rows take mla_fp8_kernel");
-    __shared__ __attribute__((aligned(16))) char kt[M_TILEB];
-    __shared__ __attribute__((aligned(16))) f32x4 xs[4][4][64];   // S^T half partials [wave][q][lane]
-    __shared__ __attribute__((aligned(16))) u32x4 xp[4][2][64];   // packed P^T [wave][half][lane]
-    __shared__ float xm[4][32];                                    // per-head stats swap
-    __shared__ int32_t sidx[2][M_TILE];
-    __shared__ int sh_flag;
-
-    const int64_t pair = xcd_pair(pairs_per_xcd);
-    if (pair >= n_rows * nsplit)
-        return;
-    const int64_t orow = pair / nsplit;
-    const int split = (int)(pair % nsplit);
-    const int layer = (int)(orow / T);
-    const int64_t i = orow % T;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 5, j = lane & 31;
-    const int hh = w & 1, dq = w >> 1, wp = w ^ 2;
-    const MlaLayerDev Ld = layers.l[layer];
-    const RowInfo r = row_info(L, i);
-    const float c2 = sm_scale * Ld.kv_scale * LOG2E;
-
-    const int ntiles_all = (k + M_TILE - 1) / M_TILE;
-    const int t_begin = split * tiles_per_split;
-    const int ntiles = max(0, min(ntiles_all, t_begin + tiles_per_split) - t_begin);
-    const int32_t *irow = indices + i * k;
-
-    auto load_idx = [&](int tt) -> int32_t {  // slot `tid` of tile tt (tid < 64)
-        const int slot = (t_begin + tt) * M_TILE + tid;
-        return (tt < ntiles && slot < k) ? irow[slot] : -1;
-    };
-    // the first three tiles' indices are loaded before Q so that their latency overlaps it
-    int32_t i0 = -1, i1 = -1, i2 = -1;
-    if (tid < M_TILE) {
-        i0 = load_idx(0);
-        i1 = load_idx(1);
-        i2 = load_idx(2);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Q^T operand: head 32*hh + j, dims 288*dq + 16t + 8g .. +7 (t < 18)
-    bf16x8 qT[18];
-    {
-        const uint16_t *qp = (const uint16_t *)Ld.q + ((i * M_H + 32 * hh + j) * M_DQK + 288 * dq + 8 * g);
-#pragma unroll
-        for (int t = 0; t < 18; ++t)
-            qT[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * t));
-    }
-
-    f32x16 O[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-        O[mt] = f32x16{};
-
-    StageRegs<KV_FP8> R;
-    constexpr int64_t ROWB = KV_FP8 ? 576 : 1152;
-    // indices address the sequence's rows, or with paged caches the whole cache (physical
-    // rows); the host keeps the range at most 4 GiB - 1 MiB (unsigned 32-bit offsets)
-    const bool paged = L.block_table != nullptr;
-    const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * ROWB;
-    const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * ROWB), (short)0, (int)(uint32_t)seq_bytes, BUF_DWORD3);
-
-    // Pass 0 fixes each head's reference max at its first non-empty tile.  If a later
-    // tile exceeds it by more than 2^100 (p would approach the fp32 range) the split is
-    // run again with the exact maximum observed in pass 0 as the reference.
-    float m_ref = -INFINITY;   // shared by the wave pair of a head half
-    float m_seen = -INFINITY;  // max over this wave's own keys
-    float l_own = 0.f;         // sum of p over this wave's own keys (this lane's 16)
-    for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 1) {
-            if (!sh_flag)
-                break;
-            if (g == 0)
-                xm[w][j] = m_seen;
-            __syncthreads();
-            m_ref = fmaxf(m_seen, xm[wp][j]);
-            l_own = 0.f;  // i0 .. i2 still hold the first three tiles' indices
-        }
-        bool ovf = false;
-        if (tid < M_TILE) {
-            sidx[0][tid] = i0;
-            sidx[1][tid] = i1;
-        }
-        if (tid == 0)
-            sh_flag = 0;
-        int32_t idx_next = i2;
-        lds_barrier();  // Q stays in flight
-        if (ntiles > 0) {
-            stage_load_rows<0, SR_V>(R, seq, sidx[0][tid >> 3], sidx[0][(tid >> 3) + 32], tid);
-            stage_store_rows(R, kt, tid);
-        }
-        // Nothing may be left in flight here (Q included): otherwise the compiler's wait
-        // for Q lands inside the loop, where it would also wait for the next tile's loads.
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
-        lds_barrier();
-
-        for (int tt = 0; tt < ntiles; ++tt) {
-            const int buf = tt & 1;
-            const bool gather_next = tt + 1 < ntiles;
-            // the next tile's two rows of this thread (written before the last barrier)
-            const int32_t nr0 = sidx[buf ^ 1][tid >> 3], nr1 = sidx[buf ^ 1][(tid >> 3) + 32];
-            const uint64_t valid = __ballot(sidx[buf][lane] >= 0);
-            const bool restart = (pass == 1 && tt == 0);
-
-            // ---- 1. S^T partials for keys 0..31 (S[0]) and 32..63 (S[1]) over this wave's
-            // dims; operands are read three k-steps ahead of the MFMAs that use them.  The
-            // next tile's gathers are issued a sixth at a time between the k-steps, so the
-            // CU's address unit works through them while the MFMAs run.
-            f32x16 S[2] = {f32x16{}, f32x16{}};
-            {
-                const char *arow = kt + j * M_ROWB + 2 * (288 * dq + 8 * g);
-                u32x4 A[2][3][2];
-#pragma unroll
-                for (int t = 0; t < 3; ++t) {
-                    A[0][t][0] = *(const u32x4 *)(arow + 32 * t);
-                    A[0][t][1] = *(const u32x4 *)(arow + 32 * M_ROWB + 32 * t);
-                }
-#pragma unroll
-                for (int c = 0; c < 6; ++c) {
-                    const int cur = c & 1;
-                    if (c + 1 < 6) {
-#pragma unroll
-                        for (int t = 0; t < 3; ++t) {
-                            const int tn = 3 * (c + 1) + t;
-                            A[cur ^ 1][t][0] = *(const u32x4 *)(arow + 32 * tn);
-                            A[cur ^ 1][t][1] = *(const u32x4 *)(arow + 32 * M_ROWB + 32 * tn);
-                        }
-                    }
-#pragma unroll
-                    for (int t = 0; t < 3; ++t) {
-                        S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[cur][t][0]),
-                                                                       qT[3 * c + t], S[0], 0, 0, 0);
-                        S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[cur][t][1]),
-                                                                       qT[3 * c + t], S[1], 0, 0, 0);
-                    }
-                    if (gather_next) {
-                        switch (c) {
-                        case 0: stage_load_rows<0, 1>(R, seq, nr0, nr1, tid); break;
-                        case 1: stage_load_rows<1, 3>(R, seq, nr0, nr1, tid); break;
-                        case 2: stage_load_rows<3, 4>(R, seq, nr0, nr1, tid); break;
-                        case 3: stage_load_rows<4, 6>(R, seq, nr0, nr1, tid); break;
-                        case 4: stage_load_rows<6, 7>(R, seq, nr0, nr1, tid); break;
-                        default: stage_load_rows<7, SR_V>(R, seq, nr0, nr1, tid); break;
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-
-            // ---- 2. swap the half partials; s = full S^T for keys 32*dq + .. (this wave's)
-            {
-                const f32x16 give = dq ? S[0] : S[1];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    xs[w][q4][lane] = f32x4{give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]};
-            }
-            lds_barrier();
-            f32x16 s = dq ? S[1] : S[0];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 o = xs[wp][q4][lane];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[4 * q4 + e] = dq ? (o[e] + s[4 * q4 + e]) : (s[4 * q4 + e] + o[e]);
-            }
-
-            // ---- 3. softmax numerators of the own 32 keys
-            const uint32_t vkeys = (uint32_t)(valid >> (32 * dq)) >> (4 * g);
-            const bool full = valid == ~0ull;
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const bool ok = full || ((vkeys >> (8 * (rr >> 2) + (rr & 3))) & 1u);
-                s[rr] = ok ? s[rr] * c2 : -INFINITY;
-                mloc = fmaxf(mloc, s[rr]);
-            }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));  // this wave's 32 keys, head j
-            if (m_ref == -INFINITY && valid != 0ull) {
-                // first non-empty tile (block-uniform): the pair agrees on the reference
-                if (g == 0)
-                    xm[w][j] = mloc;
-                lds_barrier();
-                m_ref = fmaxf(mloc, xm[wp][j]);
-                lds_barrier();
-            }
-            m_seen = fmaxf(m_seen, mloc);
-            ovf |= mloc > m_ref + 100.f;
-            uint32_t pk[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float p0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q] - m_ref);
-                const float p1 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[2 * q + 1] - m_ref);
-                l_own += p0 + p1;
-                pk[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
-            }
-            xp[w][0][lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-            xp[w][1][lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-            lds_barrier();
-            const u32x4 pp0 = xp[wp][0][lane], pp1 = xp[wp][1][lane];
-
-            // ---- 4. O^T += V^T . P^T over the 64 keys (4 steps of 16 keys); the transposed V
-            // operands of step u + 1 are read while step u's MFMAs run.
-            {
-                typedef short s16x8 __attribute__((ext_vector_type(8)));
-                const int dcol = 256 * dq + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-                const char *vbase = kt + (4 * g + ((lane & 15) >> 2)) * M_ROWB + 2 * dcol;
-                s16x4 V[2][8][2];
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt) {
-                    V[0][mt][0] = lds_tr16(vbase + 64 * mt);
-                    V[0][mt][1] = lds_tr16(vbase + 8 * M_ROWB + 64 * mt);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int cur = u & 1;
-                    if (u + 1 < 4) {
-                        const int un = u + 1;
-                        const char *vb = vbase + (32 * (un >> 1) + 16 * (un & 1)) * M_ROWB;
-#pragma unroll
-                        for (int mt = 0; mt < 8; ++mt) {
-                            V[cur ^ 1][mt][0] = lds_tr16(vb + 64 * mt);
-                            V[cur ^ 1][mt][1] = lds_tr16(vb + 8 * M_ROWB + 64 * mt);
-                        }
-                    }
-                    const int khu = u >> 1, jj = u & 1;
-                    u32x4 bw;
-                    if (khu == dq)
-                        bw = jj ? u32x4{pk[4], pk[5], pk[6], pk[7]} : u32x4{pk[0], pk[1], pk[2], pk[3]};
-                    else
-                        bw = jj ? pp1 : pp0;
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-#pragma unroll
-                    for (int mt = 0; mt < 8; ++mt) {
-                        const s16x4 lo = V[cur][mt][0], hi = V[cur][mt][1];
-                        const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        if (restart && u == 0)  // first MFMA of a rerun: drop pass 0's sums
-                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), bop,
-                                                                            f32x16{}, 0, 0, 0);
-                        else
-                            O[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), bop,
-                                                                            O[mt], 0, 0, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            lds_barrier();  // tile, S partials and P fully consumed
-            if (tt + 1 < ntiles)
-                stage_store_rows(R, kt, tid);
-            if (tid < M_TILE) {
-                sidx[buf][tid] = idx_next;  // tile tt + 2
-                idx_next = load_idx(tt + 3);
-            }
-            lds_barrier();
-        }
-        if (ovf)
-            sh_flag = 1;
-        __syncthreads();
-    }
-
-    // ---- row sum over all keys: lane halves, then the pair (dq 0 + dq 1)
-    float l_run = l_own + __shfl_xor(l_own, 32, 64);
-    __syncthreads();
-    if (g == 0)
-        xm[w][j] = l_run;
-    __syncthreads();
-    l_run = dq ? (xm[wp][j] + l_run) : (l_run + xm[wp][j]);
-
-    mla_store<OUT_F32>(O, l_run, m_ref, Ld, i, orow, split, nsplit, dq, g, 32 * hh + j, ws_o, ws_ml, kt, tid);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -508,9 +100,10 @@ __global__ __launch_bounds__(M_THREADS, 1) void mla_kernel(LayoutDev L, int64_t 
 // 2s+4 are issued at the start of step s, into the slots tile s - 2 left, and the step ends
 // once 2s+2 and 2s+3 have landed.
 //
-// Softmax without rescaling, as in mla_kernel: the reference maximum is fixed at the split's
-// first non-empty tile; a later logit above it by more than 2^100 makes that split run again
-// (a cold second pass) with the exact maximum of the first pass.
+// Softmax without rescaling: the reference maximum is fixed at the split's first non-empty
+// tile, so the fp32 O accumulators are never rescaled (exact either way, since l and O share
+// the reference); a later logit above it by more than 2^100 makes that split run again (a
+// cold second pass) with the exact maximum of the first pass.
 // ------------------------------------------------------------------------------------------
 constexpr int F_ROWB = 592;                      // fp8 LDS row stride (576 + 16 pad)
 constexpr int TM_THREADS = 512;
@@ -522,7 +115,6 @@ constexpr int TM_DMA_PER_WAVE = (TM_DMA + 3) / 4;    // 5 (4 on the last PV wave
 constexpr int TM_PROWB = 144;                    // P^T row of one head: 64 keys bf16 + 16 pad
 constexpr int TM_PBUFB = M_H * TM_PROWB;         // 9216 B
 static_assert(TM_DMA == 19 && TM_SLOTB - 18 * 1024 == 512, "the last load of a slot is 32 lanes wide");
-static_assert(E_STAGE_BYTES <= TM_SLOTS * TM_SLOTB, "output staging must fit in the ring");
 
 // Value of lane l ^ 32 (g = lane >> 5), through one v_permlane32_swap (no LDS round trip).
 __device__ __forceinline__ float other_half(float x, int g)
@@ -540,45 +132,66 @@ __device__ __forceinline__ i32x2 lds_tr8(const char *lds_generic_ptr)
 constexpr int F_IDX = 2048;  // index slots of one split (32 tiles) held in LDS
 static_assert(F_IDX >= DSA_TOPK_MAX, "a split never holds more than k index slots");
 
-// Lane geometry of a slot's gather, fixed per lane: load q of PV wave b covers bytes
-// 1024*(4q + b) + 16*lane of the slot, i.e. row rc & 0xFF, column rc >> 8 (0xFFFF: the pad
-// bytes, which read zeros).  Load 18 exists on wave 2 only, for lanes 0-31.
-__device__ __forceinline__ void slot_geometry(int b, int lane, uint32_t (&rc)[TM_DMA_PER_WAVE])
-{
-#pragma unroll
-    for (int q = 0; q < TM_DMA_PER_WAVE; ++q) {
-        const int o = 1024 * (4 * q + b) + 16 * lane;
-        const int row = min(o / F_ROWB, TM_HALF - 1);
-        const int col = o - (o / F_ROWB) * F_ROWB;
-        const bool real = o < TM_SLOTB && col < 576;
-        rc[q] = (uint32_t)row | ((real ? (uint32_t)col : 0xFFFFu) << 8);
-    }
-}
+// Gathers into a ring slot of 32 rows (fp8: 32 x 592 B, 19 wave-wide 1 KB loads; bf16:
+// 32 x 1168 B, 37 loads; the last load of a slot is 32 lanes wide), shared by NW waves.  Load q
+// of issuing wave w covers slot bytes 1024 (NW q + w) + 16 lane, i.e. row rc & 0xFF, column
+// rc >> 8 (0xFFFF: the pad bytes, which read zeros); the row's source is index * RB (RB = 576
+// or 1152 bytes).
+template <int RB, int NW = 4>
+struct SlotDma {
+    static constexpr int ROWB = RB + 16;
+    static constexpr int SLOTB = 32 * ROWB;
+    static constexpr int LOADS = (SLOTB + 1023) / 1024;
+    static constexpr int PER_WAVE = (LOADS + NW - 1) / NW;
+    static_assert(SLOTB - (LOADS - 1) * 1024 == 512, "the last load of a slot is 32 lanes wide");
 
-// Gather the 32 rows given by sidx (index -1: zeros) into the slot at lds_base.
-__device__ __forceinline__ void dma_slot(const i32x4 &seq, uint32_t lds_base, const int32_t *sidx, int b, int lane,
-                                         const uint32_t (&rc)[TM_DMA_PER_WAVE])
-{
-    int voff[TM_DMA_PER_WAVE];
+    __device__ static void geometry(int w, int lane, uint32_t (&rc)[PER_WAVE])
+    {
 #pragma unroll
-    for (int q = 0; q < TM_DMA_PER_WAVE; ++q) {
-        const int32_t idx = sidx[rc[q] & 0xFFu];
-        const uint32_t col = rc[q] >> 8;
-        // unsigned 32-bit offsets (buffers up to 4 GB); pads and missing rows read zeros
-        voff[q] = (col != 0xFFFFu && idx >= 0) ? (int)((uint32_t)idx * 576u + col) : (int)0xFFFFFFF0u;
+        for (int q = 0; q < PER_WAVE; ++q) {
+            const int o = 1024 * (NW * q + w) + 16 * lane;
+            const int row = min(o / ROWB, 31);
+            const int col = o - (o / ROWB) * ROWB;
+            const bool real = o < SLOTB && col < RB;
+            rc[q] = (uint32_t)row | ((real ? (uint32_t)col : 0xFFFFu) << 8);
+        }
     }
+    // Source offsets of this wave's loads for the 32 rows given by sidx (index -1: zeros).
+    __device__ static void offsets(const int32_t *sidx, const uint32_t (&rc)[PER_WAVE], int (&voff)[PER_WAVE])
+    {
 #pragma unroll
-    for (int q = 0; q < TM_DMA_PER_WAVE; ++q) {
-        const int u = 4 * q + b;
-        if (u < TM_DMA - 1)
-            dma16(seq, lds_base + 1024u * (uint32_t)u, voff[q]);
-        else if (u == TM_DMA - 1 && lane < 32)
-            dma16(seq, lds_base + 1024u * (uint32_t)u, voff[q]);
+        for (int q = 0; q < PER_WAVE; ++q) {
+            const int32_t idx = sidx[rc[q] & 0xFFu];
+            const uint32_t col = rc[q] >> 8;
+            // unsigned 32-bit offsets (buffers up to 4 GB); pads and missing rows read zeros
+            voff[q] = (col != 0xFFFFu && idx >= 0) ? (int)((uint32_t)idx * (uint32_t)RB + col) : (int)0xFFFFFFF0u;
+        }
     }
-}
+    // Load q of wave w (nothing past the slot's last load).
+    __device__ static void one(const i32x4 &seq, uint32_t lds_base, int w, int lane, int q, int voff)
+    {
+        const int u = NW * q + w;
+        if (u < LOADS - 1)
+            dma16(seq, lds_base + 1024u * (uint32_t)u, voff);
+        else if (u == LOADS - 1 && lane < 32)
+            dma16(seq, lds_base + 1024u * (uint32_t)u, voff);
+    }
+    // Gather this wave's share of the 32 rows given by sidx into the slot at lds_base.
+    __device__ static void issue(const i32x4 &seq, uint32_t lds_base, const int32_t *sidx, int w, int lane,
+                                 const uint32_t (&rc)[PER_WAVE])
+    {
+        int voff[PER_WAVE];
+        offsets(sidx, rc, voff);
+#pragma unroll
+        for (int q = 0; q < PER_WAVE; ++q)
+            one(seq, lds_base, w, lane, q, voff[q]);
+    }
+};
+typedef SlotDma<576> Fp8Slot;
+static_assert(Fp8Slot::SLOTB == TM_SLOTB && Fp8Slot::PER_WAVE == TM_DMA_PER_WAVE, "fp8 slot geometry");
 
-// Wait until only the most recent slot's loads (5 on PV waves 0-2, 4 on wave 3) may still be
-// outstanding: every earlier slot has landed.
+// Wait until only the most recent fp8 slot's loads (5 on PV waves 0-2, 4 on wave 3) may still
+// be outstanding: every earlier slot has landed.
 __device__ __forceinline__ void wait_but_last_slot(int b)
 {
     static_assert(TM_DMA_PER_WAVE == 5, "loads per wave and slot");
@@ -590,15 +203,15 @@ __device__ __forceinline__ void wait_but_last_slot(int b)
 
 // Partial (or, with one split, final) result of one split from the PV team's registers:
 // wave b holds dims 128 b + 32 mt + 8 q4 + 4 g + 0..3 of heads j (nh = 0) and 32 + j (nh = 1).
-// bf16 results are staged through LDS in the wave's own columns 128 b .. +127 of the 64 rows
-// the split's last tile left in slots sa, sb (no other wave reads those bytes): 32 heads at a
-// time, each head's 256 bytes in two stage rows, then stored as whole 256-byte pieces, four
-// heads per instruction.  fp32 results are stored straight from the MFMA layout.
-template <bool OUT_F32>
-__device__ __forceinline__ void mla_fp8_store(const f32x16 (&O)[4][2], const float (&l)[2], const float (&m)[2],
-                                              const MlaLayerDev &Ld, int64_t i, int64_t orow, int split, int nsplit,
-                                              int b, int g, int j, int lane, char *slot_a, char *slot_b,
-                                              float *__restrict__ ws_o, float *__restrict__ ws_ml)
+// bf16 results are staged through LDS, 32 heads at a time, in bytes of the split's last tile
+// that only this wave reads (its own V columns): stage(r, c) is the address of byte c of head
+// r's 256-byte piece.  They are then stored as whole 256-byte pieces, four heads per
+// instruction.  fp32 results are stored straight from the MFMA layout.
+template <bool OUT_F32, typename Stage>
+__device__ __forceinline__ void mla_team_store(const f32x16 (&O)[4][2], const float (&l)[2], const float (&m)[2],
+                                               const MlaLayerDev &Ld, int64_t i, int64_t orow, int split, int nsplit,
+                                               int b, int g, int j, int lane, Stage stage, float *__restrict__ ws_o,
+                                               float *__restrict__ ws_ml)
 {
     const int64_t base = (nsplit == 1) ? i * M_H * M_DC : (orow * nsplit + split) * M_H * M_DC;
 #pragma unroll
@@ -615,25 +228,20 @@ __device__ __forceinline__ void mla_fp8_store(const f32x16 (&O)[4][2], const flo
                         f32x4{o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv};
                 }
         } else {
-            // stage row R: row R & 31 of slot_a (R < 32) or slot_b, bytes 128 b .. +127
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int c = 2 * (32 * mt + 8 * q4 + 4 * g);  // byte of the head's 256
-                    const int R = 2 * j + (c >> 7);
-                    char *sp = (R < 32 ? slot_a : slot_b) + (R & 31) * F_ROWB + 128 * b + (c & 127);
                     const f32x16 &o = O[mt][nh];
-                    *(u32x2 *)sp = u32x2{pack_bf16x2(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
-                                         pack_bf16x2(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv)};
+                    *(u32x2 *)stage(j, 2 * (32 * mt + 8 * q4 + 4 * g)) =
+                        u32x2{pack_bf16x2(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
+                              pack_bf16x2(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv)};
                 }
             uint16_t *dst = ((nsplit == 1) ? (uint16_t *)Ld.out : (uint16_t *)ws_o) + base + 128 * b;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int r = 4 * u + (lane >> 4), c = 16 * (lane & 15);
-                const int R = 2 * r + (c >> 7);
-                const u32x4 v = *(const u32x4 *)((R < 32 ? slot_a : slot_b) + (R & 31) * F_ROWB + 128 * b + (c & 127));
-                *(u32x4 *)((char *)(dst + (32 * nh + r) * M_DC) + c) = v;
+                *(u32x4 *)((char *)(dst + (32 * nh + r) * M_DC) + c) = *(const u32x4 *)stage(r, c);
             }
         }
         if (b == 0 && g == 0) {
@@ -881,7 +489,7 @@ __global__ __launch_bounds__(TM_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int
         const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * 576, seq_bytes);
         const uint32_t lds0 = lds_addr_of(&ring[0][0]);
         uint32_t rc[TM_DMA_PER_WAVE];
-        slot_geometry(b, lane, rc);
+        Fp8Slot::geometry(b, lane, rc);
         // V^T read geometry: 16-lane group G covers dims +16 (G & 1), keys +8 (G >> 1)
         const int mq = lane & 15;
         const int voffs = (8 * g + (mq >> 1)) * F_ROWB + 128 * b + 16 * ((lane >> 4) & 1) + 8 * (mq & 1);
@@ -921,13 +529,19 @@ __global__ __launch_bounds__(TM_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int
             const int gs = t / tps;
             const int h0 = 2 * (t - t0);
             char *sa = &ring[0][0] + (h0 % TM_SLOTS) * TM_SLOTB, *sb = &ring[0][0] + ((h0 + 1) % TM_SLOTS) * TM_SLOTB;
+            // head r's 256 bytes in stage rows 2r, 2r + 1 (rows 0..31 of sa, then of sb), the
+            // wave's columns 128 b .. +127
+            auto stage = [&](int r, int c) __attribute__((always_inline)) {
+                const int R = 2 * r + (c >> 7);
+                return (R < 32 ? sa : sb) + (R & 31) * F_ROWB + 128 * b + (c & 127);
+            };
             float l[2], m[2];
 #pragma unroll
             for (int nh = 0; nh < 2; ++nh) {
                 l[nh] = xl[gs & 1][0][32 * nh + j] + xl[gs & 1][1][32 * nh + j];
                 m[nh] = xr[gs & 1][32 * nh + j];
             }
-            mla_fp8_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, sa, sb, ws_o, ws_ml);
+            mla_team_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, stage, ws_o, ws_ml);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
                 O[mt][0] = O[mt][1] = f32x16{};
@@ -935,7 +549,7 @@ __global__ __launch_bounds__(TM_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int
         auto run = [&](int t0, int t1, bool need_ref) __attribute__((always_inline)) {
             const int nslots = 2 * (t1 - t0);
             for (int h = 0; h < min(3, nslots); ++h)
-                dma_slot(seq, lds0 + (uint32_t)h * TM_SLOTB, sidx + (2 * t0 + h) * TM_HALF, b, lane, rc);
+                Fp8Slot::issue(seq, lds0 + (uint32_t)h * TM_SLOTB, sidx + (2 * t0 + h) * TM_HALF, b, lane, rc);
             lds_barrier();  // (first pass: the S team has its copy of Q and clears slots 3..6)
             if (nslots > 2)
                 wait_but_last_slot(b);  // tile t0 has landed
@@ -947,8 +561,8 @@ __global__ __launch_bounds__(TM_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int
                 // half tiles hs+3, hs+4 into the slots of tile s - 2 (consumed in step s - 1)
                 for (int h = hs + 3; h <= hs + 4; ++h)
                     if (h < nslots)
-                        dma_slot(seq, lds0 + (uint32_t)(h % TM_SLOTS) * TM_SLOTB, sidx + (2 * t0 + h) * TM_HALF,
-                                 b, lane, rc);
+                        Fp8Slot::issue(seq, lds0 + (uint32_t)(h % TM_SLOTS) * TM_SLOTB, sidx + (2 * t0 + h) * TM_HALF,
+                                       b, lane, rc);
                 if (need_ref && s < t1 && first_of_split(s)) {
                     lds_barrier();  // the S team's two exchange barriers
                     lds_barrier();
@@ -984,8 +598,426 @@ __global__ __launch_bounds__(TM_THREADS, 1) void mla_fp8_kernel(LayoutDev L, int
         for (int gs = 0; gs < group; ++gs)
             if (gs * tps >= nt) {
                 const float l[2] = {0.f, 0.f}, m[2] = {-INFINITY, -INFINITY};
-                mla_fp8_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, &ring[0][0],
-                                       &ring[1][0], ws_o, ws_ml);
+                auto stage = [&](int r, int c) __attribute__((always_inline)) {
+                    const int R = 2 * r + (c >> 7);
+                    return &ring[R >> 5][0] + (R & 31) * F_ROWB + 128 * b + (c & 127);
+                };
+                mla_team_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, stage, ws_o, ws_ml);
+            }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 latent rows, more than MLA_HH_MAX_ROWS rows (prefill): the two-team layout of
+// mla_fp8_kernel with 32-key steps.  A 32-row bf16 slot takes 37 KB, so the LDS ring holds
+// three: in step s the S team reads tile s, the PV team tile s - 1, and tile s + 1 is in
+// flight (issued at the start of step s into the slot tile s - 2 left).
+//   * S team wave a: heads 32 (a & 1) .. +31 as two 16-head blocks, keys 16 (a >> 1) .. +15
+//     of each 32-key tile: S^T [16 keys x 16 heads] per block over all 576 dims
+//     (v_mfma_f32_16x16x32_bf16, 2 x 18 per step; the wave's Q^T in 144 registers, each K
+//     operand shared by the two blocks);
+//   * PV team wave b: dims 128 b .. +127 of all 64 heads, O^T += V^T . P^T over 2 steps of 16
+//     keys (v_mfma_f32_32x32x16_bf16, 4 dim blocks x 2 head blocks each), V^T read with
+//     ds_read_b64_tr_b16, P^T from LDS in the same key order.
+// The gathers of tile s + 1 are shared by all eight waves and issued between the MFMAs of
+// step s (the S team's between its k-steps, the PV team's between its key steps), so the
+// address unit works through them while the matrix cores run.
+// Splits, grouping, the reference maximum, the rerun and the staged split results are those
+// of mla_fp8_kernel; split boundaries are the policy's 64-key tiles (two 32-key tiles each).
+// ------------------------------------------------------------------------------------------
+typedef SlotDma<1152, 8> Bf16Slot;  // all 8 waves gather: 5 loads on waves 0-4, 4 on 5-7
+constexpr int TB_ROWB = Bf16Slot::ROWB;          // 1168
+constexpr int TB_SLOTB = Bf16Slot::SLOTB;        // 37376
+constexpr int TB_SLOTS = 3;
+constexpr int TB_PROWB = 80;                     // P^T row of one head: 32 keys bf16 + 16 pad
+constexpr int TB_PBUFB = M_H * TB_PROWB;         // 5120 B
+constexpr int TB_QOFF = TB_SLOTB;                // Q staged in slots 1..2 before the first gathers
+static_assert(M_H * TM_QROWB <= 2 * TB_SLOTB, "Q staging fits slots 1..2");
+static_assert(TB_ROWB == TM_QROWB, "Q staging rows and K rows share the stride");
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(TM_THREADS, 1) void mla_bf16_team_kernel(LayoutDev L, int64_t T, int64_t n_rows,
+                                                                      MlaLayersDev layers,
+                                                                      const int32_t *__restrict__ indices, int k,
+                                                                      float sm_scale, int nsplit, int tiles_per_split,
+                                                                      int group, int64_t pairs_per_xcd,
+                                                                      float *__restrict__ ws_o,
+                                                                      float *__restrict__ ws_ml)
+{
+    __shared__ __attribute__((aligned(16))) char ring[TB_SLOTS][TB_SLOTB];
+    __shared__ __attribute__((aligned(16))) char pbuf[2][TB_PBUFB];  // P^T of tiles s, s - 1
+    __shared__ int32_t sidx[F_IDX];                                   // the group's index slots
+    __shared__ float xm[2][M_H];                  // reference-maximum exchange (key quarters)
+    __shared__ float xl[2][2][M_H];               // row sums of the two S waves, by split parity
+    __shared__ float xr[2][M_H];                  // reference maximum, by split parity
+    __shared__ float xs[TM_MAX_GROUP][2][M_H];    // largest logit per split and S wave (reruns)
+    __shared__ uint32_t sh_ne[2], sh_ovf;         // non-empty 32-key tiles; splits to run again
+
+    const int ngroups = nsplit / group;
+    const int64_t pair = xcd_pair(pairs_per_xcd);
+    if (pair >= n_rows * ngroups)
+        return;
+    const int64_t orow = pair / ngroups;
+    const int split0 = (int)(pair % ngroups) * group;
+    const int layer = (int)(orow / T);
+    const int64_t i = orow % T;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tw = w & 3;  // wave within its team
+    const int g = lane >> 5, j = lane & 31;
+    const MlaLayerDev Ld = layers.l[layer];
+    const RowInfo r = row_info(L, i);
+    const float c2 = sm_scale * Ld.kv_scale * LOG2E;
+
+    // the group's 32-key tiles: split split0 + gs covers tiles [gs tps, min(nt, (gs + 1) tps))
+    const int tps = tiles_per_split;
+    const int ntiles_all = (k + 31) / 32;
+    const int g_begin = split0 * tps;
+    const int nt = max(0, min(ntiles_all, (split0 + group) * tps) - g_begin);
+    const int32_t *irow = indices + i * k + (int64_t)g_begin * 32;
+    const int nidx = min(k - g_begin * 32, nt * 32);
+
+    // ---- prologue (all 512 threads): the group's index list and the row's Q to LDS, slot 0
+    //      cleared; the non-empty tiles noted
+    {
+        int32_t v[F_IDX / TM_THREADS];
+#pragma unroll
+        for (int u = 0; u < F_IDX / TM_THREADS; ++u) {
+            const int e = tid + TM_THREADS * u;
+            v[u] = e < nidx ? irow[e] : -1;
+        }
+        u32x4 qv[(M_H * 72 + TM_THREADS - 1) / TM_THREADS];
+        const u32x4 *qsrc = (const u32x4 *)((const uint16_t *)Ld.q + i * M_H * M_DQK);
+#pragma unroll
+        for (int u = 0; u < (M_H * 72 + TM_THREADS - 1) / TM_THREADS; ++u) {
+            const int c = tid + TM_THREADS * u;
+            if (c < M_H * 72)
+                qv[u] = qsrc[c];
+        }
+        for (int e = tid; e < TB_SLOTB / 16; e += TM_THREADS)
+            ((u32x4 *)&ring[0][0])[e] = u32x4{0u, 0u, 0u, 0u};
+        if (tid < 2)
+            sh_ne[tid] = 0u;
+        if (tid == 0)
+            sh_ovf = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < F_IDX / TM_THREADS; ++u) {
+            const int e = tid + TM_THREADS * u;  // a wave covers tiles 2m, 2m + 1 (m = e >> 6)
+            const bool in = e < nt * 32;
+            if (in)
+                sidx[e] = v[u];
+            const uint64_t bal = __ballot(in && v[u] >= 0);
+            if (lane == 0 && bal != 0ull) {
+                const int t2 = (e >> 5) & ~1;  // this wave's even tile
+                const uint32_t bits = ((uint32_t)bal != 0u ? 1u : 0u) | ((bal >> 32) != 0ull ? 2u : 0u);
+                atomicOr(&sh_ne[t2 >> 5], bits << (t2 & 31));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < (M_H * 72 + TM_THREADS - 1) / TM_THREADS; ++u) {
+            const int c = tid + TM_THREADS * u;
+            if (c < M_H * 72)
+                *(u32x4 *)(&ring[0][0] + TB_QOFF + (c / 72) * TM_QROWB + 16 * (c % 72)) = qv[u];
+        }
+        __syncthreads();
+    }
+    const uint64_t ne = ((uint64_t)sh_ne[1] << 32) | sh_ne[0];
+    // tile s is the first non-empty tile of its split
+    auto first_of_split = [&](int s) __attribute__((always_inline)) {
+        const int st = (s / tps) * tps;
+        const uint64_t below = ((1ull << s) - 1ull) & ~((1ull << st) - 1ull);
+        return ((ne >> s) & 1ull) != 0ull && (ne & below) == 0ull;
+    };
+    auto last_of_split = [&](int s) __attribute__((always_inline)) {
+        return s + 1 == nt || (s + 1) % tps == 0;
+    };
+
+    // The two teams run separate code with the same sequence of block barriers (see
+    // mla_fp8_kernel).
+    if (w < 4) {
+        // ================================ S team ================================
+        const int hh = tw & 1, kq = tw >> 1;
+        const int hd0 = 32 * hh + (lane & 15);  // head of block 0 (block 1: + 16)
+        const int qg = lane >> 4;               // key group: keys 16 kq + 4 qg + 0..3
+        // Q^T of block hb: head hd0 + 16 hb, dims 32t + 8 qg .. +7 (the 16x16x32 B operand)
+        bf16x8 qT[2][18];
+        float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY}, l_own[2] = {0.f, 0.f};
+        bool ovf = false;
+        const bool paged = L.block_table != nullptr;
+        const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * 1152,
+                                      (paged ? L.cache_rows : r.n) * 1152);
+        const uint32_t lds0 = lds_addr_of(&ring[0][0]);
+        uint32_t rc[Bf16Slot::PER_WAVE];
+        Bf16Slot::geometry(tw, lane, rc);
+
+        // step s (tile s of the pass starting at tile t0): logits of this wave's 16 keys for
+        // its 32 heads, softmax numerators against the split's reference maximum, P^T to LDS;
+        // with gather, this wave's share of tile s + 1 issued between the k-steps
+        auto s_step = [&](int s, int t0, bool need_ref, bool gather) __attribute__((always_inline)) {
+            int voff[Bf16Slot::PER_WAVE];
+            const uint32_t nslot = lds0 + (uint32_t)((s + 1 - t0) % TB_SLOTS) * TB_SLOTB;
+            if (gather)
+                Bf16Slot::offsets(sidx + 32 * (s + 1), rc, voff);
+            const int gs = s / tps;
+            if (s % tps == 0 || s == t0) {  // a split starts
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    const int hd = hd0 + 16 * hb;
+                    m_ref[hb] = need_ref ? -INFINITY : fmaxf(xs[gs][0][hd], xs[gs][1][hd]);
+                    m_seen[hb] = -INFINITY;
+                    l_own[hb] = 0.f;
+                }
+                ovf = false;
+            }
+            const char *slot = &ring[0][0] + ((s - t0) % TB_SLOTS) * TB_SLOTB;
+            char *pw = &pbuf[(s - t0) & 1][0] + hd0 * TB_PROWB + 2 * (16 * kq + 4 * qg);
+            const uint32_t valid = (uint32_t)__ballot(lane < 32 && sidx[s * 32 + (lane & 31)] >= 0);
+            if (valid == 0u) {  // no key of the tile: P = 0 (also before the reference is fixed)
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+                    *(u32x2 *)(pw + 16 * hb * TB_PROWB) = u32x2{0u, 0u};
+                if (gather)
+#pragma unroll
+                    for (int q = 0; q < Bf16Slot::PER_WAVE; ++q)
+                        Bf16Slot::one(seq, nslot, tw, lane, q, voff[q]);
+            } else {
+                f32x4 S[2] = {f32x4{}, f32x4{}};
+                const char *arow = slot + (16 * kq + (lane & 15)) * TB_ROWB + 16 * qg;
+                constexpr int AD = 4;  // K operands read this many k-steps ahead
+                u32x4 A[AD];
+#pragma unroll
+                for (int t = 0; t < AD - 1; ++t)
+                    A[t] = *(const u32x4 *)(arow + 64 * t);
+#pragma unroll
+                for (int t = 0; t < 18; ++t) {
+                    if (t + AD - 1 < 18)
+                        A[(t + AD - 1) % AD] = *(const u32x4 *)(arow + 64 * (t + AD - 1));
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, A[t % AD]);
+                    S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[0][t], S[0], 0, 0, 0);
+                    S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qT[1][t], S[1], 0, 0, 0);
+                    if (gather && t % 3 == 1 && t / 3 < Bf16Slot::PER_WAVE)
+                        Bf16Slot::one(seq, nslot, tw, lane, t / 3, voff[t / 3]);
+                }
+                // lane holds keys 16 kq + 4 qg + e of heads hd0 (S[0]) and hd0 + 16 (S[1])
+                const bool full = valid == ~0u;
+                float mloc[2];
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    mloc[hb] = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = full || ((valid >> (16 * kq + 4 * qg + e)) & 1u);
+                        S[hb][e] = ok ? S[hb][e] * c2 : -INFINITY;
+                        mloc[hb] = fmaxf(mloc[hb], S[hb][e]);
+                    }
+                }
+                if (need_ref && first_of_split(s)) {  // the maximum over all 32 keys of the tile
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb) {
+                        float m = fmaxf(mloc[hb], __shfl_xor(mloc[hb], 16, 64));
+                        m = fmaxf(m, __shfl_xor(m, 32, 64));
+                        if (qg == 0)
+                            xm[kq][hd0 + 16 * hb] = m;
+                    }
+                    lds_barrier();
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb)
+                        m_ref[hb] = fmaxf(xm[0][hd0 + 16 * hb], xm[1][hd0 + 16 * hb]);
+                    lds_barrier();
+                }
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    m_seen[hb] = fmaxf(m_seen[hb], mloc[hb]);
+                    ovf |= mloc[hb] > m_ref[hb] + 100.f;
+                    float p[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        p[e] = __builtin_amdgcn_exp2f(S[hb][e] - m_ref[hb]);  // masked: exp2(-inf) = 0
+                    l_own[hb] += p[0] + p[1];
+                    l_own[hb] += p[2] + p[3];
+                    *(u32x2 *)(pw + 16 * hb * TB_PROWB) = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                }
+            }
+            if (last_of_split(s)) {  // (row sum, reference maximum) to the PV team
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    float l = l_own[hb] + __shfl_xor(l_own[hb], 16, 64);
+                    l = l + __shfl_xor(l, 32, 64);
+                    float ms = fmaxf(m_seen[hb], __shfl_xor(m_seen[hb], 16, 64));
+                    ms = fmaxf(ms, __shfl_xor(ms, 32, 64));
+                    const int hd = hd0 + 16 * hb;
+                    if (qg == 0) {
+                        xl[gs & 1][kq][hd] = l;
+                        if (kq == 0)
+                            xr[gs & 1][hd] = m_ref[hb];
+                        if (need_ref)
+                            xs[gs][kq][hd] = ms;
+                    }
+                }
+                if (ovf)
+                    atomicOr(&sh_ovf, 1u << gs);
+            }
+        };
+
+        // Q^T from LDS; the staging slots are cleared once every S wave has its copy
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int t = 0; t < 18; ++t)
+                qT[hb][t] = __builtin_bit_cast(
+                    bf16x8, *(const u32x4 *)(&ring[0][0] + TB_QOFF + (hd0 + 16 * hb) * TM_QROWB + 64 * t + 16 * qg));
+        // pass 0: every tile of the group; pass 1 + gs: split gs again, if it overflowed
+        uint32_t rerun = 0u;
+        for (int pass = 0; pass <= group; ++pass) {
+            const int t0 = pass == 0 ? 0 : (pass - 1) * tps;
+            const int t1 = pass == 0 ? nt : min(nt, pass * tps);
+            if ((pass == 0 && nt > 0) || (pass > 0 && ((rerun >> (pass - 1)) & 1u))) {
+                Bf16Slot::issue(seq, lds0, sidx + 32 * t0, tw, lane, rc);  // tile t0, this wave's share
+                lds_barrier();
+                if (pass == 0)
+                    for (int e = tid; e < 2 * TB_SLOTB / 16; e += 256)
+                        ((u32x4 *)(&ring[0][0] + TB_QOFF))[e] = u32x4{0u, 0u, 0u, 0u};
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                lds_barrier();  // tile t0 has landed
+                for (int s = t0; s <= t1; ++s) {
+                    if (s < t1)
+                        s_step(s, t0, pass == 0, s + 1 < t1);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's share of tile s + 1
+                    lds_barrier();
+                }
+            }
+            if (pass == 0) {
+                __syncthreads();
+                rerun = sh_ovf;
+            }
+        }
+    } else {
+        // ================================ PV team ================================
+        // wave b: dims 128 b .. +127 of all 64 heads
+        const int b = tw;
+        f32x16 O[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            O[mt][0] = O[mt][1] = f32x16{};
+
+        // this sequence's rows, or with paged caches the whole cache (host: at most 4 GiB - 1 MiB)
+        const bool paged = L.block_table != nullptr;
+        const int64_t seq_bytes = (paged ? L.cache_rows : r.n) * 1152;
+        const i32x4 seq = buffer_desc((const uint8_t *)Ld.kv + (paged ? 0 : r.kv_base) * 1152, seq_bytes);
+        const uint32_t lds0 = lds_addr_of(&ring[0][0]);
+        uint32_t rc[Bf16Slot::PER_WAVE];
+        Bf16Slot::geometry(4 + b, lane, rc);
+        // V^T read geometry (ds_read_b64_tr_b16): lane reads rows 4g + ((lane & 15) >> 2) and
+        // +8 of a 16-key step at dims 128 b + 16 ((lane >> 4) & 1) + 4 (lane & 3) (+32 mt): the
+        // operand's keys 4g + 0..3 and 8 + 4g + 0..3 of the step
+        const int voffs = (4 * g + ((lane & 15) >> 2)) * TB_ROWB + 2 * (128 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+        // O^T += V^T . P^T over the 32 keys of tile t (pass starting at t0); with gather, this
+        // wave's share of tile t + 2 issued between the MFMAs
+        auto pv_tile = [&](int t, int t0, bool gather) __attribute__((always_inline)) {
+            int voff[Bf16Slot::PER_WAVE];
+            const uint32_t nslot = lds0 + (uint32_t)((t + 2 - t0) % TB_SLOTS) * TB_SLOTB;
+            if (gather)
+                Bf16Slot::offsets(sidx + 32 * (t + 2), rc, voff);
+            const char *vb0 = &ring[0][0] + ((t - t0) % TB_SLOTS) * TB_SLOTB + voffs;
+            const char *pb = &pbuf[(t - t0) & 1][0] + j * TB_PROWB + 8 * g;
+            s16x4 V[2][4][2];
+            auto v_load = [&](int u, s16x4 (&Vd)[4][2]) __attribute__((always_inline)) {
+                const char *vb = vb0 + 16 * u * TB_ROWB;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    Vd[mt][0] = lds_tr16(vb + 64 * mt);
+                    Vd[mt][1] = lds_tr16(vb + 8 * TB_ROWB + 64 * mt);
+                }
+            };
+            v_load(0, V[0]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (u + 1 < 2)
+                    v_load(u + 1, V[1]);
+                // keys 16u + 4g + 0..3 and 16u + 8 + 4g + 0..3 of heads j, 32 + j
+                bf16x8 pp[2];
+#pragma unroll
+                for (int nh = 0; nh < 2; ++nh) {
+                    const char *pr = pb + 32 * nh * TB_PROWB + 32 * u;
+                    const u32x2 lo = *(const u32x2 *)pr, hi = *(const u32x2 *)(pr + 16);
+                    pp[nh] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const s16x4 lo = V[u][mt][0], hi = V[u][mt][1];
+                    typedef short s16x8 __attribute__((ext_vector_type(8)));
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                    O[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[0], O[mt][0], 0, 0, 0);
+                    O[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[1], O[mt][1], 0, 0, 0);
+                    const int q = 4 * u + mt;  // loads 0..4 after the first five MFMA pairs
+                    if (gather && q < Bf16Slot::PER_WAVE)
+                        Bf16Slot::one(seq, nslot, 4 + b, lane, q, voff[q]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // the split of tile t (pass starting at t0) is complete: its result out, O cleared
+        auto finish_split = [&](int t, int t0) __attribute__((always_inline)) {
+            const int gs = t / tps;
+            char *slot = &ring[0][0] + ((t - t0) % TB_SLOTS) * TB_SLOTB;
+            // head r's 256 bytes in row r of the tile's slot, the wave's columns 256 b .. +255
+            auto stage = [&](int rr, int c) __attribute__((always_inline)) { return slot + rr * TB_ROWB + 256 * b + c; };
+            float l[2], m[2];
+#pragma unroll
+            for (int nh = 0; nh < 2; ++nh) {
+                l[nh] = xl[gs & 1][0][32 * nh + j] + xl[gs & 1][1][32 * nh + j];
+                m[nh] = xr[gs & 1][32 * nh + j];
+            }
+            mla_team_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, stage, ws_o, ws_ml);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                O[mt][0] = O[mt][1] = f32x16{};
+        };
+        auto run = [&](int t0, int t1, bool need_ref) __attribute__((always_inline)) {
+            Bf16Slot::issue(seq, lds0, sidx + 32 * t0, 4 + b, lane, rc);  // tile t0, this wave's share
+            lds_barrier();  // (first pass: the S team has its copy of Q and clears slots 1..2)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();  // tile t0 has landed
+            for (int s = t0; s <= t1; ++s) {
+                // tile s + 1 goes into the slot of tile s - 2 (consumed in step s - 1)
+                if (need_ref && s < t1 && first_of_split(s)) {
+                    lds_barrier();  // the S team's two exchange barriers
+                    lds_barrier();
+                }
+                if (s > t0)
+                    pv_tile(s - 1, t0, s + 1 < t1);
+                else if (s + 1 < t1)  // the pass's first step has no PV work
+                    Bf16Slot::issue(seq, lds0 + (uint32_t)((s + 1 - t0) % TB_SLOTS) * TB_SLOTB, sidx + 32 * (s + 1),
+                                    4 + b, lane, rc);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's share of tile s + 1
+                // after the wait, so that the result's stores are the newest memory operations
+                if (s > t0 && last_of_split(s - 1))
+                    finish_split(s - 1, t0);
+                lds_barrier();
+            }
+        };
+        uint32_t rerun = 0u;
+        for (int pass = 0; pass <= group; ++pass) {
+            const int t0 = pass == 0 ? 0 : (pass - 1) * tps;
+            const int t1 = pass == 0 ? nt : min(nt, pass * tps);
+            if ((pass == 0 && nt > 0) || (pass > 0 && ((rerun >> (pass - 1)) & 1u)))
+                run(t0, t1, pass == 0);
+            if (pass == 0) {
+                __syncthreads();
+                rerun = sh_ovf;
+            }
+        }
+        // splits past the end of the index list (none under the split policy): empty results
+        for (int gs = 0; gs < group; ++gs)
+            if (gs * tps >= nt) {
+                const float l[2] = {0.f, 0.f}, m[2] = {-INFINITY, -INFINITY};
+                auto stage = [&](int rr, int c) __attribute__((always_inline)) {
+                    return &ring[0][0] + rr * TB_ROWB + 256 * b + c;
+                };
+                mla_team_store<OUT_F32>(O, l, m, Ld, i, orow, split0 + gs, nsplit, b, g, j, lane, stage, ws_o, ws_ml);
             }
     }
 }
@@ -1472,6 +1504,60 @@ __global__ __launch_bounds__(G_THREADS) void mla_generic_kernel(LayoutDev L, int
 // list, Q, the first gathers' latency, the partial's store) are ~20K cycles against ~7.5K per
 // tile, so 4-tile splits lose even with twice the blocks (64-row ragged decode: 512 blocks of 4
 // tiles 59 us, 256 blocks of 8 tiles 48 us).
+// ------------------------------------------------------------------------------------------
+// Gather ceiling (a measurement aid, no method arithmetic): the row traffic of the sparse-MLA
+// stage alone.  One 512-thread block per 256 index slots of one index row gathers those rows
+// into LDS with the same buffer-to-LDS loads and slot geometry as the team kernels (eight
+// waves share each 32-row slot, three slots in flight, then a wait), and discards them.
+// ------------------------------------------------------------------------------------------
+constexpr int GC_ROWS = 256;  // index slots per block
+template <int RB>
+__global__ __launch_bounds__(TM_THREADS) void gather_ceiling_kernel(const uint8_t *__restrict__ rows,
+                                                                    int64_t n_rows,
+                                                                    const int32_t *__restrict__ indices,
+                                                                    int k, int chunks, uint32_t *sink)
+{
+    typedef SlotDma<RB, 8> Slot;
+    __shared__ __attribute__((aligned(16))) char ring[3][Slot::SLOTB];
+    __shared__ int32_t sidx[GC_ROWS];
+    const int64_t row = blockIdx.x / chunks;
+    const int c0 = (int)(blockIdx.x % chunks) * GC_ROWS;
+    const int n = min(GC_ROWS, k - c0);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid < GC_ROWS)
+        sidx[tid] = tid < n ? indices[row * k + c0 + tid] : -1;
+    __syncthreads();
+    const i32x4 seq = buffer_desc(rows, n_rows * RB);
+    const uint32_t lds0 = lds_addr_of(&ring[0][0]);
+    uint32_t rc[Slot::PER_WAVE];
+    Slot::geometry(w, lane, rc);
+    const int ntile = (n + 31) / 32;
+    for (int t = 0; t < ntile; ++t) {
+        Slot::issue(seq, lds0 + (uint32_t)(t % 3) * Slot::SLOTB, sidx + 32 * t, w, lane, rc);
+        if (t % 3 == 2 || t + 1 == ntile) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    }
+    if (tid == 0 && blockIdx.x == 0)
+        sink[0] = *(const uint32_t *)&ring[0][0];
+}
+
+hipError_t launch_gather_ceiling(const void *rows, int64_t n_rows, int row_bytes, const int32_t *indices, int64_t T,
+                                 int k, uint32_t *sink, hipStream_t stream)
+{
+    const int chunks = (k + GC_ROWS - 1) / GC_ROWS;
+    const dim3 grid((unsigned)(T * chunks));
+    if (row_bytes == 576)
+        hipLaunchKernelGGL(gather_ceiling_kernel<576>, grid, dim3(TM_THREADS), 0, stream, (const uint8_t *)rows,
+                           n_rows, indices, k, chunks, sink);
+    else
+        hipLaunchKernelGGL(gather_ceiling_kernel<1152>, grid, dim3(TM_THREADS), 0, stream, (const uint8_t *)rows,
+                           n_rows, indices, k, chunks, sink);
+    return hipGetLastError();
+}
+
 int mla_num_splits(int64_t rows, int k, int min_tiles)
 {
     const int ntiles = (k + M_TILE - 1) / M_TILE;
@@ -1522,11 +1608,6 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
         wml = wo + (size_t)rows * ns * M_H * M_DC;
     }
     const int64_t pairs = rows * ns;
-    const int64_t ppx = (pairs + 7) / 8;
-    dim3 grid((unsigned)(8 * ppx));
-#define DSA_MLA_LAUNCH(F8, OF)                                                                   \
-    hipLaunchKernelGGL((mla_kernel<F8, OF>), grid, dim3(M_THREADS), 0, stream, L, T, rows, layers,  \
-                       indices, k, sm_scale, ns, tps, ppx, wo, wml)
     if (kv_fp8) {
         // consecutive splits of a row share a block while that leaves a block per CU: the
         // splits (and so every result bit) stay those of the policy above, only their
@@ -1553,12 +1634,19 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
             hipLaunchKernelGGL((mla_hh_kernel<false>), hgrid, dim3(M_THREADS), 0, stream, L, T, rows, layers,
                                indices, k, sm_scale, ns, tps, hppx, wo, wml);
     } else {
+        // many rows (prefill): the two-team kernel, 32-key tiles (two per policy tile)
+        int group = 1;
+        while (group * 2 <= TM_MAX_GROUP && ns % (group * 2) == 0 && pairs / (group * 2) >= MLA_TARGET_BLOCKS)
+            group *= 2;
+        const int64_t gpx = (pairs / group + 7) / 8;
+        dim3 bgrid((unsigned)(8 * gpx));
         if (out_f32)
-            DSA_MLA_LAUNCH(false, true);
+            hipLaunchKernelGGL((mla_bf16_team_kernel<true>), bgrid, dim3(TM_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, 2 * tps, group, gpx, wo, wml);
         else
-            DSA_MLA_LAUNCH(false, false);
+            hipLaunchKernelGGL((mla_bf16_team_kernel<false>), bgrid, dim3(TM_THREADS), 0, stream, L, T, rows, layers,
+                               indices, k, sm_scale, ns, 2 * tps, group, gpx, wo, wml);
     }
-#undef DSA_MLA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1)
         return e;

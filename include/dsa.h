@@ -368,6 +368,26 @@ dsa_status sparse_mla_decode_shared(const dsa_layout *layout, int H, int D_c, in
                                     const int32_t *indices, int k, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/*
+ * dsa_gather_ceiling -- a measurement aid; no step of the method.  Gathers the
+ * rows of a latent cache that an index set selects, with the buffer-to-LDS
+ * loads and slot geometry of the tuned sparse-MLA kernels, and discards them:
+ * the row traffic of the sparse-MLA stage without its arithmetic, so the
+ * bandwidth it reaches on a workload's own indices bounds that stage.
+ *   rows        device, n_rows rows of row_bytes bytes (576: fp8 latent
+ *               rows, 1152: bf16), read only
+ *   indices     device int32 [T][k]: rows of `rows` (absolute; -1 = none)
+ *   sink        device, >= 4 bytes: receives one word of the gathered data
+ *   stream      hipStream_t, or NULL for the default stream
+ * One 512-thread block per 256 index slots of a row, three 32-row slots in
+ * flight.  Errors: DSA_ERR_INVALID_ARG for NULL pointers, row_bytes other than
+ * 576 or 1152, T < 1, k outside 1 .. DSA_TOPK_MAX, n_rows < 1 or a table of
+ * 4 GiB - 1 MiB or more; DSA_ERR_HIP if the launch fails.  Nothing is
+ * allocated.
+ */
+dsa_status dsa_gather_ceiling(const void *rows, int64_t n_rows, int row_bytes, const int32_t *indices,
+                              int64_t T, int k, uint32_t *sink, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *dsa_last_error(void);
 
