@@ -1336,81 +1336,85 @@ constexpr int MLA_MAX_SPLITS = 32;  // the split count never exceeds this (mla_n
 constexpr int MLA_MIN_TILES_BF16 = 2;  // fewest tiles per split (see mla_num_splits)
 constexpr int MLA_MIN_TILES_FP8 = 8;
 
-// Combine the split partials of every (output row, head), in split order.  One 128-thread
-// block per (row, head); thread t owns dims 4t .. 4t + 3.  Partial s holds O_s / l_s, so
-// its weight is l_s 2^(m_s - M) / sum over splits of the same.
-template <bool OUT_F32>
-__global__ __launch_bounds__(128) void mla_combine_kernel(int64_t T, MlaLayersDev layers, int nsplit,
+// Combine the split partials of every (output row, head), in split order.  One 256-thread
+// block per (row, 4 heads): wave w takes head 4 blockIdx.y + w, lane l its dims 8l .. 8l + 7
+// (16 bytes of a bf16 partial).  Partial s holds O_s / l_s, so its weight is l_s 2^(m_s - M) /
+// sum over splits of the same; the wave works the weights out itself (lane s holds split s),
+// so the block has no barrier.  NSB bounds the split count (register arrays).
+template <bool OUT_F32, int NSB>
+__global__ __launch_bounds__(256) void mla_combine_kernel(int64_t T, MlaLayersDev layers, int nsplit,
                                                           const float *__restrict__ ws_o,
                                                           const float *__restrict__ ws_ml)
 {
-    __shared__ float wts[32];
-    __shared__ float lse_s;
     const int64_t orow = blockIdx.x;
-    const int head = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int head = 4 * (int)blockIdx.y + (tid >> 6);
     const int layer = (int)(orow / T);
     const int64_t i = orow % T;
     const MlaLayerDev Ld = layers.l[layer];
-    const int tid = threadIdx.x;
     // every split's partial is requested first (independent of the weights), so their
     // latencies overlap each other and the weight computation
-    const int64_t pbase = (orow * nsplit * M_H + head) * M_DC + 4 * tid;
-    typedef typename std::conditional<OUT_F32, f32x4, u32x2>::type Piece;
-    Piece pv[MLA_MAX_SPLITS];
+    const int64_t pbase = (orow * nsplit * M_H + head) * M_DC + 8 * lane;
+    typedef typename std::conditional<OUT_F32, f32x4, u32x4>::type Piece;
+    Piece pv[NSB][OUT_F32 ? 2 : 1];
 #pragma unroll
-    for (int sp = 0; sp < MLA_MAX_SPLITS; ++sp) {
+    for (int sp = 0; sp < NSB; ++sp) {
         if (sp < nsplit) {
             const int64_t pe = pbase + (int64_t)sp * M_H * M_DC;
-            if constexpr (OUT_F32)
-                pv[sp] = *(const f32x4 *)(ws_o + pe);
-            else
-                pv[sp] = *(const u32x2 *)((const uint16_t *)ws_o + pe);
-        }
-    }
-    if (tid < 64) {
-        const float *ml = ws_ml + (orow * nsplit * M_H + head) * 2;
-        const int sp = tid;
-        const float ms = sp < nsplit ? ml[sp * M_H * 2] : -INFINITY;
-        const float ls = sp < nsplit ? ml[sp * M_H * 2 + 1] : 0.f;
-        const float mx = wave_max(ms);
-        const float e = (mx == -INFINITY || sp >= nsplit) ? 0.f : exp2f(ms - mx);
-        // fixed-order total: splits are summed in index order by lane 0
-        float tot = 0.f;
-        for (int s2 = 0; s2 < nsplit; ++s2)
-            tot += __shfl(e * ls, s2, 64);
-        const float inv = tot > 0.f ? Ld.kv_scale / tot : 0.f;
-        if (sp < nsplit)
-            wts[sp] = e * ls * inv;  // partials are O / l
-        if (tid == 0)
-            lse_s = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
-    }
-    __syncthreads();
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sp = 0; sp < MLA_MAX_SPLITS; ++sp) {
-        if (sp < nsplit) {
-            f32x4 v;
             if constexpr (OUT_F32) {
-                v = pv[sp];
+                pv[sp][0] = *(const f32x4 *)(ws_o + pe);
+                pv[sp][OUT_F32 ? 1 : 0] = *(const f32x4 *)(ws_o + pe + 4);
             } else {
-                const u32x2 bw = pv[sp];
-                v = f32x4{__uint_as_float(bw[0] << 16), __uint_as_float(bw[0] & 0xFFFF0000u),
-                          __uint_as_float(bw[1] << 16), __uint_as_float(bw[1] & 0xFFFF0000u)};
+                pv[sp][0] = *(const u32x4 *)((const uint16_t *)ws_o + pe);
             }
-            const float wgt = wts[sp];
-            acc[0] = fmaf(wgt, v[0], acc[0]);
-            acc[1] = fmaf(wgt, v[1], acc[1]);
-            acc[2] = fmaf(wgt, v[2], acc[2]);
-            acc[3] = fmaf(wgt, v[3], acc[3]);
         }
     }
-    const int64_t o = (i * M_H + head) * M_DC + 4 * tid;
-    if (OUT_F32)
-        *(f32x4 *)((float *)Ld.out + o) = acc;
-    else
-        *(u32x2 *)((uint16_t *)Ld.out + o) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    if (Ld.lse && tid == 0)
-        Ld.lse[i * M_H + head] = lse_s;
+    const float *ml = ws_ml + (orow * nsplit * M_H + head) * 2;
+    const float ms = lane < nsplit ? ml[lane * M_H * 2] : -INFINITY;
+    const float ls = lane < nsplit ? ml[lane * M_H * 2 + 1] : 0.f;
+    const float mx = wave_max(ms);
+    const float e = (mx == -INFINITY || lane >= nsplit) ? 0.f : exp2f(ms - mx);
+    // fixed-order total: splits summed in index order (every lane the same sum)
+    float tot = 0.f;
+    for (int s2 = 0; s2 < nsplit; ++s2)
+        tot += __shfl(e * ls, s2, 64);
+    const float inv = tot > 0.f ? Ld.kv_scale / tot : 0.f;
+    const float wl = e * ls * inv;  // split `lane`'s weight (partials are O / l)
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < NSB; ++sp) {
+        if (sp < nsplit) {
+            float v[8];
+            if constexpr (OUT_F32) {
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    v[e2] = pv[sp][0][e2];
+                    v[4 + e2] = pv[sp][OUT_F32 ? 1 : 0][e2];
+                }
+            } else {
+                const u32x4 bw = pv[sp][0];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    v[2 * e2] = __uint_as_float(bw[e2] << 16);
+                    v[2 * e2 + 1] = __uint_as_float(bw[e2] & 0xFFFF0000u);
+                }
+            }
+            const float wgt = __shfl(wl, sp, 64);
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2)
+                acc[e2] = fmaf(wgt, v[e2], acc[e2]);
+        }
+    }
+    const int64_t o = (i * M_H + head) * M_DC + 8 * lane;
+    if (OUT_F32) {
+        *(f32x4 *)((float *)Ld.out + o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *(f32x4 *)((float *)Ld.out + o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    } else {
+        *(u32x4 *)((uint16_t *)Ld.out + o) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    }
+    if (Ld.lse && lane == 0)
+        Ld.lse[i * M_H + head] = tot > 0.f ? (mx + __log2f(tot)) * LN2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1650,11 +1654,23 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1)
         return e;
-    dim3 cgrid((unsigned)rows, M_H);
-    if (out_f32)
-        hipLaunchKernelGGL((mla_combine_kernel<true>), cgrid, dim3(128), 0, stream, T, layers, ns, wo, wml);
+    dim3 cgrid((unsigned)rows, M_H / 4);
+#define DSA_COMBINE(NSB)                                                                                         \
+    do {                                                                                                         \
+        if (out_f32)                                                                                             \
+            hipLaunchKernelGGL((mla_combine_kernel<true, NSB>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml); \
+        else                                                                                                     \
+            hipLaunchKernelGGL((mla_combine_kernel<false, NSB>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml); \
+    } while (0)
+    if (ns <= 4)
+        DSA_COMBINE(4);
+    else if (ns <= 8)
+        DSA_COMBINE(8);
+    else if (ns <= 16)
+        DSA_COMBINE(16);
     else
-        hipLaunchKernelGGL((mla_combine_kernel<false>), cgrid, dim3(128), 0, stream, T, layers, ns, wo, wml);
+        DSA_COMBINE(MLA_MAX_SPLITS);
+#undef DSA_COMBINE
     return hipGetLastError();
 }
 
