@@ -172,7 +172,7 @@ class Runner:
         if paged:
             self.layout, self.ik, self.ik_scale, self.kvs = paged
         dev = case.iq.device
-        self.ld = case.max_ctx
+        self.ld = dsa.score_pitch(case.max_ctx)
         self.scores = torch.empty((case.T, self.ld), dtype=torch.float32, device=dev)
         self.idx = torch.empty((case.T, case.topk), dtype=torch.int32, device=dev)
         odt = torch.float32 if case.out_dt == "f32" else torch.bfloat16

@@ -280,20 +280,27 @@ def dsa_index_front_end(q: torch.Tensor, k: torch.Tensor, slots: torch.Tensor, c
     return q_fp8, q_scale
 
 
+def score_pitch(max_ctx: int) -> int:
+    """Default row pitch of a score array: max_ctx rounded up to 32 floats, so that every row
+    starts on a 128-byte line and the indexer stores whole lines."""
+    return (int(max_ctx) + 31) & ~31
+
+
 def dsa_index_scores(layout: Layout, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor,
                      k_scale: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
                      scores: Optional[torch.Tensor] = None, ld: Optional[int] = None,
                      k_row_stride: Optional[int] = None, k_scale_stride: int = 1,
                      k_dtype: Optional[int] = None, stream=None) -> torch.Tensor:
-    """Indexer scores [T, ld] fp32.  q: [T, H_I, D_I]; k: [rows, D_I] (or a raw uint8 byte
-    buffer with k_row_stride bytes per row and k_dtype given)."""
+    """Indexer scores [T, ld] fp32 (ld defaults to score_pitch(max_ctx)).  q: [T, H_I, D_I];
+    k: [rows, D_I] (or a raw uint8 byte buffer with k_row_stride bytes per row and k_dtype
+    given)."""
     lib = load_library()
     T, H_I, D_I = q.shape
     kd = _dt(k) if k_dtype is None else k_dtype
     if k_row_stride is None:
         k_row_stride = k.shape[-1] * k.element_size()
     if ld is None:
-        ld = scores.shape[1] if scores is not None else layout.max_ctx
+        ld = scores.shape[1] if scores is not None else score_pitch(layout.max_ctx)
     if scores is None:
         scores = torch.empty((T, ld), dtype=torch.float32, device=q.device)
     _dev(scores, "scores", torch.float32)
@@ -347,7 +354,7 @@ def dsa_index_topk(layout: Layout, q: torch.Tensor, w: torch.Tensor, k: torch.Te
     if k_row_stride is None:
         k_row_stride = k.shape[-1] * k.element_size()
     if ld is None:
-        ld = scores.shape[1] if scores is not None else layout.max_ctx
+        ld = scores.shape[1] if scores is not None else score_pitch(layout.max_ctx)
     if scores is None:
         scores = torch.empty((T, ld), dtype=torch.float32, device=q.device)
     if indices is None:

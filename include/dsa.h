@@ -206,7 +206,9 @@ dsa_status dsa_index_front_end(int64_t T, int H_I, dsa_dtype dt, const void *q, 
  *   k_scale       fp32 scale of row r at k_scale[r * k_scale_stride];
  *                 required iff k_dt is FP8_E4M3FN.
  *   scores, ld    fp32 output, row i at scores + i * ld; ld >= max_ctx.  Only
- *                 s < n_i is written.
+ *                 s < n_i is written.  With ld a multiple of 32 and scores
+ *                 128-byte aligned every row starts on a cache line and the
+ *                 decode kernel stores whole lines (faster on ragged batches).
  * The fp8 x bf16 products are exact in fp32; sums are fp32.
  * The tuned fp8-query kernel addresses keys with 32-bit offsets: it needs
  * max_ctx * k_row_stride (cache_rows * k_row_stride with paged caches)
