@@ -12,6 +12,10 @@ One step = one pass of the whole path over one batch of synthetic input.  The de
 workload is the largest decode workload, IndexShare decode: 32 sequences of 131072 tokens,
 one indexer pass over the fp8 index cache (32 heads x 128) and one top-2048 whose indices
 feed four sparse-MLA layers, each over its own fp8 latent cache (64 heads, 512 + 64).
+A step makes three library calls: dsa_index_scores_hist (the indexer, which also builds the
+top-k's score histogram where the kernels allow), dsa_topk_after_hist (the selection) and
+the sparse-MLA call; the same steps with the two plain calls (dsa_index_scores, then dsa_topk
+with its own histogram pass) are timed beside it.
 Smaller workloads fit in the 256 MB Infinity Cache, so the timed loop rotates over enough
 independent input sets (> 1 GB in total) that every step reads HBM.  The line prints one
 JSON object; after the headline workload the two other decode workloads (batch 8 x 8192
@@ -52,8 +56,9 @@ def parse():
     p.add_argument("--workload", default="share", choices=sorted(WORKLOADS))
     p.add_argument("--no-others", action="store_true",
                    help="measure the headline workload only (no other_workloads summary)")
-    p.add_argument("--no-fused", action="store_true",
-                   help="skip the fused indexer + top-k timing (profiler runs: only the headline's kernels)")
+    p.add_argument("--no-compare", "--no-fused", dest="no_compare", action="store_true",
+                   help="skip the comparison timing of indexer and top-k as the two plain calls "
+                        "(profiler runs: only the headline's kernels)")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough for > 1 GB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
@@ -180,20 +185,27 @@ class Runner:
         self.ws = dsa.mla_workspace(self.layout, case.H, case.Dc, case.Dr, case.topk, len(case.layers), dev)
         self.tk_ws = dsa.topk_workspace(self.layout, self.ld, case.topk, dev)
         self.prefill = case.q_indptr is not None
+        self.hist_built = 0
 
     def indexer(self):
+        """The indexer; where the kernels allow it also builds the top-k's histogram."""
+        c = self.case
+        _, self.hist_built = self.dsa.dsa_index_scores_hist(self.layout, c.iq, c.iw, self.ik, c.topk, self.tk_ws,
+                                                            k_scale=self.ik_scale, q_scale=c.iq_scale,
+                                                            scores=self.scores)
+
+    def topk(self):
+        """The selection (on the indexer's histogram when it built one)."""
+        self.dsa.dsa_topk_after_hist(self.layout, self.scores, self.case.topk, self.hist_built, indices=self.idx,
+                                     workspace=self.tk_ws)
+
+    def indexer_alone(self):
         c = self.case
         self.dsa.dsa_index_scores(self.layout, c.iq, c.iw, self.ik, k_scale=self.ik_scale, q_scale=c.iq_scale,
                                   scores=self.scores)
 
-    def topk(self):
+    def topk_alone(self):
         self.dsa.dsa_topk(self.layout, self.scores, self.case.topk, indices=self.idx, workspace=self.tk_ws)
-
-    def index_topk(self):
-        """Indexer and top-k as the one fused call (the top-k's histogram built by the indexer)."""
-        c = self.case
-        self.dsa.dsa_index_topk(self.layout, c.iq, c.iw, self.ik, c.topk, k_scale=self.ik_scale, q_scale=c.iq_scale,
-                                scores=self.scores, indices=self.idx, workspace=self.tk_ws)
 
     def mla(self):
         c = self.case
@@ -557,7 +569,7 @@ def main():
                 "ms_per_step": o["ms_per_step"], "value": o["value"], "unit": o["unit"],
                 "step_ms_events": o["step_ms_events"], "path_hbm": o["path_hbm"],
                 "kernels_ms": o["kernels_ms"], "roofline": o["roofline"], "steps": o["steps"],
-                "dtype": o["dtype"], "fused_index_topk": o["fused_index_topk"]}
+                "dtype": o["dtype"], "plain_index_topk": o["plain_index_topk"]}
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
@@ -657,19 +669,24 @@ def measure(workload, args, steps, warmup, headline):
         return {"median": round(a[len(a) // 2] if len(a) % 2 else 0.5 * (a[len(a) // 2 - 1] + a[len(a) // 2]), 5),
                 "min": round(a[0], 5), "max": round(a[-1], 5), "mean": round(sum(a) / len(a), 5)}
 
-    # the same steps with indexer and top-k as the fused call (reported beside the headline)
-    fz = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for s in range(0 if args.no_fused else steps):
+    # the same steps with indexer and top-k as the two plain calls, the top-k with its own
+    # histogram pass (reported beside the headline)
+    ncmp = 0 if args.no_compare else steps
+    fz = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ncmp)]
+    for s in range(ncmp):
         r = runners[s % nsets]
         e = fz[s]
         e[0].record(stream)
-        r.index_topk()
+        r.indexer_alone()
         e[1].record(stream)
-        r.mla()
+        r.topk_alone()
         e[2].record(stream)
+        r.mla()
+        e[3].record(stream)
     torch.cuda.synchronize()
-    fused_it = [fz[s][0].elapsed_time(fz[s][1]) for s in range(0 if args.no_fused else steps)]
-    fused_step = [fz[s][0].elapsed_time(fz[s][2]) for s in range(0 if args.no_fused else steps)]
+    alone_idx = [fz[s][0].elapsed_time(fz[s][1]) for s in range(ncmp)]
+    alone_topk = [fz[s][1].elapsed_time(fz[s][2]) for s in range(ncmp)]
+    alone_step = [fz[s][0].elapsed_time(fz[s][3]) for s in range(ncmp)]
 
     T = probe.T
     value = T * steps / elapsed
@@ -686,12 +703,15 @@ def measure(workload, args, steps, warmup, headline):
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
         achieved = st_model["bytes"] / (dur[dominant] * 1e-3) / 1e9
     split = runners[0].ws is not None and runners[0].ws.numel() > 0
+    hist = runners[0].hist_built  # the indexer built the top-k's histogram
     kernel_names = {
-        "indexer": "dsa_index_scores: " + ("idx_fp8_kernel" if prefill else "idx_decode_kernel"),
-        "topk": "dsa_topk: " + ("topk_direct_kernel" if probe.max_ctx <= 32768 else
-                                "topk_hist_kernel + topk_mark_kernel + topk_select_kernel"
-                                if probe.T <= 512 or probe.max_ctx > (1 << 18) else
-                                "topk_hist_kernel + topk_select_kernel"),
+        "indexer": "dsa_index_scores_hist: " + ("idx_fp8_kernel" if prefill else "idx_decode_kernel")
+        + (" (+ top-k histogram)" if hist else ""),
+        "topk": "dsa_topk_after_hist: " + ("topk_direct_kernel" if probe.max_ctx <= 32768 else
+                                           ("" if hist else "topk_hist_kernel + ")
+                                           + ("topk_mark_kernel + topk_select_kernel"
+                                              if probe.T <= 512 or probe.max_ctx > (1 << 18) else
+                                              "topk_select_kernel")),
         "mla": ("sparse_mla_prefill: " if prefill else "sparse_mla_decode%s: " % ("_shared" if len(probe.layers) > 1 else ""))
         + ("mla_fp8_kernel" if probe.layers[0].kv_dt == "fp8" else
            "mla_hh_kernel" if probe.T <= 64 else "mla_bf16_team_kernel")
@@ -725,10 +745,10 @@ def measure(workload, args, steps, warmup, headline):
         "step_ms_events": spread(per_step),
         "kernels_ms": {kernel_names[s]: round(dur[s], 5) for s in stages},
         "kernels_ms_spread": {kernel_names[s]: spread(per[s]) for s in stages},
-        "fused_index_topk": None if args.no_fused else {
-            "call": "dsa_index_topk (indexer with the top-k histogram, then the selection)",
-            "stage_ms": spread(fused_it), "step_ms_events": spread(fused_step),
-            "separate_stage_ms": round(dur["indexer"] + dur["topk"], 5)},
+        "plain_index_topk": None if args.no_compare else {
+            "calls": "dsa_index_scores, then dsa_topk with its own histogram pass",
+            "indexer_ms": spread(alone_idx), "topk_ms": spread(alone_topk),
+            "step_ms_events": spread(alone_step)},
         "roofline": {"kernel": kernel_names[dominant], "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic": st_model["bytes"] if bound == "hbm" else st_model["flops"],

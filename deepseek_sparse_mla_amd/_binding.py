@@ -23,7 +23,8 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = 0, 1, 2
 DSA_TOPK_MAX = 2048
 DSA_MAX_SHARED_LAYERS = 8
 
-EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_index_topk", "sparse_mla_workspace_size",
+EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_index_topk",
+           "dsa_index_scores_hist", "dsa_topk_after_hist", "sparse_mla_workspace_size",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "sparse_mla_decode_no_alloc",
            "dsa_gather_ceiling", "dsa_last_error",
            "dsa_abi_version")
@@ -71,6 +72,9 @@ def load_library(path: str = LIB_PATH):
         lib.dsa_topk_workspace_size.restype = S
         lib.dsa_topk.argtypes = [LP, P, L, I, P, P, S, P]
         lib.dsa_index_topk.argtypes = [LP, I, I, I, P, P, P, I, P, L, P, L, P, L, I, P, P, S, P]
+        lib.dsa_index_scores_hist.argtypes = [LP, I, I, I, P, P, P, I, P, L, P, L, P, L, I, P, S,
+                                              ctypes.POINTER(ctypes.c_int), P]
+        lib.dsa_topk_after_hist.argtypes = [LP, P, L, I, P, P, S, I, P]
         lib.sparse_mla_workspace_size.argtypes = [LP, I, I, I, I, I]
         lib.sparse_mla_workspace_size.restype = S
         mla = [LP, I, I, I, F, I, P, I, P, F, P, I, I, P, P, P, S, P]
@@ -81,7 +85,8 @@ def load_library(path: str = LIB_PATH):
                                                  ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
         lib.dsa_gather_ceiling.argtypes = [P, L, I, P, L, I, P, P]
         for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_front_end,
-                  lib.dsa_index_scores, lib.dsa_topk, lib.dsa_index_topk, lib.sparse_mla_decode, lib.sparse_mla_prefill,
+                  lib.dsa_index_scores, lib.dsa_topk, lib.dsa_index_topk, lib.dsa_index_scores_hist,
+                  lib.dsa_topk_after_hist, lib.sparse_mla_decode, lib.sparse_mla_prefill,
                   lib.sparse_mla_decode_shared, lib.sparse_mla_decode_no_alloc, lib.dsa_gather_ceiling,
                   lib.dsa_abi_version):
             f.restype = I
@@ -281,8 +286,8 @@ def dsa_index_front_end(q: torch.Tensor, k: torch.Tensor, slots: torch.Tensor, c
 
 
 def score_pitch(max_ctx: int) -> int:
-    """Default row pitch of a score array: max_ctx rounded up to 32 floats, so that every row
-    starts on a 128-byte line and the indexer stores whole lines."""
+    """Default row pitch of a score array: max_ctx rounded up to 32 floats (every row starts
+    on a 128-byte line)."""
     return (int(max_ctx) + 31) & ~31
 
 
@@ -370,6 +375,51 @@ def dsa_index_topk(layout: Layout, q: torch.Tensor, w: torch.Tensor, k: torch.Te
                             workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(lib, st)
     return scores, indices
+
+
+def dsa_index_scores_hist(layout: Layout, q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, k_top: int,
+                          workspace: Optional[torch.Tensor], k_scale: Optional[torch.Tensor] = None,
+                          q_scale: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                          ld: Optional[int] = None, k_row_stride: Optional[int] = None, k_scale_stride: int = 1,
+                          k_dtype: Optional[int] = None, stream=None):
+    """The first half of dsa_index_topk: scores, plus the top-k histogram in `workspace` where
+    the kernels fold it in.  Returns (scores [T, ld] fp32, hist_built) for dsa_topk_after_hist."""
+    lib = load_library()
+    T, H_I, D_I = q.shape
+    kd = _dt(k) if k_dtype is None else k_dtype
+    if k_row_stride is None:
+        k_row_stride = k.shape[-1] * k.element_size()
+    if ld is None:
+        ld = scores.shape[1] if scores is not None else score_pitch(layout.max_ctx)
+    if scores is None:
+        scores = torch.empty((T, ld), dtype=torch.float32, device=q.device)
+    built = ctypes.c_int(0)
+    st = lib.dsa_index_scores_hist(ctypes.byref(layout.c), H_I, D_I, _dt(q), _dev(q, "q"),
+                                   _dev(q_scale, "q_scale", torch.float32), _dev(w, "w", torch.float32),
+                                   kd, _dev(k, "k", contiguous=False), int(k_row_stride),
+                                   _dev(k_scale, "k_scale", torch.float32, contiguous=False), int(k_scale_stride),
+                                   _dev(scores, "scores", torch.float32), int(ld), int(k_top),
+                                   _dev(workspace, "workspace"), workspace.numel() if workspace is not None else 0,
+                                   ctypes.byref(built), _stream(stream))
+    _check(lib, st)
+    return scores, int(built.value)
+
+
+def dsa_topk_after_hist(layout: Layout, scores: torch.Tensor, k: int, hist_built: int,
+                        indices: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """The second half of dsa_index_topk: the selection, on the histogram that
+    dsa_index_scores_hist left in `workspace` when it returned hist_built = 1."""
+    lib = load_library()
+    T, ld = scores.shape
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    st = lib.dsa_topk_after_hist(ctypes.byref(layout.c), _dev(scores, "scores", torch.float32), int(ld), int(k),
+                                 _dev(indices, "indices", torch.int32), _dev(workspace, "workspace"),
+                                 workspace.numel() if workspace is not None else 0, int(hist_built),
+                                 _stream(stream))
+    _check(lib, st)
+    return indices
 
 
 def sparse_mla_workspace_size(layout: Layout, H: int, D_c: int, D_r: int, k: int, n_layers: int = 1) -> int:

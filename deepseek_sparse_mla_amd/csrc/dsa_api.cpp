@@ -521,14 +521,18 @@ dsa_status dsa_topk(const dsa_layout *layout, const float *scores, int64_t ld, i
                       "top-k launch");
 }
 
-dsa_status dsa_index_topk(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt, const void *q,
-                          const float *q_scale, const float *w, dsa_dtype k_dt, const void *k,
-                          int64_t k_row_stride, const float *k_scale, int64_t k_scale_stride,
-                          float *scores, int64_t ld, int k_top, int32_t *indices, void *workspace,
-                          size_t workspace_bytes, void *stream)
+dsa_status dsa_index_scores_hist(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt, const void *q,
+                                 const float *q_scale, const float *w, dsa_dtype k_dt, const void *k,
+                                 int64_t k_row_stride, const float *k_scale, int64_t k_scale_stride,
+                                 float *scores, int64_t ld, int k_top, void *workspace, size_t workspace_bytes,
+                                 int *hist_built, void *stream)
 {
-    // the top-k's own checks first: the indexer launch below is the first thing that runs
-    dsa_status st = check_topk(layout, scores, ld, k_top, indices, workspace, workspace_bytes);
+    if (!hist_built)
+        return fail(DSA_ERR_INVALID_ARG, "hist_built must not be NULL");
+    *hist_built = 0;
+    // the top-k's checks (indices aside: this call does not write them) come first
+    int32_t probe;
+    dsa_status st = check_topk(layout, scores, ld, k_top, &probe, workspace, workspace_bytes);
     if (st != DSA_OK)
         return st;
     const int64_t T = layout->total_q;
@@ -536,11 +540,42 @@ dsa_status dsa_index_topk(const dsa_layout *layout, int H_I, int D_I, dsa_dtype 
     bool fused = false;
     st = index_scores_impl(layout, H_I, D_I, q_dt, q, q_scale, w, k_dt, k, k_row_stride, k_scale,
                            k_scale_stride, scores, ld, stream, hist, &fused);
-    if (st != DSA_OK || T == 0)
+    if (st == DSA_OK)
+        *hist_built = fused ? 1 : 0;
+    return st;
+}
+
+dsa_status dsa_topk_after_hist(const dsa_layout *layout, const float *scores, int64_t ld, int k,
+                               int32_t *indices, void *workspace, size_t workspace_bytes, int hist_built,
+                               void *stream)
+{
+    dsa_status st = check_topk(layout, scores, ld, k, indices, workspace, workspace_bytes);
+    if (st != DSA_OK)
         return st;
-    return hip_status(dsa::launch_topk(to_dev(layout), T, layout->max_ctx, scores, ld, k_top, indices,
-                                       workspace, (hipStream_t)stream, fused),
+    const int64_t T = layout->total_q;
+    if (T == 0)
+        return ok();
+    return hip_status(dsa::launch_topk(to_dev(layout), T, layout->max_ctx, scores, ld, k, indices, workspace,
+                                       (hipStream_t)stream, hist_built != 0),
                       "top-k launch");
+}
+
+dsa_status dsa_index_topk(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt, const void *q,
+                          const float *q_scale, const float *w, dsa_dtype k_dt, const void *k,
+                          int64_t k_row_stride, const float *k_scale, int64_t k_scale_stride,
+                          float *scores, int64_t ld, int k_top, int32_t *indices, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    // both calls' checks first: the indexer launch is the first thing that runs
+    dsa_status st = check_topk(layout, scores, ld, k_top, indices, workspace, workspace_bytes);
+    if (st != DSA_OK)
+        return st;
+    int built = 0;
+    st = dsa_index_scores_hist(layout, H_I, D_I, q_dt, q, q_scale, w, k_dt, k, k_row_stride, k_scale,
+                               k_scale_stride, scores, ld, k_top, workspace, workspace_bytes, &built, stream);
+    if (st != DSA_OK)
+        return st;
+    return dsa_topk_after_hist(layout, scores, ld, k_top, indices, workspace, workspace_bytes, built, stream);
 }
 
 size_t sparse_mla_workspace_size(const dsa_layout *layout, int H, int D_c, int D_r, int k,

@@ -64,7 +64,7 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     // before the current tile's MFMAs, so every wave keeps a tile in flight.
     auto load_tile = [&](int64_t s0, u32x4 (&kv)[4], float &ksv) {
         const int64_t s = s0 + j;
-        const int64_t sc = min(max(s, s_begin), s_end - 1);
+        const int64_t sc = s < s_end ? s : s_end - 1;
         const int64_t row = pages ? ((int64_t)pages[(sc >> lg) - p0] << lg) | (sc & ((1 << lg) - 1))
                                   : kv_base + sc;
         const u32x4 *kp = (const u32x4 *)(k + row * kstride + 64 * g);
@@ -91,7 +91,7 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
         part += __shfl_xor(part, 32, 64);
         const int64_t s = s0 + j;
         const float v = part * ksv;
-        if (g == 0 && s >= s_begin && s < s_end) {
+        if (g == 0 && s < s_end) {
             out[s] = v;
             if (wh)  // the top-k's histogram bin of exactly the stored score (this wave's LDS copy)
                 atomicAdd(&wh[score_key(v) >> SCORE_BIN_SHIFT], 1u);
@@ -103,10 +103,7 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     // row), so the loop body is straight-line code and only the computed tile is waited for.
     u32x4 bufA[4], bufB[4];
     float kA = 0.f, kB = 0.f;
-    // tiles on 32-token boundaries of the row, so that a tile's 128-byte score store is one
-    // whole line when the row pitch is a multiple of 32 (a stream segment may start inside a
-    // tile: its tokens below s_begin are another block's, loaded but not stored)
-    int64_t s0 = (s_begin & ~(int64_t)31) + wave * 32;
+    int64_t s0 = s_begin + wave * 32;
     if (s0 >= s_end)
         return;
     load_tile(s0, bufA, kA);

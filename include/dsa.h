@@ -206,9 +206,7 @@ dsa_status dsa_index_front_end(int64_t T, int H_I, dsa_dtype dt, const void *q, 
  *   k_scale       fp32 scale of row r at k_scale[r * k_scale_stride];
  *                 required iff k_dt is FP8_E4M3FN.
  *   scores, ld    fp32 output, row i at scores + i * ld; ld >= max_ctx.  Only
- *                 s < n_i is written.  With ld a multiple of 32 and scores
- *                 128-byte aligned every row starts on a cache line and the
- *                 decode kernel stores whole lines (faster on ragged batches).
+ *                 s < n_i is written.
  * The fp8 x bf16 products are exact in fp32; sums are fp32.
  * The tuned fp8-query kernel addresses keys with 32-bit offsets: it needs
  * max_ctx * k_row_stride (cache_rows * k_row_stride with paged caches)
@@ -269,6 +267,35 @@ dsa_status dsa_index_topk(const dsa_layout *layout, int H_I, int D_I, dsa_dtype 
                           int64_t k_scale_stride, float *scores, int64_t ld_scores, int k_top,
                           int32_t *indices, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * dsa_index_scores_hist / dsa_topk_after_hist -- dsa_index_topk as two calls
+ * (same passages), so that a caller can time the two stages or put other
+ * work between them.
+ *   dsa_index_scores_hist takes dsa_index_topk's arguments without indices
+ *   and one more, hist_built (host int, not NULL): it writes the scores and,
+ *   for the shapes where dsa_index_topk folds the histogram into the
+ *   indexer, adds each row's histogram to the workspace and sets *hist_built
+ *   to 1; otherwise it sets 0 (the workspace is then untouched).
+ *   dsa_topk_after_hist takes dsa_topk's arguments and the hist_built value:
+ *   with 1 it runs only the selection, on the histogram the indexer call
+ *   left in the workspace; with 0 it is dsa_topk.
+ * Between the two calls nothing else may use the workspace, and the layout,
+ * scores, ld and workspace must be the same in both; hist_built = 1 without
+ * a preceding dsa_index_scores_hist that returned it gives undefined indices.
+ * Together they give dsa_index_topk's scores and indices, bit for bit, and
+ * leave the workspace zero as it does.  Checks: those of dsa_index_topk
+ * (hist_built NULL is DSA_ERR_INVALID_ARG), each before its own launch.
+ */
+dsa_status dsa_index_scores_hist(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
+                                 const void *q, const float *q_scale, const float *w,
+                                 dsa_dtype k_dt, const void *k, int64_t k_row_stride_bytes,
+                                 const float *k_scale, int64_t k_scale_stride, float *scores,
+                                 int64_t ld_scores, int k_top, void *workspace,
+                                 size_t workspace_bytes, int *hist_built, void *stream);
+dsa_status dsa_topk_after_hist(const dsa_layout *layout, const float *scores, int64_t ld, int k,
+                               int32_t *indices, void *workspace, size_t workspace_bytes,
+                               int hist_built, void *stream);
 
 /*
  * sparse_mla_decode / sparse_mla_prefill -- attention over the selected

@@ -281,6 +281,49 @@ def _it(lib, layout, **kw):
                               a["idx"], a["ws"], a["wsb"], None)
 
 
+def _ish(lib, layout, built, **kw):
+    a = dict(H=32, D=128, q_dt=B.DSA_BF16, q=FAKE, qs=None, w=FAKE, k_dt=B.DSA_FP8_E4M3FN, k=FAKE,
+             kstride=128, ks=FAKE, ks_stride=1, scores=FAKE, ld=4096, k_top=2048, ws=None, wsb=0)
+    a.update(kw)
+    return lib.dsa_index_scores_hist(ctypes.byref(layout), a["H"], a["D"], a["q_dt"], a["q"], a["qs"], a["w"],
+                                     a["k_dt"], a["k"], a["kstride"], a["ks"], a["ks_stride"], a["scores"], a["ld"],
+                                     a["k_top"], a["ws"], a["wsb"], built, None)
+
+
+def test_two_call_form_checks_before_launching(lib):
+    """dsa_index_scores_hist refuses what dsa_index_topk refuses (bar indices) and a NULL
+    hist_built, and reports hist_built = 0 on failure; dsa_topk_after_hist refuses what dsa_topk
+    refuses."""
+    built = ctypes.c_int(7)
+    assert _ish(lib, _layout(), None) == B.DSA_ERR_INVALID_ARG               # no hist_built
+    assert _ish(lib, _layout(), ctypes.byref(built), k_top=0) == B.DSA_ERR_INVALID_ARG
+    assert built.value == 0
+    assert _ish(lib, _layout(), ctypes.byref(built), H=0) == B.DSA_ERR_INVALID_ARG
+    assert _ish(lib, _layout(), ctypes.byref(built), ld=100) == B.DSA_ERR_INVALID_ARG
+    long_rows = _layout(batch=4, total_q=4, max_ctx=70000)
+    assert _ish(lib, long_rows, ctypes.byref(built), ld=70000) == B.DSA_ERR_WORKSPACE
+    L = ctypes.byref(_layout())
+    assert lib.dsa_topk_after_hist(L, FAKE, 4096, 0, FAKE, None, 0, 1, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_after_hist(L, FAKE, 4096, 16, None, None, 0, 1, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_after_hist(L, FAKE, 10, 16, FAKE, None, 0, 0, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_after_hist(ctypes.byref(long_rows), FAKE, 70000, 16, FAKE, None, 0, 1,
+                                   None) == B.DSA_ERR_WORKSPACE
+
+
+def test_gather_ceiling_rejects(lib):
+    """The gather measurement entry checks its arguments on the host (nothing is launched)."""
+    g = lib.dsa_gather_ceiling
+    assert g(None, 100, 576, FAKE, 1, 16, FAKE, None) == B.DSA_ERR_INVALID_ARG        # no rows
+    assert g(FAKE, 100, 576, None, 1, 16, FAKE, None) == B.DSA_ERR_INVALID_ARG        # no indices
+    assert g(FAKE, 100, 576, FAKE, 1, 16, None, None) == B.DSA_ERR_INVALID_ARG        # no sink
+    assert g(FAKE, 100, 600, FAKE, 1, 16, FAKE, None) == B.DSA_ERR_INVALID_ARG        # row size
+    assert g(FAKE, 100, 1152, FAKE, 0, 16, FAKE, None) == B.DSA_ERR_INVALID_ARG       # no rows of indices
+    assert g(FAKE, 100, 1152, FAKE, 1, 0, FAKE, None) == B.DSA_ERR_INVALID_ARG        # k out of range
+    assert g(FAKE, 100, 1152, FAKE, 1, 2049, FAKE, None) == B.DSA_ERR_INVALID_ARG
+    assert g(FAKE, 0, 1152, FAKE, 1, 16, FAKE, None) == B.DSA_ERR_INVALID_ARG         # empty table
+    assert g(FAKE, 1 << 23, 576, FAKE, 1, 16, FAKE, None) == B.DSA_ERR_INVALID_ARG    # table past 4 GiB
+
+
 def test_index_topk_checks_both_calls_before_launching(lib):
     """The fused entry refuses, on the host, whatever either separate call would refuse."""
     assert _it(lib, _layout(), k_top=0) == B.DSA_ERR_INVALID_ARG            # top-k: k out of range

@@ -1,8 +1,9 @@
-"""The fused indexer + top-k entry (dsa_index_topk) on the GPU, through the C ABI.
+"""The fused indexer + top-k entry (dsa_index_topk) and its two-call form
+(dsa_index_scores_hist, then dsa_topk_after_hist) on the GPU, through the C ABI.
 
-Where the decode indexer builds the top-k's histogram itself, the fused call must give the
-same scores and indices, bit for bit, as dsa_index_scores followed by dsa_topk, and leave the
-top-k workspace all zero.  Shapes: rows past 32768 scores in the decode stream grid (one query
+Where the decode indexer builds the top-k's histogram itself, both must give the same scores
+and indices, bit for bit, as dsa_index_scores followed by dsa_topk, and leave the top-k
+workspace all zero.  Shapes: rows past 32768 scores in the decode stream grid (one query
 per sequence), in the per-(chunk, row) grid (several bf16 queries per sequence), on paged
 caches, more than 512 long rows (the selection's ROW mode), and the shapes that fall back to
 the two separate launches (rows of at most 32768 scores; fp8 index queries).  The fused
@@ -41,6 +42,20 @@ def _compare(case, layout=None, ik=None, ik_scale=None, check_rows=()):
     assert torch.equal(i_sep, i_fus), "indices differ from the two separate calls"
     if ws is not None:
         assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
+    # the two-call form of the fused entry
+    s_two = torch.full((case.T, ld), 5.0, dtype=torch.float32, device=DEV)
+    s_two, built = dsa.dsa_index_scores_hist(lay, case.iq, case.iw, ik, case.topk, ws, k_scale=ik_scale,
+                                             q_scale=case.iq_scale, scores=s_two)
+    i_two = dsa.dsa_topk_after_hist(lay, s_two, case.topk, built, workspace=ws)
+    torch.cuda.synchronize()
+    c = s_two.cpu().numpy()
+    for r in range(case.T):
+        assert np.array_equal(a[r, :n[r]], c[r, :n[r]]), "two-call scores row %d" % r
+    assert torch.equal(i_sep, i_two), "two-call indices differ from the two separate calls"
+    expect_built = (ws is not None and case.iq_dt == "bf16")
+    assert built == int(expect_built), (built, expect_built)
+    if ws is not None:
+        assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero by the two-call form"
     if check_rows and layout is None:
         o = tl.oracle_scores_rows(case, check_rows)
         ih = i_fus.cpu().numpy()
