@@ -83,15 +83,19 @@ def parse():
 # ------------------------------------------------------------------------------- byte models
 
 def algorithmic_model(case):
-    """Algorithmic bytes / flops per stage for one step (the score round trip excluded from
-    the path total; it is the top-k kernel's own input and is counted for that kernel)."""
+    """Algorithmic bytes / flops per stage for one step.  Each stage counts the bytes it must
+    read and write: the indexer its keys, scales, q and w and its score output; the top-k the
+    scores and its indices; sparse MLA the selected rows, q, indices and its output.  The path
+    total counts the score array's round trip (the indexer's write, the top-k's read) zero
+    times: it exists only because the two stages are separate calls."""
     n = [case.ctx[b] - case.q_len[b] + j + 1 for b in range(case.B) for j in range(case.q_len[b])]
     sum_n = float(sum(n))
     T = case.T
     H_I, D_I = case.H_I, case.D_I
     q_bytes = {"f32": 4, "bf16": 2, "fp8": 1}[case.iq_dt]
     k_row = D_I * {"f32": 4, "bf16": 2, "fp8": 1}[case.ik_dt] + (4 if case.ik_scale is not None else 0)
-    idx_bytes = sum_n * k_row + T * H_I * (D_I * q_bytes + 4 + (4 if case.iq_scale is not None else 0))
+    idx_in = sum_n * k_row + T * H_I * (D_I * q_bytes + 4 + (4 if case.iq_scale is not None else 0))
+    idx_bytes = idx_in + sum_n * 4  # + the scores written
     idx_flops = 2.0 * H_I * D_I * sum_n
     sel = [min(case.topk, x) for x in n]
     topk_bytes = sum_n * 4 + T * case.topk * 4
@@ -106,7 +110,7 @@ def algorithmic_model(case):
         "indexer": {"bytes": idx_bytes, "flops": idx_flops},
         "topk": {"bytes": topk_bytes, "flops": 0.0},
         "mla": {"bytes": mla_bytes, "flops": mla_flops},
-        "path_bytes": idx_bytes + T * case.topk * 4 + mla_bytes,
+        "path_bytes": idx_in + T * case.topk * 4 + mla_bytes,
     }
 
 

@@ -76,14 +76,16 @@ def _case(ctx, q_len, iq_dt, kv_dt, topk=2048):
 
 
 def test_decode_model_closed_forms():
-    """8 x 8192 decode: 132 B per visible token plus q and w; the MLA stage gathers 2048
-    rows of 1152 B per row and reads q [64, 576] bf16, writes [64, 512] bf16, reads 2048
-    indices."""
+    """8 x 8192 decode: the indexer reads 132 B and writes a 4-B score per visible token, plus
+    q and w; the MLA stage gathers 2048 rows of 1152 B per row and reads q [64, 576] bf16,
+    writes [64, 512] bf16, reads 2048 indices; the path total leaves out the score array's
+    write and read."""
     m = bench.algorithmic_model(_case([8192] * 8, [1] * 8, "bf16", "bf16"))
-    assert m["indexer"]["bytes"] == 8 * 8192 * 132 + 8 * 32 * (128 * 2 + 4)
+    idx_in = 8 * 8192 * 132 + 8 * 32 * (128 * 2 + 4)
+    assert m["indexer"]["bytes"] == idx_in + 8 * 8192 * 4
     assert m["mla"]["bytes"] == 8 * 2048 * 1152 + 8 * 64 * (576 * 2 + 512 * 2) + 8 * 2048 * 4 == 20054016
     assert m["topk"]["bytes"] == 8 * 8192 * 4 + 8 * 2048 * 4
-    assert m["path_bytes"] == m["indexer"]["bytes"] + 8 * 2048 * 4 + m["mla"]["bytes"]
+    assert m["path_bytes"] == idx_in + 8 * 2048 * 4 + m["mla"]["bytes"]
 
 
 def test_prefill_model_closed_forms():
