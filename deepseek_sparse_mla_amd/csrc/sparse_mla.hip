@@ -1336,8 +1336,9 @@ constexpr int MLA_MAX_SPLITS = 32;  // the split count never exceeds this (mla_n
 constexpr int MLA_MIN_TILES_BF16 = 2;  // fewest tiles per split (see mla_num_splits)
 constexpr int MLA_MIN_TILES_FP8 = 8;
 
-// Combine the split partials of every (output row, head), in split order.  One 256-thread
-// block per (row, 4 heads): wave w takes head 4 blockIdx.y + w, lane l its dims 8l .. 8l + 7
+// Combine the split partials of every (output row, head), in split order.  One block of 4
+// waves (or of 1 wave, when there are few rows) per (row, head group): wave w takes head
+// (waves per block) blockIdx.y + w, lane l its dims 8l .. 8l + 7
 // (16 bytes of a bf16 partial).  Partial s holds O_s / l_s, so its weight is l_s 2^(m_s - M) /
 // sum over splits of the same; the wave works the weights out itself (lane s holds split s),
 // so the block has no barrier.  NSB bounds the split count (register arrays).
@@ -1348,7 +1349,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int64_t T, MlaLayersDe
 {
     const int64_t orow = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int head = 4 * (int)blockIdx.y + (tid >> 6);
+    const int head = (int)(blockDim.x >> 6) * (int)blockIdx.y + (tid >> 6);
     const int layer = (int)(orow / T);
     const int64_t i = orow % T;
     const MlaLayerDev Ld = layers.l[layer];
@@ -1654,13 +1655,16 @@ hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &l
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1)
         return e;
-    dim3 cgrid((unsigned)rows, M_H / 4);
+    // four heads per block, or one when that would leave fewer than 512 blocks
+    const int hpb = rows * (M_H / 4) >= 512 ? 4 : 1;
+    dim3 cgrid((unsigned)rows, M_H / hpb);
+    const dim3 cblock(64 * hpb);
 #define DSA_COMBINE(NSB)                                                                                         \
     do {                                                                                                         \
         if (out_f32)                                                                                             \
-            hipLaunchKernelGGL((mla_combine_kernel<true, NSB>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml); \
+            hipLaunchKernelGGL((mla_combine_kernel<true, NSB>), cgrid, cblock, 0, stream, T, layers, ns, wo, wml); \
         else                                                                                                     \
-            hipLaunchKernelGGL((mla_combine_kernel<false, NSB>), cgrid, dim3(256), 0, stream, T, layers, ns, wo, wml); \
+            hipLaunchKernelGGL((mla_combine_kernel<false, NSB>), cgrid, cblock, 0, stream, T, layers, ns, wo, wml); \
     } while (0)
     if (ns <= 4)
         DSA_COMBINE(4);
