@@ -74,7 +74,7 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
         kv[3] = kp[3];
         ksv = ks[row * ks_stride];
     };
-    auto compute_tile = [&](int64_t s0, const u32x4 (&kv)[4], float ksv) {
+    auto compute_tile = [&](const u32x4 (&kv)[4], float ksv) -> float {
         f32x16 acc = {};
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp8x8_to_bf16x8(kv[0][0], kv[0][1]), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp8x8_to_bf16x8(kv[0][2], kv[0][3]), acc, 0, 0, 0);
@@ -89,8 +89,10 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
         for (int rr = 0; rr < 16; ++rr)
             part = fmaf(wr[rr], relu(acc[rr]), part);
         part += __shfl_xor(part, 32, 64);
+        return part * ksv;
+    };
+    auto put = [&](int64_t s0, float v) {
         const int64_t s = s0 + j;
-        const float v = part * ksv;
         if (g == 0 && s < s_end) {
             out[s] = v;
             if (wh)  // the top-k's histogram bin of exactly the stored score (this wave's LDS copy)
@@ -107,15 +109,35 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     if (s0 >= s_end)
         return;
     load_tile(s0, bufA, kA);
+    // Long runs: eight tiles per round with their scores stored together at its end.  A
+    // wait for a load issued before a store also waits for that store here (the store is
+    // counted by the hardware's counter, not by the compiler's wait placement), so storing
+    // once per eight tiles leaves one such wait per round instead of one per two tiles.
+    constexpr int NB = 8;
+    for (; s0 + 128 * (NB - 1) < s_end; s0 += 128 * NB) {
+        float vb[NB];
+#pragma unroll
+        for (int h = 0; h < NB / 2; ++h) {
+            load_tile(s0 + 256 * h + 128, bufB, kB);
+            __builtin_amdgcn_sched_barrier(0);
+            vb[2 * h] = compute_tile(bufA, kA);
+            load_tile(s0 + 256 * h + 256, bufA, kA);
+            __builtin_amdgcn_sched_barrier(0);
+            vb[2 * h + 1] = compute_tile(bufB, kB);
+        }
+#pragma unroll
+        for (int t = 0; t < NB; ++t)
+            put(s0 + 128 * t, vb[t]);
+    }
     for (; s0 < s_end; s0 += 256) {
         load_tile(s0 + 128, bufB, kB);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the wait below
-        compute_tile(s0, bufA, kA);
+        put(s0, compute_tile(bufA, kA));
         if (s0 + 128 >= s_end)
             break;
         load_tile(s0 + 256, bufA, kA);
         __builtin_amdgcn_sched_barrier(0);
-        compute_tile(s0 + 128, bufB, kB);
+        put(s0 + 128, compute_tile(bufB, kB));
     }
 }
 
@@ -150,7 +172,7 @@ __device__ __forceinline__ void idx_hist_flush(uint32_t *lh, uint32_t *__restric
 }
 
 template <bool PAGED, bool HIST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
                                                          const float *__restrict__ w,
                                                          const uint8_t *__restrict__ k, int64_t kstride,
                                                          const float *__restrict__ ks, int64_t ks_stride,
