@@ -296,6 +296,7 @@ __global__ __launch_bounds__(H_THREADS) void topk_hist_kernel(LayoutDev L, const
 // ------------------------------------------------------------------------------------------
 // K2 (MB mode): mark the bitmap words and collect the members of one 8192-score chunk
 // ------------------------------------------------------------------------------------------
+template <bool AL16>  // every row 16-byte aligned (scores and ld): 16-byte loads
 __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const float *__restrict__ scores,
                                                               int64_t ld, int k, TkWs ws)
 {
@@ -322,10 +323,26 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     for (int e = 0; e < HB; ++e)
         hv[e] = gh[e * H_THREADS + tid];
     constexpr int U = H_CHUNK / (4 * H_THREADS);  // 8 wave steps of 256 positions
+    // unconditional buffer loads (zeros past n): the wait for the histogram above then leaves
+    // every score load in flight through the digit pick
+    const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)row, (short)0, __builtin_amdgcn_readfirstlane((int)(uint32_t)(n * 4)), 0x00020000);
     f32x4 v[U];
+    if constexpr (AL16) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        v[u] = load4(row, s0 + (int64_t)u * 4 * H_THREADS + 256 * wave + 4 * lane, n);
+        for (int u = 0; u < U; ++u) {
+            const int sp = (int)(s0 + (int64_t)u * 4 * H_THREADS) + 256 * wave + 4 * lane;
+            v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrow, 4 * sp, 0, 0));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int sp = (int)(s0 + (int64_t)u * 4 * H_THREADS) + 256 * wave + 4 * lane;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrow, 4 * (sp + e), 0, 0));
+        }
+    }
 #pragma unroll
     for (int e = 0; e < HB; ++e)
         hist[e * H_THREADS + tid] = hv[e];
@@ -1052,7 +1069,10 @@ hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const flo
             return e;
     }
     if (mode == TK_MB) {
-        hipLaunchKernelGGL(topk_mark_kernel, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, k, ws);
+        if (((uintptr_t)scores & 15) == 0 && (ld & 3) == 0)
+            hipLaunchKernelGGL(topk_mark_kernel<true>, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, k, ws);
+        else
+            hipLaunchKernelGGL(topk_mark_kernel<false>, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, k, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

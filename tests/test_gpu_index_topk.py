@@ -101,3 +101,29 @@ def test_fused_indexshare_workload():
     _compare(case, check_rows=[0, 31])
     del case
     torch.cuda.empty_cache()
+
+
+def test_long_rows_with_an_unaligned_pitch():
+    """Rows of an odd pitch (40001 scores: rows not 16-byte aligned) through the long-row
+    selection, plain and with the indexer's histogram: the mark kernel's 4-byte load path."""
+    case = synth.make_case("odd_pitch", 2, ctx=[40001, 35003, 33001], sm_scale=1.0 / 16, kv_dt="fp8",
+                           iq_dt="bf16", device=DEV)
+    lay = dsa.Layout.of_case(case)
+    ld = case.max_ctx
+    assert ld % 4 != 0
+    sc = torch.empty((case.T, ld), dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(lay, case.iq, case.iw, case.ik, k_scale=case.ik_scale, scores=sc)
+    ws = dsa.topk_workspace(lay, ld, case.topk, DEV)
+    assert ws is not None
+    i_plain = dsa.dsa_topk(lay, sc, case.topk, workspace=ws)
+    s2, built = dsa.dsa_index_scores_hist(lay, case.iq, case.iw, case.ik, case.topk, ws, k_scale=case.ik_scale,
+                                          scores=torch.empty_like(sc))
+    assert built == 1
+    i_two = dsa.dsa_topk_after_hist(lay, s2, case.topk, built, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(i_plain, i_two)
+    assert int(torch.count_nonzero(ws)) == 0
+    n = tl.visible(case)
+    s_host, i_host = sc.cpu().numpy(), i_plain.cpu().numpy()
+    for r in range(case.T):
+        tl.check_topk_same_array(i_host[r], s_host[r, :n[r]], case.topk, "odd pitch row %d" % r)
