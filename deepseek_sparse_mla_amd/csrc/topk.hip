@@ -392,7 +392,7 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
 }
 
 // ------------------------------------------------------------------------------------------
-// DIRECT mode: rows of at most 1024 PER scores (PER = 8, 16: in registers; 32: in LDS), one
+// DIRECT mode: rows of at most 1024 PER scores (PER = 8, 16, 32, in registers), one
 // 1024-thread block per row, which reads its row once.  Thread t owns the positions
 // 4096 q + 4 t + e (q < PER / 4, e < 4): every load instruction reads 1 KB of consecutive
 // scores.
@@ -450,7 +450,7 @@ __device__ __forceinline__ float uni(float x)
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
-template <int PER, bool LDSROW>
+template <int PER>
 __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, const float *__restrict__ scores,
                                                                  int64_t ld, int k, int32_t *__restrict__ out)
 {
@@ -458,9 +458,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     constexpr int NQ = PER / 4;                      // groups of 4 positions per thread
     constexpr int GROUP = 4 * TK_THREADS;            // positions per group (4096)
     constexpr int NB = NQ * TK_WAVES;                // (group, wave) totals
-    constexpr int CAP = LDSROW ? 2048 : TK_CAP;      // members held in LDS
+    constexpr int CAP = TK_CAP;                      // members held in LDS
     static_assert(PER <= 32, "per-thread masks are 32 bits");
-    __shared__ __attribute__((aligned(16))) float srow[LDSROW ? TK_THREADS * PER : 4];
     __shared__ uint64_t cand[CAP];
     __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS + 4];  // + a bin for positions past n
     __shared__ float red[2][TK_WAVES];
@@ -490,12 +489,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         for (int e = 0; e < 4; ++e)
             valid |= (pos(q, e) < n32 ? 1u : 0u) << (4 * q + e);
 
-    // ---- 0. the row.  In registers: four dword loads per group through a buffer resource
-    // over the n scores (zeros past the end), all issued before any is used.  In LDS:
-    // wave-wide 1 KB DMA loads (16-byte aligned rows), else the same dword loads.
+    // ---- 0. the row, in registers: four dword loads per group through a buffer resource over
+    // the n scores (zeros past the end), all issued before any is used.
     const __amdgpu_buffer_rsrc_t rrow =
         __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, n32 * 4, 0x00020000);
-    const bool al16 = ((uintptr_t)row & 15) == 0;
     auto load_group = [&](int q) -> f32x4 {
         const int p = pos(q, 0);
         f32x4 v;
@@ -504,12 +501,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
             v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrow, 4 * (p + e), 0, 0));
         return v;
     };
-    f32x4 xr[LDSROW ? 1 : NQ];
-    auto get = [&](int q) -> f32x4 {
-        if (LDSROW)
-            return *(const f32x4 *)&srow[pos(q, 0)];
-        return xr[q];
-    };
+    f32x4 xr[NQ];
+    auto get = [&](int q) -> f32x4 { return xr[q]; };
     float mx = -INFINITY, mn = INFINITY;
     auto range_of = [&](const f32x4 &v, int q) {
 #pragma unroll
@@ -519,36 +512,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
             mn = fminf(mn, ok ? v[e] : INFINITY);
         }
     };
-    if (LDSROW) {
-        if (al16) {
-            // the whole row in flight at once: group q of wave w lands at srow[4096 q + 256 w ..];
-            // positions past n are never used
-            const i32x4 desc = buffer_desc(row, (int64_t)n32 * 4);
-            const uint32_t lds_row = lds_addr_of(&srow[0]);
-            const int w = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                dma16(desc, lds_row + 4u * (uint32_t)(GROUP * q + 256 * w), 4 * pos(q, 0));
-            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        } else {
+    for (int q = 0; q < NQ; ++q)
+        xr[q] = load_group(q);
 #pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                *(f32x4 *)&srow[pos(q, 0)] = load_group(q);
-        }
-        // each thread reads back exactly the positions it loaded or DMA'd (its own wave's
-        // bytes): no barrier needed before this pass
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            range_of(get(q), q);
-    } else {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            xr[q] = load_group(q);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            range_of(xr[q], q);
-    }
+    for (int q = 0; q < NQ; ++q)
+        range_of(xr[q], q);
 
     // ---- 1. range of the row, histogram of the value bins
     mx = wave_max_f32(mx);
@@ -1081,11 +1050,11 @@ hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const flo
     if (mode == TK_DIRECT) {
         const dim3 g((unsigned)T), b(TK_THREADS);
         if (max_ctx <= 8 * TK_THREADS)
-            hipLaunchKernelGGL((topk_direct_kernel<8, false>), g, b, 0, stream, L, scores, ld, k, indices);
+            hipLaunchKernelGGL((topk_direct_kernel<8>), g, b, 0, stream, L, scores, ld, k, indices);
         else if (max_ctx <= 16 * TK_THREADS)
-            hipLaunchKernelGGL((topk_direct_kernel<16, false>), g, b, 0, stream, L, scores, ld, k, indices);
+            hipLaunchKernelGGL((topk_direct_kernel<16>), g, b, 0, stream, L, scores, ld, k, indices);
         else
-            hipLaunchKernelGGL((topk_direct_kernel<32, true>), g, b, 0, stream, L, scores, ld, k, indices);
+            hipLaunchKernelGGL((topk_direct_kernel<32>), g, b, 0, stream, L, scores, ld, k, indices);
     } else if (mode == TK_ROW)
         hipLaunchKernelGGL(topk_select_kernel<TK_ROW>, dim3((unsigned)T), dim3(TK_THREADS), dyn, stream, L,
                            scores, ld, k, indices, ws);
