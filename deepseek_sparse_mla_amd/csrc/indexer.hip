@@ -109,10 +109,10 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     if (s0 >= s_end)
         return;
     load_tile(s0, bufA, kA);
-    // Long runs: eight tiles per round with their scores stored together at its end.  A
-    // wait for a load issued before a store also waits for that store here (the store is
-    // counted by the hardware's counter, not by the compiler's wait placement), so storing
-    // once per eight tiles leaves one such wait per round instead of one per two tiles.
+    // Long runs: eight tiles per round with their scores stored together at its end.  With a
+    // store after every tile, the wait for the next tile's loads (issued before that store)
+    // was placed so that it also waited for the store; storing once per eight tiles leaves
+    // one such wait per round instead of one per two tiles.
     constexpr int NB = 8;
     for (; s0 + 128 * (NB - 1) < s_end; s0 += 128 * NB) {
         float vb[NB];
