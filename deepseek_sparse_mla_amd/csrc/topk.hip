@@ -458,10 +458,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
     constexpr int NQ = PER / 4;                      // groups of 4 positions per thread
     constexpr int GROUP = 4 * TK_THREADS;            // positions per group (4096)
     constexpr int NB = NQ * TK_WAVES;                // (group, wave) totals
-    constexpr int CAP = TK_CAP;                      // members held in LDS
+    constexpr int CAP = 2048;                        // members held in LDS (value bins: ~20 per row)
+    constexpr int HC = 4;                            // histogram copies, one per lane & 3
+    constexpr int HS = TK_BINS + 4;                  // copy stride: + a bin for positions past n
     static_assert(PER <= 32, "per-thread masks are 32 bits");
     __shared__ uint64_t cand[CAP];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS + 4];  // + a bin for positions past n
+    __shared__ __attribute__((aligned(16))) uint32_t hist[HC * HS];
     __shared__ float red[2][TK_WAVES];
     __shared__ uint32_t base[NB];
     __shared__ uint32_t sh[4];
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         red[0][wave] = mx;
         red[1][wave] = mn;
     }
-    for (int b = tid; b < TK_BINS; b += TK_THREADS)
+    for (int b = tid; b < HC * HS; b += TK_THREADS)
         hist[b] = 0u;
     if (tid == 0)
         sh_cnt = 0u;
@@ -559,7 +561,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
         else
             pass(bin_key);
     };
-    // positions past n count into the spare bin TK_BINS (never read)
+    // positions past n count into the spare bin TK_BINS (never read).  Scores crowd a few
+    // bins near the row's mode, so the lanes of a wave add into four copies of the histogram
+    // (lane & 3) to cut the LDS atomic collisions, then the copies are summed.
+    uint32_t *hcopy = hist + (lane & 3) * HS;
     with_bins([&](auto bin_of) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -567,10 +572,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_direct_kernel(LayoutDev L, co
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t b = bin_of(v[e]);
-                atomicAdd(&hist[((valid >> (4 * q + e)) & 1u) ? b : (uint32_t)TK_BINS], 1u);
+                atomicAdd(&hcopy[((valid >> (4 * q + e)) & 1u) ? b : (uint32_t)TK_BINS], 1u);
             }
         }
     });
+    __syncthreads();
+    for (int b = tid; b < TK_BINS; b += TK_THREADS)
+        hist[b] += hist[HS + b] + hist[2 * HS + b] + hist[3 * HS + b];
     __syncthreads();
     const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
     const uint32_t d = uni(p0.digit), c = uni(p0.count);
