@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--workload", default="share", choices=sorted(WORKLOADS))
     p.add_argument("--no-others", action="store_true",
                    help="measure the headline workload only (no other_workloads summary)")
-    p.add_argument("--no-compare", "--no-fused", dest="no_compare", action="store_true",
+    p.add_argument("--no-compare", dest="no_compare", action="store_true",
                    help="skip the comparison timing of indexer and top-k as the two plain calls "
                         "(profiler runs: only the headline's kernels)")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough for > 1 GB)")
