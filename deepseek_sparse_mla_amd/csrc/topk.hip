@@ -63,12 +63,13 @@ static int topk_mode(int64_t T, int64_t max_ctx)
     return TK_ROW;
 }
 
-// Workspace of the ROW and MB modes (MB only: counters, bitmaps and member lists).
+// Workspace of the ROW and MB modes (MB only: counters, bitmaps, member lists and picks).
 struct TkWs {
     uint32_t *hist;  // [T][2048]
     uint32_t *cnt;   // [T]
     uint32_t *bits;  // [T][W]
     uint64_t *memb;  // [T][TK_CAP]
+    uint32_t *pick;  // [T][2]: threshold bin d and the count above it, from the mark kernel
     int64_t W;       // bitmap words per row
 };
 
@@ -85,7 +86,7 @@ size_t topk_workspace_bytes(int64_t T, int64_t max_ctx)
     size_t b = al256((size_t)T * TK_BINS * 4);
     if (mode == TK_MB) {
         const size_t W = (size_t)((max_ctx + 31) / 32);
-        b += al256((size_t)T * 4) + al256((size_t)T * W * 4) + al256((size_t)T * TK_CAP * 8);
+        b += al256((size_t)T * 4) + al256((size_t)T * W * 4) + al256((size_t)T * TK_CAP * 8) + al256((size_t)T * 8);
     }
     return b;
 }
@@ -102,6 +103,8 @@ static TkWs carve(void *ws, int64_t T, int64_t max_ctx)
     w.bits = (uint32_t *)p;
     p += al256((size_t)T * w.W * 4);
     w.memb = (uint64_t *)p;
+    p += al256((size_t)T * TK_CAP * 8);
+    w.pick = (uint32_t *)p;  // MB mode only (the ROW mode's workspace ends at hist)
     return w;
 }
 
@@ -349,25 +352,46 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     if (tid == 0)
         lcnt = 0u;
     lds_sync();
-    const uint32_t d = pick_digit<TK_BINS>(hist, kk, sh).digit;
+    const DigitPick pk = pick_digit<TK_BINS>(hist, kk, sh);
+    const uint32_t d = pk.digit;
+    if (blockIdx.x == 0 && tid == 0) {  // handed to the select kernel, which then skips the pick
+        ws.pick[2 * i] = d;
+        ws.pick[2 * i + 1] = pk.above;
+    }
 
     // bitmap words of this chunk; the members of bin d are noted per lane (bit 4u + e) and
     // appended to lmem with one LDS reservation per wave, in (lane, u, e) order
+    // (unconditional: take_wave writes no word and notes no member at or past n, and a branch
+    // here would leave the compiler unsure whether the scores had arrived, so that it waited
+    // for them again below, behind the reservation)
     uint32_t mflag = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t base = s0 + (int64_t)u * 4 * H_THREADS + 256 * wave;
-        if (base < n)
-            take_wave(
-                base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bits[w] = word; },
-                [&](uint64_t, uint32_t, bool m, uint64_t) {},
-                [&](int e, bool m) { mflag |= (m ? 1u : 0u) << (4 * u + e); });
+        take_wave(
+            base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bits[w] = word; },
+            [&](uint64_t, uint32_t, bool m, uint64_t) {},
+            [&](int e, bool m) { mflag |= (m ? 1u : 0u) << (4 * u + e); });
     }
     const uint32_t mc = (uint32_t)__popc(mflag);
     const uint32_t incl = wave_incl_scan(mc, lane);
     uint32_t wbase = 0;
     if (lane == 63 && incl != 0u)
         wbase = atomicAdd(&lcnt, incl);
+    __syncthreads();  // every wave has reserved its slots: lcnt is the block's member count
+    // one reservation per block in the row's member list (a device-wide atomic, whose
+    // latency the members' copy to LDS overlaps), then a coalesced copy
+    const uint32_t m = lcnt;
+    if (m == 0u)
+        return;
+    uint32_t gb = 0;
+    if (tid == 0) {
+        // an address the compiler cannot prove uniform: it then issues the plain atomic, not
+        // its wave-reduction form, which consumes the result (waits for it) on the spot
+        int zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+        gb = atomicAdd(ws.cnt + i + zero, m);
+    }
     uint32_t at = (uint32_t)__shfl((int)wbase, 63, 64) + incl - mc;
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -375,13 +399,8 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
         for (int e = 0; e < 4; ++e)
             if ((mflag >> (4 * u + e)) & 1u)  // at < H_CHUNK: one slot per position
                 lmem[at++] = composite(score_key(v[u][e]), s0 + (int64_t)u * 4 * H_THREADS + 256 * wave + 4 * lane + e);
-    __syncthreads();
-    // one reservation per block in the row's member list, then a coalesced copy
-    const uint32_t m = lcnt;
-    if (m == 0u)
-        return;
     if (tid == 0)
-        gbase = atomicAdd(ws.cnt + i, m);
+        gbase = gb;
     __syncthreads();
     uint64_t *memb = ws.memb + i * TK_CAP;
     for (uint32_t e = tid; e < m; e += H_THREADS) {
@@ -822,18 +841,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
         }
     }
 
-    // ---- 1. threshold bin d from the histogram of the top 11 key bits
+    // ---- 1. threshold bin d from the histogram of the top 11 key bits (MB: as the mark
+    // kernel picked it from the same histogram)
     if (tid == 0)
         sh_cnt = 0u;
-    for (int b = tid; b < TK_BINS; b += TK_THREADS) {
+    uint32_t d, above;
+    if (MODE == TK_MB) {
+        d = ws.pick[2 * i];
+        above = ws.pick[2 * i + 1];
         uint32_t *gh = ws.hist + i * TK_BINS;
-        hist[b] = gh[b];
-        gh[b] = 0u;  // the workspace is left zero for the next call
+        for (int b = tid; b < TK_BINS; b += TK_THREADS)
+            gh[b] = 0u;  // the workspace is left zero for the next call
+    } else {
+        for (int b = tid; b < TK_BINS; b += TK_THREADS) {
+            uint32_t *gh = ws.hist + i * TK_BINS;
+            hist[b] = gh[b];
+            gh[b] = 0u;
+        }
+        __syncthreads();
+        const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
+        d = p0.digit;
+        above = p0.above;
     }
-    __syncthreads();
-    const DigitPick p0 = pick_digit<TK_BINS>(hist, kk, sh);
-    const uint32_t d = p0.digit;
-    const uint32_t need = kk - p0.above;  // 1 .. p0.count members of bin d are taken
+    const uint32_t need = kk - above;  // 1 .. (count of bin d) members of bin d are taken
 
     // ---- 2. bitmap of the positions above bin d; members of bin d into cand
     if (MODE == TK_ROW) {
@@ -885,8 +915,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
             }
         }
         __syncthreads();
-        if (tid == 0)
+        if (tid == 0) {
             ws.cnt[i] = 0u;
+            ws.pick[2 * i] = ws.pick[2 * i + 1] = 0u;
+        }
     }
 
     // ---- 3. the need-th largest member; it and every member above it are marked
