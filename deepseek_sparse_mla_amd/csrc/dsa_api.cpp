@@ -377,8 +377,10 @@ static dsa_status index_scores_impl(const dsa_layout *layout, int H_I, int D_I, 
         !aligned(k, (size_t)elem_size(k_dt)))
         return fail(DSA_ERR_INVALID_ARG, "pointer not aligned to its element size");
 
-    const bool shape32 = H_I == 32 && D_I == 128 && k_dt == DSA_FP8_E4M3FN && aligned(k, 16) &&
-                         (k_row_stride % 16) == 0 && aligned(q, 16) && tuned_pages(layout);
+    // key rows 4-byte aligned: key planes, or 132-byte index-cache entries read in place (the
+    // kernels' 16-byte key loads need only dword alignment)
+    const bool shape32 = H_I == 32 && D_I == 128 && k_dt == DSA_FP8_E4M3FN && aligned(q, 16) &&
+                         aligned(k, 4) && (k_row_stride % 4) == 0 && tuned_pages(layout);
     const bool tuned_decode = shape32 && q_dt == DSA_BF16 && !force_generic();
     // the prefill kernel addresses a sequence's keys with 32-bit buffer offsets
     const bool tuned_fp8 = shape32 && q_dt == DSA_FP8_E4M3FN && !force_generic() &&

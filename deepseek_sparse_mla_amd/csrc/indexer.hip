@@ -34,6 +34,10 @@ __device__ __forceinline__ float relu(float x)
 // Rows are heads, columns tokens.  The 128-long contraction is split so that lane half g
 // owns dims [64g, 64g+64): MFMA t consumes dims 64g + 8t .. 64g + 8t + 7 of both q and k.
 // ------------------------------------------------------------------------------------------
+// 16 key bytes of a lane: rows need only be 4-byte aligned (a 132-byte index-cache entry puts
+// the 128 code bytes of token r at byte 132 r); the loads are still single 16-byte loads.
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 // Tokens [s_begin, s_end) of query row i, whose keys start at cache row kv_base; with paged
 // caches (pages != nullptr) token s is instead in row pages[(s >> lg) - p0] << lg | (s & page-1),
 // the segment's block-table entries having been copied to LDS.
@@ -67,7 +71,7 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
         const int64_t sc = s < s_end ? s : s_end - 1;
         const int64_t row = pages ? ((int64_t)pages[(sc >> lg) - p0] << lg) | (sc & ((1 << lg) - 1))
                                   : kv_base + sc;
-        const u32x4 *kp = (const u32x4 *)(k + row * kstride + 64 * g);
+        const u32x4a4 *kp = (const u32x4a4 *)(k + row * kstride + 64 * g);
         kv[0] = kp[0];
         kv[1] = kp[1];
         kv[2] = kp[2];
@@ -337,7 +341,8 @@ __global__ __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(4
     __syncthreads();
 
     // DMA geometry, fixed per lane: load qd of this wave covers tile bytes 1024 (8 qd + wave)
-    // + 16 lane, i.e. one row and column (-1: pad columns, or a load past the tile).
+    // + 16 lane, i.e. one row and column (-1: pad columns, or a load past the tile).  A source
+    // piece needs only dword alignment, so key rows of 132-byte entries are read in place.
     // (paged caches: toff holds row | col << 16 instead, the row mapped per tile)
     int toff[PF_DMA_PER_WAVE];
 #pragma unroll

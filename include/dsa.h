@@ -208,9 +208,12 @@ dsa_status dsa_index_front_end(int64_t T, int H_I, dsa_dtype dt, const void *q, 
  *   scores, ld    fp32 output, row i at scores + i * ld; ld >= max_ctx.  Only
  *                 s < n_i is written.
  * The fp8 x bf16 products are exact in fp32; sums are fp32.
- * The tuned fp8-query kernel addresses keys with 32-bit offsets: it needs
- * max_ctx * k_row_stride (cache_rows * k_row_stride with paged caches)
- * below 2^31; beyond it the generic kernel runs (same results, slower).
+ * The tuned kernels (H_I = 32, D_I = 128, fp8 keys) need k 4-byte aligned and
+ * k_row_stride a multiple of 4, which the interleaved 132-byte entries meet;
+ * other keys run the generic kernel.  The tuned fp8-query kernel addresses
+ * keys with 32-bit offsets: it needs max_ctx * k_row_stride (cache_rows *
+ * k_row_stride with paged caches) below 2^31; beyond it the generic kernel
+ * runs (same results, slower).
  */
 dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtype q_dt,
                             const void *q, const float *q_scale, const float *w,

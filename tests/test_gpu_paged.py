@@ -129,7 +129,8 @@ def test_writer_fills_the_paged_index_cache():
     """Keys written with rope straight into the physical rows the block table gives (slots)
     land byte for byte where the contiguous write puts them, and the paged indexer over that
     pool (other rows junk) equals the contiguous indexer bit for bit, for the plane layout and
-    for 132-byte interleaved entries (generic indexer on both sides)."""
+    for 132-byte interleaved entries (read in place by the same tuned kernel, so they also equal
+    the plane layout's scores)."""
     case = synth.make_case("paged_writer", 2, ctx=[700, 1300, 257], kv_dt="bf16", device=DEV)
     page = 16
     n = int(case.kv_indptr[-1])
@@ -156,8 +157,8 @@ def test_writer_fills_the_paged_index_cache():
     for r in range(case.T):
         assert torch.equal(got[r, :vis[r]], ref[r, :vis[r]]), "plane layout, row %d" % r
 
-    # 132-byte entries run the generic indexer (its own summation order): paged against
-    # contiguous entries, both written by the writer
+    # 132-byte entries: paged against contiguous entries, both written by the writer, and both
+    # against the plane layout (the same kernel and summation order)
     def entries(n_rows, slots, layout):
         ent = torch.full((n_rows, 132), 0x3C, dtype=torch.uint8, device=DEV)
         dsa.dsa_index_k_cache_write(keys, slots, ent, ent.view(-1)[128:], positions=pos, cos_sin=tab,
@@ -166,12 +167,14 @@ def test_writer_fills_the_paged_index_cache():
                                          k_scale=ent.view(torch.float32).view(-1)[32:], k_row_stride=132,
                                          k_scale_stride=33, k_dtype=dsa.DSA_FP8_E4M3FN)
 
+    planes = ref
     ent_c, ref = entries(n, torch.arange(n, device=DEV), dsa.Layout.of_case(case))
     ent_p, got = entries(rows, dst, lay_p)
     torch.cuda.synchronize()
     assert torch.equal(ent_p[dst], ent_c) and torch.equal(ent_c[:, :128], cache_c)
     for r in range(case.T):
         assert torch.equal(got[r, :vis[r]], ref[r, :vis[r]]), "132-byte entries, row %d" % r
+        assert torch.equal(ref[r, :vis[r]], planes[r, :vis[r]]), "132-byte entries against planes, row %d" % r
 
 
 def test_paged_latent_pool_past_2gib():

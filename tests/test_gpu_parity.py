@@ -175,6 +175,39 @@ def test_interleaved_132_byte_index_cache():
         tl.check_scores(s_aos[r, :n[r]].cpu().numpy(), o[r], "aos row %d" % r)
 
 
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_132_byte_entries_match_key_planes_bitwise(kind):
+    """132-byte index-cache entries (128 fp8 codes, then the fp32 scale: rows only 4-byte
+    aligned) run on the tuned indexer kernels and give the same bits as separate key and scale
+    planes, over many tiles with ragged ends; the fused indexer + top-k selects the same
+    indices (rows past 32768 scores: the indexer also builds the top-k histogram)."""
+    if kind == "decode":  # bf16 index queries, one per sequence: the streamed decode grid
+        case = synth.make_case("aos_decode", 2, ctx=[40001, 1300, 70], device=DEV)
+    else:  # fp8 index queries, several per sequence: the prefill GEMM kernel
+        case = synth.make_case("aos_prefill", 4, ctx=[2600, 700], q_len=[70, 20], iq_dt="fp8", device=DEV)
+    N = case.N
+    slab = torch.zeros((N, 132), dtype=torch.uint8, device=DEV)
+    slab[:, :128] = case.ik
+    slab[:, 128:] = case.ik_scale.view(torch.uint8).view(N, 4)
+    scale_slots = slab.view(torch.float32).view(-1)[32:]
+    layout = dsa.Layout.of_case(case)
+    aos = dict(k_scale=scale_slots, k_row_stride=132, k_scale_stride=33, k_dtype=dsa.DSA_FP8_E4M3FN,
+               q_scale=case.iq_scale)
+    planes = dict(k_scale=case.ik_scale, q_scale=case.iq_scale)
+    s_pl = dsa.dsa_index_scores(layout, case.iq, case.iw, case.ik, **planes)
+    s_ao = dsa.dsa_index_scores(layout, case.iq, case.iw, slab, **aos)
+    _, i_pl = dsa.dsa_index_topk(layout, case.iq, case.iw, case.ik, case.topk, **planes)
+    _, i_ao = dsa.dsa_index_topk(layout, case.iq, case.iw, slab, case.topk, **aos)
+    torch.cuda.synchronize()
+    n = tl.visible(case)
+    for r in range(case.T):
+        assert torch.equal(s_ao[r, :n[r]], s_pl[r, :n[r]]), "row %d: 132-byte entries and planes differ" % r
+    assert torch.equal(i_ao, i_pl)
+    o = tl.oracle_scores_rows(case, [0, case.T - 1])
+    for r, osr in zip([0, case.T - 1], o):
+        tl.check_scores(s_ao[r, :n[r]].cpu().numpy(), osr, "row %d" % r)
+
+
 # ------------------------------------------------------------------------------ top-k edge cases
 
 def _topk_rows(rows, k=2048, workspace=None):
