@@ -5,6 +5,7 @@
     python bench.py --workload writer               # the index-cache writer at the prefill shape
     python bench.py --copy-calibration MIB          # a plain device copy, for counter scaling
     python bench.py --gather-ceiling [--workload W] # the sparse-MLA row gathers alone (a bound)
+    python bench.py --read-ceiling [--workload W]   # the indexer's load stream alone (a bound)
     python bench.py --rocprof-summary CSV [CSV ..]  # per-kernel table of rocprofv3 output
     python bench.py --traffic-from FETCH WRITE COPY_FETCH COPY_WRITE [--workload W] [--copy-mib M]
 
@@ -66,6 +67,9 @@ def parse():
                    help="only run --steps device-to-device copies of MIB MiB (counter calibration)")
     p.add_argument("--gather-ceiling", action="store_true",
                    help="time the workload's sparse-MLA row gathers alone (dsa_gather_ceiling) beside the stage")
+    p.add_argument("--read-ceiling", action="store_true",
+                   help="decode workloads: time the indexer's load stream alone (dsa_read_ceiling) beside "
+                        "the indexer stage")
     p.add_argument("--rocprof-summary", nargs="+", metavar="CSV", help="summarise rocprofv3 CSV files")
     p.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="HBM bytes per stage call from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
@@ -416,6 +420,51 @@ def gather_ceiling(workload, steps, warmup):
         "steps": steps, "warmup": warmup}))
 
 
+def _timed(fn, steps, warmup):
+    """HIP-event times (ms) of `steps` calls of fn after `warmup` untimed ones."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record()
+        fn()
+    ev[steps].record()
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return {"median": round(t[steps // 2], 5), "min": round(t[0], 5), "max": round(t[-1], 5)}
+
+
+def read_ceiling(workload, steps, warmup):
+    """The decode indexer's load stream with no arithmetic and no stores (dsa_read_ceiling, the
+    same shares, tiles and lanes), on the workload's own index cache, timed beside the indexer
+    stage (plain call): 132 bytes read per token either way.  Pattern 0 keeps the indexer's
+    lanes, pattern 1 reads 1 KB of consecutive bytes per load instruction."""
+    import torch
+    from deepseek_sparse_mla_amd import synth
+    if workload not in ("share", "ragged", "decode"):
+        print("--read-ceiling applies to the decode workloads (share, ragged, decode)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    case = synth.config(WORKLOADS[workload], "cuda:0")
+    run = Runner(case)
+    n = int(case.kv_indptr[-1].item())
+    sink = torch.zeros(512, dtype=torch.int32, device="cuda:0")
+    rb = n * 132
+    out = {"workload": case.name, "tokens": n, "bytes_read": rb}
+    for pattern in (0, 1):
+        t = _timed(lambda: run.dsa.dsa_read_ceiling(case.ik, case.ik_scale, sink, n, pattern), steps, warmup)
+        out["pattern%d_ms" % pattern] = t
+        out["pattern%d_GBps" % pattern] = round(rb / (t["median"] * 1e-3) / 1e9, 1)
+    t = _timed(run.indexer_alone, steps, warmup)
+    out["indexer_ms"] = t
+    out["indexer_GBps_read"] = round(rb / (t["median"] * 1e-3) / 1e9, 1)
+    out["indexer_over_pattern0"] = round(t["median"] / out["pattern0_ms"]["median"], 3)
+    out.update({"steps": steps, "warmup": warmup})
+    print(json.dumps(out))
+
+
 def copy_calibration(mib, copies):
     import torch
     n = mib << 20
@@ -558,6 +607,8 @@ def main():
         return copy_calibration(args.copy_calibration, args.steps)
     if args.gather_ceiling:
         return gather_ceiling(args.workload, min(args.steps, 20), min(args.warmup, 3))
+    if args.read_ceiling:
+        return read_ceiling(args.workload, min(args.steps, 20), min(args.warmup, 3))
     if args.workload == "writer":
         return writer_main(args)
     import torch

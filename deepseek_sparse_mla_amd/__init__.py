@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     Layout, dsa_abi_version, dsa_index_front_end, dsa_index_k_cache_write, dsa_index_q_quant,
     dsa_index_scores, dsa_index_scores_hist, dsa_index_topk, dsa_topk, dsa_topk_after_hist,
     dsa_topk_workspace_size, load_library, mla_workspace, sparse_mla_decode,
-    sparse_mla_decode_no_alloc, sparse_mla_decode_shared, dsa_gather_ceiling, score_pitch, sparse_mla_prefill,
+    sparse_mla_decode_no_alloc, sparse_mla_decode_shared, dsa_gather_ceiling, dsa_read_ceiling, score_pitch,
+    sparse_mla_prefill,
     sparse_mla_workspace_size, topk_workspace,
 )

@@ -26,7 +26,7 @@ DSA_MAX_SHARED_LAYERS = 8
 EXPORTS = ("dsa_index_k_cache_write", "dsa_index_q_quant", "dsa_index_front_end", "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_index_topk",
            "dsa_index_scores_hist", "dsa_topk_after_hist", "sparse_mla_workspace_size",
            "sparse_mla_decode", "sparse_mla_prefill", "sparse_mla_decode_shared", "sparse_mla_decode_no_alloc",
-           "dsa_gather_ceiling", "dsa_last_error",
+           "dsa_gather_ceiling", "dsa_read_ceiling", "dsa_last_error",
            "dsa_abi_version")
 
 
@@ -84,10 +84,11 @@ def load_library(path: str = LIB_PATH):
         lib.sparse_mla_decode_shared.argtypes = [LP, I, I, I, F, I, I, I, I,
                                                  ctypes.POINTER(dsa_mla_layer), P, I, P, S, P]
         lib.dsa_gather_ceiling.argtypes = [P, L, I, P, L, I, P, P]
+        lib.dsa_read_ceiling.argtypes = [P, L, P, L, L, I, I, P, P]
         for f in (lib.dsa_index_k_cache_write, lib.dsa_index_q_quant, lib.dsa_index_front_end,
                   lib.dsa_index_scores, lib.dsa_topk, lib.dsa_index_topk, lib.dsa_index_scores_hist,
                   lib.dsa_topk_after_hist, lib.sparse_mla_decode, lib.sparse_mla_prefill,
-                  lib.sparse_mla_decode_shared, lib.sparse_mla_decode_no_alloc, lib.dsa_gather_ceiling,
+                  lib.sparse_mla_decode_shared, lib.sparse_mla_decode_no_alloc, lib.dsa_gather_ceiling, lib.dsa_read_ceiling,
                   lib.dsa_abi_version):
             f.restype = I
         lib.dsa_last_error.restype = ctypes.c_char_p
@@ -489,6 +490,23 @@ def dsa_gather_ceiling(rows: torch.Tensor, indices: torch.Tensor, sink: torch.Te
     T, k = indices.shape
     st = lib.dsa_gather_ceiling(_dev(rows, "rows"), n, rb, _dev(indices, "indices", torch.int32), T, k,
                                 _dev(sink, "sink"), _stream(stream))
+    _check(lib, st)
+
+
+def dsa_read_ceiling(k: torch.Tensor, k_scale: torch.Tensor, sink: torch.Tensor, n_tokens: Optional[int] = None,
+                     pattern: int = 0, blocks: int = 512, k_row_stride: Optional[int] = None,
+                     k_scale_stride: int = 1, stream=None) -> None:
+    """Measurement aid: stream the index cache's first n_tokens rows (keys and scales) the way
+    the decode indexer does, with no arithmetic; sink (>= blocks int32 words) receives one xor of
+    the words read per block."""
+    if sink.numel() * sink.element_size() < 4 * int(blocks):
+        raise ValueError("sink must hold one 32-bit word per block")
+    lib = load_library()
+    n = k.shape[0] if n_tokens is None else int(n_tokens)
+    if k_row_stride is None:
+        k_row_stride = k.shape[-1] * k.element_size()
+    st = lib.dsa_read_ceiling(_dev(k, "k", contiguous=False), int(k_row_stride), _dev(k_scale, "k_scale"),
+                              int(k_scale_stride), n, int(pattern), int(blocks), _dev(sink, "sink"), _stream(stream))
     _check(lib, st)
 
 

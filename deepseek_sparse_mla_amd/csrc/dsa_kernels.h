@@ -66,6 +66,8 @@ size_t mla_workspace_bytes(int64_t T, int n_layers, int k);
 hipError_t launch_mla_tuned(const LayoutDev &L, int64_t T, const MlaLayersDev &layers, int n_layers,
                             bool kv_fp8, bool out_f32, const int32_t *indices, int k,
                             float sm_scale, void *workspace, hipStream_t stream);
+hipError_t launch_read_ceiling(const uint8_t *k, int64_t kstride, const float *ks, int64_t ks_stride, int64_t N,
+                               int pattern, int blocks, uint32_t *sink, hipStream_t stream);
 hipError_t launch_gather_ceiling(const void *rows, int64_t n_rows, int row_bytes, const int32_t *indices, int64_t T,
                                  int k, uint32_t *sink, hipStream_t stream);
 hipError_t launch_mla_generic(const LayoutDev &L, int64_t T, int H, int Dc, int Dr,

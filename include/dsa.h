@@ -420,6 +420,30 @@ dsa_status sparse_mla_decode_shared(const dsa_layout *layout, int H, int D_c, in
 dsa_status dsa_gather_ceiling(const void *rows, int64_t n_rows, int row_bytes, const int32_t *indices,
                               int64_t T, int k, uint32_t *sink, void *stream);
 
+/*
+ * dsa_read_ceiling -- a measurement aid; no step of the method.  Reads the
+ * index cache the way the tuned decode indexer streams it (the same share of
+ * tokens per block, 32-token tiles per wave, two tiles in flight) and does no
+ * arithmetic and no stores, so the bandwidth it reaches bounds the indexer.
+ *   k, k_row_stride   device key rows as for dsa_index_scores (row r at byte
+ *                     r * k_row_stride; >= 128, a multiple of 4, k 4-byte
+ *                     aligned); the first 128 bytes of rows 0 .. n_tokens-1
+ *                     are read
+ *   k_scale, k_scale_stride  the rows' fp32 scales (k_scale[r * stride])
+ *   pattern   0: the indexer's lanes (each 16-byte load of a wave touches 32
+ *             rows); 1: each load reads 1 KB of consecutive bytes (needs
+ *             k_row_stride = 128 and k 16-byte aligned)
+ *   blocks    the grid (the indexer streams with 512 blocks on MI355X)
+ *   sink      device uint32 [blocks]: block b stores in sink[b] the xor of
+ *             every word it read (so the xor of all entries is that of the
+ *             first n_tokens key rows and scales)
+ * Errors: DSA_ERR_INVALID_ARG for NULL pointers, n_tokens < 1, blocks
+ * outside 1 .. 65536, another pattern or a layout the pattern cannot read;
+ * DSA_ERR_HIP if the launch fails.  Nothing is allocated.
+ */
+dsa_status dsa_read_ceiling(const void *k, int64_t k_row_stride, const float *k_scale, int64_t k_scale_stride,
+                            int64_t n_tokens, int pattern, int blocks, uint32_t *sink, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *dsa_last_error(void);
 

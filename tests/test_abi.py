@@ -324,6 +324,21 @@ def test_gather_ceiling_rejects(lib):
     assert g(FAKE, 1 << 23, 576, FAKE, 1, 16, FAKE, None) == B.DSA_ERR_INVALID_ARG    # table past 4 GiB
 
 
+def test_read_ceiling_rejects(lib):
+    """The read measurement entry checks its arguments on the host (nothing is launched)."""
+    r = lib.dsa_read_ceiling
+    assert r(None, 128, FAKE, 1, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # no keys
+    assert r(FAKE, 128, None, 1, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # no scales
+    assert r(FAKE, 128, FAKE, 1, 100, 0, 512, None, None) == B.DSA_ERR_INVALID_ARG     # no sink
+    assert r(FAKE, 128, FAKE, 1, 0, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG       # no tokens
+    assert r(FAKE, 128, FAKE, 1, 100, 0, 0, FAKE, None) == B.DSA_ERR_INVALID_ARG       # no blocks
+    assert r(FAKE, 128, FAKE, 1, 100, 2, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # unknown pattern
+    assert r(FAKE, 126, FAKE, 1, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # short / unaligned rows
+    assert r(FAKE, 130, FAKE, 1, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG
+    assert r(FAKE, 128, FAKE, 0, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # scale stride
+    assert r(FAKE, 132, FAKE, 33, 100, 1, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG    # pattern 1: 128-byte rows
+
+
 def test_index_topk_checks_both_calls_before_launching(lib):
     """The fused entry refuses, on the host, whatever either separate call would refuse."""
     assert _it(lib, _layout(), k_top=0) == B.DSA_ERR_INVALID_ARG            # top-k: k out of range
