@@ -527,83 +527,6 @@ __global__ __launch_bounds__(256) void idx_generic_kernel(LayoutDev L, int H, in
 }
 
 // ------------------------------------------------------------------------------------------
-// read ceiling (a measurement aid): the decode kernel's load stream with no arithmetic and no
-// stores.  The N tokens are cut into equal shares, one per block (multiples of 32 tokens); a
-// wave takes 32-token tiles of its block's share, waves interleaved, two tiles in flight.
-// pattern 0: the decode kernel's lanes (lane (g, j): token j, bytes 64 g .. +63, as four
-// 16-byte loads) and its scale load; pattern 1: each load instruction reads 1 KB of
-// consecutive bytes (rows of exactly 128 bytes), scales as in pattern 0.  Every byte read is
-// folded once into an xor; block b stores its xor in sink[b] (plain stores: one address
-// shared by every block would serialise the grid's atomics), so the host can check that
-// exactly the N rows and their scales were read.
-// ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void idx_read_ceiling_kernel(const uint8_t *__restrict__ k, int64_t kstride,
-                                                               const float *__restrict__ ks, int64_t ks_stride,
-                                                               int64_t N, int pattern, uint32_t *sink)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5, j = lane & 31;
-    const int64_t per = ((N + gridDim.x - 1) / gridDim.x + 31) & ~(int64_t)31;
-    const int64_t t0 = (int64_t)blockIdx.x * per, t1 = min(t0 + per, N);
-    uint32_t acc = 0;
-    auto load = [&](int64_t s0, u32x4 (&v)[4], uint32_t &sc) {
-        if (pattern == 0) {
-            const int64_t s = min(s0 + j, t1 - 1);
-            const u32x4a4 *kp = (const u32x4a4 *)(k + s * kstride + 64 * g);
-            v[0] = kp[0];
-            v[1] = kp[1];
-            v[2] = kp[2];
-            v[3] = kp[3];
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int b = 1024 * u + 16 * lane;  // byte of the 4 KB tile
-                const int64_t s = min(s0 + b / 128, t1 - 1);
-                v[u] = *(const u32x4 *)(k + s * 128 + (b & 127));
-            }
-        }
-        sc = __float_as_uint(ks[min(s0 + j, t1 - 1) * ks_stride]);
-    };
-    auto fold = [&](int64_t s0, const u32x4 (&v)[4], uint32_t sc) {  // tokens past t1 (clamped) are left out
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t s = pattern == 0 ? s0 + j : s0 + (1024 * u + 16 * lane) / 128;
-            if (s < t1)
-                acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
-        }
-        if (g == 0 && s0 + j < t1)
-            acc ^= sc;
-    };
-    int64_t s0 = t0 + 32 * wave;
-    if (s0 < t1) {
-        u32x4 a[4], b[4];
-        uint32_t sa, sb;
-        load(s0, a, sa);
-        for (; s0 < t1; s0 += 256) {
-            load(s0 + 128, b, sb);
-            fold(s0, a, sa);
-            load(s0 + 256, a, sa);
-            fold(s0 + 128, b, sb);
-        }
-    }
-    __shared__ uint32_t wx[4];
-    for (int o = 32; o > 0; o >>= 1)
-        acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
-    if (lane == 0)
-        wx[wave] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        sink[blockIdx.x] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
-}
-
-hipError_t launch_read_ceiling(const uint8_t *k, int64_t kstride, const float *ks, int64_t ks_stride, int64_t N,
-                               int pattern, int blocks, uint32_t *sink, hipStream_t stream)
-{
-    hipLaunchKernelGGL(idx_read_ceiling_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, kstride, ks,
-                       ks_stride, N, pattern, sink);
-    return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
 constexpr int IDX_STREAM_BLOCKS = 512;  // two blocks per CU: measured as good as or better than four
