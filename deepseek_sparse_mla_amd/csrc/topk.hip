@@ -785,7 +785,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
                                                                  TkWs ws)
 {
     __shared__ uint64_t cand[TK_CAP];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS + 4];  // + a spare slot (see step 4)
     __shared__ uint32_t wsum[TK_WAVES];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t sh_cnt;
@@ -1029,10 +1029,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
 #pragma unroll
         for (int q = 0; q < WPT; ++q) {
             uint32_t b = wv[q];
-            while (b) {
-                const int bit = __ffs(b) - 1;
-                if (slot < (uint32_t)TK_BINS)
-                    slots[slot] = (uint32_t)(32 * (w0 + q) + bit);
+            while (b) {  // slots past the k kept ones go to the spare entry: no branch
+                slots[min(slot, (uint32_t)TK_BINS)] = (uint32_t)(32 * (w0 + q) + __ffs(b) - 1);
                 ++slot;
                 b &= b - 1u;
             }
@@ -1046,9 +1044,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select_kernel(LayoutDev L, co
             uint32_t b = word(w);
             gbits[w] = 0u;  // left zero for the next call
             while (b) {
-                const int bit = __ffs(b) - 1;
-                if (slot < (uint32_t)TK_BINS)
-                    slots[slot] = (uint32_t)(32 * w + bit);
+                slots[min(slot, (uint32_t)TK_BINS)] = (uint32_t)(32 * w + __ffs(b) - 1);
                 ++slot;
                 b &= b - 1u;
             }
