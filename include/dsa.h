@@ -239,8 +239,9 @@ dsa_status dsa_index_scores(const dsa_layout *layout, int H_I, int D_I, dsa_dtyp
  *   workspace     device scratch of dsa_topk_workspace_size() bytes, needed
  *                 when max_ctx exceeds what one block holds (32768): a
  *                 score histogram per row and, for up to 512 long rows, each
- *                 row's bitmap of selected positions and its threshold-bin
- *                 candidates; may be NULL when the size is 0.  It must be
+ *                 row's bitmap of selected positions, its threshold-bin
+ *                 candidates and the threshold bin itself (handed from one
+ *                 kernel to the next); may be NULL when the size is 0.  It must be
  *                 zero-filled before its first use; every completed call leaves
  *                 all of it zero again, whatever the layout.  Calls that overlap
  *                 in time must not share it.
