@@ -49,8 +49,10 @@ constexpr int TK_BINS = 2048;         // 11-bit digits
 constexpr int TK_ROW_BITS = 1 << 18;  // longest row of the ROW mode (32 KB LDS bitmap)
 constexpr int TK_MB_ROWS = 512;       // up to this many rows, long rows use the MB mode
 constexpr int TD_MAX_PER = 32;        // longest DIRECT row: 1024 threads x 32 = 32768 scores
-constexpr int H_THREADS = 256;        // histogram and mark kernels
-constexpr int H_CHUNK = 8192;         // scores per histogram / mark block
+constexpr int H_THREADS = 256;        // histogram kernel
+constexpr int H_CHUNK = 8192;         // scores per histogram block
+constexpr int MK_THREADS = 512;       // mark kernel: 8 waves per block (256 threads and 8192
+constexpr int MK_CHUNK = 16384;       // scores per block measured 1.4 us slower on IndexShare)
 
 enum TkMode { TK_DIRECT = 0, TK_ROW = 1, TK_MB = 2 };
 
@@ -297,20 +299,20 @@ __global__ __launch_bounds__(H_THREADS) void topk_hist_kernel(LayoutDev L, const
 }
 
 // ------------------------------------------------------------------------------------------
-// K2 (MB mode): mark the bitmap words and collect the members of one 8192-score chunk
+// K2 (MB mode): mark the bitmap words and collect the members of one 16384-score chunk
 // ------------------------------------------------------------------------------------------
 template <bool AL16>  // every row 16-byte aligned (scores and ld): 16-byte loads
-__global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const float *__restrict__ scores,
+__global__ __launch_bounds__(MK_THREADS) void topk_mark_kernel(LayoutDev L, const float *__restrict__ scores,
                                                               int64_t ld, int k, TkWs ws)
 {
     __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
-    __shared__ uint64_t lmem[H_CHUNK];  // this chunk's members, before one reservation
+    __shared__ uint64_t lmem[MK_CHUNK];  // this chunk's members, before one reservation
     __shared__ uint32_t sh[4];
     __shared__ uint32_t lcnt, gbase;
     const int64_t i = blockIdx.y;
     const RowInfo r = row_info(L, i);
     const int64_t n = r.n > 0 ? r.n : 0;
-    const int64_t s0 = (int64_t)blockIdx.x * H_CHUNK;
+    const int64_t s0 = (int64_t)blockIdx.x * MK_CHUNK;
     if (s0 >= n)
         return;
     const uint32_t kk = (uint32_t)min((int64_t)k, n);
@@ -320,12 +322,12 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     // the row's histogram first, then this chunk's scores: waiting for the histogram (in
     // issue order) leaves the score loads in flight through the digit pick
     const uint32_t *gh = ws.hist + i * TK_BINS;
-    constexpr int HB = TK_BINS / H_THREADS;
+    constexpr int HB = TK_BINS / MK_THREADS;
     uint32_t hv[HB];
 #pragma unroll
     for (int e = 0; e < HB; ++e)
-        hv[e] = gh[e * H_THREADS + tid];
-    constexpr int U = H_CHUNK / (4 * H_THREADS);  // 8 wave steps of 256 positions
+        hv[e] = gh[e * MK_THREADS + tid];
+    constexpr int U = MK_CHUNK / (4 * MK_THREADS);  // 8 wave steps of 256 positions
     // unconditional buffer loads (zeros past n): the wait for the histogram above then leaves
     // every score load in flight through the digit pick
     const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(
@@ -334,13 +336,13 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     if constexpr (AL16) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int sp = (int)(s0 + (int64_t)u * 4 * H_THREADS) + 256 * wave + 4 * lane;
+            const int sp = (int)(s0 + (int64_t)u * 4 * MK_THREADS) + 256 * wave + 4 * lane;
             v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrow, 4 * sp, 0, 0));
         }
     } else {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int sp = (int)(s0 + (int64_t)u * 4 * H_THREADS) + 256 * wave + 4 * lane;
+            const int sp = (int)(s0 + (int64_t)u * 4 * MK_THREADS) + 256 * wave + 4 * lane;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 v[u][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrow, 4 * (sp + e), 0, 0));
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     }
 #pragma unroll
     for (int e = 0; e < HB; ++e)
-        hist[e * H_THREADS + tid] = hv[e];
+        hist[e * MK_THREADS + tid] = hv[e];
     if (tid == 0)
         lcnt = 0u;
     lds_sync();
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     uint32_t mflag = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t base = s0 + (int64_t)u * 4 * H_THREADS + 256 * wave;
+        const int64_t base = s0 + (int64_t)u * 4 * MK_THREADS + 256 * wave;
         take_wave(
             base, v[u], n, d, lane, [&](int64_t w, uint32_t word) { bits[w] = word; },
             [&](uint64_t, uint32_t, bool m, uint64_t) {},
@@ -397,13 +399,13 @@ __global__ __launch_bounds__(H_THREADS) void topk_mark_kernel(LayoutDev L, const
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if ((mflag >> (4 * u + e)) & 1u)  // at < H_CHUNK: one slot per position
-                lmem[at++] = composite(score_key(v[u][e]), s0 + (int64_t)u * 4 * H_THREADS + 256 * wave + 4 * lane + e);
+            if ((mflag >> (4 * u + e)) & 1u)  // at < MK_CHUNK: one slot per position
+                lmem[at++] = composite(score_key(v[u][e]), s0 + (int64_t)u * 4 * MK_THREADS + 256 * wave + 4 * lane + e);
     if (tid == 0)
         gbase = gb;
     __syncthreads();
     uint64_t *memb = ws.memb + i * TK_CAP;
-    for (uint32_t e = tid; e < m; e += H_THREADS) {
+    for (uint32_t e = tid; e < m; e += MK_THREADS) {
         const uint32_t at = gbase + e;
         if (at < (uint32_t)TK_CAP)
             memb[at] = lmem[e];
@@ -1074,10 +1076,11 @@ hipError_t launch_topk(const LayoutDev &L, int64_t T, int64_t max_ctx, const flo
             return e;
     }
     if (mode == TK_MB) {
+        const dim3 mgrid((unsigned)((max_ctx + MK_CHUNK - 1) / MK_CHUNK), (unsigned)T);
         if (((uintptr_t)scores & 15) == 0 && (ld & 3) == 0)
-            hipLaunchKernelGGL(topk_mark_kernel<true>, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, k, ws);
+            hipLaunchKernelGGL(topk_mark_kernel<true>, mgrid, dim3(MK_THREADS), 0, stream, L, scores, ld, k, ws);
         else
-            hipLaunchKernelGGL(topk_mark_kernel<false>, hgrid, dim3(H_THREADS), 0, stream, L, scores, ld, k, ws);
+            hipLaunchKernelGGL(topk_mark_kernel<false>, mgrid, dim3(MK_THREADS), 0, stream, L, scores, ld, k, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
