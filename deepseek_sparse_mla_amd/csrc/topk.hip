@@ -51,8 +51,8 @@ constexpr int TK_MB_ROWS = 512;       // up to this many rows, long rows use the
 constexpr int TD_MAX_PER = 32;        // longest DIRECT row: 1024 threads x 32 = 32768 scores
 constexpr int H_THREADS = 256;        // histogram kernel
 constexpr int H_CHUNK = 8192;         // scores per histogram block
-constexpr int MK_THREADS = 512;       // mark kernel: 8 waves per block (256 threads and 8192
-constexpr int MK_CHUNK = 16384;       // scores per block measured 1.4 us slower on IndexShare)
+constexpr int MK_THREADS = 1024;      // mark kernel: 16 waves per block (measured against
+constexpr int MK_CHUNK = 16384;       // 256 x 8192, 512 x 8192 and 512 x 16384: all slower)
 
 enum TkMode { TK_DIRECT = 0, TK_ROW = 1, TK_MB = 2 };
 
