@@ -38,16 +38,26 @@ __device__ __forceinline__ float relu(float x)
 // the 128 code bytes of token r at byte 132 r); the loads are still single 16-byte loads.
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
+// Contiguous tiles (unpaged 128-byte rows, 16-byte aligned): a wave reads its 32-token tile
+// as four 1 KB runs of consecutive bytes with nontemporal loads (lane l: token 8u + l / 8,
+// bytes 16 (l % 8) of run u), which streams faster than the lane layout of the MFMA, and
+// rearranges it through a wave-private LDS tile (rows of 144 bytes, so the eight lanes of a
+// 16-byte LDS access hit disjoint banks).
+constexpr int IDX_STAGE_ROWB = 144;
+constexpr int IDX_STAGE_BYTES = 32 * IDX_STAGE_ROWB;  // per wave
+
 // Tokens [s_begin, s_end) of query row i, whose keys start at cache row kv_base; with paged
 // caches (pages != nullptr) token s is instead in row pages[(s >> lg) - p0] << lg | (s & page-1),
-// the segment's block-table entries having been copied to LDS.
+// the segment's block-table entries having been copied to LDS.  CONTIG: the keys are read as
+// contiguous tiles and rearranged in the wave's LDS tile `stage`.
+template <bool CONTIG>
 __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ q, const float *__restrict__ w,
                                                    const uint8_t *__restrict__ k, int64_t kstride,
                                                    const float *__restrict__ ks, int64_t ks_stride,
                                                    float *__restrict__ scores, int64_t ld, int64_t i,
                                                    int64_t kv_base, int64_t s_begin, int64_t s_end,
                                                    const int32_t *pages = nullptr, int lg = 0, int64_t p0 = 0,
-                                                   uint32_t *wh = nullptr)
+                                                   uint32_t *wh = nullptr, char *stage = nullptr)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform loop bounds
@@ -67,6 +77,15 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
     // Double-buffered: the next tile's 64 key bytes per lane (and its scale) are requested
     // before the current tile's MFMAs, so every wave keeps a tile in flight.
     auto load_tile = [&](int64_t s0, u32x4 (&kv)[4], float &ksv) {
+        if constexpr (CONTIG) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t s = min(s0 + 8 * u + (lane >> 3), s_end - 1);
+                kv[u] = __builtin_nontemporal_load((const u32x4 *)(k + (kv_base + s) * 128 + 16 * (lane & 7)));
+            }
+            ksv = ks[(kv_base + min(s0 + j, s_end - 1)) * ks_stride];
+            return;
+        }
         const int64_t s = s0 + j;
         const int64_t sc = s < s_end ? s : s_end - 1;
         const int64_t row = pages ? ((int64_t)pages[(sc >> lg) - p0] << lg) | (sc & ((1 << lg) - 1))
@@ -78,7 +97,20 @@ __device__ __forceinline__ void idx_decode_segment(const uint16_t *__restrict__ 
         kv[3] = kp[3];
         ksv = ks[row * ks_stride];
     };
-    auto compute_tile = [&](const u32x4 (&kv)[4], float ksv) -> float {
+    auto compute_tile = [&](const u32x4 (&kin)[4], float ksv) -> float {
+        u32x4 kv[4];
+        if constexpr (CONTIG) {  // to the MFMA layout: lane (g, j) takes bytes 64 g .. +63 of token j
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *(u32x4 *)(stage + (8 * u + (lane >> 3)) * IDX_STAGE_ROWB + 16 * (lane & 7)) = kin[u];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kv[c] = *(const u32x4 *)(stage + j * IDX_STAGE_ROWB + 64 * g + 16 * c);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kv[c] = kin[c];
+        }
         f32x16 acc = {};
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp8x8_to_bf16x8(kv[0][0], kv[0][1]), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp8x8_to_bf16x8(kv[0][2], kv[0][3]), acc, 0, 0, 0);
@@ -176,7 +208,7 @@ __device__ __forceinline__ void idx_hist_flush(uint32_t *lh, uint32_t *__restric
     __syncthreads();
 }
 
-template <bool PAGED, bool HIST>
+template <bool PAGED, bool HIST, bool CONTIG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void idx_decode_kernel(LayoutDev L, const uint16_t *__restrict__ q,
                                                          const float *__restrict__ w,
                                                          const uint8_t *__restrict__ k, int64_t kstride,
@@ -184,10 +216,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                                                          float *__restrict__ scores, int64_t ld, int chunk,
                                                          int stream, uint32_t *__restrict__ hist)
 {
-    // dynamic LDS: with HIST the four waves' histograms, then (paged) a segment's table entries
+    // dynamic LDS: with HIST the four waves' histograms, then (paged) a segment's table
+    // entries or (CONTIG) the four waves' staging tiles
+    static_assert(!(PAGED && CONTIG), "paged rows are not contiguous tiles");
     extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];
     uint32_t *lh = s_dyn;
     int32_t *s_pages = (int32_t *)(s_dyn + (HIST ? 4 * SCORE_BINS : 0));
+    char *stage = CONTIG ? (char *)s_pages + IDX_STAGE_BYTES * (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)
+                         : nullptr;
     uint32_t *wh = HIST ? lh + SCORE_BINS * (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : nullptr;
     if (HIST) {
         for (int b = threadIdx.x; b < 4 * SCORE_BINS; b += 256)
@@ -203,8 +239,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             return;
         const int64_t s_end = min(s_begin + (int64_t)chunk, r.n);
         if (!PAGED) {
-            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin, s_end,
-                               nullptr, 0, 0, wh);
+            idx_decode_segment<CONTIG>(q, w, k, kstride, ks, ks_stride, scores, ld, i, r.kv_base, s_begin, s_end,
+                                       nullptr, 0, 0, wh, stage);
             idx_hist_flush<HIST>(lh, hist, i);
             return;
         }
@@ -213,7 +249,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
             s_pages[p - p0] = L.block_table[(int64_t)r.b * L.bt_stride + p];
         __syncthreads();
-        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, i, 0, s_begin, s_end, s_pages, lg, p0, wh);
+        idx_decode_segment<false>(q, w, k, kstride, ks, ks_stride, scores, ld, i, 0, s_begin, s_end, s_pages, lg, p0,
+                                  wh);
         idx_hist_flush<HIST>(lh, hist, i);
         return;
     }
@@ -241,8 +278,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         if (se <= sb)
             continue;
         if (!PAGED) {
-            idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, rb, sb - rb, se - rb,
-                               nullptr, 0, 0, wh);
+            idx_decode_segment<CONTIG>(q, w, k, kstride, ks, ks_stride, scores, ld, b, rb, sb - rb, se - rb,
+                                       nullptr, 0, 0, wh, stage);
             idx_hist_flush<HIST>(lh, hist, b);
             continue;
         }
@@ -253,7 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         for (int64_t p = p0 + threadIdx.x; p <= p1; p += 256)
             s_pages[p - p0] = L.block_table[(int64_t)b * L.bt_stride + p];
         __syncthreads();
-        idx_decode_segment(q, w, k, kstride, ks, ks_stride, scores, ld, b, 0, s0, s1, s_pages, lg, p0, wh);
+        idx_decode_segment<false>(q, w, k, kstride, ks, ks_stride, scores, ld, b, 0, s0, s1, s_pages, lg, p0, wh);
         idx_hist_flush<HIST>(lh, hist, b);
     }
 }
@@ -580,20 +617,32 @@ hipError_t launch_index_decode(const LayoutDev &L, int64_t T, int64_t max_ctx, c
     const int st = as_stream ? 1 : 0;
     const uint16_t *qh = (const uint16_t *)q;
     const uint8_t *kk = (const uint8_t *)k;
-    if (hist) {
+    // unpaged 128-byte rows at a 16-byte aligned base: contiguous tiles
+    const bool contig = !L.block_table && kstride == 128 && ((uintptr_t)k & 15) == 0;
+    if (hist)
         lds += IDX_HIST_LDS;
-        if (L.block_table)
-            hipLaunchKernelGGL((idx_decode_kernel<true, true>), grid, dim3(256), lds, stream, L, qh, w, kk, kstride, ks,
-                               ks_stride, scores, ld, chunk, st, hist);
+    if (contig)
+        lds += 4 * IDX_STAGE_BYTES;
+#define DSA_IDX_DECODE(P, H, C)                                                                                  \
+    hipLaunchKernelGGL((idx_decode_kernel<P, H, C>), grid, dim3(256), lds, stream, L, qh, w, kk, kstride, ks, ks_stride, \
+                       scores, ld, chunk, st, hist)
+    if (L.block_table) {
+        if (hist)
+            DSA_IDX_DECODE(true, true, false);
         else
-            hipLaunchKernelGGL((idx_decode_kernel<false, true>), grid, dim3(256), lds, stream, L, qh, w, kk, kstride, ks,
-                               ks_stride, scores, ld, chunk, st, hist);
-    } else if (L.block_table)
-        hipLaunchKernelGGL((idx_decode_kernel<true, false>), grid, dim3(256), lds, stream, L, qh, w, kk, kstride, ks,
-                           ks_stride, scores, ld, chunk, st, nullptr);
-    else
-        hipLaunchKernelGGL((idx_decode_kernel<false, false>), grid, dim3(256), 0, stream, L, qh, w, kk, kstride, ks,
-                           ks_stride, scores, ld, chunk, st, nullptr);
+            DSA_IDX_DECODE(true, false, false);
+    } else if (contig) {
+        if (hist)
+            DSA_IDX_DECODE(false, true, true);
+        else
+            DSA_IDX_DECODE(false, false, true);
+    } else {
+        if (hist)
+            DSA_IDX_DECODE(false, true, false);
+        else
+            DSA_IDX_DECODE(false, false, false);
+    }
+#undef DSA_IDX_DECODE
     return hipGetLastError();
 }
 
