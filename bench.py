@@ -440,7 +440,9 @@ def read_ceiling(workload, steps, warmup):
     """The decode indexer's load stream with no arithmetic and no stores (dsa_read_ceiling, the
     same shares, tiles and lanes), on the workload's own index cache, timed beside the indexer
     stage (plain call): 132 bytes read per token either way.  Pattern 0 keeps the indexer's
-    lanes, pattern 1 reads 1 KB of consecutive bytes per load instruction."""
+    lanes for rows it cannot read as contiguous tiles, pattern 1 reads 1 KB of consecutive bytes
+    per load instruction, pattern 2 does so with nontemporal loads: the indexer's own stream on
+    these key planes."""
     import torch
     from deepseek_sparse_mla_amd import synth
     if workload not in ("share", "ragged", "decode"):
@@ -453,7 +455,7 @@ def read_ceiling(workload, steps, warmup):
     sink = torch.zeros(512, dtype=torch.int32, device="cuda:0")
     rb = n * 132
     out = {"workload": case.name, "tokens": n, "bytes_read": rb}
-    for pattern in (0, 1):
+    for pattern in (0, 1, 2):
         t = _timed(lambda: run.dsa.dsa_read_ceiling(case.ik, case.ik_scale, sink, n, pattern), steps, warmup)
         out["pattern%d_ms" % pattern] = t
         out["pattern%d_GBps" % pattern] = round(rb / (t["median"] * 1e-3) / 1e9, 1)
@@ -461,6 +463,7 @@ def read_ceiling(workload, steps, warmup):
     out["indexer_ms"] = t
     out["indexer_GBps_read"] = round(rb / (t["median"] * 1e-3) / 1e9, 1)
     out["indexer_over_pattern0"] = round(t["median"] / out["pattern0_ms"]["median"], 3)
+    out["indexer_over_pattern2"] = round(t["median"] / out["pattern2_ms"]["median"], 3)
     out.update({"steps": steps, "warmup": warmup})
     print(json.dumps(out))
 

@@ -655,12 +655,13 @@ dsa_status dsa_read_ceiling(const void *k, int64_t k_row_stride, const float *k_
         return fail(DSA_ERR_INVALID_ARG, "k, k_scale and sink must not be NULL");
     if (n_tokens < 1 || blocks < 1 || blocks > 65536)
         return fail(DSA_ERR_INVALID_ARG, "need n_tokens >= 1 and 1 <= blocks <= 65536");
-    if (pattern != 0 && pattern != 1)
-        return fail(DSA_ERR_INVALID_ARG, "pattern must be 0 (the indexer's lanes) or 1 (1 KB per load)");
+    if (pattern < 0 || pattern > 2)
+        return fail(DSA_ERR_INVALID_ARG,
+                    "pattern must be 0 (the indexer's lanes), 1 (1 KB per load) or 2 (1 KB per nontemporal load)");
     if (k_row_stride < 128 || k_row_stride % 4 != 0 || !aligned(k, 4) || !aligned(k_scale, 4) || k_scale_stride < 1)
         return fail(DSA_ERR_INVALID_ARG, "key rows of >= 128 bytes, 4-byte aligned, and a scale stride >= 1");
-    if (pattern == 1 && (k_row_stride != 128 || !aligned(k, 16)))
-        return fail(DSA_ERR_INVALID_ARG, "pattern 1 reads a 16-byte aligned plane of 128-byte rows");
+    if (pattern != 0 && (k_row_stride != 128 || !aligned(k, 16)))
+        return fail(DSA_ERR_INVALID_ARG, "patterns 1 and 2 read a 16-byte aligned plane of 128-byte rows");
     return hip_status(dsa::launch_read_ceiling((const uint8_t *)k, k_row_stride, k_scale, k_scale_stride, n_tokens,
                                                pattern, blocks, sink, (hipStream_t)stream),
                       "read ceiling launch");

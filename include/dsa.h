@@ -431,9 +431,12 @@ dsa_status dsa_gather_ceiling(const void *rows, int64_t n_rows, int row_bytes, c
  *                     aligned); the first 128 bytes of rows 0 .. n_tokens-1
  *                     are read
  *   k_scale, k_scale_stride  the rows' fp32 scales (k_scale[r * stride])
- *   pattern   0: the indexer's lanes (each 16-byte load of a wave touches 32
- *             rows); 1: each load reads 1 KB of consecutive bytes (needs
- *             k_row_stride = 128 and k 16-byte aligned)
+ *   pattern   0: the indexer's lanes for rows it cannot read as contiguous
+ *             tiles (each 16-byte load of a wave touches 32 rows); 1: each
+ *             load reads 1 KB of consecutive bytes; 2: as 1 with nontemporal
+ *             loads, the indexer's stream for a 16-byte aligned plane of
+ *             128-byte rows (1 and 2 need k_row_stride = 128 and k 16-byte
+ *             aligned)
  *   blocks    the grid (the indexer streams with 512 blocks on MI355X)
  *   sink      device uint32 [blocks]: block b stores in sink[b] the xor of
  *             every word it read (so the xor of all entries is that of the

@@ -332,11 +332,13 @@ def test_read_ceiling_rejects(lib):
     assert r(FAKE, 128, FAKE, 1, 100, 0, 512, None, None) == B.DSA_ERR_INVALID_ARG     # no sink
     assert r(FAKE, 128, FAKE, 1, 0, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG       # no tokens
     assert r(FAKE, 128, FAKE, 1, 100, 0, 0, FAKE, None) == B.DSA_ERR_INVALID_ARG       # no blocks
-    assert r(FAKE, 128, FAKE, 1, 100, 2, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # unknown pattern
+    assert r(FAKE, 128, FAKE, 1, 100, 3, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # unknown pattern
+    assert r(FAKE, 128, FAKE, 1, 100, -1, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG
     assert r(FAKE, 126, FAKE, 1, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # short / unaligned rows
     assert r(FAKE, 130, FAKE, 1, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG
     assert r(FAKE, 128, FAKE, 0, 100, 0, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG     # scale stride
-    assert r(FAKE, 132, FAKE, 33, 100, 1, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG    # pattern 1: 128-byte rows
+    assert r(FAKE, 132, FAKE, 33, 100, 1, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG    # patterns 1, 2: 128-byte rows
+    assert r(FAKE, 132, FAKE, 33, 100, 2, 512, FAKE, None) == B.DSA_ERR_INVALID_ARG
 
 
 def test_index_topk_checks_both_calls_before_launching(lib):

@@ -1,5 +1,5 @@
 """The two measurement aids on the GPU: the indexer's load stream (dsa_read_ceiling) reads every
-key row and scale of the index cache exactly once, for both load patterns, on key planes and on
+key row and scale of the index cache exactly once, for each load pattern, on key planes and on
 132-byte entries; bench.py --read-ceiling prints its line."""
 import json
 import os
@@ -23,7 +23,7 @@ def _xor(words: np.ndarray) -> int:
 
 
 @pytest.mark.parametrize("n,blocks", [(1, 512), (70001, 512), (70001, 7), (4096, 3)])
-@pytest.mark.parametrize("pattern", [0, 1])
+@pytest.mark.parametrize("pattern", [0, 1, 2])
 def test_read_ceiling_reads_every_row_once(n, blocks, pattern):
     g = torch.Generator(device=DEV).manual_seed(n + blocks)
     keys = torch.randint(0, 256, (n + 40, 128), generator=g, device=DEV, dtype=torch.uint8)
@@ -55,5 +55,5 @@ def test_bench_read_ceiling_line():
     assert r.returncode == 0, r.stderr[-2000:]
     d = json.loads([l for l in r.stdout.splitlines() if l.startswith("{")][-1])
     assert d["tokens"] == 8 * 8192 and d["bytes_read"] == 8 * 8192 * 132
-    for key in ("pattern0_GBps", "pattern1_GBps", "indexer_GBps_read"):
+    for key in ("pattern0_GBps", "pattern1_GBps", "pattern2_GBps", "indexer_GBps_read"):
         assert d[key] > 0
